@@ -1,0 +1,410 @@
+"""Plain CPU oracle for the TurboQuant hot path (NumPy/SciPy, float64).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests under ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, tables
+or constants with the HIP library; both sides are written independently from
+the pages and from the published definitions named below.
+
+Sources (pages are cited by title and section; short names used below):
+
+  [ttakun]  "KV缓存52GB瞬间爆内存？TurboQuant随机旋转+标量量化如何把LLM长上下文推理
+            成本砍到1/16且失真逼近理论极限" (ttakun.com), sections
+            "为什么随机旋转是整个算法的底层杠杆" (rotation, coordinate law,
+            Lloyd–Max, 2.7x claim) and "TurboQuant_mse vs TurboQuant_prod"
+            (normalise / rotate / per-coordinate codebook / inverse rotate;
+            (b-1)-bit mse stage + 1-bit QJL residual stage; 36% claim).
+  [tmdm]    "谷歌悄悄扔下一颗'性能核弹'" (tmdm.cn), section "双剑合璧：PolarQuant + QJL"
+            (QJL: JL projection, 1-bit sign, unbiased inner-product estimator).
+  [admirer] admirer.cn TurboQuant article, section "第二步：1 bit 算力带来的「神級校準」"
+            (residual reduced to sign bits; high-precision query balanced
+            against them; unbiased inner product).
+  [tqnet]   "TurboQuant 最近的进展和外溢影响" (turboquant.net/zh), section
+            "TurboQuant 两阶段算法 › 坐标分布公式" (density f_d) and section
+            "实现步骤草图" (Lloyd–Max centroids for the Beta law; Pi from QR of a
+            Gaussian matrix; quant y = Pi x, nearest centroid; dequant
+            x = Pi^T c[idx]); section "工程风险与应对" (pre-generate and reuse
+            Pi; one extra scalar for the residual norm).
+
+Readings where the pages are silent (each is listed in the design doc):
+  * QJL scale sqrt(pi/2)/m * gamma; m = d projections; sign(0) = +1.
+  * QR sign convention diag(R) > 0; forward map Pi, inverse Pi^T.
+  * ties at a boundary go to the lower index (strict t_k < y).
+  * centroids and boundaries computed in float64, rounded to float32 for
+    storage; boundaries are midpoints of the float64 centroids.
+  * zero input vector: norm 0, y = 0, gamma = 0, all signs +1.
+  * residual norm kept in float32 (pages mention a float16 scalar).
+  * random numbers: the counter-based SplitMix64 finaliser (Steele, Lea and
+    Flood, "Fast splittable pseudorandom number generators", OOPSLA 2014)
+    keyed by (seed, group, matrix, element), fed to the Box–Muller transform
+    (Box and Muller, 1958).
+  * packed layout: LSB-first contiguous fields, rows zero-padded to 16 bytes.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+from scipy import special
+
+# ---------------------------------------------------------------------------
+# Counter-based Gaussian generator (the one random source of the method).
+# ---------------------------------------------------------------------------
+_M64 = np.uint64(0xFFFFFFFFFFFFFFFF)
+_MIX_A = np.uint64(0xBF58476D1CE4E5B9)
+_MIX_B = np.uint64(0x94D049BB133111EB)
+MAT_PI = 0
+MAT_S = 1
+
+
+def mix64(z):
+    """SplitMix64 output finaliser: xor-shift 30, multiply, xor-shift 27,
+    multiply, xor-shift 31 (Steele, Lea, Flood 2014).  Works on uint64 arrays
+    with wrap-around multiplication."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * _MIX_A
+        z = (z ^ (z >> np.uint64(27))) * _MIX_B
+    return z ^ (z >> np.uint64(31))
+
+
+def gaussian_stream(seed: int, group, mat: int, elems) -> np.ndarray:
+    """Standard normal value number ``elems`` of stream (seed, group, mat).
+
+    key  = mix64(seed) xor ((16*group + mat) << 32)
+    h_t  = mix64(key xor (2*elem + t)),  t in {0, 1}
+    u1   = ((h_0 >> 11) + 1) * 2^-53   in (0, 1]
+    u2   =  (h_1 >> 11)      * 2^-53   in [0, 1)
+    z    = sqrt(-2 ln u1) * cos(2 pi u2)        (Box–Muller)
+    ``group`` and ``elems`` broadcast against each other.
+    """
+    seed_mixed = mix64(np.uint64(seed & 0xFFFFFFFFFFFFFFFF))
+    group = np.asarray(group, dtype=np.uint64)
+    elems = np.asarray(elems, dtype=np.uint64)
+    key = seed_mixed ^ ((np.uint64(16) * group + np.uint64(mat)) << np.uint64(32))
+    two_e = np.uint64(2) * elems
+    h0 = mix64(key ^ two_e)
+    h1 = mix64(key ^ (two_e + np.uint64(1)))
+    u1 = ((h0 >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53
+    u2 = (h1 >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    return np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
+
+
+def gaussian_matrix(seed: int, group: int, mat: int, rows: int, cols: int) -> np.ndarray:
+    """rows x cols matrix, entry (i, j) = element i*cols + j of the stream."""
+    e = np.arange(rows * cols, dtype=np.uint64)
+    return gaussian_stream(seed, group, mat, e).reshape(rows, cols)
+
+
+# ---------------------------------------------------------------------------
+# Random rotation Pi and QJL matrix S.
+# ---------------------------------------------------------------------------
+def rotation(d: int, seed: int, group: int = 0) -> np.ndarray:
+    """Pi = Q of the QR factorisation of a seeded d x d Gaussian matrix
+    ([tqnet] 实现步骤草图, "生成随机旋转矩阵"; [ttakun] rotation by QR of a random
+    Gaussian matrix).  Columns of Q are flipped so that diag(R) > 0, which
+    makes Pi unique for a given G and Haar distributed."""
+    g = gaussian_matrix(seed, group, MAT_PI, d, d)
+    q, r = np.linalg.qr(g)
+    s = np.where(np.diag(r) < 0.0, -1.0, 1.0)
+    return q * s[None, :]
+
+
+def qjl_matrix(d: int, seed: int, group: int = 0) -> np.ndarray:
+    """S: m x d iid N(0,1) JL projection with m = d ([tmdm] QJL; [admirer] 第二步)."""
+    return gaussian_matrix(seed, group, MAT_S, d, d)
+
+
+# ---------------------------------------------------------------------------
+# Post-rotation coordinate law and its Lloyd–Max quantizer.
+# ---------------------------------------------------------------------------
+def _log_norm_const(d: int) -> float:
+    # log of Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2))
+    return special.gammaln(d / 2.0) - special.gammaln((d - 1) / 2.0) - 0.5 * math.log(math.pi)
+
+
+def coord_density(x, d: int):
+    """f_d(x) = Gamma(d/2)/(sqrt(pi) Gamma((d-1)/2)) (1-x^2)^((d-3)/2) on [-1, 1]
+    ([tqnet] 两阶段算法 › 坐标分布公式)."""
+    x = np.asarray(x, dtype=np.float64)
+    inside = np.abs(x) < 1.0
+    out = np.zeros_like(x)
+    xi = x[inside]
+    out[inside] = np.exp(_log_norm_const(d) + 0.5 * (d - 3) * np.log1p(-xi * xi))
+    return out
+
+
+def coord_cdf(x, d: int):
+    """F_d(x) = 1/2 + sgn(x)/2 * I_{x^2}(1/2, (d-1)/2): substitute s = x^2 in the
+    integral of f_d (the half-integral is a regularised incomplete beta)."""
+    x = np.clip(np.asarray(x, dtype=np.float64), -1.0, 1.0)
+    return 0.5 + 0.5 * np.sign(x) * special.betainc(0.5, (d - 1) / 2.0, x * x)
+
+
+def cell_first_moment(a, b, d: int):
+    """Integral of x f_d(x) over [a, b]:
+    C/(d-1) [(1-a^2)^((d-1)/2) - (1-b^2)^((d-1)/2)], since the derivative of
+    (1-x^2)^((d-1)/2) is -(d-1) x (1-x^2)^((d-3)/2)."""
+    a = np.clip(np.asarray(a, dtype=np.float64), -1.0, 1.0)
+    b = np.clip(np.asarray(b, dtype=np.float64), -1.0, 1.0)
+    lc = _log_norm_const(d) - math.log(d - 1)
+
+    def power(x):
+        inside = np.abs(x) < 1.0
+        safe = np.where(inside, x, 0.0)
+        return np.where(inside, np.exp(lc + 0.5 * (d - 1) * np.log1p(-safe * safe)), 0.0)
+
+    pa, pb = power(a), power(b)
+    return pa - pb
+
+
+@dataclass
+class LloydMax:
+    d: int
+    bits: int
+    centroids: np.ndarray      # float64, ascending, length 2^bits
+    boundaries: np.ndarray     # float64, length 2^bits - 1 (midpoints)
+    distortion: float          # d * E[(X - Q(X))^2] for X ~ f_d  (= mse of a unit vector)
+    iterations: int
+
+
+def lloyd_max(d: int, bits: int, max_iter: int = 100000) -> LloydMax:
+    """Lloyd–Max scalar quantizer for f_d with L = 2^bits levels ([ttakun]
+    "用Lloyd-Max算法预计算的最优标量量化器"; [tqnet] 预计算 Lloyd-Max 质心).
+
+    Alternates the two optimality conditions: boundaries at the midpoints of
+    neighbouring centroids, centroids at the conditional means of their cells.
+    Starts from Gaussian quantiles scaled by 1/sqrt(d) (f_d approaches
+    N(0, 1/d)); keeps the codebook symmetric; stops when the largest centroid
+    move is below 1e-12/sqrt(d)."""
+    if d < 3:
+        raise ValueError("the coordinate law needs d >= 3")
+    L = 1 << bits
+    p = (np.arange(L) + 0.5) / L
+    c = special.ndtri(p) / math.sqrt(d)
+    tol = 1e-12 / math.sqrt(d)
+    it = 0
+    for it in range(1, max_iter + 1):
+        t = 0.5 * (c[:-1] + c[1:])
+        edges = np.concatenate(([-1.0], t, [1.0]))
+        mass = coord_cdf(edges[1:], d) - coord_cdf(edges[:-1], d)
+        m1 = cell_first_moment(edges[:-1], edges[1:], d)
+        new = m1 / mass
+        new = 0.5 * (new - new[::-1])          # exact symmetry of f_d
+        step = np.max(np.abs(new - c))
+        c = new
+        if step < tol:
+            break
+    t = 0.5 * (c[:-1] + c[1:])
+    edges = np.concatenate(([-1.0], t, [1.0]))
+    mass = coord_cdf(edges[1:], d) - coord_cdf(edges[:-1], d)
+    dist = 1.0 - d * float(np.sum(c * c * mass))
+    return LloydMax(d, bits, c, t, dist, it)
+
+
+# ---------------------------------------------------------------------------
+# Codec tables.
+# ---------------------------------------------------------------------------
+MSE = 0
+PROD = 1
+
+
+@dataclass
+class Codec:
+    d: int
+    bits: int                  # total bits per coordinate (b)
+    variant: int               # MSE or PROD
+    seed: int
+    groups: int
+    mse_bits: int              # b for mse, b-1 for prod
+    pis: list = field(default_factory=list)       # float64 Pi per group
+    ss: list = field(default_factory=list)        # float64 S per group (prod)
+    centroids64: np.ndarray | None = None
+    boundaries64: np.ndarray | None = None
+    centroids: np.ndarray | None = None           # float32 values (as float64)
+    boundaries: np.ndarray | None = None          # float32 values (as float64)
+    distortion: float = 0.0
+
+    @property
+    def m(self) -> int:
+        return self.d
+
+
+def make_codec(d: int, bits: int, variant: int, seed: int, groups: int = 1) -> Codec:
+    mse_bits = bits if variant == MSE else bits - 1
+    cd = Codec(d, bits, variant, seed, groups, mse_bits)
+    for g in range(groups):
+        cd.pis.append(rotation(d, seed, g))
+        if variant == PROD:
+            cd.ss.append(qjl_matrix(d, seed, g))
+    if mse_bits > 0:
+        lm = lloyd_max(d, mse_bits)
+        cd.centroids64 = lm.centroids
+        cd.boundaries64 = lm.boundaries
+        cd.centroids = lm.centroids.astype(np.float32).astype(np.float64)
+        cd.boundaries = lm.boundaries.astype(np.float32).astype(np.float64)
+        cd.distortion = lm.distortion
+    return cd
+
+
+# ---------------------------------------------------------------------------
+# Bit packing: LSB-first contiguous fields, rows padded to 16 bytes.
+# ---------------------------------------------------------------------------
+def row_bytes(count: int, bits: int) -> int:
+    raw = (count * bits + 7) // 8
+    return (raw + 15) // 16 * 16
+
+
+def pack(idx: np.ndarray, bits: int, rbytes: int | None = None) -> np.ndarray:
+    """idx[..., count] with values < 2^bits -> uint8[..., rbytes].  Field j
+    occupies stream bits [j*bits, j*bits+bits); stream bit k is bit k%8 of
+    byte k//8.  Padding bits are zero."""
+    idx = np.asarray(idx, dtype=np.int64)
+    count = idx.shape[-1]
+    if rbytes is None:
+        rbytes = row_bytes(count, bits)
+    lead = idx.shape[:-1]
+    stream = np.zeros(lead + (rbytes * 8,), dtype=np.uint8)
+    for k in range(bits):
+        stream[..., np.arange(count) * bits + k] = (idx >> k) & 1
+    stream = stream.reshape(lead + (rbytes, 8))
+    weights = (1 << np.arange(8)).astype(np.int64)
+    return (stream.astype(np.int64) * weights).sum(axis=-1).astype(np.uint8)
+
+
+def unpack(packed: np.ndarray, bits: int, count: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    lead = packed.shape[:-1]
+    stream = (packed[..., :, None] >> np.arange(8, dtype=np.uint8)) & 1
+    stream = stream.reshape(lead + (-1,)).astype(np.int64)
+    out = np.zeros(lead + (count,), dtype=np.int64)
+    for k in range(bits):
+        out |= stream[..., np.arange(count) * bits + k] << k
+    return out
+
+
+# ---------------------------------------------------------------------------
+# TurboQuant_mse and TurboQuant_prod.
+# ---------------------------------------------------------------------------
+QJL_SCALE = math.sqrt(math.pi / 2.0)
+
+
+def _normalise(x: np.ndarray):
+    x = np.asarray(x, dtype=np.float64)
+    nu = np.sqrt(np.sum(x * x, axis=-1))
+    safe = np.where(nu > 0.0, nu, 1.0)
+    u = np.where(nu[..., None] > 0.0, x / safe[..., None], 0.0)
+    return nu, u
+
+
+def rotate(cd: Codec, u: np.ndarray, group: int = 0) -> np.ndarray:
+    """y = Pi u for each row of u ([tqnet] quant: y = Pi @ x)."""
+    return u @ cd.pis[group].T
+
+
+def nearest_index(cd: Codec, y: np.ndarray) -> np.ndarray:
+    """idx = #{k : t_k < y} -- the nearest centroid, ties to the lower index
+    ([tqnet] find_nearest; [ttakun] independent branch-free scalar lookup)."""
+    t = cd.boundaries
+    return np.searchsorted(t, y, side="left").astype(np.int64)
+
+
+def quantize_mse(cd: Codec, x: np.ndarray, group: int = 0):
+    """Store ||x|| (float32), normalise, rotate, per-coordinate nearest centroid
+    ([ttakun] TurboQuant_mse steps).  Returns (idx int64[n,d], norms float64[n],
+    y float64[n,d] the rotated unit-vector coordinates)."""
+    nu, u = _normalise(x)
+    y = rotate(cd, u, group)
+    return nearest_index(cd, y), nu, y
+
+
+def dequantize_rotated(cd: Codec, idx: np.ndarray) -> np.ndarray:
+    """c[idx]: the reconstruction in the rotated domain (centroid gather)."""
+    return cd.centroids[np.asarray(idx)]
+
+
+def dequantize_mse(cd: Codec, idx: np.ndarray, norms: np.ndarray, group: int = 0) -> np.ndarray:
+    """x_hat = ||x|| Pi^T c[idx] ([ttakun] inverse rotation and rescale;
+    [tqnet] dequant: x = Pi.T @ centroids[idx])."""
+    y = dequantize_rotated(cd, idx)
+    return np.asarray(norms, dtype=np.float64)[..., None] * (y @ cd.pis[group])
+
+
+def quantize_prod(cd: Codec, x: np.ndarray, group: int = 0):
+    """TurboQuant_prod ([ttakun]; [admirer] 第一步/第二步): (b-1)-bit mse code
+    of the unit vector u, residual r = u - Pi^T c[idx], gamma = ||r||,
+    z = sign(S r) with sign(0) = +1.  b = 1 has no mse stage (r = u).
+    Returns dict(idx, signs (+1/-1 int8), norms, rnorms, proj = S r)."""
+    nu, u = _normalise(x)
+    S = cd.ss[group]
+    if cd.mse_bits > 0:
+        y = rotate(cd, u, group)
+        idx = nearest_index(cd, y)
+        u_hat = cd.centroids[idx] @ cd.pis[group]
+    else:
+        y = None
+        idx = None
+        u_hat = np.zeros_like(u)
+    r = u - u_hat
+    gamma = np.sqrt(np.sum(r * r, axis=-1))
+    proj = r @ S.T
+    zero = nu == 0.0
+    gamma = np.where(zero, 0.0, gamma)
+    proj = np.where(zero[..., None], 0.0, proj)
+    signs = np.where(proj >= 0.0, 1, -1).astype(np.int8)
+    return dict(idx=idx, signs=signs, norms=nu, rnorms=gamma, proj=proj, y=y)
+
+
+def dequantize_prod(cd: Codec, idx, signs, norms, rnorms, group: int = 0) -> np.ndarray:
+    """x_tilde = ||x|| (Pi^T c[idx] + sqrt(pi/2)/m * gamma * S^T z): the QJL
+    reconstruction whose inner product with any fixed vector is unbiased."""
+    signs = np.asarray(signs, dtype=np.float64)
+    nu = np.asarray(norms, dtype=np.float64)
+    gamma = np.asarray(rnorms, dtype=np.float64)
+    if cd.mse_bits > 0:
+        u_hat = cd.centroids[np.asarray(idx)] @ cd.pis[group]
+    else:
+        u_hat = np.zeros(signs.shape[:-1] + (cd.d,))
+    qjl = (QJL_SCALE / cd.m) * gamma[..., None] * (signs @ cd.ss[group])
+    return nu[..., None] * (u_hat + qjl)
+
+
+def signs_to_bits(signs: np.ndarray) -> np.ndarray:
+    """+1 -> bit 1, -1 -> bit 0."""
+    return (np.asarray(signs) > 0).astype(np.int64)
+
+
+def bits_to_signs(bits: np.ndarray) -> np.ndarray:
+    return np.where(np.asarray(bits) > 0, 1, -1).astype(np.int8)
+
+
+# ---------------------------------------------------------------------------
+# Attention logits / inner products scored against quantized keys.
+# ---------------------------------------------------------------------------
+def logits_plain(cd: Codec, q: np.ndarray, keys: dict, group: int = 0) -> np.ndarray:
+    """<q, k_hat> for every (query, key): dequantize each key, then dot
+    (the plain definition).  q: [nq, d]; returns [nq, n_keys]."""
+    if cd.variant == MSE:
+        kh = dequantize_mse(cd, keys["idx"], keys["norms"], group)
+    else:
+        kh = dequantize_prod(cd, keys.get("idx"), keys["signs"], keys["norms"], keys["rnorms"], group)
+    return np.asarray(q, dtype=np.float64) @ kh.T
+
+
+def logits_fast(cd: Codec, q: np.ndarray, keys: dict, group: int = 0) -> np.ndarray:
+    """The same quantity evaluated in the rotated/projected domain:
+    <q, Pi^T c> = <Pi q, c> and <q, S^T z> = <S q, z> ([admirer] 第二步: the
+    full-precision query is balanced against the low-precision codes).  Used
+    for timing at full size; equal to logits_plain up to rounding."""
+    q = np.asarray(q, dtype=np.float64)
+    nu = np.asarray(keys["norms"], dtype=np.float64)
+    out = np.zeros((q.shape[0], nu.shape[0]))
+    if cd.mse_bits > 0:
+        qt = q @ cd.pis[group].T
+        out += qt @ cd.centroids[np.asarray(keys["idx"])].T
+    if cd.variant == PROD:
+        p = q @ cd.ss[group].T
+        z = np.asarray(keys["signs"], dtype=np.float64)
+        out += (QJL_SCALE / cd.m) * (p @ z.T) * np.asarray(keys["rnorms"], dtype=np.float64)[None, :]
+    return out * nu[None, :]

@@ -1,0 +1,135 @@
+"""Pins for the coordinate law and its Lloyd–Max codebook (CPU only)."""
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, special
+
+from oracle import tq_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _quad(f, a, b):
+    v, _ = integrate.quad(f, a, b, limit=400, epsabs=1e-14, epsrel=1e-12)
+    return v
+
+
+def _dens(d):
+    return lambda x: float(O.coord_density(np.array([x]), d)[0])
+
+
+@pytest.mark.parametrize("d", [3, 4, 16, 128, 200, 1536])
+def test_density_normalised_and_unit_second_moment(d):
+    f = _dens(d)
+    s = 4.0 / math.sqrt(d) if d > 50 else 1.0
+    pts = [-s, 0.0, s]
+    mass = integrate.quad(f, -1, 1, points=pts, limit=400)[0]
+    m2 = integrate.quad(lambda x: x * x * f(x), -1, 1, points=pts, limit=400)[0]
+    assert mass == pytest.approx(1.0, abs=1e-9)
+    assert d * m2 == pytest.approx(1.0, abs=1e-8)
+
+
+@pytest.mark.parametrize("d", [5, 128, 1536])
+def test_cdf_and_first_moment_match_quadrature(d):
+    f = _dens(d)
+    for a, b in [(-0.05, 0.02), (0.01, 0.09), (0.1, 0.3), (-1.0, -0.02)]:
+        assert O.coord_cdf(b, d) - O.coord_cdf(a, d) == pytest.approx(_quad(f, a, b), abs=1e-11)
+        assert O.cell_first_moment(a, b, d) == pytest.approx(_quad(lambda x: x * f(x), a, b), abs=1e-11)
+
+
+@pytest.mark.parametrize("d", [3, 128, 200, 1536, 3072])
+def test_one_bit_centroid_closed_form(d):
+    lm = O.lloyd_max(d, 1)
+    # conditional mean of the positive half by quadrature ...
+    f = _dens(d)
+    s = min(1.0, 6.0 / math.sqrt(d))
+    half_mean = 2.0 * integrate.quad(lambda x: x * f(x), 0.0, 1.0, points=[s], limit=400)[0]
+    assert lm.centroids[1] == pytest.approx(half_mean, rel=1e-8)
+    # ... and the Gamma-ratio closed form Gamma(d/2)/(sqrt(pi) Gamma((d+1)/2))
+    cf = math.exp(special.gammaln(d / 2) - special.gammaln((d + 1) / 2)) / math.sqrt(math.pi)
+    assert lm.centroids[1] == pytest.approx(cf, rel=1e-10)
+    assert lm.centroids[0] == -lm.centroids[1]
+
+
+def test_one_bit_shrinkage_is_about_36_percent():
+    # [ttakun]: the 1-bit mse quantizer underestimates inner products by ~36%;
+    # the shrinkage d*c_1^2 tends to 2/pi.
+    a128 = 128 * O.lloyd_max(128, 1).centroids[1] ** 2
+    assert a128 == pytest.approx(0.639111, abs=2e-6)
+    assert 1.0 - a128 == pytest.approx(0.36, abs=0.005)
+    big = 200000
+    assert big * O.lloyd_max(big, 1).centroids[1] ** 2 == pytest.approx(2.0 / math.pi, abs=1e-5)
+
+
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3), (128, 4), (200, 3), (1536, 4)])
+def test_lloyd_max_optimality_conditions_by_quadrature(d, bits):
+    lm = O.lloyd_max(d, bits)
+    f = _dens(d)
+    c, t = lm.centroids, lm.boundaries
+    assert np.all(np.diff(c) > 0)
+    assert np.allclose(c, -c[::-1], atol=1e-15)
+    assert np.allclose(t, 0.5 * (c[:-1] + c[1:]), atol=0)
+    edges = np.concatenate(([-1.0], t, [1.0]))
+    for k in range(len(c)):
+        a, b = edges[k], edges[k + 1]
+        mass = _quad(f, a, b)
+        mean = _quad(lambda x: x * f(x), a, b) / mass
+        assert mean == pytest.approx(c[k], rel=1e-7, abs=1e-12)
+    # distortion by direct quadrature of (x - Q(x))^2
+    dist = sum(_quad(lambda x, ck=c[k]: (x - ck) ** 2 * f(x), edges[k], edges[k + 1]) for k in range(len(c)))
+    assert d * dist == pytest.approx(lm.distortion, rel=1e-7)
+
+
+def _gaussian_table():
+    out = {}
+    with open(os.path.join(GOLDEN, "gaussian_lloyd_max.txt")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            left, right = line.split("|")
+            parts = left.split()
+            out[int(parts[0])] = ([float(v) for v in parts[1:]], float(right))
+    return out
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_large_d_limit_is_the_gaussian_lloyd_max_quantizer(bits):
+    levels, mse = _gaussian_table()[bits]
+    d = 400000
+    lm = O.lloyd_max(d, bits)
+    pos = lm.centroids[len(lm.centroids) // 2:] * math.sqrt(d)
+    assert np.allclose(pos, levels, atol=2e-4)
+    assert lm.distortion == pytest.approx(mse, rel=2e-3)
+
+
+def test_distortion_within_2_7x_of_the_shannon_bound():
+    # [ttakun]: the mse is only ~2.7x above the information-theoretic lower
+    # bound 4^-b; the ratio stays below sqrt(3)*pi/2 ~ 2.72 for b = 1..4.
+    ratios = []
+    for bits in (1, 2, 3, 4):
+        r = O.lloyd_max(128, bits).distortion * 4 ** bits
+        ratios.append(r)
+        assert 1.0 < r < math.sqrt(3) * math.pi / 2
+    assert all(a < b for a, b in zip(ratios, ratios[1:]))
+
+
+def test_nearest_index_equals_brute_force_argmin():
+    cd = O.make_codec(128, 4, O.MSE, 0)
+    rng = np.random.default_rng(3)
+    y = rng.normal(0, 1 / math.sqrt(128), 200000)
+    t = cd.boundaries
+    near = np.concatenate([t, np.nextafter(t, 1), np.nextafter(t, -1), [0.0, -0.0, 0.9, -0.9]])
+    y = np.concatenate([y, near])
+    got = O.nearest_index(cd, y)
+    # brute force: count boundaries strictly below, in pure Python
+    for i in range(0, len(y), 997):
+        assert got[i] == sum(1 for tk in t if tk < y[i])
+    for tk_i, tk in enumerate(t):
+        assert O.nearest_index(cd, np.array([tk]))[0] == tk_i          # tie -> lower index
+        assert O.nearest_index(cd, np.array([np.nextafter(tk, 1)]))[0] == tk_i + 1
+    # away from the boundaries the index is the nearest (f64) centroid
+    c = cd.centroids64
+    far = np.min(np.abs(y[:, None] - cd.boundaries64[None, :]), axis=1) > 1e-8
+    assert np.array_equal(got[far], np.argmin(np.abs(y[far, None] - c[None, :]), axis=1))
