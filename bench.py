@@ -1,0 +1,217 @@
+"""Benchmark of the TurboQuant hot path on one MI355X.
+
+Default workload (the metric's configuration): KV-cache compression of one
+layer of a Llama-3.1-8B-shaped model -- K and V, each 8 KV heads x 32768 tokens
+x head_dim 128 in bf16 with 4 outlier channels per head (x10), TurboQuant_mse
+at b = 4 with one rotation per head.  One step = one tq_quantize call over both
+tensors (524,288 vectors), inputs resident in HBM and rotated over enough
+copies to defeat the 256 MB Infinity Cache.
+
+The same JSON line also carries the decode-attention-logits phase: 16 batch x
+8 KV heads x 131072 cached tokens stored as TurboQuant_prod b = 4 (3-bit mse +
+1-bit QJL), 4 query heads per KV head, float32 logits -- timed the same way.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def _parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--skip-logits", action="store_true")
+    return p.parse_args()
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def time_launches(torch, fn, steps, warmup, copies):
+    """Run fn(i) `warmup` then `steps` times; return (wall ms per step, mean
+    per-launch ms from events recorded on the launch stream)."""
+    for i in range(warmup):
+        fn(i % copies)
+    torch.cuda.synchronize()
+    ev = _events(torch, 2 * steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[2 * i].record()
+        fn(i % copies)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+    return wall, float(np.mean(per)), float(np.median(per))
+
+
+def quantize_phase(torch, tq, workloads, steps, warmup):
+    k = workloads.kv_tensor(2)
+    v = workloads.kv_tensor(3)
+    x = torch.cat([k, v], 0).contiguous()          # [16 sets][32768][128] bf16
+    sets, n, d = x.shape
+    copies = 4                                      # 4 x 128 MiB inputs > MALL
+    xs = [x.cuda()] + [x.cuda() for _ in range(copies - 1)]
+    codec = tq.Codec(d, 4, tq.TQ_MSE, seed=0, groups=workloads.KV_HEADS)
+    outs = [codec.empty_codes(sets, n) for _ in range(copies)]
+
+    def step(i):
+        codec.quantize(xs[i], out=outs[i])
+
+    wall, kern, kmed = time_launches(torch, step, steps, warmup, copies)
+    vectors = sets * n
+    bytes_per_vec = d * 2 + codec.code_row + 4      # bf16 in, packed codes, f32 norm
+    flops_per_vec = 2 * 2 * d * d                   # two bf16 passes (Pi hi + lo)
+    achieved = vectors * bytes_per_vec / (kern * 1e-3) / 1e9
+    return dict(vectors=vectors, wall_ms=wall, kernel_ms=kern, kernel_ms_median=kmed,
+                bytes_per_vector=bytes_per_vec, achieved_gbs=achieved,
+                mfma_tflops=vectors * flops_per_vec / (kern * 1e-3) / 1e12, codec=codec, x=x)
+
+
+def quantize_b3_phase(torch, tq, workloads, x, steps, warmup):
+    sets, n, d = x.shape
+    xs = [x.cuda() for _ in range(4)]
+    codec = tq.Codec(d, 3, tq.TQ_MSE, seed=0, groups=workloads.KV_HEADS)
+    outs = [codec.empty_codes(sets, n) for _ in range(4)]
+    wall, kern, _ = time_launches(torch, lambda i: codec.quantize(xs[i], out=outs[i]), steps, warmup, 4)
+    bpv = d * 2 + codec.code_row + 4
+    return dict(kernel_ms=kern, vectors_per_s=sets * n / (kern * 1e-3),
+                achieved_gbs=sets * n * bpv / (kern * 1e-3) / 1e9)
+
+
+def logits_phase(torch, tq, workloads, steps, warmup):
+    B, H, QH, T, d = (workloads.DEC_BATCH, workloads.DEC_KV_HEADS, workloads.DEC_Q_PER_KV,
+                      workloads.DEC_TOKENS, workloads.DEC_DIM)
+    sets = B * H
+    codec = tq.Codec(d, 4, tq.TQ_PROD, seed=0, groups=H)
+    cache = codec.empty_codes(sets, T)
+    # build the cache: float32 N(0,1) keys drawn on the device, 8 sets at a time
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    chunk = 8
+    kbuf = torch.empty((chunk, T, d), dtype=torch.float32, device="cuda")
+    t0 = time.perf_counter()
+    for s0 in range(0, sets, chunk):
+        kbuf.normal_(generator=gen)
+        view = {k: (None if v is None else v[s0:s0 + chunk]) for k, v in cache.items()}
+        # the chunk's sets map to groups s % H because chunk is a multiple of H
+        codec.quantize(kbuf, out=view)
+    torch.cuda.synchronize()
+    build_s = time.perf_counter() - t0
+    del kbuf
+    q = torch.from_numpy(workloads.decode_queries().reshape(sets, QH, d)).cuda()
+    out = torch.empty((sets, QH, T), dtype=torch.float32, device="cuda")
+    wall, kern, kmed = time_launches(torch, lambda i: codec.logits(q, cache, out=out), steps, warmup, 1)
+    keys = sets * T
+    packed = keys * (codec.code_row + codec.sign_row + 8)
+    written = sets * QH * T * 4
+    return dict(keys=keys, wall_ms=wall, kernel_ms=kern, kernel_ms_median=kmed, cache_build_s=build_s,
+                packed_bytes=packed, logits_bytes=written,
+                packed_gbs=packed / (kern * 1e-3) / 1e9,
+                total_gbs=(packed + written) / (kern * 1e-3) / 1e9)
+
+
+def cpu_baseline(workloads, x_bf16, budget_s=15.0):
+    """The oracle (float64 NumPy) quantizing a bounded sample of the same KV
+    workload; vectors/s extrapolated from the sample."""
+    from oracle import tq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    xf = x_bf16.float().numpy()
+    cd = O.make_codec(128, 4, O.MSE, 0, groups=workloads.KV_HEADS)
+    done, t0, rows = 0, time.perf_counter(), 8192
+    sets = xf.shape[0]
+    while time.perf_counter() - t0 < budget_s and done < sets * xf.shape[1]:
+        s = (done // rows) % sets
+        off = (done // (rows * sets)) * rows
+        chunk = xf[s, off:off + rows].astype(np.float64)
+        idx, nu, _ = O.quantize_mse(cd, chunk, s % cd.groups)
+        O.pack(idx, 4)
+        done += chunk.shape[0]
+    el = time.perf_counter() - t0
+    return dict(value=done / el, unit="vectors/s", cores=int(threads), kind="oracle",
+                sample=f"{done} of the {sets * xf.shape[1]} KV vectors (mse b=4: norm, rotate, "
+                       f"boundary search, pack) in {el:.1f} s")
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(the multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+    import torch
+
+    import kv_cache_compression_tq_amd as tq
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    qp = quantize_phase(torch, tq, workloads, args.steps, args.warmup)
+    q3 = quantize_b3_phase(torch, tq, workloads, qp["x"], args.steps, args.warmup)
+    lp = None if args.skip_logits else logits_phase(torch, tq, workloads, args.steps, args.warmup)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, qp["x"])
+
+    value = qp["vectors"] / (qp["wall_ms"] * 1e-3)
+    line = {
+        "metric": "quantized vectors/s and q·K̂ logit GB/s (d=128, b=4) vs MI355X HBM roofline",
+        "value": value,
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": qp["wall_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KV-cache quantize, K+V of one Llama-3.1-8B-shaped layer: 2 x 8 KV heads x "
+                               "32768 tokens x 128, bf16, 4 outlier channels/head x10, TurboQuant_mse b=4, "
+                               "one rotation per head",
+                   "vectors_per_step": qp["vectors"], "d": 128, "bits": 4, "variant": "mse"},
+        "roofline": {"bound": "hbm", "kernel": "k_quant128<4,mse,bf16>", "achieved": qp["achieved_gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": qp["achieved_gbs"] / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_vector": qp["bytes_per_vector"],
+                     "kernel_ms": qp["kernel_ms"],
+                     "mfma_bf16_tflops": qp["mfma_tflops"],
+                     "mfma_frac": qp["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS},
+        "quantize_b3": {"kernel_ms": q3["kernel_ms"], "vectors_per_s": q3["vectors_per_s"],
+                        "achieved_gbs": q3["achieved_gbs"], "frac": q3["achieved_gbs"] / HBM_PEAK_GBS},
+    }
+    if lp is not None:
+        line["logits"] = {
+            "metric": "q·K̂ logit GB/s on packed-code bytes",
+            "value": lp["packed_gbs"], "unit": "GB/s", "ms_per_step": lp["wall_ms"],
+            "config": {"workload": "decode attention logits: 16 batch x 8 KV heads x 131072 cached tokens, "
+                                   "TurboQuant_prod b=4 (3-bit mse + 1-bit QJL), 32 query heads (4 per KV head), "
+                                   "fp32 queries and logits", "keys": lp["keys"]},
+            "roofline": {"bound": "hbm", "kernel": "k_logits128<3,prod>", "achieved": lp["packed_gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lp["packed_gbs"] / HBM_PEAK_GBS,
+                         "traffic": None, "kernel_ms": lp["kernel_ms"],
+                         "achieved_incl_logits_written": lp["total_gbs"],
+                         "frac_incl_logits_written": lp["total_gbs"] / HBM_PEAK_GBS},
+            "cache_build_s": lp["cache_build_s"],
+        }
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

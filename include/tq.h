@@ -1,0 +1,135 @@
+/*
+ * tq.h -- C ABI of the TurboQuant hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, section):
+ *   [ttakun]  "KV缓存52GB瞬间爆内存？TurboQuant随机旋转+标量量化如何把LLM长上下文推理成本砍到1/16
+ *             且失真逼近理论极限", sections "为什么随机旋转是整个算法的底层杠杆" and
+ *             "TurboQuant_mse vs TurboQuant_prod两个变体的精确分工".
+ *   [tmdm]    "谷歌悄悄扔下一颗'性能核弹'", section "双剑合璧：PolarQuant + QJL".
+ *   [admirer] admirer.cn TurboQuant article, sections "第一步" and "第二步".
+ *   [tqnet]   turboquant.net/zh, sections "TurboQuant 两阶段算法 › 坐标分布公式",
+ *             "实现步骤草图" and "工程风险与应对".
+ *
+ * Conventions shared by every entry point
+ *   - Status: TQ_OK (0) or a negative TQ_E* code; tq_last_error() returns a
+ *     thread-local message for the last failure on the calling thread.  C++
+ *     exceptions never cross this boundary.
+ *   - Validation failures return before anything is enqueued.  A failed kernel
+ *     launch returns TQ_EHIP.  Faults inside a kernel surface at the caller's
+ *     next synchronisation.
+ *   - Data calls are asynchronous: they enqueue on `stream` (a hipStream_t,
+ *     NULL = the default stream) and return.  Every data pointer is a device
+ *     pointer owned by the caller; the library allocates no memory per call.
+ *   - The handle owns its device tables (rotation, projection, codebook),
+ *     allocated on the HIP device current at tq_init and freed by tq_destroy.
+ *     A handle is immutable after init: concurrent calls on it are safe.
+ *   - Identical inputs give bitwise identical outputs (no atomics).
+ *
+ * Stored layout (the pages leave it open)
+ *   - codes : [n_sets][n][code_row_bytes] uint8.  Coordinate j's index
+ *             occupies bits [j*mb, j*mb+mb) of the row's little-endian,
+ *             LSB-first bit stream (stream bit k = bit k%8 of byte k/8);
+ *             mb = mse bits.  Rows are zero-padded to a multiple of 16 bytes.
+ *   - signs : [n_sets][n][sign_row_bytes] uint8, same layout with 1 bit per
+ *             projection; bit 1 <=> sign +1 (sign(0) = +1).
+ *   - norms : [n_sets][n] float32 = ||x||;  rnorms : [n_sets][n] float32 =
+ *             ||r|| of the prod residual of the unit vector.
+ *   - Block s of n_sets uses codec group s % groups.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tq_codec *tq_handle;
+
+enum { TQ_MSE = 0, TQ_PROD = 1 };
+enum { TQ_F32 = 0, TQ_BF16 = 1 };
+enum { TQ_OK = 0, TQ_EINVAL = -1, TQ_EUNSUPPORTED = -2, TQ_ENOMEM = -3, TQ_EHIP = -4 };
+
+/* Build a codec: d dimensions, b bits per coordinate, variant TQ_MSE or
+ * TQ_PROD, deterministic from `seed`.  Equivalent to tq_init_groups(..., 1).
+ * [tqnet] 实现步骤草图 (precompute the Lloyd–Max centroids once, generate the
+ * rotation by QR of a Gaussian matrix); [tqnet] 工程风险与应对 (pre-generate
+ * and reuse the matrix).  Valid: 3 <= d <= 4096; mse: 1 <= b <= 8;
+ * prod: 1 <= b <= 5 (b-1 mse bits, b = 1 is QJL only).  *out receives the
+ * handle (unchanged on failure).  Errors: TQ_EINVAL, TQ_ENOMEM, TQ_EHIP. */
+int tq_init(int d, int b, int variant, uint64_t seed, tq_handle *out);
+
+/* As tq_init with `groups` independent (Pi, S) pairs; group g draws its
+ * matrices from stream (seed, g).  The codebook is shared.  1 <= groups <= 4096. */
+int tq_init_groups(int d, int b, int variant, uint64_t seed, int groups, tq_handle *out);
+
+/* Free the handle and its device tables.  NULL is a no-op. */
+int tq_destroy(tq_handle h);
+
+/* Row sizes of the stored arrays and the number of mse bits per coordinate
+ * (b for mse, b-1 for prod).  Any output pointer may be NULL. */
+int tq_layout(tq_handle h, int64_t *code_row_bytes, int64_t *sign_row_bytes, int *mse_bits);
+
+/* Quantize n_sets blocks of n vectors x[n_sets][n][d] (dtype TQ_F32 or TQ_BF16).
+ * mse ([ttakun] TurboQuant_mse: normalise and store ||x|| as float32, rotate,
+ * index each coordinate against the precomputed codebook): writes codes and
+ * norms.  prod ([ttakun] TurboQuant_prod; [admirer] 第一步/第二步: (b-1)-bit mse
+ * stage, residual r, 1-bit QJL signs of S r): also writes signs and rnorms.
+ * The index of coordinate j is #{k : t_k < (Pi x/||x||)_j} (ties to the lower
+ * index).  A zero vector gets norm 0, rnorm 0 and all signs +1.
+ * codes may be NULL only when the handle has 0 mse bits; signs/rnorms must be
+ * NULL for mse and non-NULL for prod.  Pointers 16-byte aligned (x: 4-byte for
+ * f32 / 2-byte for bf16; norms 4-byte).  n == 0 or n_sets == 0 is a no-op.
+ * Errors: TQ_EINVAL, TQ_EHIP. */
+int tq_quantize(tq_handle h, const void *x, int dtype, int64_t n_sets, int64_t n,
+                void *codes, void *signs, float *norms, float *rnorms, void *stream);
+
+/* Reconstruct x_out[n_sets][n][d] float32.  mse: ||x|| Pi^T c[idx] ([ttakun]
+ * inverse rotation and rescale; [tqnet] dequant x = Pi.T @ centroids[idx]).
+ * prod: ||x|| (Pi^T c[idx] + sqrt(pi/2)/d * ||r|| S^T z), the unbiased QJL
+ * reconstruction.  Arguments as in tq_quantize.  Errors: TQ_EINVAL, TQ_EHIP. */
+int tq_dequantize(tq_handle h, const void *codes, const void *signs, const float *norms,
+                  const float *rnorms, int64_t n_sets, int64_t n, float *x_out, void *stream);
+
+/* Attention logits / inner products scored directly on packed keys
+ * ([admirer] 第二步: the full-precision query balanced against the 1-bit codes;
+ * [tmdm] unbiased estimator at attention time).  For set s, query i and key t:
+ *   out[s][i][t] = <q[s][i], k_hat[s][t]>   (no 1/sqrt(d), no softmax),
+ * where k_hat is the tq_dequantize reconstruction.  q: [n_sets][nq][d] float32
+ * (grouped-query attention passes the query heads of one KV head as one set).
+ * The kernel rotates and projects each query once and never materialises
+ * k_hat.  1 <= nq <= 64.  Errors: TQ_EINVAL, TQ_EHIP. */
+int tq_logits(tq_handle h, const float *q, int64_t nq, const void *codes, const void *signs,
+              const float *norms, const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
+              void *stream);
+
+/* Static text for a status code. */
+const char *tq_strerror(int status);
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char *tq_last_error(void);
+
+/* ---- test hooks (not used by the hot path) ---- */
+
+/* Host copies of group g's tables as the device holds them: Pi [d][d]
+ * row-major (y = Pi x), S [d][d] (prod only, else ignored), centroids
+ * [2^mb] ascending, boundaries [2^mb - 1].  Any pointer may be NULL.
+ * Synchronous.  Errors: TQ_EINVAL, TQ_EHIP. */
+int tq_get_tables(tq_handle h, int g, float *Pi, float *S, float *centroids, float *bounds);
+
+/* The same tables computed on the host only (no device needed). */
+int tq_host_tables(int d, int b, int variant, uint64_t seed, int g, float *Pi, float *S,
+                   float *centroids, float *bounds);
+
+/* Pack rows x d indices (uint8, each < 2^bits) into the stored layout with
+ * h's dimension d: out[rows][row_bytes(d, bits)].  1 <= bits <= 8.
+ * Errors: TQ_EINVAL, TQ_EHIP. */
+int tq_pack(tq_handle h, const uint8_t *idx, int bits, int64_t rows, void *out, void *stream);
+/* Inverse of tq_pack. */
+int tq_unpack(tq_handle h, const void *in, int bits, int64_t rows, uint8_t *idx, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

@@ -1,0 +1,232 @@
+"""Python binding of libtq.so, the TurboQuant hot path for AMD MI355X.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.  Importing this
+package does not load the library; the first call does, and it raises if the
+built library is missing (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["Codec", "lib", "library_path", "TQ_MSE", "TQ_PROD", "TQ_F32", "TQ_BF16", "TQError",
+           "EXPORTED_SYMBOLS", "row_bytes"]
+
+TQ_MSE, TQ_PROD = 0, 1
+TQ_F32, TQ_BF16 = 0, 1
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ENOMEM, TQ_EHIP = 0, -1, -2, -3, -4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_SIGS = {
+    "tq_init": (_INT, [_INT, _INT, _INT, ctypes.c_uint64, ctypes.POINTER(_P)]),
+    "tq_init_groups": (_INT, [_INT, _INT, _INT, ctypes.c_uint64, _INT, ctypes.POINTER(_P)]),
+    "tq_destroy": (_INT, [_P]),
+    "tq_layout": (_INT, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_INT)]),
+    "tq_quantize": (_INT, [_P, _P, _INT, _I64, _I64, _P, _P, _P, _P, _P]),
+    "tq_dequantize": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _P, _P]),
+    "tq_logits": (_INT, [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P]),
+    "tq_strerror": (ctypes.c_char_p, [_INT]),
+    "tq_last_error": (ctypes.c_char_p, []),
+    "tq_get_tables": (_INT, [_P, _INT, _P, _P, _P, _P]),
+    "tq_host_tables": (_INT, [_INT, _INT, _INT, ctypes.c_uint64, _INT, _P, _P, _P, _P]),
+    "tq_pack": (_INT, [_P, _P, _INT, _I64, _P, _P]),
+    "tq_unpack": (_INT, [_P, _P, _INT, _I64, _P, _P]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("TQ_LIBRARY", os.path.join(_HERE, "libtq.so"))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtq.so (once).  Raises FileNotFoundError when it is not built."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"{path} is not built: run `python -m kv_cache_compression_tq_amd.build`")
+        L = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ_OK:
+        detail = lib().tq_last_error().decode() or lib().tq_strerror(status).decode()
+        raise TQError(status, where, detail)
+
+
+def row_bytes(count: int, bits: int) -> int:
+    return ((count * bits + 7) // 8 + 15) // 16 * 16
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Codec:
+    """A TurboQuant codec: d dimensions, b bits, variant TQ_MSE / TQ_PROD.
+
+    Data methods take CUDA (HIP) torch tensors and enqueue on the current
+    stream; outputs are allocated here with torch unless given.
+    """
+
+    def __init__(self, d: int, bits: int, variant: int = TQ_MSE, seed: int = 0, groups: int = 1):
+        self.d, self.bits, self.variant, self.seed, self.groups = d, bits, variant, seed, groups
+        h = ctypes.c_void_p()
+        _check(lib().tq_init_groups(d, bits, variant, seed, groups, ctypes.byref(h)), "tq_init_groups")
+        self._h = h
+        cr, sr, mb = _I64(), _I64(), _INT()
+        _check(lib().tq_layout(self._h, ctypes.byref(cr), ctypes.byref(sr), ctypes.byref(mb)), "tq_layout")
+        self.code_row, self.sign_row, self.mse_bits = cr.value, sr.value, mb.value
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            lib().tq_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def handle(self):
+        return self._h
+
+    # -- storage -----------------------------------------------------------
+    def empty_codes(self, n_sets: int, n: int, device="cuda"):
+        import torch
+
+        codes = torch.zeros((n_sets, n, self.code_row), dtype=torch.uint8, device=device) if self.code_row else None
+        norms = torch.empty((n_sets, n), dtype=torch.float32, device=device)
+        signs = rnorms = None
+        if self.variant == TQ_PROD:
+            signs = torch.empty((n_sets, n, self.sign_row), dtype=torch.uint8, device=device)
+            rnorms = torch.empty((n_sets, n), dtype=torch.float32, device=device)
+        return dict(codes=codes, signs=signs, norms=norms, rnorms=rnorms)
+
+    # -- hot path ----------------------------------------------------------
+    def quantize(self, x, out=None, stream=None):
+        """x: [n_sets, n, d] (or [n, d]) float32 or bfloat16 CUDA tensor."""
+        import torch
+
+        if x.dim() == 2:
+            x = x.unsqueeze(0)
+        if not x.is_contiguous():
+            raise ValueError("x must be contiguous")
+        dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}.get(x.dtype)
+        if dtype is None:
+            raise TypeError("x must be float32 or bfloat16")
+        n_sets, n, d = x.shape
+        if d != self.d:
+            raise ValueError(f"last dimension {d} != codec d {self.d}")
+        out = out or self.empty_codes(n_sets, n, x.device)
+        _check(lib().tq_quantize(self._h, _ptr(x), dtype, n_sets, n, _ptr(out["codes"]), _ptr(out["signs"]),
+                                 _ptr(out["norms"]), _ptr(out["rnorms"]), _stream(stream)), "tq_quantize")
+        return out
+
+    def dequantize(self, keys, out=None, stream=None):
+        import torch
+
+        norms = keys["norms"]
+        n_sets, n = norms.shape
+        if out is None:
+            out = torch.empty((n_sets, n, self.d), dtype=torch.float32, device=norms.device)
+        _check(lib().tq_dequantize(self._h, _ptr(keys.get("codes")), _ptr(keys.get("signs")), _ptr(norms),
+                                   _ptr(keys.get("rnorms")), n_sets, n, _ptr(out), _stream(stream)),
+               "tq_dequantize")
+        return out
+
+    def logits(self, q, keys, out=None, stream=None):
+        """q: [n_sets, nq, d] float32; keys: dict from quantize.  Returns
+        [n_sets, nq, n_keys] float32 raw inner products."""
+        import torch
+
+        if q.dim() == 2:
+            q = q.unsqueeze(0)
+        if q.dtype != torch.float32 or not q.is_contiguous():
+            raise TypeError("q must be contiguous float32")
+        norms = keys["norms"]
+        n_sets, n_keys = norms.shape
+        nq = q.shape[1]
+        if q.shape[0] != n_sets or q.shape[2] != self.d:
+            raise ValueError("q shape does not match the keys")
+        if out is None:
+            out = torch.empty((n_sets, nq, n_keys), dtype=torch.float32, device=norms.device)
+        _check(lib().tq_logits(self._h, _ptr(q), nq, _ptr(keys.get("codes")), _ptr(keys.get("signs")), _ptr(norms),
+                               _ptr(keys.get("rnorms")), n_sets, n_keys, _ptr(out), _stream(stream)), "tq_logits")
+        return out
+
+    # -- test hooks ----------------------------------------------------------
+    def tables(self, group: int = 0):
+        import numpy as np
+
+        d = self.d
+        pi = np.empty((d, d), np.float32)
+        s = np.empty((d, d), np.float32)
+        L = 1 << self.mse_bits if self.mse_bits else 0
+        c = np.empty(max(L, 1), np.float32)
+        t = np.empty(max(L - 1, 1), np.float32)
+        _check(lib().tq_get_tables(self._h, group, pi.ctypes.data, s.ctypes.data, c.ctypes.data, t.ctypes.data),
+               "tq_get_tables")
+        return dict(Pi=pi, S=s if self.variant == TQ_PROD else None, centroids=c[:L], boundaries=t[:max(L - 1, 0)])
+
+    def pack(self, idx, bits: int, stream=None):
+        import torch
+
+        rows = idx.shape[0]
+        out = torch.empty((rows, row_bytes(self.d, bits)), dtype=torch.uint8, device=idx.device)
+        _check(lib().tq_pack(self._h, _ptr(idx), bits, rows, _ptr(out), _stream(stream)), "tq_pack")
+        return out
+
+    def unpack(self, packed, bits: int, stream=None):
+        import torch
+
+        rows = packed.shape[0]
+        out = torch.empty((rows, self.d), dtype=torch.uint8, device=packed.device)
+        _check(lib().tq_unpack(self._h, _ptr(packed), bits, rows, _ptr(out), _stream(stream)), "tq_unpack")
+        return out
+
+
+def host_tables(d: int, bits: int, variant: int, seed: int, group: int = 0):
+    """The codec tables computed on the host only (no device needed)."""
+    import numpy as np
+
+    mse_bits = bits if variant == TQ_MSE else bits - 1
+    L = 1 << mse_bits if mse_bits else 0
+    pi = np.empty((d, d), np.float32)
+    s = np.empty((d, d), np.float32)
+    c = np.empty(max(L, 1), np.float32)
+    t = np.empty(max(L - 1, 1), np.float32)
+    _check(lib().tq_host_tables(d, bits, variant, seed, group, pi.ctypes.data, s.ctypes.data, c.ctypes.data,
+                                t.ctypes.data), "tq_host_tables")
+    return dict(Pi=pi, S=s if variant == TQ_PROD else None, centroids=c[:L], boundaries=t[:max(L - 1, 0)])

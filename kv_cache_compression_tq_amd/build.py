@@ -1,0 +1,72 @@
+"""Build libtq.so (HIP kernels for gfx950 + host C++), in-tree.
+
+    python -m kv_cache_compression_tq_amd.build
+
+Host C++ is compiled with g++; device code with hipcc for gfx950 only.  All
+device code is built with packed FP32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+OUT = os.path.join(HERE, "libtq.so")
+BUILD = os.path.join(HERE, "_build")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+HOST_SOURCES = ["host_codec.cpp", "tq_api.cpp"]
+DEVICE_SOURCES = ["generic.hip", "fast128.hip"]
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include",
+              f"-I{os.path.join(ROOT, 'include')}", "-Wall", "-Wno-unused-function"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + r.stdout)
+    return r.stdout
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        jobs.append((["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    for src in DEVICE_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        jobs.append(([HIPCC, *HIP_FLAGS, f"-I{os.path.join(ROOT, 'include')}", "-c",
+                      os.path.join(CSRC, src), "-o", obj], obj))
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        outs = list(ex.map(lambda j: _run(j[0]), jobs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    tmp = OUT + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[j[1] for j in jobs],
+          "-lpthread"])
+    os.replace(tmp, OUT)
+    return OUT
+
+
+def clean() -> None:
+    shutil.rmtree(BUILD, ignore_errors=True)
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,27 @@
+// Host-side construction of the operand images used by the d = 128 MFMA
+// kernels (fast128.hip).  Built once per codec at init.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+namespace tq {
+
+// True when the d = 128 kernels handle this configuration.
+bool fast128_supported(int d, int mse_bits, int variant);
+
+// 32-bit words of one rotation (or QJL) image per group.
+size_t fast128_rotation_words(int d);
+
+// Image of a d x d float64 matrix (row-major, out = mat * in) as the
+// bf16 hi/lo MFMA A-operand fragments, rows permuted so that each lane ends up
+// holding 32 consecutive output coordinates.  k_order 0: the contraction index
+// follows the input-vector load order (rotation of x); k_order 1: it follows
+// the lane-chunk order of register-resident rotated coordinates (QJL
+// projection of the residual).
+void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out);
+
+// Words of the logits decode tables for `mse_bits` (pair LUTs + sign LUT).
+size_t fast128_lut_words(int mse_bits);
+void fast128_build_logit_lut(const float *centroids, int mse_bits, uint32_t *out);
+
+}  // namespace tq

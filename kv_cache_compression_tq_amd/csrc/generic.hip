@@ -1,0 +1,314 @@
+// Dimension-generic kernels (any 3 <= d <= 4096): one workgroup per vector for
+// quantize/dequantize, one thread per key for logits.  Plain fp32 VALU
+// arithmetic.  They serve every shape the d = 128 MFMA kernels do not.
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace tq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline float load_x(const float *p, int64_t i) { return p[i]; }
+__device__ inline float load_x(const uint16_t *p, int64_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);  // bf16 -> f32 exactly
+}
+
+__device__ float block_sum(float v, float *red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+  return s;
+}
+
+// Read field j (width mb bits) of an LSB-first bit stream.
+__device__ inline int read_field(const uint8_t *row, int j, int mb) {
+  const int bit = j * mb;
+  const int byte = bit >> 3, sh = bit & 7;
+  uint32_t w = row[byte];
+  if (sh + mb > 8) w |= (uint32_t)row[byte + 1] << 8;
+  return (int)((w >> sh) & ((1u << mb) - 1u));
+}
+
+// TurboQuant_mse / _prod quantize of one vector per workgroup.
+// Shared memory: x[d], y[d] (later the residual), idx[d] (int; reused for the
+// sign bits once the codes are packed).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_quant_generic(
+    const T *__restrict__ x, int d, int64_t n, int groups, int mse_bits, int prod,
+    const float *__restrict__ PiT, const float *__restrict__ MT, const float *__restrict__ cent,
+    const float *__restrict__ bnd, uint8_t *__restrict__ codes, int64_t code_row,
+    uint8_t *__restrict__ signs, int64_t sign_row, float *__restrict__ norms,
+    float *__restrict__ rnorms) {
+  extern __shared__ float sm[];
+  __shared__ float red[kThreads / 64];
+  float *xs = sm, *ys = sm + d;
+  int *is = (int *)(sm + 2 * d), *bs = is;
+  const int64_t row = blockIdx.x;
+  const int g = (int)((row / n) % groups);
+  const int tid = threadIdx.x;
+  const T *xv = x + row * d;
+
+  float acc = 0.f;
+  for (int j = tid; j < d; j += kThreads) {
+    const float v = load_x(xv, j);
+    xs[j] = v;
+    acc = fmaf(v, v, acc);
+  }
+  const float nu = sqrtf(block_sum(acc, red));
+  const float nthr = nu > 0.f ? nu : 1.f;  // a zero vector has y = 0
+  __syncthreads();
+
+  // y = Pi x  (PiT[k][j] = Pi[j][k]; consecutive threads read consecutive j)
+  const float *P = PiT + (size_t)g * d * d;
+  const int L = 1 << mse_bits;
+  for (int j = tid; j < d; j += kThreads) {
+    float y = 0.f;
+    for (int k = 0; k < d; ++k) y = fmaf(P[(size_t)k * d + j], xs[k], y);
+    int idx = 0;
+    if (mse_bits > 0)
+      for (int k = 0; k + 1 < L; ++k) idx += (nthr * bnd[k] < y) ? 1 : 0;
+    is[j] = idx;
+    // prod residual in the rotated domain: Pi r * ||x|| = y - ||x|| c[idx]
+    ys[j] = mse_bits > 0 ? y - nu * cent[idx] : y;
+  }
+  __syncthreads();
+
+  if (mse_bits > 0) {
+    uint8_t *crow = codes + row * code_row;
+    for (int byte = tid; byte < code_row; byte += kThreads) {
+      uint32_t v = 0;
+      for (int p = 0; p < 8; ++p) {
+        const int sb = byte * 8 + p, j = sb / mse_bits, k = sb % mse_bits;
+        if (j < d) v |= (uint32_t)((is[j] >> k) & 1) << p;
+      }
+      crow[byte] = (uint8_t)v;
+    }
+  }
+  if (tid == 0) norms[row] = nu;
+  if (!prod) return;
+
+  float r2 = 0.f;
+  for (int j = tid; j < d; j += kThreads) r2 = fmaf(ys[j], ys[j], r2);
+  const float rn = sqrtf(block_sum(r2, red));
+  // sign(S r) = sign(M (Pi r)), M = S Pi^T
+  const float *M = MT + (size_t)g * d * d;
+  for (int i = tid; i < d; i += kThreads) {
+    float p = 0.f;
+    for (int j = 0; j < d; ++j) p = fmaf(M[(size_t)j * d + i], ys[j], p);
+    bs[i] = p >= 0.f ? 1 : 0;
+  }
+  __syncthreads();
+  uint8_t *srow = signs + row * sign_row;
+  for (int byte = tid; byte < sign_row; byte += kThreads) {
+    uint32_t v = 0;
+    for (int p = 0; p < 8; ++p) {
+      const int i = byte * 8 + p;
+      if (i < d) v |= (uint32_t)bs[i] << p;
+    }
+    srow[byte] = (uint8_t)v;
+  }
+  if (tid == 0) rnorms[row] = nu > 0.f ? rn / nu : 0.f;
+}
+
+// Reconstruction of one vector per workgroup:
+// out = nu (Pi^T c[idx] + sqrt(pi/2)/d * gamma * S^T z).
+__global__ __launch_bounds__(kThreads) void k_dequant_generic(
+    const uint8_t *__restrict__ codes, const uint8_t *__restrict__ signs,
+    const float *__restrict__ norms, const float *__restrict__ rnorms, int d, int64_t n,
+    int groups, int mse_bits, int prod, const float *__restrict__ Pi, const float *__restrict__ S,
+    const float *__restrict__ cent, int64_t code_row, int64_t sign_row, float *__restrict__ out) {
+  extern __shared__ float sm[];
+  float *cv = sm, *zv = sm + d;
+  const int64_t row = blockIdx.x;
+  const int g = (int)((row / n) % groups);
+  const int tid = threadIdx.x;
+  const uint8_t *crow = codes ? codes + row * code_row : nullptr;
+  const uint8_t *srow = prod ? signs + row * sign_row : nullptr;
+  for (int j = tid; j < d; j += kThreads) {
+    cv[j] = mse_bits > 0 ? cent[read_field(crow, j, mse_bits)] : 0.f;
+    if (prod) zv[j] = ((srow[j >> 3] >> (j & 7)) & 1) ? 1.f : -1.f;
+  }
+  __syncthreads();
+  const float nu = norms[row];
+  const float w = prod ? kQjlScale / (float)d * rnorms[row] : 0.f;
+  const float *P = Pi + (size_t)g * d * d, *Sg = S ? S + (size_t)g * d * d : nullptr;
+  for (int i = tid; i < d; i += kThreads) {
+    float a = 0.f, b = 0.f;
+    if (mse_bits > 0)
+      for (int j = 0; j < d; ++j) a = fmaf(P[(size_t)j * d + i], cv[j], a);
+    if (prod)
+      for (int j = 0; j < d; ++j) b = fmaf(Sg[(size_t)j * d + i], zv[j], b);
+    out[row * d + i] = nu * fmaf(w, b, a);
+  }
+}
+
+// Logits: each workgroup rotates/projects the queries of its set into LDS
+// (heads in chunks of `hc`), then each thread scores keys one at a time.
+constexpr int kMaxHeads = 8;
+constexpr int kKeysPerThread = 8;
+
+__global__ __launch_bounds__(kThreads) void k_logits_generic(
+    const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ signs, const float *__restrict__ norms,
+    const float *__restrict__ rnorms, int d, int64_t n_keys, int groups, int mse_bits, int prod,
+    const float *__restrict__ PiT, const float *__restrict__ ST, const float *__restrict__ cent,
+    int64_t code_row, int64_t sign_row, float *__restrict__ out) {
+  extern __shared__ float sm[];
+  float *qs = sm, *qt = sm + hc * d, *pp = sm + 2 * hc * d;
+  const int s = blockIdx.y;
+  const int g = s % groups;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < hc * d; e += kThreads) qs[e] = q[((int64_t)s * nq + h0) * d + e];
+  __syncthreads();
+  const float *P = PiT + (size_t)g * d * d;
+  const float *Sg = prod ? ST + (size_t)g * d * d : nullptr;
+  for (int e = tid; e < hc * d; e += kThreads) {
+    const int h = e / d, j = e % d;
+    float a = 0.f, b = 0.f;
+    for (int k = 0; k < d; ++k) {
+      a = fmaf(P[(size_t)k * d + j], qs[h * d + k], a);            // (Pi q)_j
+      if (prod) b = fmaf(Sg[(size_t)k * d + j], qs[h * d + k], b);  // (S q)_j
+    }
+    qt[e] = a;
+    pp[e] = b;
+  }
+  __syncthreads();
+  const float ks = kQjlScale / (float)d;
+  for (int kk = 0; kk < kKeysPerThread; ++kk) {
+    const int64_t t = ((int64_t)blockIdx.x * kKeysPerThread + kk) * kThreads + tid;
+    if (t >= n_keys) break;
+    const int64_t row = (int64_t)s * n_keys + t;
+    float am[kMaxHeads], as[kMaxHeads];
+    for (int h = 0; h < kMaxHeads; ++h) am[h] = as[h] = 0.f;
+    if (mse_bits > 0) {
+      const uint8_t *crow = codes + row * code_row;
+      for (int j = 0; j < d; ++j) {
+        const float c = cent[read_field(crow, j, mse_bits)];
+        for (int h = 0; h < kMaxHeads; ++h)
+          if (h < hc) am[h] = fmaf(qt[h * d + j], c, am[h]);
+      }
+    }
+    if (prod) {
+      const uint8_t *srow = signs + row * sign_row;
+      for (int i = 0; i < d; ++i) {
+        const bool pos = (srow[i >> 3] >> (i & 7)) & 1;
+        for (int h = 0; h < kMaxHeads; ++h)
+          if (h < hc) as[h] += pos ? pp[h * d + i] : -pp[h * d + i];
+      }
+    }
+    const float nu = norms[row];
+    const float w = prod ? ks * rnorms[row] : 0.f;
+    for (int h = 0; h < kMaxHeads; ++h)
+      if (h < hc) out[((int64_t)s * nq + h0 + h) * n_keys + t] = nu * fmaf(w, as[h], am[h]);
+  }
+}
+
+__global__ void k_pack(const uint8_t *__restrict__ idx, int bits, int64_t rows, int count,
+                       int64_t row_bytes, uint8_t *__restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= rows * row_bytes) return;
+  const int64_t r = e / row_bytes;
+  const int byte = (int)(e % row_bytes);
+  const uint8_t *ir = idx + r * count;
+  uint32_t v = 0;
+  for (int p = 0; p < 8; ++p) {
+    const int sb = byte * 8 + p, j = sb / bits, k = sb % bits;
+    if (j < count) v |= (uint32_t)((ir[j] >> k) & 1) << p;
+  }
+  out[e] = (uint8_t)v;
+}
+
+__global__ void k_unpack(const uint8_t *__restrict__ in, int bits, int64_t rows, int count,
+                         int64_t row_bytes, uint8_t *__restrict__ idx) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= rows * count) return;
+  const int64_t r = e / count;
+  const int j = (int)(e % count);
+  const uint8_t *row = in + r * row_bytes;
+  uint32_t v = 0;
+  for (int k = 0; k < bits; ++k) {
+    const int sb = j * bits + k;
+    v |= (uint32_t)((row[sb >> 3] >> (sb & 7)) & 1) << k;
+  }
+  idx[e] = (uint8_t)v;
+}
+
+}  // namespace
+
+hipError_t launch_quant_generic(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
+                                int64_t n, uint8_t *codes, uint8_t *signs, float *norms,
+                                float *rnorms, hipStream_t st) {
+  const int64_t rows = n_sets * n;
+  if (rows == 0) return hipSuccess;
+  const size_t shmem = (size_t)3 * t.d * sizeof(float);
+  const int prod = t.variant == 1;
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_quant_generic<float>, dim3((unsigned)rows), dim3(kThreads), shmem, st,
+                       (const float *)x, t.d, n, t.groups, t.mse_bits, prod, t.PiT, t.MT, t.cent,
+                       t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms);
+  else
+    hipLaunchKernelGGL(k_quant_generic<uint16_t>, dim3((unsigned)rows), dim3(kThreads), shmem, st,
+                       (const uint16_t *)x, t.d, n, t.groups, t.mse_bits, prod, t.PiT, t.MT,
+                       t.cent, t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_generic(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs,
+                                  const float *norms, const float *rnorms, int64_t n_sets, int64_t n,
+                                  float *out, hipStream_t st) {
+  const int64_t rows = n_sets * n;
+  if (rows == 0) return hipSuccess;
+  const size_t shmem = (size_t)2 * t.d * sizeof(float);
+  hipLaunchKernelGGL(k_dequant_generic, dim3((unsigned)rows), dim3(kThreads), shmem, st, codes,
+                     signs, norms, rnorms, t.d, n, t.groups, t.mse_bits, (int)(t.variant == 1),
+                     t.Pi, t.S, t.cent, t.code_row, t.sign_row, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_generic(const DeviceTables &t, const float *q, int64_t nq,
+                                 const uint8_t *codes, const uint8_t *signs, const float *norms,
+                                 const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
+                                 hipStream_t st) {
+  if (n_sets == 0 || n_keys == 0) return hipSuccess;
+  int hc_max = 4096 / t.d;  // 3 * hc * d floats of LDS <= 48 KB
+  if (hc_max < 1) hc_max = 1;
+  if (hc_max > kMaxHeads) hc_max = kMaxHeads;
+  const int64_t per_block = (int64_t)kThreads * kKeysPerThread;
+  const dim3 grid((unsigned)((n_keys + per_block - 1) / per_block), (unsigned)n_sets);
+  for (int h0 = 0; h0 < nq; h0 += hc_max) {
+    const int hc = (int)((nq - h0) < hc_max ? (nq - h0) : hc_max);
+    const size_t shmem = (size_t)3 * hc * t.d * sizeof(float);
+    hipLaunchKernelGGL(k_logits_generic, grid, dim3(kThreads), shmem, st, q, (int)nq, h0, hc,
+                       codes, signs, norms, rnorms, t.d, n_keys, t.groups, t.mse_bits,
+                       (int)(t.variant == 1), t.PiT, t.ST, t.cent, t.code_row, t.sign_row, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_pack(const uint8_t *idx, int bits, int64_t rows, int count, int64_t row_bytes,
+                       uint8_t *out, hipStream_t st) {
+  const int64_t total = rows * row_bytes;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, idx, bits,
+                     rows, count, row_bytes, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t *in, int bits, int64_t rows, int count, int64_t row_bytes,
+                         uint8_t *idx, hipStream_t st) {
+  const int64_t total = rows * (int64_t)count;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_unpack, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, in, bits,
+                     rows, count, row_bytes, idx);
+  return hipGetLastError();
+}
+
+}  // namespace tq

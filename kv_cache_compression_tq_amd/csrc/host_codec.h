@@ -1,0 +1,38 @@
+// Host-side construction of a TurboQuant codec's tables (float64, once per
+// codec; never on the hot path).
+#pragma once
+#include <cstdint>
+#include <vector>
+
+namespace tq {
+
+constexpr int kMatPi = 0;
+constexpr int kMatS = 1;
+
+// Standard normal number `elem` of the counter-based stream (seed, group, mat):
+// SplitMix64 finaliser keyed by (seed, group, mat, elem) -> two uniforms ->
+// Box–Muller.
+double gaussian(uint64_t seed, uint64_t group, int mat, uint64_t elem);
+
+// rows x cols Gaussian matrix, row-major, entry (i,j) = element i*cols+j.
+void gaussian_matrix(uint64_t seed, uint64_t group, int mat, int rows, int cols, double *out);
+
+// Orthogonal factor Q of A = QR (A: n x n row-major) with diag(R) > 0, by
+// Householder reflections.  Q is written row-major into q.
+void orthogonal_factor(int n, const double *a, double *q);
+
+// Regularised incomplete beta I_x(a, b).
+double incomplete_beta(double x, double a, double b);
+
+struct Codebook {
+  std::vector<double> centroids;   // ascending, 2^bits
+  std::vector<double> boundaries;  // midpoints, 2^bits - 1
+  double distortion = 0.0;         // d * E[(X - Q(X))^2]
+  int iterations = 0;
+};
+
+// Lloyd–Max quantizer for the post-rotation coordinate density
+// f_d(x) ∝ (1 - x^2)^((d-3)/2) on [-1, 1] with 2^bits levels.
+Codebook lloyd_max(int d, int bits);
+
+}  // namespace tq

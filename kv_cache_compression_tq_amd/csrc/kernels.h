@@ -1,0 +1,57 @@
+// Launchers of the HIP kernels (device code lives in *.hip).  Plain C++
+// signatures: device pointers, sizes and a stream.
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace tq {
+
+// Device tables of one codec (all groups concatenated, group stride d*d).
+struct DeviceTables {
+  int d = 0, groups = 0, variant = 0, mse_bits = 0;
+  int64_t code_row = 0, sign_row = 0;
+  const float *Pi = nullptr;   // [G][d][d] row-major: y = Pi x
+  const float *PiT = nullptr;  // [G][d][d] = Pi^T
+  const float *S = nullptr;    // [G][d][d] QJL projection (prod)
+  const float *ST = nullptr;   // [G][d][d] = S^T
+  const float *MT = nullptr;   // [G][d][d] = (S Pi^T)^T (prod)
+  const float *cent = nullptr; // [2^mse_bits]
+  const float *bnd = nullptr;  // [2^mse_bits - 1]
+  // d == 128 fast path: MFMA operand images (see quant128.hip)
+  const uint32_t *pi_frag = nullptr;  // [G][...] bf16 hi/lo pairs, permuted rows
+  const uint32_t *m_frag = nullptr;   // [G][...] same for M (prod)
+  const uint32_t *logit_lut = nullptr; // packed f16 decode tables for logits128
+  // positive halves of the codebook (host values, passed as launch arguments)
+  float pos_bnd[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // t_{L/2} .. t_{L-2}
+  float pos_cent[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // c_{L/2} .. c_{L-1}
+};
+
+constexpr float kQjlScale = 1.2533141373155003f;  // sqrt(pi/2)
+
+hipError_t launch_quant_generic(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
+                                int64_t n, uint8_t *codes, uint8_t *signs, float *norms,
+                                float *rnorms, hipStream_t st);
+hipError_t launch_dequant_generic(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs,
+                                  const float *norms, const float *rnorms, int64_t n_sets, int64_t n,
+                                  float *out, hipStream_t st);
+hipError_t launch_logits_generic(const DeviceTables &t, const float *q, int64_t nq,
+                                 const uint8_t *codes, const uint8_t *signs, const float *norms,
+                                 const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
+                                 hipStream_t st);
+hipError_t launch_pack(const uint8_t *idx, int bits, int64_t rows, int count, int64_t row_bytes,
+                       uint8_t *out, hipStream_t st);
+hipError_t launch_unpack(const uint8_t *in, int bits, int64_t rows, int count, int64_t row_bytes,
+                         uint8_t *idx, hipStream_t st);
+
+// d == 128 fast paths (return hipErrorNotSupported when a shape is outside
+// what they handle, so the caller can use the generic kernels).
+hipError_t launch_quant128(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
+                           int64_t n, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
+                           hipStream_t st);
+hipError_t launch_logits128(const DeviceTables &t, const float *q, int64_t nq,
+                            const uint8_t *codes, const uint8_t *signs, const float *norms,
+                            const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
+                            hipStream_t st);
+
+}  // namespace tq

@@ -1,0 +1,434 @@
+// C ABI of the TurboQuant hot path: argument validation, codec construction
+// (host, float64, once), device table upload and kernel dispatch.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <exception>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/tq.h"
+#include "fast128.h"
+#include "host_codec.h"
+#include "kernels.h"
+
+struct tq_codec {
+  int d = 0, b = 0, variant = 0, groups = 0, mse_bits = 0;
+  int device = 0;
+  void *arena = nullptr;  // one device allocation holding every table
+  tq::DeviceTables dev;
+  // host copies (float32, as stored on the device)
+  std::vector<float> h_pi, h_s, h_c, h_t;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string &msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(TQ_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int64_t row_bytes(int64_t count, int bits) {
+  const int64_t raw = (count * bits + 7) / 8;
+  return (raw + 15) / 16 * 16;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validate (d, b, variant) and return the number of mse bits.
+int check_config(int d, int b, int variant, int groups, int *mse_bits) {
+  if (d < 3 || d > 4096) return fail(TQ_EINVAL, "d must be in [3, 4096]");
+  if (groups < 1 || groups > 4096) return fail(TQ_EINVAL, "groups must be in [1, 4096]");
+  if (variant == TQ_MSE) {
+    if (b < 1 || b > 8) return fail(TQ_EINVAL, "mse needs 1 <= b <= 8");
+    *mse_bits = b;
+  } else if (variant == TQ_PROD) {
+    if (b < 1 || b > 5) return fail(TQ_EINVAL, "prod needs 1 <= b <= 5");
+    *mse_bits = b - 1;
+  } else {
+    return fail(TQ_EINVAL, "variant must be TQ_MSE or TQ_PROD");
+  }
+  return TQ_OK;
+}
+
+// Host tables of group g in float64: Pi (row-major), S, M = S Pi^T.
+void group_matrices(int d, uint64_t seed, int g, bool prod, std::vector<double> &pi,
+                    std::vector<double> &s, std::vector<double> &m) {
+  std::vector<double> gm((size_t)d * d);
+  tq::gaussian_matrix(seed, (uint64_t)g, tq::kMatPi, d, d, gm.data());
+  pi.assign((size_t)d * d, 0.0);
+  tq::orthogonal_factor(d, gm.data(), pi.data());
+  if (!prod) return;
+  s.assign((size_t)d * d, 0.0);
+  tq::gaussian_matrix(seed, (uint64_t)g, tq::kMatS, d, d, s.data());
+  m.assign((size_t)d * d, 0.0);
+  // M[i][j] = sum_k S[i][k] Pi[j][k]
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      double acc = 0.0;
+      const double *si = &s[(size_t)i * d], *pj = &pi[(size_t)j * d];
+      for (int k = 0; k < d; ++k) acc += si[k] * pj[k];
+      m[(size_t)i * d + j] = acc;
+    }
+}
+
+template <class T>
+T *carve(char *base, size_t &off, size_t count) {
+  off = (off + 255) / 256 * 256;
+  T *p = reinterpret_cast<T *>(base + off);
+  off += count * sizeof(T);
+  return p;
+}
+
+int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *out) {
+  int mse_bits = 0;
+  int st = check_config(d, b, variant, groups, &mse_bits);
+  if (st != TQ_OK) return st;
+  if (!out) return fail(TQ_EINVAL, "out is NULL");
+  const bool prod = variant == TQ_PROD;
+  const size_t dd = (size_t)d * d;
+  const int L = mse_bits > 0 ? 1 << mse_bits : 0;
+
+  auto *h = new (std::nothrow) tq_codec;
+  if (!h) return fail(TQ_ENOMEM, "host allocation failed");
+  h->d = d;
+  h->b = b;
+  h->variant = variant;
+  h->groups = groups;
+  h->mse_bits = mse_bits;
+
+  // Codebook (shared by all groups): float64 Lloyd–Max, rounded to float32.
+  if (mse_bits > 0) {
+    const tq::Codebook cb = tq::lloyd_max(d, mse_bits);
+    for (double c : cb.centroids) h->h_c.push_back((float)c);
+    for (double t : cb.boundaries) h->h_t.push_back((float)t);
+  }
+  const bool fast = tq::fast128_supported(d, mse_bits, variant);
+  const size_t rot_words = fast ? tq::fast128_rotation_words(d) : 0;
+  const size_t lut_words = fast ? tq::fast128_lut_words(mse_bits) : 0;
+
+  // Host images of every device table.
+  std::vector<float> pi_all(groups * dd), pit_all(groups * dd);
+  std::vector<float> s_all, st_all, mt_all;
+  std::vector<uint32_t> pi_img(groups * rot_words), m_img(prod ? groups * rot_words : 0);
+  if (prod) {
+    s_all.resize(groups * dd);
+    st_all.resize(groups * dd);
+    mt_all.resize(groups * dd);
+  }
+  std::vector<double> pi, s, m;
+  for (int g = 0; g < groups; ++g) {
+    group_matrices(d, seed, g, prod, pi, s, m);
+    float *P = &pi_all[g * dd], *PT = &pit_all[g * dd];
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        P[(size_t)i * d + j] = (float)pi[(size_t)i * d + j];
+        PT[(size_t)j * d + i] = (float)pi[(size_t)i * d + j];
+      }
+    if (fast) tq::fast128_build_rotation_image(pi.data(), 0, &pi_img[g * rot_words]);
+    if (prod) {
+      float *S = &s_all[g * dd], *ST = &st_all[g * dd], *MT = &mt_all[g * dd];
+      for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+          S[(size_t)i * d + j] = (float)s[(size_t)i * d + j];
+          ST[(size_t)j * d + i] = (float)s[(size_t)i * d + j];
+          MT[(size_t)j * d + i] = (float)m[(size_t)i * d + j];
+        }
+      if (fast) tq::fast128_build_rotation_image(m.data(), 1, &m_img[g * rot_words]);
+    }
+    if (g == 0) {
+      h->h_pi.assign(P, P + dd);
+      if (prod) h->h_s.assign(&s_all[0], &s_all[0] + dd);
+    }
+  }
+  std::vector<uint32_t> lut(lut_words);
+  if (fast && lut_words) tq::fast128_build_logit_lut(h->h_c.data(), mse_bits, lut.data());
+
+  // One device arena.
+  size_t off = 0;
+  char *const base0 = nullptr;
+  auto plan = [&](char *base) {
+    off = 0;
+    h->dev.Pi = carve<float>(base, off, groups * dd);
+    h->dev.PiT = carve<float>(base, off, groups * dd);
+    if (prod) {
+      h->dev.S = carve<float>(base, off, groups * dd);
+      h->dev.ST = carve<float>(base, off, groups * dd);
+      h->dev.MT = carve<float>(base, off, groups * dd);
+    }
+    h->dev.cent = carve<float>(base, off, L ? L : 1);
+    h->dev.bnd = carve<float>(base, off, L > 1 ? L - 1 : 1);
+    if (fast) {
+      h->dev.pi_frag = carve<uint32_t>(base, off, groups * rot_words);
+      if (prod) h->dev.m_frag = carve<uint32_t>(base, off, groups * rot_words);
+      if (lut_words) h->dev.logit_lut = carve<uint32_t>(base, off, lut_words);
+    }
+    return off;
+  };
+  const size_t bytes = plan(base0);
+  const char *env_fault = std::getenv("TQ_FAULT");
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipGetDevice");
+  }
+  if (env_fault && std::strcmp(env_fault, "alloc") == 0) {
+    delete h;
+    return fail(TQ_ENOMEM, "device allocation failed (TQ_FAULT=alloc)");
+  }
+  e = hipMalloc(&h->arena, bytes);
+  if (e != hipSuccess) {
+    delete h;
+    return e == hipErrorOutOfMemory ? fail(TQ_ENOMEM, "hipMalloc of the codec tables failed")
+                                    : hip_fail(e, "hipMalloc");
+  }
+  plan((char *)h->arena);
+  auto up = [&](const void *dst, const void *src, size_t n) {
+    if (n == 0 || e != hipSuccess) return;
+    e = hipMemcpy(const_cast<void *>(dst), src, n, hipMemcpyHostToDevice);
+  };
+  up(h->dev.Pi, pi_all.data(), pi_all.size() * 4);
+  up(h->dev.PiT, pit_all.data(), pit_all.size() * 4);
+  if (prod) {
+    up(h->dev.S, s_all.data(), s_all.size() * 4);
+    up(h->dev.ST, st_all.data(), st_all.size() * 4);
+    up(h->dev.MT, mt_all.data(), mt_all.size() * 4);
+  }
+  up(h->dev.cent, h->h_c.data(), h->h_c.size() * 4);
+  up(h->dev.bnd, h->h_t.data(), h->h_t.size() * 4);
+  if (fast) {
+    up(h->dev.pi_frag, pi_img.data(), pi_img.size() * 4);
+    if (prod) up(h->dev.m_frag, m_img.data(), m_img.size() * 4);
+    up(h->dev.logit_lut, lut.data(), lut.size() * 4);
+  }
+  if (e != hipSuccess) {
+    (void)hipFree(h->arena);
+    delete h;
+    return hip_fail(e, "hipMemcpy of the codec tables");
+  }
+  if (mse_bits > 0 && mse_bits <= 4) {
+    for (int k = 0; k < L / 2; ++k) h->dev.pos_cent[k] = h->h_c[L / 2 + k];
+    for (int k = 0; k + 1 < L / 2; ++k) h->dev.pos_bnd[k] = h->h_t[L / 2 + k];
+  }
+  h->dev.d = d;
+  h->dev.groups = groups;
+  h->dev.variant = variant;
+  h->dev.mse_bits = mse_bits;
+  h->dev.code_row = mse_bits > 0 ? row_bytes(d, mse_bits) : 0;
+  h->dev.sign_row = prod ? row_bytes(d, 1) : 0;
+  *out = h;
+  return TQ_OK;
+}
+
+int check_handle(tq_handle h) {
+  if (!h) return fail(TQ_EINVAL, "handle is NULL");
+  return TQ_OK;
+}
+
+int check_rows(tq_handle h, int64_t n_sets, int64_t n) {
+  if (n_sets < 0 || n < 0) return fail(TQ_EINVAL, "n_sets and n must be >= 0");
+  if (n_sets > 65535) return fail(TQ_EINVAL, "n_sets must be <= 65535");
+  if (n_sets * n > (int64_t)0x7fffffff) return fail(TQ_EINVAL, "n_sets * n must be < 2^31");
+  (void)h;
+  return TQ_OK;
+}
+
+int check_code_ptrs(tq_handle h, const void *codes, const void *signs, const void *norms,
+                    const void *rnorms, bool writing) {
+  const bool prod = h->variant == TQ_PROD;
+  if (h->mse_bits > 0 && !codes) return fail(TQ_EINVAL, "codes is NULL");
+  if (codes && !aligned16(codes)) return fail(TQ_EINVAL, "codes must be 16-byte aligned");
+  if (!norms || ((uintptr_t)norms & 3u)) return fail(TQ_EINVAL, "norms NULL or misaligned");
+  if (prod) {
+    if (!signs || !aligned16(signs)) return fail(TQ_EINVAL, "signs NULL or not 16-byte aligned");
+    if (!rnorms || ((uintptr_t)rnorms & 3u)) return fail(TQ_EINVAL, "rnorms NULL or misaligned");
+  } else if (writing && (signs || rnorms)) {
+    return fail(TQ_EINVAL, "signs/rnorms must be NULL for an mse codec");
+  }
+  return TQ_OK;
+}
+
+template <class F>
+int guarded(F f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc &) {
+    return fail(TQ_ENOMEM, "host allocation failed");
+  } catch (const std::exception &ex) {
+    return fail(TQ_EINVAL, ex.what());
+  } catch (...) {
+    return fail(TQ_EINVAL, "unknown error");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_init(int d, int b, int variant, uint64_t seed, tq_handle *out) {
+  return tq_init_groups(d, b, variant, seed, 1, out);
+}
+
+int tq_init_groups(int d, int b, int variant, uint64_t seed, int groups, tq_handle *out) {
+  g_last_error.clear();
+  return guarded([&]() -> int { return make_codec(d, b, variant, seed, groups, out); });
+}
+
+int tq_destroy(tq_handle h) {
+  if (!h) return TQ_OK;
+  if (h->arena) (void)hipFree(h->arena);
+  delete h;
+  return TQ_OK;
+}
+
+int tq_layout(tq_handle h, int64_t *code_row_bytes, int64_t *sign_row_bytes, int *mse_bits) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (code_row_bytes) *code_row_bytes = h->dev.code_row;
+  if (sign_row_bytes) *sign_row_bytes = h->dev.sign_row;
+  if (mse_bits) *mse_bits = h->mse_bits;
+  return TQ_OK;
+}
+
+int tq_quantize(tq_handle h, const void *x, int dtype, int64_t n_sets, int64_t n, void *codes,
+                void *signs, float *norms, float *rnorms, void *stream) {
+  int st = check_handle(h);
+  if (st) return st;
+  if ((st = check_rows(h, n_sets, n))) return st;
+  if (n_sets == 0 || n == 0) return TQ_OK;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_EINVAL, "dtype must be TQ_F32 or TQ_BF16");
+  if (!x || ((uintptr_t)x & (dtype == TQ_F32 ? 3u : 1u))) return fail(TQ_EINVAL, "x NULL or misaligned");
+  if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, true))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = tq::launch_quant128(h->dev, x, dtype, n_sets, n, (uint8_t *)codes,
+                                     (uint8_t *)signs, norms, rnorms, s);
+  if (e == hipErrorNotSupported)
+    e = tq::launch_quant_generic(h->dev, x, dtype, n_sets, n, (uint8_t *)codes, (uint8_t *)signs,
+                                 norms, rnorms, s);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "quantize launch");
+}
+
+int tq_dequantize(tq_handle h, const void *codes, const void *signs, const float *norms,
+                  const float *rnorms, int64_t n_sets, int64_t n, float *x_out, void *stream) {
+  int st = check_handle(h);
+  if (st) return st;
+  if ((st = check_rows(h, n_sets, n))) return st;
+  if (n_sets == 0 || n == 0) return TQ_OK;
+  if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, false))) return st;
+  if (!x_out || ((uintptr_t)x_out & 3u)) return fail(TQ_EINVAL, "x_out NULL or misaligned");
+  hipError_t e = tq::launch_dequant_generic(h->dev, (const uint8_t *)codes, (const uint8_t *)signs,
+                                            norms, rnorms, n_sets, n, x_out, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "dequantize launch");
+}
+
+int tq_logits(tq_handle h, const float *q, int64_t nq, const void *codes, const void *signs,
+              const float *norms, const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
+              void *stream) {
+  int st = check_handle(h);
+  if (st) return st;
+  if ((st = check_rows(h, n_sets, n_keys))) return st;
+  if (nq < 1 || nq > 64) return fail(TQ_EINVAL, "nq must be in [1, 64]");
+  if (n_sets == 0 || n_keys == 0) return TQ_OK;
+  if (!q || ((uintptr_t)q & 3u)) return fail(TQ_EINVAL, "q NULL or misaligned");
+  if (!out || ((uintptr_t)out & 3u)) return fail(TQ_EINVAL, "out NULL or misaligned");
+  if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, false))) return st;
+  if (n_sets * nq * n_keys > ((int64_t)1 << 40)) return fail(TQ_EINVAL, "output too large");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = tq::launch_logits128(h->dev, q, nq, (const uint8_t *)codes, (const uint8_t *)signs,
+                                      norms, rnorms, n_sets, n_keys, out, s);
+  if (e == hipErrorNotSupported)
+    e = tq::launch_logits_generic(h->dev, q, nq, (const uint8_t *)codes, (const uint8_t *)signs,
+                                  norms, rnorms, n_sets, n_keys, out, s);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "logits launch");
+}
+
+const char *tq_strerror(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_EUNSUPPORTED: return "unsupported configuration";
+    case TQ_ENOMEM: return "out of memory";
+    case TQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *tq_last_error(void) { return g_last_error.c_str(); }
+
+int tq_get_tables(tq_handle h, int g, float *Pi, float *S, float *centroids, float *bounds) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (g < 0 || g >= h->groups) return fail(TQ_EINVAL, "group out of range");
+  const size_t dd = (size_t)h->d * h->d;
+  hipError_t e = hipSuccess;
+  if (Pi) e = hipMemcpy(Pi, h->dev.Pi + g * dd, dd * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && S && h->variant == TQ_PROD)
+    e = hipMemcpy(S, h->dev.S + g * dd, dd * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && centroids && h->mse_bits > 0)
+    e = hipMemcpy(centroids, h->dev.cent, h->h_c.size() * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && bounds && h->mse_bits > 0)
+    e = hipMemcpy(bounds, h->dev.bnd, h->h_t.size() * 4, hipMemcpyDeviceToHost);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "hipMemcpy of the tables");
+}
+
+int tq_host_tables(int d, int b, int variant, uint64_t seed, int g, float *Pi, float *S,
+                   float *centroids, float *bounds) {
+  g_last_error.clear();
+  return guarded([&]() -> int {
+    int mse_bits = 0;
+    int st = check_config(d, b, variant, 1, &mse_bits);
+    if (st) return st;
+    if (g < 0) return fail(TQ_EINVAL, "group must be >= 0");
+    std::vector<double> pi, s, m;
+    group_matrices(d, seed, g, variant == TQ_PROD, pi, s, m);
+    const size_t dd = (size_t)d * d;
+    if (Pi)
+      for (size_t i = 0; i < dd; ++i) Pi[i] = (float)pi[i];
+    if (S && variant == TQ_PROD)
+      for (size_t i = 0; i < dd; ++i) S[i] = (float)s[i];
+    if (mse_bits > 0 && (centroids || bounds)) {
+      const tq::Codebook cb = tq::lloyd_max(d, mse_bits);
+      if (centroids)
+        for (size_t k = 0; k < cb.centroids.size(); ++k) centroids[k] = (float)cb.centroids[k];
+      if (bounds)
+        for (size_t k = 0; k < cb.boundaries.size(); ++k) bounds[k] = (float)cb.boundaries[k];
+    }
+    return TQ_OK;
+  });
+}
+
+int tq_pack(tq_handle h, const uint8_t *idx, int bits, int64_t rows, void *out, void *stream) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (bits < 1 || bits > 8) return fail(TQ_EINVAL, "bits must be in [1, 8]");
+  if (rows < 0) return fail(TQ_EINVAL, "rows must be >= 0");
+  if (rows == 0) return TQ_OK;
+  if (!idx || !out || !aligned16(out)) return fail(TQ_EINVAL, "idx/out NULL or out misaligned");
+  hipError_t e = tq::launch_pack(idx, bits, rows, h->d, row_bytes(h->d, bits), (uint8_t *)out,
+                                 (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "pack launch");
+}
+
+int tq_unpack(tq_handle h, const void *in, int bits, int64_t rows, uint8_t *idx, void *stream) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (bits < 1 || bits > 8) return fail(TQ_EINVAL, "bits must be in [1, 8]");
+  if (rows < 0) return fail(TQ_EINVAL, "rows must be >= 0");
+  if (rows == 0) return TQ_OK;
+  if (!idx || !in || !aligned16(in)) return fail(TQ_EINVAL, "in/idx NULL or in misaligned");
+  hipError_t e = tq::launch_unpack((const uint8_t *)in, bits, rows, h->d, row_bytes(h->d, bits),
+                                   idx, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "unpack launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/tq.h
+declares, validates arguments, and its host-built tables match the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_compression_tq_amd as tq
+from oracle import tq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "tq.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tq.lib()
+    declared = _header_functions()
+    assert len(declared) >= 13
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(tq.EXPORTED_SYMBOLS)
+
+
+def test_strerror_and_validation_without_device():
+    L = tq.lib()
+    assert L.tq_strerror(0) == b"ok"
+    assert L.tq_strerror(-1) == b"invalid argument"
+    h = ctypes.c_void_p()
+    for args in [(2, 2, 0), (5000, 2, 0), (128, 0, 0), (128, 9, 0), (128, 6, 1), (128, 2, 7)]:
+        assert L.tq_init(*args, 0, ctypes.byref(h)) == tq.TQ_EINVAL
+        assert L.tq_last_error() != b""
+    assert L.tq_init_groups(128, 2, 0, 0, 0, ctypes.byref(h)) == tq.TQ_EINVAL
+    # calls on a NULL handle are rejected before touching the device
+    assert L.tq_quantize(None, None, 0, 1, 1, None, None, None, None, None) == tq.TQ_EINVAL
+    assert L.tq_logits(None, None, 1, None, None, None, None, 1, 1, None, None) == tq.TQ_EINVAL
+    assert L.tq_destroy(None) == tq.TQ_OK
+
+
+@pytest.mark.parametrize("d,bits,variant", [(128, 4, O.MSE), (128, 4, O.PROD), (200, 2, O.PROD), (17, 3, O.MSE)])
+def test_host_tables_match_the_oracle(d, bits, variant):
+    got = tq.host_tables(d, bits, variant, seed=1234, group=3)
+    cd = O.make_codec(d, bits, variant, 1234, groups=4)
+    assert np.max(np.abs(got["Pi"] - cd.pis[3])) < 1e-6
+    if variant == O.PROD:
+        assert np.max(np.abs(got["S"] - cd.ss[3])) < 1e-6
+    if cd.mse_bits:
+        assert np.allclose(got["centroids"], cd.centroids, rtol=2e-7, atol=0)
+        assert np.allclose(got["boundaries"], cd.boundaries, rtol=2e-7, atol=0)
+
+
+def test_host_tables_large_d_lloyd_max_converges():
+    got = tq.host_tables(1536, 4, O.MSE, seed=0)
+    lm = O.lloyd_max(1536, 4)
+    assert np.allclose(got["centroids"], lm.centroids, rtol=1e-6)

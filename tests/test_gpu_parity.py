@@ -1,0 +1,337 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every expected value comes from oracle/ on the same seeded inputs; nothing the
+library computes is fed back into the oracle.  GPU codes are decoded with the
+library's own unpack (itself checked bit-exact against the oracle's packing).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_tq_amd as tq
+import workloads
+from oracle import tq_oracle as O
+from parity import check_indices, check_rows, check_signs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    torch.cuda.init()
+
+
+def _cuda(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def _bf16_round(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def _gpu_idx(codec, packed, bits):
+    """Decode the library's packed rows with the library's unpack."""
+    rows = packed.reshape(-1, packed.shape[-1]).contiguous()
+    return codec.unpack(rows, bits).cpu().numpy().astype(np.int64)
+
+
+def _oracle_sets(cd, x, fn):
+    return [fn(cd, x[s].astype(np.float64), s % cd.groups) for s in range(x.shape[0])]
+
+
+# --------------------------------------------------------------- tables ----
+def test_device_tables_equal_host_tables_and_match_oracle():
+    codec = tq.Codec(128, 4, tq.TQ_PROD, seed=77, groups=3)
+    cd = O.make_codec(128, 4, O.PROD, 77, groups=3)
+    for g in range(3):
+        dev = codec.tables(g)
+        host = tq.host_tables(128, 4, tq.TQ_PROD, 77, g)
+        for k in ("Pi", "S", "centroids", "boundaries"):
+            assert np.array_equal(dev[k], host[k]), k
+        assert np.max(np.abs(dev["Pi"] - cd.pis[g])) < 1e-6
+        assert np.max(np.abs(dev["S"] - cd.ss[g])) < 1e-6
+        assert np.allclose(dev["centroids"], cd.centroids, rtol=2e-7, atol=0)
+        p = dev["Pi"].astype(np.float64)
+        assert np.max(np.abs(p @ p.T - np.eye(128))) < 1e-6
+
+
+# ------------------------------------------------------------- packing -----
+@pytest.mark.parametrize("d", [3, 128, 200])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 8])
+def test_pack_unpack_bit_exact(d, bits):
+    codec = tq.Codec(d, 2, tq.TQ_MSE, seed=0)
+    rng = np.random.default_rng(d * 10 + bits)
+    idx = rng.integers(0, 1 << bits, (257, d)).astype(np.uint8)
+    packed = codec.pack(_cuda(idx), bits).cpu().numpy()
+    assert np.array_equal(packed, O.pack(idx, bits))
+    back = codec.unpack(_cuda(O.pack(idx, bits)), bits).cpu().numpy()
+    assert np.array_equal(back, idx)
+
+
+# ------------------------------------------------------------ quantize -----
+MSE_CASES = [
+    # d, bits, dtype, n_sets, n, groups
+    (128, 2, "f32", 1, 4096, 1),
+    (128, 4, "f32", 1, 4096, 1),
+    (128, 4, "bf16", 3, 1000, 2),
+    (128, 3, "bf16", 2, 777, 2),
+    (128, 1, "f32", 1, 95, 1),
+    (128, 2, "bf16", 1, 33, 1),
+    (200, 2, "f32", 1, 513, 1),
+    (200, 4, "bf16", 2, 300, 2),
+    (3, 2, "f32", 1, 64, 1),
+    (96, 3, "f32", 2, 100, 2),
+]
+
+
+def _inputs(d, dtype, n_sets, n, seed):
+    if d == 128 and n_sets == 1 and n == 4096:
+        x = workloads.parity_vectors()[None]
+    else:
+        x = np.random.default_rng(seed).standard_normal((n_sets, n, d)).astype(np.float32)
+        x[..., 0] *= 10.0  # an outlier channel
+    if dtype == "bf16":
+        x = _bf16_round(x)
+        xt = _cuda(x, torch.bfloat16)
+    else:
+        xt = _cuda(x)
+    return x, xt
+
+
+@pytest.mark.parametrize("d,bits,dtype,n_sets,n,groups", MSE_CASES)
+def test_quantize_mse_matches_oracle(d, bits, dtype, n_sets, n, groups):
+    x, xt = _inputs(d, dtype, n_sets, n, seed=bits * 7 + d)
+    codec = tq.Codec(d, bits, tq.TQ_MSE, seed=5, groups=groups)
+    cd = O.make_codec(d, bits, O.MSE, 5, groups=groups)
+    out = codec.quantize(xt)
+    torch.cuda.synchronize()
+    gidx = _gpu_idx(codec, out["codes"], bits).reshape(n_sets, n, d)
+    codes = out["codes"].cpu().numpy()
+    used = (d * bits + 7) // 8
+    assert not codes[..., used:].any(), "padding bytes must be zero"
+    norms = out["norms"].cpu().numpy()
+    for s, (idx, nu, y) in enumerate(_oracle_sets(cd, x, O.quantize_mse)):
+        check_indices(gidx[s], idx, y, cd.boundaries, f"set {s}")
+        assert np.allclose(norms[s], nu, rtol=1e-5)
+
+
+PROD_CASES = [
+    (128, 4, "f32", 1, 4096, 1),
+    (128, 2, "f32", 1, 4096, 1),
+    (128, 1, "f32", 1, 500, 1),
+    (128, 4, "bf16", 2, 600, 2),
+    (128, 3, "bf16", 1, 61, 1),
+    (128, 5, "f32", 1, 300, 1),
+    (200, 3, "f32", 1, 400, 1),
+    (3, 2, "f32", 1, 64, 1),
+]
+
+
+@pytest.mark.parametrize("d,bits,dtype,n_sets,n,groups", PROD_CASES)
+def test_quantize_prod_matches_oracle(d, bits, dtype, n_sets, n, groups):
+    x, xt = _inputs(d, dtype, n_sets, n, seed=bits * 11 + d)
+    codec = tq.Codec(d, bits, tq.TQ_PROD, seed=9, groups=groups)
+    cd = O.make_codec(d, bits, O.PROD, 9, groups=groups)
+    out = codec.quantize(xt)
+    torch.cuda.synchronize()
+    mb = bits - 1
+    gbits = _gpu_idx(codec, out["signs"], 1).reshape(n_sets, n, d)
+    gidx = _gpu_idx(codec, out["codes"], mb).reshape(n_sets, n, d) if mb else None
+    norms, rnorms = out["norms"].cpu().numpy(), out["rnorms"].cpu().numpy()
+    for s, res in enumerate(_oracle_sets(cd, x, O.quantize_prod)):
+        same = np.ones(n, bool)
+        if mb:
+            check_indices(gidx[s], res["idx"], res["y"], cd.boundaries, f"set {s}")
+            same = np.all(gidx[s] == res["idx"], axis=1)
+        assert same.mean() > 0.97
+        check_signs(gbits[s][same], O.signs_to_bits(res["signs"][same]), res["proj"][same],
+                    res["rnorms"][same], f"set {s}")
+        assert np.allclose(norms[s], res["norms"], rtol=1e-5)
+        assert np.allclose(rnorms[s][same], res["rnorms"][same], rtol=1e-4, atol=1e-6)
+
+
+def test_quantize_zero_and_tiny_vectors():
+    x = np.zeros((1, 40, 128), np.float32)
+    x[0, 1, 3] = 1e-30
+    x[0, 2, :] = 1.0
+    for variant, bits in ((tq.TQ_MSE, 4), (tq.TQ_PROD, 4), (tq.TQ_PROD, 1)):
+        codec = tq.Codec(128, bits, variant, seed=3)
+        out = codec.quantize(_cuda(x))
+        torch.cuda.synchronize()
+        mb = codec.mse_bits
+        assert out["norms"][0, 0].item() == 0.0
+        if mb:
+            idx = _gpu_idx(codec, out["codes"], mb)
+            assert np.all(idx[0] == (1 << mb) // 2 - 1)
+        if variant == tq.TQ_PROD:
+            assert out["rnorms"][0, 0].item() == 0.0
+            assert np.all(_gpu_idx(codec, out["signs"], 1)[0] == 1)
+        rec = codec.dequantize(out)
+        assert torch.all(rec[0, 0] == 0)
+
+
+def test_empty_inputs_are_noops():
+    codec = tq.Codec(128, 3, tq.TQ_PROD, seed=1)
+    x = torch.zeros((2, 0, 128), device="cuda")
+    out = codec.quantize(x)
+    assert out["norms"].numel() == 0
+    q = torch.zeros((2, 4, 128), device="cuda")
+    assert codec.logits(q, out).numel() == 0
+
+
+def test_quantize_is_deterministic():
+    x, xt = _inputs(128, "bf16", 4, 2048, seed=3)
+    codec = tq.Codec(128, 4, tq.TQ_PROD, seed=2, groups=4)
+    a = codec.quantize(xt)
+    b = codec.quantize(xt)
+    torch.cuda.synchronize()
+    for k in ("codes", "signs", "norms", "rnorms"):
+        assert torch.equal(a[k], b[k]), k
+
+
+# ------------------------------------------------- dequantize / logits -----
+def _oracle_keys(cd, x, group):
+    """Oracle codes for x, in the stored layout (float32 norms)."""
+    if cd.variant == O.MSE:
+        idx, nu, _ = O.quantize_mse(cd, x, group)
+        res = dict(idx=idx, norms=nu.astype(np.float32).astype(np.float64))
+    else:
+        r = O.quantize_prod(cd, x, group)
+        res = dict(idx=r["idx"], signs=r["signs"], norms=r["norms"].astype(np.float32).astype(np.float64),
+                   rnorms=r["rnorms"].astype(np.float32).astype(np.float64))
+    return res
+
+
+def _stored(cd, keys_per_set):
+    out = {}
+    if cd.mse_bits:
+        out["codes"] = _cuda(np.stack([O.pack(k["idx"], cd.mse_bits) for k in keys_per_set]))
+    out["norms"] = _cuda(np.stack([k["norms"] for k in keys_per_set]).astype(np.float32))
+    if cd.variant == O.PROD:
+        out["signs"] = _cuda(np.stack([O.pack(O.signs_to_bits(k["signs"]), 1) for k in keys_per_set]))
+        out["rnorms"] = _cuda(np.stack([k["rnorms"] for k in keys_per_set]).astype(np.float32))
+    return out
+
+
+DEQ_CASES = [(128, 4, O.MSE), (128, 2, O.MSE), (128, 4, O.PROD), (128, 1, O.PROD), (200, 3, O.PROD), (200, 2, O.MSE)]
+
+
+@pytest.mark.parametrize("d,bits,variant", DEQ_CASES)
+def test_dequantize_oracle_codes(d, bits, variant):
+    groups, n = 2, 700
+    x = np.random.default_rng(d + bits).standard_normal((groups, n, d))
+    cd = O.make_codec(d, bits, variant, 21, groups=groups)
+    codec = tq.Codec(d, bits, variant, seed=21, groups=groups)
+    keys = [_oracle_keys(cd, x[s], s) for s in range(groups)]
+    got = codec.dequantize(_stored(cd, keys)).cpu().numpy()
+    for s in range(groups):
+        k = keys[s]
+        if variant == O.MSE:
+            ref = O.dequantize_mse(cd, k["idx"], k["norms"], s)
+        else:
+            ref = O.dequantize_prod(cd, k["idx"], k["signs"], k["norms"], k["rnorms"], s)
+        check_rows(got[s], ref, f"dequant set {s}")
+
+
+LOGIT_CASES = [
+    # d, bits, variant, n_sets, nq, n_keys
+    (128, 4, O.PROD, 2, 4, 4096),
+    (128, 3, O.PROD, 3, 4, 1000),
+    (128, 2, O.PROD, 1, 12, 777),     # n_keys % 4 != 0 and nq > 8
+    (128, 1, O.PROD, 2, 4, 512),
+    (128, 4, O.MSE, 2, 4, 2048),
+    (128, 3, O.MSE, 1, 1, 1200),
+    (128, 5, O.PROD, 1, 3, 640),
+    (200, 4, O.PROD, 2, 4, 600),
+    (200, 2, O.MSE, 1, 5, 301),
+]
+
+
+@pytest.mark.parametrize("d,bits,variant,n_sets,nq,n_keys", LOGIT_CASES)
+def test_logits_oracle_codes(d, bits, variant, n_sets, nq, n_keys):
+    groups = min(n_sets, 2)
+    rng = np.random.default_rng(d * bits + nq)
+    x = rng.standard_normal((n_sets, n_keys, d))
+    q = rng.standard_normal((n_sets, nq, d)).astype(np.float32)
+    cd = O.make_codec(d, bits, variant, 31, groups=groups)
+    codec = tq.Codec(d, bits, variant, seed=31, groups=groups)
+    keys = [_oracle_keys(cd, x[s], s % groups) for s in range(n_sets)]
+    got = codec.logits(_cuda(q), _stored(cd, keys)).cpu().numpy()
+    for s in range(n_sets):
+        ref = O.logits_plain(cd, q[s].astype(np.float64), keys[s], s % groups)
+        check_rows(got[s], ref, f"logits set {s}")
+
+
+def test_logits_decode_config_full_size_sampled():
+    """16 batch x 8 KV heads x 131072 keys, 4 query heads per KV head, prod
+    b=4, on a synthetic packed cache; sampled keys checked against the oracle."""
+    sets, T, d = workloads.DEC_BATCH * workloads.DEC_KV_HEADS, workloads.DEC_TOKENS, workloads.DEC_DIM
+    codec = tq.Codec(d, 4, tq.TQ_PROD, seed=0, groups=workloads.DEC_KV_HEADS)
+    cd = O.make_codec(d, 4, O.PROD, 0, groups=workloads.DEC_KV_HEADS)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    codes = torch.randint(0, 256, (sets, T, codec.code_row), dtype=torch.uint8, device="cuda", generator=gen)
+    signs = torch.randint(0, 256, (sets, T, codec.sign_row), dtype=torch.uint8, device="cuda", generator=gen)
+    norms = (10.0 + torch.randn((sets, T), device="cuda", generator=gen)).float()
+    rnorms = torch.rand((sets, T), device="cuda", generator=gen) * 0.45 + 0.05
+    q = workloads.decode_queries().reshape(sets, workloads.DEC_Q_PER_KV, d)
+    out = codec.logits(_cuda(q), dict(codes=codes, signs=signs, norms=norms, rnorms=rnorms))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    for s in rng.choice(sets, 12, replace=False):
+        ks = np.sort(rng.choice(T, 300, replace=False))
+        kt = torch.from_numpy(ks).cuda()
+        keys = dict(idx=O.unpack(codes[s, kt].cpu().numpy(), 3, d),
+                    signs=O.bits_to_signs(O.unpack(signs[s, kt].cpu().numpy(), 1, d)),
+                    norms=norms[s, kt].cpu().numpy().astype(np.float64),
+                    rnorms=rnorms[s, kt].cpu().numpy().astype(np.float64))
+        ref = O.logits_fast(cd, q[s].astype(np.float64), keys, int(s) % 8)
+        check_rows(out[s][:, kt].cpu().numpy(), ref, f"set {s}")
+
+
+def test_quantize_kv_config_full_size_sampled():
+    """8 KV heads x 32768 tokens x 128 bf16 with outlier channels, mse b=4,
+    one codec group per head; sampled vectors checked against the oracle."""
+    k = workloads.kv_tensor(2)
+    codec = tq.Codec(128, 4, tq.TQ_MSE, seed=0, groups=8)
+    cd = O.make_codec(128, 4, O.MSE, 0, groups=8)
+    out = codec.quantize(k.cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    xf = k.float().numpy()
+    for h in range(8):
+        sel = np.sort(rng.choice(xf.shape[1], 512, replace=False))
+        gidx = _gpu_idx(codec, out["codes"][h, torch.from_numpy(sel).cuda()], 4)
+        idx, nu, y = O.quantize_mse(cd, xf[h, sel].astype(np.float64), h)
+        check_indices(gidx, idx, y, cd.boundaries, f"head {h}")
+        assert np.allclose(out["norms"][h].cpu().numpy()[sel], nu, rtol=1e-5)
+
+
+# --------------------------------------------------------- statistics -----
+@pytest.mark.parametrize("bits", [2, 4])
+def test_gpu_mse_distortion_matches_codebook(bits):
+    x = workloads.parity_vectors()
+    codec = tq.Codec(128, bits, tq.TQ_MSE, seed=0)
+    cd = O.make_codec(128, bits, O.MSE, 0)
+    rec = codec.dequantize(codec.quantize(_cuda(x))).cpu().numpy().astype(np.float64)
+    nu = np.linalg.norm(x.astype(np.float64), axis=1)
+    err = np.sum((rec / nu[:, None] - x / nu[:, None]) ** 2, axis=1)
+    assert abs(err.mean() - cd.distortion) < 4 * err.std() / math.sqrt(err.size)
+
+
+def test_gpu_prod_inner_products_unbiased_over_vectors():
+    x = workloads.parity_vectors()
+    q = workloads.parity_queries()[:64]
+    codec = tq.Codec(128, 3, tq.TQ_PROD, seed=0)
+    keys = codec.quantize(_cuda(x))
+    lg = codec.logits(_cuda(q)[None], keys)[0].cpu().numpy().astype(np.float64)
+    err = lg - q.astype(np.float64) @ x.astype(np.float64).T
+    # per-query mean error over 4096 keys, compared with its own spread
+    z = err.mean(axis=1) / (err.std(axis=1) / math.sqrt(x.shape[0]))
+    assert np.abs(z).max() < 5.0 and abs(z.mean()) < 5.0 / math.sqrt(z.size) * 3
