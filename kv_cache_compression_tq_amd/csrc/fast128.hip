@@ -79,28 +79,138 @@ struct QuantParams {
 };
 
 // #{k : T_k < a} over the L/2 - 1 positive scaled boundaries (sorted), by a
-// branch-free binary search.
+// branch-free binary search.  Each comparison is consumed at once (one mask
+// live at a time) and the count is built bit by bit.
 template <int MB>
-__device__ __forceinline__ int count_below(float a, const float *T) {
+__device__ __forceinline__ uint32_t count_below(float a, const float *T) {
   if constexpr (MB <= 1) {
-    return 0;
+    return 0u;
   } else if constexpr (MB == 2) {
-    return T[0] < a ? 1 : 0;
+    return T[0] < a ? 1u : 0u;
   } else if constexpr (MB == 3) {
-    const int b1 = T[1] < a;
-    const int b0 = (b1 ? T[2] : T[0]) < a;
-    return 2 * b1 + b0;
+    const bool c1 = T[1] < a;
+    uint32_t cnt = c1 ? 1u : 0u;
+    const float t = c1 ? T[2] : T[0];
+    return 2u * cnt + (t < a ? 1u : 0u);
   } else {
-    const int b2 = T[3] < a;
-    const int b1 = (b2 ? T[5] : T[1]) < a;
-    const float t = b2 ? (b1 ? T[6] : T[4]) : (b1 ? T[2] : T[0]);
-    const int b0 = t < a;
-    return 4 * b2 + 2 * b1 + b0;
+    const bool c2 = T[3] < a;
+    uint32_t cnt = c2 ? 1u : 0u;
+    const float t2 = c2 ? T[5] : T[1];
+    const float tl = c2 ? T[4] : T[0];
+    const float th = c2 ? T[6] : T[2];
+    const bool c1 = t2 < a;
+    cnt = 2u * cnt + (c1 ? 1u : 0u);
+    const float t3 = c1 ? th : tl;
+    return 2u * cnt + (t3 < a ? 1u : 0u);
+  }
+}
+
+// Bitwise select m ? a : b for an all-ones / all-zeros mask m as one
+// v_bitop3_b32 (truth table 0xCA); written as a compare + lane-mask select it
+// would put a mask in SGPRs and a wait state before each use.
+__device__ __forceinline__ float fsel(int32_t m, float a, float b) {
+  return __uint_as_float(
+      __builtin_amdgcn_bitop3_b32((uint32_t)m, __float_as_uint(a), __float_as_uint(b), 0xCA));
+}
+// (w << 1) | signbit(x)
+__device__ __forceinline__ uint32_t push_sign(uint32_t w, float x) {
+  return __builtin_amdgcn_alignbit(w, __float_as_uint(x), 31);
+}
+__device__ __forceinline__ uint32_t push_bit(uint32_t w, uint32_t x) {
+  return __builtin_amdgcn_alignbit(w, x, 31);
+}
+__device__ __forceinline__ int32_t sign_mask(float d) { return __float_as_int(d) >> 31; }
+
+// Stored word i of a lane's 32 fields when every field holds L/2 - 1 (the
+// index of y = 0): the zero vector.
+template <int MB>
+__host__ __device__ constexpr uint32_t zero_word(int i) {
+  uint32_t w = 0;
+  for (int b = 0; b < 32; ++b) {
+    const int p = 32 * i + b, bit = p % MB;
+    const uint32_t v = (1u << (MB - 1)) - 1u;
+    w |= ((v >> bit) & 1u) << b;
+  }
+  return w;
+}
+// Mask of the field MSBs inside stored word i.
+template <int MB>
+__host__ __device__ constexpr uint32_t msb_word(int i) {
+  uint32_t w = 0;
+  for (int b = 0; b < 32; ++b)
+    if ((32 * i + b) % MB == MB - 1) w |= 1u << b;
+  return w;
+}
+
+// Quantize and pack the lane's 32 rotated coordinates y[j] (j = 4 m + q,
+// coordinate 32 grp + j of its vector) against the scaled positive boundaries
+// T.  Symmetric codebook: the index is L/2 + c for y > 0 and L/2 - 1 - c
+// otherwise, c = #{k : T_k < |y|}.  Each comparison is a subtraction whose
+// sign bit is the answer; sign bits are shifted straight into the code words
+// (fields are written from the highest bit of the lane's chunk down), and the
+// flip for negative y is applied afterwards on whole words.  y = +0 takes the
+// positive branch: it lies on the middle boundary, where either neighbour is
+// within any boundary tolerance.
+template <int MB>
+__device__ __forceinline__ void quantize_pack(const f32x4 (&acc)[8], const float *T, bool zero,
+                                              uint32_t *w) {
+  if constexpr (MB == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t raw = 0;
+#pragma unroll
+      for (int jj = 7; jj >= 0; --jj) {
+        const int j = 8 * i + jj;
+        const float y = acc[j >> 2][j & 3];
+        const float a = fabsf(y);
+        const float d2 = T[3] - a;
+        const int32_t m2 = sign_mask(d2);
+        const float t2 = fsel(m2, T[5], T[1]);
+        const float tl = fsel(m2, T[4], T[0]), th = fsel(m2, T[6], T[2]);
+        const float d1 = t2 - a;
+        const float t3 = fsel(sign_mask(d1), th, tl);
+        const float d0 = t3 - a;
+        raw = push_sign(raw, y);
+        raw = push_sign(raw, d2);
+        raw = push_sign(raw, d1);
+        raw = push_sign(raw, d0);
+      }
+      // nibble [s_y, c2, c1, c0] -> [~s_y, c2^s_y, c1^s_y, c0^s_y]
+      const uint32_t sy = (raw >> 3) & 0x11111111u;
+      const uint32_t sy7 = sy | (sy << 1) | (sy << 2);
+      const uint32_t v = raw ^ sy7 ^ 0x88888888u;
+      w[i] = zero ? 0x77777777u : v;
+    }
+  } else if constexpr (MB >= 1) {
+    uint32_t ww[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) ww[i] = 0;
+    // stream bits p = MB j + k; pushed from p = 32 MB - 1 down to 0
+#pragma unroll
+    for (int j = 31; j >= 0; --j) {
+      const float y = acc[j >> 2][j & 3];
+      const float a = fabsf(y);
+      const uint32_t sy = __float_as_uint(y);
+      const int top = MB * j + MB - 1;
+      ww[top >> 5] = push_sign(ww[top >> 5], y);  // field MSB: flipped below
+      if constexpr (MB == 2) {
+        const float d0 = T[0] - a;
+        ww[(top - 1) >> 5] = push_bit(ww[(top - 1) >> 5], __float_as_uint(d0) ^ sy);
+      } else if constexpr (MB == 3) {
+        const float d1 = T[1] - a;
+        const float t = fsel(sign_mask(d1), T[2], T[0]);
+        const float d0 = t - a;
+        ww[(top - 1) >> 5] = push_bit(ww[(top - 1) >> 5], __float_as_uint(d1) ^ sy);
+        ww[(top - 2) >> 5] = push_bit(ww[(top - 2) >> 5], __float_as_uint(d0) ^ sy);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) w[i] = zero ? zero_word<MB>(i) : (ww[i] ^ msb_word<MB>(i));
   }
 }
 
 template <int MB>
-__device__ __forceinline__ float pos_centroid(int cnt, const float *C) {
+__device__ __forceinline__ float pos_centroid(uint32_t cnt, const float *C) {
   if constexpr (MB <= 1) {
     return C[0];
   } else if constexpr (MB == 2) {
@@ -129,10 +239,102 @@ __device__ __forceinline__ void store_codes(uint8_t *p, const uint32_t *w) {
   }
 }
 
-// One wave quantizes 32 vectors per iteration (two 16-column tiles); a
-// workgroup of 4 waves shares the rotation image (and the QJL image) in LDS.
+// Input fragments of one 32-vector tile: lane (col, grp) holds vectors col and
+// 16 + col, elements 32 k + 8 grp .. + 8 for K steps k (bf16 pairs, or raw
+// float32 for float32 input).
+template <bool F32IN>
+struct XRegs {
+  u32x4 v[2][4][F32IN ? 2 : 1];
+};
+
+template <bool F32IN>
+__device__ __forceinline__ void load_x(XRegs<F32IN> &r, const void *xin, int64_t set_row0, int64_t n,
+                                       int64_t v0, int col, int grp) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    int64_t v = v0 + 16 * t + col;
+    v = v < n ? v : n - 1;  // ragged tail: a valid row, results discarded
+    const int64_t row = set_row0 + v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (!F32IN) {
+        r.v[t][k][0] = *(const u32x4 *)((const uint16_t *)xin + row * D + 32 * k + 8 * grp);
+      } else {
+        const u32x4 *p = (const u32x4 *)((const float *)xin + row * D + 32 * k + 8 * grp);
+        r.v[t][k][0] = p[0];
+        r.v[t][k][1] = p[1];
+      }
+    }
+  }
+}
+
+// Rotation of one 32-vector tile: acc[t][m] = rows 16 m .. 16 m + 15 of the
+// permuted Pi (hi and lo bf16 fragments read from LDS) times column tile t.
+// K steps outermost so that 16 independent accumulator chains interleave.
+// Also returns ||x||^2 of the lane's two vectors from the Gram matrices of the
+// same fragments (the A and B layouts coincide, so one fragment serves as both
+// operands; the diagonal holds the squared norms).
+template <bool F32IN>
+__device__ __forceinline__ void rotate_tile(const XRegs<F32IN> &xr, const u32x4 *img, int frag_lane,
+                                            f32x4 (&acc)[2][8], float (&nsq)[2], int col) {
+  u32x4 bh[2][4], bl[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (!F32IN) {
+        bh[t][k] = xr.v[t][k][0];
+      } else {
+        const f32x4 a = __builtin_bit_cast(f32x4, xr.v[t][k][0]);
+        const f32x4 b = __builtin_bit_cast(f32x4, xr.v[t][k][1]);
+        const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        split8(f, bh[t][k], bl[t][k]);
+      }
+    }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int f = (m * 4 + k) * 2;
+      const u32x4 ah = img[f * kFragVec + frag_lane];
+      const u32x4 al = img[(f + 1) * kFragVec + frag_lane];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        acc[t][m] = mfma_bf16(ah, bh[t][k], acc[t][m]);
+        acc[t][m] = mfma_bf16(al, bh[t][k], acc[t][m]);
+        if constexpr (F32IN) acc[t][m] = mfma_bf16(ah, bl[t][k], acc[t][m]);
+      }
+    }
+  }
+  // G[v][v] sits in lane 16 (v/4) + v, register v%4
+  const int r = col & 3;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x4 gm = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      gm = mfma_bf16(bh[t][k], bh[t][k], gm);
+      if constexpr (F32IN) {
+        gm = mfma_bf16(bh[t][k], bl[t][k], gm);
+        gm = mfma_bf16(bl[t][k], bh[t][k], gm);
+      }
+    }
+    const float mine = r == 0 ? gm[0] : (r == 1 ? gm[1] : (r == 2 ? gm[2] : gm[3]));
+    nsq[t] = __shfl(mine, ((col >> 2) << 4) + col);
+  }
+}
+
+// One wave quantizes 32 vectors per iteration (two 16-column tiles) and
+// prefetches the next tile's input; a workgroup of 8 waves shares the rotation
+// image (and the QJL image) staged in LDS.
+constexpr int kQuantThreads = 512;
+
 template <int MB, bool PROD, bool F32IN>
-__global__ __launch_bounds__(256) void k_quant128(
+__global__ __launch_bounds__(kQuantThreads, 2) void k_quant128(
     const void *__restrict__ xin, int64_t n, int groups, const uint32_t *__restrict__ pi_img,
     const uint32_t *__restrict__ m_img, QuantParams qp, uint8_t *__restrict__ codes,
     uint8_t *__restrict__ signs, float *__restrict__ norms, float *__restrict__ rnorms) {
@@ -146,78 +348,38 @@ __global__ __launch_bounds__(256) void k_quant128(
 
   {
     const u32x4 *src = (const u32x4 *)(pi_img + (size_t)g * kImageWords);
-    for (int i = tid; i < kImageVec; i += 256) lds[i] = src[i];
+    for (int i = tid; i < kImageVec; i += kQuantThreads) lds[i] = src[i];
     if constexpr (PROD) {
       const u32x4 *srcm = (const u32x4 *)(m_img + (size_t)g * kImageWords);
-      for (int i = tid; i < kImageVec; i += 256) lds[kImageVec + i] = srcm[i];
+      for (int i = tid; i < kImageVec; i += kQuantThreads) lds[kImageVec + i] = srcm[i];
     }
   }
   __syncthreads();
 
   const int64_t ntiles = (n + 31) / 32;
   const int64_t set_row0 = (int64_t)s * n;
-  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += (int64_t)gridDim.x * 4) {
-    const int64_t v0 = tile * 32;
-    // prod: both images (128 KB) cannot live in registers; re-read them from LDS
-    // each tile (an opaque offset keeps the reads inside the loop)
+  constexpr int kWaves = kQuantThreads / 64;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  int64_t tile = (int64_t)blockIdx.x * kWaves + wave;
+  if (tile >= ntiles) return;  // no barrier follows
+
+  auto process = [&](const XRegs<F32IN> &xr, int64_t v0) {
+    // The images are re-read from LDS for every tile (an opaque offset keeps
+    // the reads inside the loop; hoisted, 64 KB of fragments would not fit in
+    // registers).
     int frag_lane = lane;
-    if constexpr (PROD) asm volatile("" : "+v"(frag_lane));
-    // ---- B operands: x[v][32 k + 8 grp + e], e = 0..7, for K steps k
-    u32x4 bx[2][4];
-    u32x4 bxl[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t v = v0 + 16 * t + col;
-      const bool ok = v < n;
-      const int64_t row = set_row0 + (ok ? v : 0);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (!F32IN) {
-          const u32x4 *p = (const u32x4 *)((const uint16_t *)xin + row * D + 32 * k + 8 * grp);
-          bx[t][k] = ok ? *p : u32x4{0, 0, 0, 0};
-        } else {
-          const f32x4 *p = (const f32x4 *)((const float *)xin + row * D + 32 * k + 8 * grp);
-          f32x4 a = ok ? p[0] : f32x4{0, 0, 0, 0}, b = ok ? p[1] : f32x4{0, 0, 0, 0};
-          const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-          split8(f, bx[t][k], bxl[t][k]);
-        }
-      }
-    }
-    // ---- rotation: acc[m][t] = rows 16m..16m+15 of the permuted Pi times x
-    f32x4 acc[8][2];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) acc[m][0] = acc[m][1] = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int f = (m * 4 + k) * 2;
-        const u32x4 ah = lds[f * kFragVec + frag_lane];
-        const u32x4 al = lds[(f + 1) * kFragVec + frag_lane];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          acc[m][t] = mfma_bf16(ah, bx[t][k], acc[m][t]);
-          acc[m][t] = mfma_bf16(al, bx[t][k], acc[m][t]);
-          if constexpr (F32IN) acc[m][t] = mfma_bf16(ah, bxl[t][k], acc[m][t]);
-        }
-      }
-    }
-    // ---- epilogue: lane holds y for coordinates 32 grp + 4 m + r of vector v
+    asm volatile("" : "+v"(frag_lane));
     u32x4 rh[2][4], rl[2][4];
     float gam2[2], nus[2];
+    f32x4 acc2[2][8];
+    float nsq2[2];
+    rotate_tile<F32IN>(xr, lds, frag_lane, acc2, nsq2, col);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      const f32x4(&acc)[8] = acc2[t];
       const int64_t v = v0 + 16 * t + col;
-      const bool ok = v < n;
-      float ss = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ss = fmaf(acc[m][t][r], acc[m][t][r], ss);
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      const float nu = sqrtf(ss);
-      const float nthr = nu > 0.f ? nu : 1.f;
+      const float nu = sqrtf(nsq2[t]);
+      const float nthr = nu > 0.f ? nu : 1.f;  // a zero vector has y = 0
       float T[NB > 0 ? NB : 1];
 #pragma unroll
       for (int k = 0; k < NB; ++k) T[k] = nthr * qp.pos_bnd[k];
@@ -226,18 +388,20 @@ __global__ __launch_bounds__(256) void k_quant128(
       for (int i = 0; i < (MB > 0 ? MB : 1); ++i) w[i] = 0;
       float res[32];
       float rs = 0.f;
+      if constexpr (!PROD) quantize_pack<MB>(acc, T, nu == 0.f, w);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
+      for (int m = 0; m < 8 && PROD; ++m) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 4 * m + r;
-          const float y = acc[m][t][r];
+        for (int q = 0; q < 4; ++q) {
+          const int j = 4 * m + q;  // coordinate 32 grp + j of the lane's vector
+          const float y = acc[m][q];
           if constexpr (MB > 0) {
+            // an exact tie with a boundary may round either way (it lies on
+            // the boundary, within any boundary tolerance)
+            const float a = fabsf(y);
             const bool pos = y > 0.f;
-            // non-positive y counts boundaries <= |y|: compare with the next float up
-            const float a = __uint_as_float((__float_as_uint(y) & 0x7fffffffu) + (pos ? 0u : 1u));
-            const int cnt = count_below<MB>(a, T);
-            const uint32_t idx = (uint32_t)(cnt ^ (pos ? L / 2 : L / 2 - 1));
+            const uint32_t cnt = count_below<MB>(a, T);
+            const uint32_t idx = cnt ^ (pos ? (uint32_t)(L / 2) : (uint32_t)(L / 2 - 1));
             const int bit = j * MB, wi = bit >> 5, sh = bit & 31;
             w[wi] |= idx << sh;
             if (sh + MB > 32) w[wi + 1] |= idx >> (32 - sh);
@@ -251,8 +415,8 @@ __global__ __launch_bounds__(256) void k_quant128(
           if constexpr (PROD) rs = fmaf(res[j], res[j], rs);
         }
       }
-      const int64_t row = set_row0 + v;
-      if (ok) {
+      if (v < n) {
+        const int64_t row = set_row0 + v;
         if constexpr (MB > 0) store_codes<MB>(codes + row * (16 * MB) + grp * (4 * MB), w);
         if (grp == 0) norms[row] = nu;
       }
@@ -266,44 +430,181 @@ __global__ __launch_bounds__(256) void k_quant128(
       }
     }
     if constexpr (PROD) {
-      // ---- QJL: p = M r (rows permuted like the rotation, K = lane chunk order)
-      f32x4 pa[8][2];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) pa[m][0] = pa[m][1] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int f = (m * 4 + k) * 2;
-          const u32x4 ah = lds[kImageVec + f * kFragVec + frag_lane];
-          const u32x4 al = lds[kImageVec + (f + 1) * kFragVec + frag_lane];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            pa[m][t] = mfma_bf16(ah, rh[t][k], pa[m][t]);
-            pa[m][t] = mfma_bf16(ah, rl[t][k], pa[m][t]);
-            pa[m][t] = mfma_bf16(al, rh[t][k], pa[m][t]);
-          }
-        }
-      }
+      // QJL: p = M r (rows permuted like the rotation, K in lane-chunk order)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int64_t v = v0 + 16 * t + col;
-        if (v >= n) continue;
         uint32_t bits = 0;
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 8; ++m) {
+          f32x4 pa = {0, 0, 0, 0};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) bits |= (pa[m][t][r] >= 0.f ? 1u : 0u) << (4 * m + r);
-        const int64_t row = set_row0 + v;
-        ((uint32_t *)(signs + row * 16))[grp] = bits;
-        if (grp == 0) rnorms[row] = nus[t] > 0.f ? sqrtf(gam2[t]) / nus[t] : 0.f;
+          for (int k = 0; k < 4; ++k) {
+            const int f = (m * 4 + k) * 2;
+            const u32x4 ah = lds[kImageVec + f * kFragVec + frag_lane];
+            const u32x4 al = lds[kImageVec + (f + 1) * kFragVec + frag_lane];
+            pa = mfma_bf16(ah, rh[t][k], pa);
+            pa = mfma_bf16(ah, rl[t][k], pa);
+            pa = mfma_bf16(al, rh[t][k], pa);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bits |= (pa[q] >= 0.f ? 1u : 0u) << (4 * m + q);
+        }
+        if (v < n) {
+          const int64_t row = set_row0 + v;
+          ((uint32_t *)(signs + row * 16))[grp] = bits;
+          if (grp == 0) rnorms[row] = nus[t] > 0.f ? sqrtf(gam2[t]) / nus[t] : 0.f;
+        }
       }
+    }
+  };
+
+  if constexpr (F32IN) {
+    // float32 input (not the bandwidth-critical path): no prefetch
+    XRegs<F32IN> xr;
+    for (; tile < ntiles; tile += stride) {
+      load_x<F32IN>(xr, xin, set_row0, n, tile * 32, col, grp);
+      process(xr, tile * 32);
+    }
+  } else {
+    // the next tile's input is loaded unconditionally (past the end it
+    // re-reads the current one) so no branch sits between load and use
+    XRegs<F32IN> xa, xb;
+    load_x<F32IN>(xa, xin, set_row0, n, tile * 32, col, grp);
+    while (true) {
+      int64_t nxt = tile + stride;
+      bool more = nxt < ntiles;
+      load_x<F32IN>(xb, xin, set_row0, n, (more ? nxt : tile) * 32, col, grp);
+      process(xa, tile * 32);
+      tile = nxt;
+      if (!more) break;
+      nxt = tile + stride;
+      more = nxt < ntiles;
+      load_x<F32IN>(xa, xin, set_row0, n, (more ? nxt : tile) * 32, col, grp);
+      process(xb, tile * 32);
+      tile = nxt;
+      if (!more) break;
     }
   }
 }
 
 // ---------------------------------------------------------------- logits --
 constexpr int kLogitTiles = 4;  // 16-key tiles per wave iteration
+
+// Per-wave registers of KT 16-key tiles: lane (col, grp) holds key col of each
+// tile -- code words of its 32 coordinates, its sign word -- and the norms of
+// accumulator rows 4 grp .. 4 grp + 3.
+template <int CW>
+struct KeyRegs {
+  uint32_t cw[kLogitTiles][CW > 0 ? CW : 1];
+  uint32_t sw[kLogitTiles];
+  f32x4 nv[kLogitTiles], gv[kLogitTiles];
+};
+
+template <int CW>
+__device__ __forceinline__ void load_codes(uint32_t *w, const uint8_t *p) {
+  if constexpr (CW == 1) {
+    w[0] = *(const uint32_t *)p;
+  } else if constexpr (CW == 2) {
+    const u32x2 v = *(const u32x2 *)p;
+    w[0] = v[0];
+    w[1] = v[1];
+  } else if constexpr (CW == 3) {
+    const u32x3 v = *(const u32x3 *)p;
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+  } else if constexpr (CW == 4) {
+    const u32x4 v = *(const u32x4 *)p;
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+    w[3] = v[3];
+  }
+}
+
+template <int CW, bool PROD, int KT>
+__device__ __forceinline__ void load_full(KeyRegs<CW> &r, int64_t t0, int col, const uint8_t *cbase,
+                                          const uint8_t *sbase, const float *nbase,
+                                          const float *gbase) {
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+    const int64_t key = t0 + 16 * u + col;
+    if constexpr (CW > 0) load_codes<CW>(r.cw[u], cbase + key * (16 * CW));
+    if constexpr (PROD) r.sw[u] = *(const uint32_t *)(sbase + key * 16);
+    r.nv[u] = *(const f32x4 *)(nbase + t0 + 16 * u);
+    if constexpr (PROD) r.gv[u] = *(const f32x4 *)(gbase + t0 + 16 * u);
+  }
+}
+
+template <int CW, bool PROD, int KT>
+__device__ __forceinline__ void load_tail(KeyRegs<CW> &r, int64_t t0, int64_t kend, int col, int grp,
+                                          const uint8_t *cbase, const uint8_t *sbase,
+                                          const float *nbase, const float *gbase) {
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+    const int64_t key = t0 + 16 * u + col;
+    const int64_t k = key < kend ? key : t0;  // t0 < kend: always a valid key
+    if constexpr (CW > 0) load_codes<CW>(r.cw[u], cbase + k * (16 * CW));
+    if constexpr (PROD) r.sw[u] = *(const uint32_t *)(sbase + k * 16);
+    const int64_t r0 = t0 + 16 * u + 4 * grp;  // row of nbase[0] relative to this lane
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = r0 + q < kend;
+      r.nv[u][q] = ok ? nbase[t0 + 16 * u + q] : 0.f;
+      if constexpr (PROD) r.gv[u][q] = ok ? gbase[t0 + 16 * u + q] : 0.f;
+    }
+  }
+}
+
+// Score one 16-key tile: decode through the LDS tables into f16 A operands,
+// one MFMA per 32 coordinates (hi and lo centroid parts), one per 32 signs,
+// then combine the hi/lo query columns and scale by the norms.
+template <int MB, bool PROD>
+__device__ __forceinline__ f32x4 score_tile(const KeyRegs<MB> &r, int u, const u32x4 *bq,
+                                            const u32x4 *bp, const uint32_t *t_hi,
+                                            const uint32_t *t_lo, const u32x2 *t_sg, float kscale) {
+  constexpr int P = MB > 0 ? 1 << (2 * MB) : 0;
+  f32x4 cm = {0, 0, 0, 0}, cq = {0, 0, 0, 0};
+  if constexpr (MB > 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x4 ah, al;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pr = 4 * k + i;  // pair of coordinates, 2 MB bits
+        const int bit = pr * 2 * MB, wi = bit >> 5, sh = bit & 31;
+        uint32_t fld;
+        if (sh + 2 * MB <= 32)
+          fld = (r.cw[u][wi] >> sh) & (uint32_t)(P - 1);
+        else
+          fld = __builtin_amdgcn_alignbit(r.cw[u][wi + 1], r.cw[u][wi], sh) & (uint32_t)(P - 1);
+        ah[i] = t_hi[fld];
+        al[i] = t_lo[fld];
+      }
+      cm = mfma_f16(ah, bq[k], cm);
+      cm = mfma_f16(al, bq[k], cm);
+    }
+  }
+  if constexpr (PROD) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t byte = (r.sw[u] >> (8 * k)) & 0xffu;
+      const u32x2 lo = t_sg[byte & 15u], hi = t_sg[byte >> 4];
+      const u32x4 as = {lo[0], lo[1], hi[0], hi[1]};
+      cq = mfma_f16(as, bp[k], cq);
+    }
+  }
+  f32x4 res;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v = cm[q];
+    if constexpr (PROD) v = fmaf(kscale * r.gv[u][q], cq[q], v);
+    const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+    res[q] = (v + o) * r.nv[u][q];
+  }
+  return res;
+}
 
 template <int MB, bool PROD>
 __global__ __launch_bounds__(256) void k_logits128(
@@ -381,102 +682,52 @@ __global__ __launch_bounds__(256) void k_logits128(
   const int64_t srow = (int64_t)s * n_keys;
   const bool writer = col < hc;
   float *obase = out + ((int64_t)s * nq + h0 + (col & 7)) * n_keys;
+  const uint8_t *cbase = MB > 0 ? codes + srow * (16 * CW) + grp * (4 * CW) : nullptr;
+  const uint8_t *sbase = PROD ? signs + srow * 16 + grp * 4 : nullptr;
+  const float *nbase = norms + srow + 4 * grp;
+  const float *gbase = PROD ? rnorms + srow + 4 * grp : nullptr;
 
-  for (int64_t t0 = kbeg + (int64_t)wave * 16 * kLogitTiles; t0 < kend; t0 += 4 * 16 * kLogitTiles) {
-    uint32_t cw[kLogitTiles][CW > 0 ? CW : 1];
-    uint32_t sw[kLogitTiles];
-    f32x4 nv[kLogitTiles], gv[kLogitTiles];
+  constexpr int KT = kLogitTiles;
+  constexpr int W = 16 * KT;  // keys per wave iteration
+  KeyRegs<CW> ra, rb;  // ping-pong: one set is scored while the other loads
+  int64_t t0 = kbeg + (int64_t)wave * W;
+  auto score_store = [&](const KeyRegs<CW> &r, int64_t tb) {
 #pragma unroll
-    for (int u = 0; u < kLogitTiles; ++u) {
-      const int64_t tb = t0 + 16 * u;
-      const int64_t key = tb + col;
-      const bool ok = key < kend;
-      const int64_t row = srow + (ok ? key : kbeg);
-      if constexpr (CW == 1) cw[u][0] = *(const uint32_t *)(codes + row * 16 + grp * 4);
-      if constexpr (CW == 2) {
-        const u32x2 v = *(const u32x2 *)(codes + row * 32 + grp * 8);
-        cw[u][0] = v[0];
-        cw[u][1] = v[1];
-      }
-      if constexpr (CW == 3) {
-        const u32x3 v = *(const u32x3 *)(codes + row * 48 + grp * 12);
-        cw[u][0] = v[0];
-        cw[u][1] = v[1];
-        cw[u][2] = v[2];
-      }
-      if constexpr (CW == 4) {
-        const u32x4 v = *(const u32x4 *)(codes + row * 64 + grp * 16);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) cw[u][i] = v[i];
-      }
-      if constexpr (PROD) sw[u] = *(const uint32_t *)(signs + row * 16 + grp * 4);
-      // norms of the accumulator rows 4 grp .. 4 grp + 3 of this tile
-      const int64_t r0 = tb + 4 * grp;
-      if (r0 + 3 < kend) {
-        nv[u] = *(const f32x4 *)(norms + srow + r0);
-        if constexpr (PROD) gv[u] = *(const f32x4 *)(rnorms + srow + r0);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool okr = r0 + r < kend;
-          nv[u][r] = okr ? norms[srow + r0 + r] : 0.f;
-          if constexpr (PROD) gv[u][r] = okr ? rnorms[srow + r0 + r] : 0.f;
-        }
-      }
+    for (int u = 0; u < KT; ++u) {
+      const f32x4 res = score_tile<MB, PROD>(r, u, bq, bp, t_hi, t_lo, t_sg, kscale);
+      if (writer) *(f32x4 *)(obase + tb + 16 * u + 4 * grp) = res;
     }
+  };
+  if (t0 + W <= kend) {
+    load_full<CW, PROD, KT>(ra, t0, col, cbase, sbase, nbase, gbase);
+    while (true) {
+      // The prefetch is unconditional (a branch around it would make the
+      // wait-count pass wait for it): past the end it re-reads tile t0.
+      int64_t t1 = t0 + 4 * W;
+      bool more = t1 + W <= kend;
+      load_full<CW, PROD, KT>(rb, more ? t1 : t0, col, cbase, sbase, nbase, gbase);
+      score_store(ra, t0);
+      t0 = t1;
+      if (!more) break;
+      t1 = t0 + 4 * W;
+      more = t1 + W <= kend;
+      load_full<CW, PROD, KT>(ra, more ? t1 : t0, col, cbase, sbase, nbase, gbase);
+      score_store(rb, t0);
+      t0 = t1;
+      if (!more) break;
+    }
+  }
+  KeyRegs<CW> &cur = ra;
+  if (t0 < kend) {  // ragged tail of this workgroup's range: guarded loads and stores
+    load_tail<CW, PROD, KT>(cur, t0, kend, col, grp, cbase, sbase, nbase, gbase);
 #pragma unroll
-    for (int u = 0; u < kLogitTiles; ++u) {
-      const int64_t tb = t0 + 16 * u;
-      if (tb >= kend) break;
-      f32x4 cm = {0, 0, 0, 0}, cq = {0, 0, 0, 0};
-      if constexpr (MB > 0) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          u32x4 ah, al;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // pair 4k + i of the lane's 32 coordinates: 2 MB bits
-            const int pr = 4 * k + i;
-            const int bit = pr * 2 * MB, wi = bit >> 5, sh = bit & 31;
-            uint32_t fld;
-            if (sh + 2 * MB <= 32)
-              fld = (cw[u][wi] >> sh) & (uint32_t)(P - 1);
-            else
-              fld = (uint32_t)((((uint64_t)cw[u][wi + 1] << 32) | cw[u][wi]) >> sh) & (uint32_t)(P - 1);
-            ah[i] = t_hi[fld];
-            al[i] = t_lo[fld];
-          }
-          cm = mfma_f16(ah, bq[k], cm);
-          cm = mfma_f16(al, bq[k], cm);
-        }
-      }
-      if constexpr (PROD) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t byte = (sw[u] >> (8 * k)) & 0xffu;
-          const u32x2 lo = t_sg[byte & 15u], hi = t_sg[byte >> 4];
-          const u32x4 as = {lo[0], lo[1], hi[0], hi[1]};
-          cq = mfma_f16(as, bp[k], cq);
-        }
-      }
-      // combine hi + lo columns (col, col ^ 8), scale, store
-      f32x4 res;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = cm[r];
-        if constexpr (PROD) v = fmaf(kscale * gv[u][r], cq[r], v);
-        const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
-        res[r] = (v + o) * nv[u][r];
-      }
-      const int64_t r0 = tb + 4 * grp;
+    for (int u = 0; u < KT; ++u) {
+      const f32x4 res = score_tile<MB, PROD>(cur, u, bq, bp, t_hi, t_lo, t_sg, kscale);
+      const int64_t r0 = t0 + 16 * u + 4 * grp;
       if (writer) {
-        if (r0 + 3 < kend) {
-          *(f32x4 *)(obase + r0) = res;
-        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (r0 + r < kend) obase[r0 + r] = res[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          if (r0 + r < kend) obase[r0 + r] = res[r];
       }
     }
   }
@@ -495,12 +746,12 @@ hipError_t run_quant(const DeviceTables &t, const void *x, int64_t n_sets, int64
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t ntiles = (n + 31) / 32;
-  const int64_t per_set_max = (ntiles + 3) / 4;  // at least one tile per wave
-  const int64_t target = PROD ? 256 : 512;        // one workgroup round (LDS-limited)
+  const int64_t per_set_max = (ntiles + 7) / 8;  // at least one tile per wave
+  const int64_t target = PROD ? 256 : 512;        // one to two workgroup rounds
   int64_t gx = (target + n_sets - 1) / n_sets;
   if (gx > per_set_max) gx = per_set_max;
   if (gx < 1) gx = 1;
-  hipLaunchKernelGGL((k_quant128<MB, PROD, F32IN>), dim3((unsigned)gx, (unsigned)n_sets), dim3(256),
+  hipLaunchKernelGGL((k_quant128<MB, PROD, F32IN>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kQuantThreads),
                      lds, st, x, n, t.groups, t.pi_frag, t.m_frag, qp, codes, signs, norms, rnorms);
   return hipGetLastError();
 }

@@ -319,7 +319,7 @@ def test_gpu_mse_distortion_matches_codebook(bits):
     x = workloads.parity_vectors()
     codec = tq.Codec(128, bits, tq.TQ_MSE, seed=0)
     cd = O.make_codec(128, bits, O.MSE, 0)
-    rec = codec.dequantize(codec.quantize(_cuda(x))).cpu().numpy().astype(np.float64)
+    rec = codec.dequantize(codec.quantize(_cuda(x))).cpu().numpy()[0].astype(np.float64)
     nu = np.linalg.norm(x.astype(np.float64), axis=1)
     err = np.sum((rec / nu[:, None] - x / nu[:, None]) ** 2, axis=1)
     assert abs(err.mean() - cd.distortion) < 4 * err.std() / math.sqrt(err.size)
