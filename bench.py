@@ -34,6 +34,8 @@ def _parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-logits", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run one plain 1 GiB device-to-device copy (counter calibration)")
     return p.parse_args()
 
 
@@ -167,6 +169,13 @@ def main():
     q3 = quantize_b3_phase(torch, tq, workloads, qp["x"], args.steps, args.warmup)
     lp = None if args.skip_logits else logits_phase(torch, tq, workloads, args.steps, args.warmup)
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, qp["x"])
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)   # plain elementwise kernel: reads and writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     value = qp["vectors"] / (qp["wall_ms"] * 1e-3)
     line = {

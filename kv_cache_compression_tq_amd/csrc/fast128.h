@@ -20,8 +20,11 @@ size_t fast128_rotation_words(int d);
 // projection of the residual).
 void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out);
 
-// Words of the logits decode tables for `mse_bits` (pair LUTs + sign LUT).
+// Words of the logits decode tables for `mse_bits` (pair LUT + sign LUT).
+// The pair LUT holds f16 values of alpha * c, with alpha > 0 chosen so that
+// every scaled centroid rounds to f16 with the smallest relative error; the
+// kernel divides the rotated query by alpha instead.  Returns 1 / alpha.
 size_t fast128_lut_words(int mse_bits);
-void fast128_build_logit_lut(const float *centroids, int mse_bits, uint32_t *out);
+float fast128_build_logit_lut(const float *centroids, int mse_bits, uint32_t *out);
 
 }  // namespace tq

@@ -19,6 +19,7 @@
 // rows 4*(l/16) .. 4*(l/16)+3.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 
 #include "fast128.h"
@@ -557,50 +558,66 @@ __device__ __forceinline__ void load_tail(KeyRegs<CW> &r, int64_t t0, int64_t ke
   }
 }
 
-// Score one 16-key tile: decode through the LDS tables into f16 A operands,
-// one MFMA per 32 coordinates (hi and lo centroid parts), one per 32 signs,
-// then combine the hi/lo query columns and scale by the norms.
+// Decode-table geometry (must match the host builder): G codes per lookup.
+template <int MB>
+struct LutGeom {
+  static constexpr int G = MB == 1 ? 8 : (MB == 4 ? 2 : 4);
+  static constexpr int W = G * MB;                       // index bits
+  static constexpr int ENTRIES = MB > 0 ? 1 << W : 1;
+  static constexpr int WORDS = MB > 0 ? ENTRIES * G / 2 : 1;
+};
+
+// Score one 16-key tile: each LDS lookup decodes G codes (or 8 signs) straight
+// into f16 A-operand registers; one MFMA per 32 coordinates of codes, one per
+// 32 signs.  Then add the hi and lo query columns (lanes col and col ^ 8) and
+// scale by the norms.  The QJL scale sqrt(pi/2)/d is folded into the
+// projected query.
 template <int MB, bool PROD>
 __device__ __forceinline__ f32x4 score_tile(const KeyRegs<MB> &r, int u, const u32x4 *bq,
-                                            const u32x4 *bp, const uint32_t *t_hi,
-                                            const uint32_t *t_lo, const u32x2 *t_sg, float kscale) {
-  constexpr int P = MB > 0 ? 1 << (2 * MB) : 0;
+                                            const u32x4 *bp, const uint32_t *t_code,
+                                            const u32x4 *t_sg) {
+  using GM = LutGeom<MB>;
+  constexpr int G = GM::G, W = GM::W;
   f32x4 cm = {0, 0, 0, 0}, cq = {0, 0, 0, 0};
   if constexpr (MB > 0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      u32x4 ah, al;
+      u32x4 ah;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pr = 4 * k + i;  // pair of coordinates, 2 MB bits
-        const int bit = pr * 2 * MB, wi = bit >> 5, sh = bit & 31;
+      for (int jj = 0; jj < 8 / G; ++jj) {
+        const int j = k * (8 / G) + jj;  // group j of the lane's 32 coordinates
+        const int bit = j * W, wi = bit >> 5, sh = bit & 31;
         uint32_t fld;
-        if (sh + 2 * MB <= 32)
-          fld = (r.cw[u][wi] >> sh) & (uint32_t)(P - 1);
+        if (sh + W <= 32)
+          fld = (r.cw[u][wi] >> sh) & (uint32_t)((1 << W) - 1);
         else
-          fld = __builtin_amdgcn_alignbit(r.cw[u][wi + 1], r.cw[u][wi], sh) & (uint32_t)(P - 1);
-        ah[i] = t_hi[fld];
-        al[i] = t_lo[fld];
+          fld = __builtin_amdgcn_alignbit(r.cw[u][wi + 1], r.cw[u][wi], sh) & (uint32_t)((1 << W) - 1);
+        if constexpr (G == 2) {
+          ah[jj] = t_code[fld];
+        } else if constexpr (G == 4) {
+          const u32x2 v = ((const u32x2 *)t_code)[fld];
+          ah[2 * jj] = v[0];
+          ah[2 * jj + 1] = v[1];
+        } else {
+          ah = ((const u32x4 *)t_code)[fld];
+        }
       }
       cm = mfma_f16(ah, bq[k], cm);
-      cm = mfma_f16(al, bq[k], cm);
     }
   }
   if constexpr (PROD) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t byte = (r.sw[u] >> (8 * k)) & 0xffu;
-      const u32x2 lo = t_sg[byte & 15u], hi = t_sg[byte >> 4];
-      const u32x4 as = {lo[0], lo[1], hi[0], hi[1]};
-      cq = mfma_f16(as, bp[k], cq);
+      cq = mfma_f16(t_sg[byte], bp[k], cq);
     }
   }
   f32x4 res;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float v = cm[q];
-    if constexpr (PROD) v = fmaf(kscale * r.gv[u][q], cq[q], v);
-    const float o = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));
+    if constexpr (PROD) v = fmaf(r.gv[u][q], cq[q], v);
+    const float o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, true));
     res[q] = (v + o) * r.nv[u][q];
   }
   return res;
@@ -611,15 +628,15 @@ __global__ __launch_bounds__(256) void k_logits128(
     const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ signs, const float *__restrict__ norms,
     const float *__restrict__ rnorms, int64_t n_keys, int groups, const float *__restrict__ PiT,
-    const float *__restrict__ ST, const uint32_t *__restrict__ lut, int64_t keys_per_wg,
-    float *__restrict__ out) {
-  constexpr int P = MB > 0 ? 1 << (2 * MB) : 0;  // pair-table entries
-  constexpr int CW = MB;                         // code words per lane (32 coords)
+    const float *__restrict__ ST, const uint32_t *__restrict__ lut, float lut_inv_scale,
+    int64_t keys_per_wg, float *__restrict__ out) {
+  constexpr int CW = MB;  // code words per lane (32 coordinates)
+  constexpr int LW = LutGeom<MB>::WORDS;
   __shared__ float qs[8 * D];
   __shared__ float qt[8 * D];
   __shared__ float pp[8 * D];
-  __shared__ uint32_t t_hi[P > 0 ? P : 1], t_lo[P > 0 ? P : 1];
-  __shared__ u32x2 t_sg[16];
+  __shared__ __attribute__((aligned(16))) uint32_t t_code[LW];
+  __shared__ u32x4 t_sg[256];
 
   const int s = blockIdx.y;
   const int g = s % groups;
@@ -630,11 +647,9 @@ __global__ __launch_bounds__(256) void k_logits128(
     const int h = e / D;
     qs[e] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + (e % D)] : 0.f;
   }
-  for (int e = tid; e < P; e += 256) {
-    t_hi[e] = lut[e];
-    t_lo[e] = lut[P + e];
-  }
-  if (PROD && tid < 16) t_sg[tid] = u32x2{lut[2 * P + 2 * tid], lut[2 * P + 2 * tid + 1]};
+  if constexpr (MB > 0)
+    for (int e = tid; e < LW / 4; e += 256) ((u32x4 *)t_code)[e] = ((const u32x4 *)lut)[e];
+  if constexpr (PROD) t_sg[tid] = ((const u32x4 *)(lut + (MB > 0 ? LW : 0)))[tid];
   __syncthreads();
   {
     // rotate (threads 0..127) and project (threads 128..255) every head once
@@ -663,8 +678,10 @@ __global__ __launch_bounds__(256) void k_logits128(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int c = 32 * grp + 8 * k + 2 * i;
-        float a0 = qt[h * D + c], a1 = qt[h * D + c + 1];
-        float p0 = pp[h * D + c], p1 = pp[h * D + c + 1];
+        // the centroid table holds alpha * c; the QJL scale sqrt(pi/2)/d
+        // multiplies every sign term
+        float a0 = qt[h * D + c] * lut_inv_scale, a1 = qt[h * D + c + 1] * lut_inv_scale;
+        float p0 = pp[h * D + c] * kQjlScale / (float)D, p1 = pp[h * D + c + 1] * kQjlScale / (float)D;
         if (part) {
           a0 -= (float)(_Float16)a0;
           a1 -= (float)(_Float16)a1;
@@ -676,7 +693,6 @@ __global__ __launch_bounds__(256) void k_logits128(
       }
     }
   }
-  const float kscale = kQjlScale / (float)D;
   const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
   const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
   const int64_t srow = (int64_t)s * n_keys;
@@ -694,7 +710,7 @@ __global__ __launch_bounds__(256) void k_logits128(
   auto score_store = [&](const KeyRegs<CW> &r, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
-      const f32x4 res = score_tile<MB, PROD>(r, u, bq, bp, t_hi, t_lo, t_sg, kscale);
+      const f32x4 res = score_tile<MB, PROD>(r, u, bq, bp, t_code, t_sg);
       if (writer) *(f32x4 *)(obase + tb + 16 * u + 4 * grp) = res;
     }
   };
@@ -722,7 +738,7 @@ __global__ __launch_bounds__(256) void k_logits128(
     load_tail<CW, PROD, KT>(cur, t0, kend, col, grp, cbase, sbase, nbase, gbase);
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
-      const f32x4 res = score_tile<MB, PROD>(cur, u, bq, bp, t_hi, t_lo, t_sg, kscale);
+      const f32x4 res = score_tile<MB, PROD>(cur, u, bq, bp, t_code, t_sg);
       const int64_t r0 = t0 + 16 * u + 4 * grp;
       if (writer) {
 #pragma unroll
@@ -772,7 +788,7 @@ hipError_t run_logits(const DeviceTables &t, const float *q, int64_t nq, const u
     const int hc = (int)(nq - h0 < 8 ? nq - h0 : 8);
     hipLaunchKernelGGL((k_logits128<MB, PROD>), dim3((unsigned)gx, (unsigned)n_sets), dim3(256), 0,
                        st, q, (int)nq, (int)h0, hc, codes, signs, norms, rnorms, n_keys, t.groups,
-                       t.PiT, t.ST, t.logit_lut, kpw, out);
+                       t.PiT, t.ST, t.logit_lut, t.lut_inv_scale, kpw, out);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -822,36 +838,67 @@ void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out)
       }
 }
 
+// Decode-table geometry: one lookup turns G codes of `mse_bits` bits (one
+// index of G * mse_bits <= 12 bits) into G f16 values.
+static int lut_group(int mse_bits) { return mse_bits == 1 ? 8 : (mse_bits == 4 ? 2 : 4); }
+
 size_t fast128_lut_words(int mse_bits) {
-  const size_t P = mse_bits > 0 ? (size_t)1 << (2 * mse_bits) : 0;
-  return 2 * P + 32;
+  size_t code_words = 0;
+  if (mse_bits > 0) {
+    const int G = lut_group(mse_bits);
+    code_words = ((size_t)1 << (G * mse_bits)) * (size_t)G / 2;
+  }
+  return code_words + 256 * 4;  // + sign table: byte -> 8 x (+1 / -1)
 }
 
-void fast128_build_logit_lut(const float *cent, int mse_bits, uint32_t *out) {
-  const int P = mse_bits > 0 ? 1 << (2 * mse_bits) : 0;
+float fast128_build_logit_lut(const float *cent, int mse_bits, uint32_t *out) {
+  const int L = mse_bits > 0 ? 1 << mse_bits : 0;
   auto h16 = [](float f) {
     _Float16 h = (_Float16)f;
     uint16_t u;
     memcpy(&u, &h, 2);
     return u;
   };
-  auto f16val = [](float f) { return (float)(_Float16)f; };
-  for (int e = 0; e < P; ++e) {
-    const int a = e & ((1 << mse_bits) - 1), b = e >> mse_bits;
-    out[e] = (uint32_t)h16(cent[a]) | ((uint32_t)h16(cent[b]) << 16);
-    out[P + e] = (uint32_t)h16(cent[a] - f16val(cent[a])) |
-                 ((uint32_t)h16(cent[b] - f16val(cent[b])) << 16);
+  // alpha in [1, 2): minimise the largest relative f16 rounding error of
+  // alpha * |c_k| (the codebook is symmetric: the positive half suffices)
+  float alpha = 1.f;
+  if (L > 0) {
+    double best = 1e30;
+    for (int i = 0; i < (1 << 18); ++i) {
+      const float a = 1.f + (float)i / (float)(1 << 18);
+      double worst = 0.0;
+      for (int k = L / 2; k < L; ++k) {
+        const float v = a * cent[k];
+        const double e = std::fabs((double)(float)(_Float16)v - (double)v) / (double)v;
+        if (e > worst) worst = e;
+      }
+      if (worst < best) {
+        best = worst;
+        alpha = a;
+      }
+    }
   }
-  for (int nib = 0; nib < 16; ++nib)
-    for (int w = 0; w < 2; ++w) {
+  size_t w = 0;
+  if (mse_bits > 0) {
+    const int G = lut_group(mse_bits);
+    const int entries = 1 << (G * mse_bits);
+    for (int e = 0; e < entries; ++e)
+      for (int h = 0; h < G; h += 2) {
+        const int i0 = (e >> (h * mse_bits)) & (L - 1);
+        const int i1 = (e >> ((h + 1) * mse_bits)) & (L - 1);
+        out[w++] = (uint32_t)h16(alpha * cent[i0]) | ((uint32_t)h16(alpha * cent[i1]) << 16);
+      }
+  }
+  for (int byte = 0; byte < 256; ++byte)
+    for (int h = 0; h < 8; h += 2) {
       uint32_t v = 0;
       for (int half = 0; half < 2; ++half) {
-        const int e = 2 * w + half;
-        const uint16_t h = ((nib >> e) & 1) ? 0x3C00u : 0xBC00u;  // +1 / -1
-        v |= (uint32_t)h << (16 * half);
+        const uint16_t x = ((byte >> (h + half)) & 1) ? 0x3C00u : 0xBC00u;  // +1 / -1
+        v |= (uint32_t)x << (16 * half);
       }
-      out[2 * P + 2 * nib + w] = v;
+      out[w++] = v;
     }
+  return 1.f / alpha;
 }
 
 hipError_t launch_quant128(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,

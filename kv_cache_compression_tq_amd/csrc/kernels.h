@@ -22,6 +22,7 @@ struct DeviceTables {
   const uint32_t *pi_frag = nullptr;  // [G][...] bf16 hi/lo pairs, permuted rows
   const uint32_t *m_frag = nullptr;   // [G][...] same for M (prod)
   const uint32_t *logit_lut = nullptr; // packed f16 decode tables for logits128
+  float lut_inv_scale = 1.f;           // 1 / alpha of the f16 centroid table
   // positive halves of the codebook (host values, passed as launch arguments)
   float pos_bnd[8] = {0, 0, 0, 0, 0, 0, 0, 0};   // t_{L/2} .. t_{L-2}
   float pos_cent[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // c_{L/2} .. c_{L-1}

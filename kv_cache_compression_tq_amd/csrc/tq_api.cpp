@@ -152,7 +152,8 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     }
   }
   std::vector<uint32_t> lut(lut_words);
-  if (fast && lut_words) tq::fast128_build_logit_lut(h->h_c.data(), mse_bits, lut.data());
+  float lut_inv_scale = 1.f;
+  if (fast && lut_words) lut_inv_scale = tq::fast128_build_logit_lut(h->h_c.data(), mse_bits, lut.data());
 
   // One device arena.
   size_t off = 0;
@@ -220,6 +221,7 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     for (int k = 0; k < L / 2; ++k) h->dev.pos_cent[k] = h->h_c[L / 2 + k];
     for (int k = 0; k + 1 < L / 2; ++k) h->dev.pos_bnd[k] = h->h_t[L / 2 + k];
   }
+  h->dev.lut_inv_scale = lut_inv_scale;
   h->dev.d = d;
   h->dev.groups = groups;
   h->dev.variant = variant;
