@@ -311,8 +311,8 @@ __device__ __forceinline__ void rotate_tile(const XRegs<F32IN> &xr, const u32x4 
       }
     }
   }
-  // G[v][v] sits in lane 16 (v/4) + v, register v%4
-  const int r = col & 3;
+  // G[v][v] sits in lane 16 (v/4) + v, register v%4 (selected without branches)
+  const int32_t m0 = -(col & 1), m1 = -((col >> 1) & 1);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     f32x4 gm = {0, 0, 0, 0};
@@ -324,7 +324,7 @@ __device__ __forceinline__ void rotate_tile(const XRegs<F32IN> &xr, const u32x4 
         gm = mfma_bf16(bl[t][k], bh[t][k], gm);
       }
     }
-    const float mine = r == 0 ? gm[0] : (r == 1 ? gm[1] : (r == 2 ? gm[2] : gm[3]));
+    const float mine = fsel(m1, fsel(m0, gm[3], gm[2]), fsel(m0, gm[1], gm[0]));
     nsq[t] = __shfl(mine, ((col >> 2) << 4) + col);
   }
 }
@@ -332,19 +332,24 @@ __device__ __forceinline__ void rotate_tile(const XRegs<F32IN> &xr, const u32x4 
 // One wave quantizes 32 vectors per iteration (two 16-column tiles) and
 // prefetches the next tile's input; a workgroup of 8 waves shares the rotation
 // image (and the QJL image) staged in LDS.
-constexpr int kQuantThreads = 512;
+// 8 waves share the rotation image (and for prod the QJL image): 64 / 128 KB
+// of LDS, 2 waves/SIMD.
+template <bool PROD>
+constexpr int quant_threads() { return 512; }
 
 template <int MB, bool PROD, bool F32IN>
-__global__ __launch_bounds__(kQuantThreads, 2) void k_quant128(
+__global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
     const void *__restrict__ xin, int64_t n, int groups, const uint32_t *__restrict__ pi_img,
     const uint32_t *__restrict__ m_img, QuantParams qp, uint8_t *__restrict__ codes,
     uint8_t *__restrict__ signs, float *__restrict__ norms, float *__restrict__ rnorms) {
   extern __shared__ u32x4 lds[];
   constexpr int L = 1 << MB;
   constexpr int NB = MB > 0 ? L / 2 - 1 : 0;  // positive boundaries
+  constexpr int kQuantThreads = quant_threads<PROD>();
   const int s = blockIdx.y;
   const int g = s % groups;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int col = lane & 15, grp = lane >> 4;
 
   {
@@ -490,16 +495,18 @@ __global__ __launch_bounds__(kQuantThreads, 2) void k_quant128(
 }
 
 // ---------------------------------------------------------------- logits --
-constexpr int kLogitTiles = 4;  // 16-key tiles per wave iteration
+constexpr int kLogitTiles = 4;     // 16-key tiles per wave iteration
+constexpr int kLogitThreads = 512;  // 8 waves share one set of decode tables
+constexpr int kLogitWaves = kLogitThreads / 64;
 
 // Per-wave registers of KT 16-key tiles: lane (col, grp) holds key col of each
-// tile -- code words of its 32 coordinates, its sign word -- and the norms of
-// accumulator rows 4 grp .. 4 grp + 3.
+// tile -- the code words of its coordinates 32 grp .. 32 grp + 31, the sign
+// word of the same projections, and the key's norm and residual norm.
 template <int CW>
 struct KeyRegs {
   uint32_t cw[kLogitTiles][CW > 0 ? CW : 1];
   uint32_t sw[kLogitTiles];
-  f32x4 nv[kLogitTiles], gv[kLogitTiles];
+  float nv[kLogitTiles], gv[kLogitTiles];
 };
 
 template <int CW>
@@ -533,13 +540,13 @@ __device__ __forceinline__ void load_full(KeyRegs<CW> &r, int64_t t0, int col, c
     const int64_t key = t0 + 16 * u + col;
     if constexpr (CW > 0) load_codes<CW>(r.cw[u], cbase + key * (16 * CW));
     if constexpr (PROD) r.sw[u] = *(const uint32_t *)(sbase + key * 16);
-    r.nv[u] = *(const f32x4 *)(nbase + t0 + 16 * u);
-    if constexpr (PROD) r.gv[u] = *(const f32x4 *)(gbase + t0 + 16 * u);
+    r.nv[u] = nbase[key];
+    if constexpr (PROD) r.gv[u] = gbase[key];
   }
 }
 
 template <int CW, bool PROD, int KT>
-__device__ __forceinline__ void load_tail(KeyRegs<CW> &r, int64_t t0, int64_t kend, int col, int grp,
+__device__ __forceinline__ void load_tail(KeyRegs<CW> &r, int64_t t0, int64_t kend, int col,
                                           const uint8_t *cbase, const uint8_t *sbase,
                                           const float *nbase, const float *gbase) {
 #pragma unroll
@@ -548,13 +555,8 @@ __device__ __forceinline__ void load_tail(KeyRegs<CW> &r, int64_t t0, int64_t ke
     const int64_t k = key < kend ? key : t0;  // t0 < kend: always a valid key
     if constexpr (CW > 0) load_codes<CW>(r.cw[u], cbase + k * (16 * CW));
     if constexpr (PROD) r.sw[u] = *(const uint32_t *)(sbase + k * 16);
-    const int64_t r0 = t0 + 16 * u + 4 * grp;  // row of nbase[0] relative to this lane
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool ok = r0 + q < kend;
-      r.nv[u][q] = ok ? nbase[t0 + 16 * u + q] : 0.f;
-      if constexpr (PROD) r.gv[u][q] = ok ? gbase[t0 + 16 * u + q] : 0.f;
-    }
+    r.nv[u] = nbase[k];
+    if constexpr (PROD) r.gv[u] = gbase[k];
   }
 }
 
@@ -567,22 +569,25 @@ struct LutGeom {
   static constexpr int WORDS = MB > 0 ? ENTRIES * G / 2 : 1;
 };
 
-// Score one 16-key tile: each LDS lookup decodes G codes (or 8 signs) straight
-// into f16 A-operand registers; one MFMA per 32 coordinates of codes, one per
-// 32 signs.  Then add the hi and lo query columns (lanes col and col ^ 8) and
-// scale by the norms.  The QJL scale sqrt(pi/2)/d is folded into the
-// projected query.
+// Score one 16-key tile.  Each LDS lookup decodes G codes (or 8 signs)
+// straight into f16 operand registers of the lane's key; the queries are the
+// A operand (row 2h + part: head h, hi or lo f16 part) and the decoded keys the
+// B operand (column = key), one MFMA per 32 coordinates of codes and one per
+// 32 signs.  The accumulator then holds, in lane (key, grp), rows 4 grp .. 4
+// grp + 3: the hi and lo parts of heads 2 grp and 2 grp + 1 for its own key.
+// Returns those two logits (norm applied).  The QJL scale sqrt(pi/2)/d is
+// folded into the projected query.
 template <int MB, bool PROD>
-__device__ __forceinline__ f32x4 score_tile(const KeyRegs<MB> &r, int u, const u32x4 *bq,
-                                            const u32x4 *bp, const uint32_t *t_code,
-                                            const u32x4 *t_sg) {
+__device__ __forceinline__ void score_tile(const KeyRegs<MB> &r, int u, const u32x4 *bq,
+                                           const u32x4 *bp, const uint32_t *t_code,
+                                           const u32x4 *t_sg, float &o0, float &o1) {
   using GM = LutGeom<MB>;
   constexpr int G = GM::G, W = GM::W;
   f32x4 cm = {0, 0, 0, 0}, cq = {0, 0, 0, 0};
   if constexpr (MB > 0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      u32x4 ah;
+      u32x4 bk;
 #pragma unroll
       for (int jj = 0; jj < 8 / G; ++jj) {
         const int j = k * (8 / G) + jj;  // group j of the lane's 32 coordinates
@@ -593,38 +598,36 @@ __device__ __forceinline__ f32x4 score_tile(const KeyRegs<MB> &r, int u, const u
         else
           fld = __builtin_amdgcn_alignbit(r.cw[u][wi + 1], r.cw[u][wi], sh) & (uint32_t)((1 << W) - 1);
         if constexpr (G == 2) {
-          ah[jj] = t_code[fld];
+          bk[jj] = t_code[fld];
         } else if constexpr (G == 4) {
           const u32x2 v = ((const u32x2 *)t_code)[fld];
-          ah[2 * jj] = v[0];
-          ah[2 * jj + 1] = v[1];
+          bk[2 * jj] = v[0];
+          bk[2 * jj + 1] = v[1];
         } else {
-          ah = ((const u32x4 *)t_code)[fld];
+          bk = ((const u32x4 *)t_code)[fld];
         }
       }
-      cm = mfma_f16(ah, bq[k], cm);
+      cm = mfma_f16(bq[k], bk, cm);
     }
   }
   if constexpr (PROD) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t byte = (r.sw[u] >> (8 * k)) & 0xffu;
-      cq = mfma_f16(t_sg[byte], bp[k], cq);
+      cq = mfma_f16(bp[k], t_sg[byte], cq);
     }
   }
-  f32x4 res;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float v = cm[q];
-    if constexpr (PROD) v = fmaf(r.gv[u][q], cq[q], v);
-    const float o = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, true));
-    res[q] = (v + o) * r.nv[u][q];
+  float v0 = cm[0] + cm[1], v1 = cm[2] + cm[3];
+  if constexpr (PROD) {
+    v0 = fmaf(r.gv[u], cq[0] + cq[1], v0);
+    v1 = fmaf(r.gv[u], cq[2] + cq[3], v1);
   }
-  return res;
+  o0 = v0 * r.nv[u];
+  o1 = v1 * r.nv[u];
 }
 
 template <int MB, bool PROD>
-__global__ __launch_bounds__(256) void k_logits128(
+__global__ __launch_bounds__(kLogitThreads, 2) void k_logits128(
     const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ signs, const float *__restrict__ norms,
     const float *__restrict__ rnorms, int64_t n_keys, int groups, const float *__restrict__ PiT,
@@ -640,21 +643,23 @@ __global__ __launch_bounds__(256) void k_logits128(
 
   const int s = blockIdx.y;
   const int g = s % groups;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
   const int col = lane & 15, grp = lane >> 4;
 
-  for (int e = tid; e < 8 * D; e += 256) {
+  for (int e = tid; e < 8 * D; e += kLogitThreads) {
     const int h = e / D;
     qs[e] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + (e % D)] : 0.f;
   }
   if constexpr (MB > 0)
-    for (int e = tid; e < LW / 4; e += 256) ((u32x4 *)t_code)[e] = ((const u32x4 *)lut)[e];
-  if constexpr (PROD) t_sg[tid] = ((const u32x4 *)(lut + (MB > 0 ? LW : 0)))[tid];
+    for (int e = tid; e < LW / 4; e += kLogitThreads) ((u32x4 *)t_code)[e] = ((const u32x4 *)lut)[e];
+  if (PROD && tid < 256) t_sg[tid] = ((const u32x4 *)(lut + (MB > 0 ? LW : 0)))[tid];
   __syncthreads();
   {
     // rotate (threads 0..127) and project (threads 128..255) every head once
     const int j = tid & 127;
-    const float *W = tid < 128 ? PiT + (size_t)g * D * D : (PROD ? ST + (size_t)g * D * D : nullptr);
+    const float *W = tid < 128 ? PiT + (size_t)g * D * D
+                               : (PROD && tid < 256 ? ST + (size_t)g * D * D : nullptr);
     if (W) {
       float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int k = 0; k < D; ++k) {
@@ -668,11 +673,11 @@ __global__ __launch_bounds__(256) void k_logits128(
     }
   }
   __syncthreads();
-  // B operands: column col = (head col & 7, part col >> 3); contraction
-  // element e of K step k is coordinate 32 grp + 8 k + e.
+  // Query operands (MFMA A): row col = (head col >> 1, part col & 1);
+  // contraction element e of K step k is coordinate 32 grp + 8 k + e.
   u32x4 bq[4], bp[4];
   {
-    const int h = col & 7, part = col >> 3;
+    const int h = col >> 1, part = col & 1;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -696,12 +701,14 @@ __global__ __launch_bounds__(256) void k_logits128(
   const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
   const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
   const int64_t srow = (int64_t)s * n_keys;
-  const bool writer = col < hc;
-  float *obase = out + ((int64_t)s * nq + h0 + (col & 7)) * n_keys;
+  const int hA = 2 * grp, hB = 2 * grp + 1;  // heads held by this lane
+  float *outA = out + ((int64_t)s * nq + h0 + hA) * n_keys;
+  float *outB = out + ((int64_t)s * nq + h0 + hB) * n_keys;
+  const bool wA = hA < hc, wB = hB < hc;
   const uint8_t *cbase = MB > 0 ? codes + srow * (16 * CW) + grp * (4 * CW) : nullptr;
   const uint8_t *sbase = PROD ? signs + srow * 16 + grp * 4 : nullptr;
-  const float *nbase = norms + srow + 4 * grp;
-  const float *gbase = PROD ? rnorms + srow + 4 * grp : nullptr;
+  const float *nbase = norms + srow;
+  const float *gbase = PROD ? rnorms + srow : nullptr;
 
   constexpr int KT = kLogitTiles;
   constexpr int W = 16 * KT;  // keys per wave iteration
@@ -710,8 +717,11 @@ __global__ __launch_bounds__(256) void k_logits128(
   auto score_store = [&](const KeyRegs<CW> &r, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
-      const f32x4 res = score_tile<MB, PROD>(r, u, bq, bp, t_code, t_sg);
-      if (writer) *(f32x4 *)(obase + tb + 16 * u + 4 * grp) = res;
+      float o0, o1;
+      score_tile<MB, PROD>(r, u, bq, bp, t_code, t_sg, o0, o1);
+      const int64_t key = tb + 16 * u + col;
+      if (wA) outA[key] = o0;
+      if (wB) outB[key] = o1;
     }
   };
   if (t0 + W <= kend) {
@@ -719,13 +729,13 @@ __global__ __launch_bounds__(256) void k_logits128(
     while (true) {
       // The prefetch is unconditional (a branch around it would make the
       // wait-count pass wait for it): past the end it re-reads tile t0.
-      int64_t t1 = t0 + 4 * W;
+      int64_t t1 = t0 + kLogitWaves * W;
       bool more = t1 + W <= kend;
       load_full<CW, PROD, KT>(rb, more ? t1 : t0, col, cbase, sbase, nbase, gbase);
       score_store(ra, t0);
       t0 = t1;
       if (!more) break;
-      t1 = t0 + 4 * W;
+      t1 = t0 + kLogitWaves * W;
       more = t1 + W <= kend;
       load_full<CW, PROD, KT>(ra, more ? t1 : t0, col, cbase, sbase, nbase, gbase);
       score_store(rb, t0);
@@ -733,17 +743,16 @@ __global__ __launch_bounds__(256) void k_logits128(
       if (!more) break;
     }
   }
-  KeyRegs<CW> &cur = ra;
   if (t0 < kend) {  // ragged tail of this workgroup's range: guarded loads and stores
-    load_tail<CW, PROD, KT>(cur, t0, kend, col, grp, cbase, sbase, nbase, gbase);
+    load_tail<CW, PROD, KT>(ra, t0, kend, col, cbase, sbase, nbase, gbase);
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
-      const f32x4 res = score_tile<MB, PROD>(cur, u, bq, bp, t_code, t_sg);
-      const int64_t r0 = t0 + 16 * u + 4 * grp;
-      if (writer) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (r0 + r < kend) obase[r0 + r] = res[r];
+      float o0, o1;
+      score_tile<MB, PROD>(ra, u, bq, bp, t_code, t_sg, o0, o1);
+      const int64_t key = t0 + 16 * u + col;
+      if (key < kend) {
+        if (wA) outA[key] = o0;
+        if (wB) outB[key] = o1;
       }
     }
   }
@@ -762,12 +771,13 @@ hipError_t run_quant(const DeviceTables &t, const void *x, int64_t n_sets, int64
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t ntiles = (n + 31) / 32;
-  const int64_t per_set_max = (ntiles + 7) / 8;  // at least one tile per wave
-  const int64_t target = PROD ? 256 : 512;        // one to two workgroup rounds
+  constexpr int threads = quant_threads<PROD>();
+  const int64_t per_set_max = (ntiles + threads / 64 - 1) / (threads / 64);  // >= 1 tile per wave
+  const int64_t target = 512;  // about two workgroup rounds
   int64_t gx = (target + n_sets - 1) / n_sets;
   if (gx > per_set_max) gx = per_set_max;
   if (gx < 1) gx = 1;
-  hipLaunchKernelGGL((k_quant128<MB, PROD, F32IN>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kQuantThreads),
+  hipLaunchKernelGGL((k_quant128<MB, PROD, F32IN>), dim3((unsigned)gx, (unsigned)n_sets), dim3(threads),
                      lds, st, x, n, t.groups, t.pi_frag, t.m_frag, qp, codes, signs, norms, rnorms);
   return hipGetLastError();
 }
@@ -776,8 +786,8 @@ template <int MB, bool PROD>
 hipError_t run_logits(const DeviceTables &t, const float *q, int64_t nq, const uint8_t *codes,
                       const uint8_t *signs, const float *norms, const float *rnorms, int64_t n_sets,
                       int64_t n_keys, float *out, hipStream_t st) {
-  const int64_t unit = 4 * 16 * kLogitTiles;  // keys per workgroup iteration
-  int64_t gx = (1024 + n_sets - 1) / n_sets;  // about one round of workgroups
+  const int64_t unit = kLogitWaves * 16 * kLogitTiles;  // keys per workgroup iteration
+  int64_t gx = (512 + n_sets - 1) / n_sets;             // about one round of workgroups
   const int64_t max_gx = (n_keys + unit - 1) / unit;
   if (gx > max_gx) gx = max_gx;
   if (gx < 1) gx = 1;
@@ -786,7 +796,7 @@ hipError_t run_logits(const DeviceTables &t, const float *q, int64_t nq, const u
   gx = (n_keys + kpw - 1) / kpw;
   for (int64_t h0 = 0; h0 < nq; h0 += 8) {
     const int hc = (int)(nq - h0 < 8 ? nq - h0 : 8);
-    hipLaunchKernelGGL((k_logits128<MB, PROD>), dim3((unsigned)gx, (unsigned)n_sets), dim3(256), 0,
+    hipLaunchKernelGGL((k_logits128<MB, PROD>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kLogitThreads), 0,
                        st, q, (int)nq, (int)h0, hc, codes, signs, norms, rnorms, n_keys, t.groups,
                        t.PiT, t.ST, t.logit_lut, t.lut_inv_scale, kpw, out);
     const hipError_t e = hipGetLastError();
@@ -922,9 +932,7 @@ hipError_t launch_logits128(const DeviceTables &t, const float *q, int64_t nq,
                             const uint8_t *codes, const uint8_t *signs, const float *norms,
                             const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
                             hipStream_t st) {
-  if (t.d != D || !t.logit_lut || t.mse_bits > 4 || (n_keys & 3) || ((uintptr_t)norms & 15u) ||
-      ((uintptr_t)out & 15u) || (rnorms && ((uintptr_t)rnorms & 15u)))
-    return hipErrorNotSupported;
+  if (t.d != D || !t.logit_lut || t.mse_bits > 4) return hipErrorNotSupported;
   const bool prod = t.variant == 1;
 #define TQ_L(MB, P) \
   if (t.mse_bits == MB && prod == P) \
