@@ -39,6 +39,26 @@ def _parse():
     return p.parse_args()
 
 
+def counted_traffic(profile):
+    """HBM bytes per launch from a committed counter summary under profiles/
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel
+    sources have changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if line.startswith(("traffic_bytes_per_launch: ", "kernel_source_sha256_16: ")))
+    h = hashlib.sha256()
+    for f in ("fast128.hip", "kernels.h"):
+        with open(os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                               "kv_cache_compression_tq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
@@ -197,7 +217,8 @@ def main():
                    "vectors_per_step": qp["vectors"], "d": 128, "bits": 4, "variant": "mse"},
         "roofline": {"bound": "hbm", "kernel": "k_quant128<4,mse,bf16>", "achieved": qp["achieved_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": qp["achieved_gbs"] / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_vector": qp["bytes_per_vector"],
+                     "traffic": counted_traffic("quant128_kv_mse_b4.md"),
+                     "bytes_per_vector": qp["bytes_per_vector"],
                      "kernel_ms": qp["kernel_ms"],
                      "mfma_bf16_tflops": qp["mfma_tflops"],
                      "mfma_frac": qp["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS},
@@ -213,7 +234,8 @@ def main():
                                    "fp32 queries and logits", "keys": lp["keys"]},
             "roofline": {"bound": "hbm", "kernel": "k_logits128<3,prod>", "achieved": lp["packed_gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": lp["packed_gbs"] / HBM_PEAK_GBS,
-                         "traffic": None, "kernel_ms": lp["kernel_ms"],
+                         "traffic": counted_traffic("logits128_decode_prod_b4.md"),
+                         "kernel_ms": lp["kernel_ms"],
                          "achieved_incl_logits_written": lp["total_gbs"],
                          "frac_incl_logits_written": lp["total_gbs"] / HBM_PEAK_GBS},
             "cache_build_s": lp["cache_build_s"],
