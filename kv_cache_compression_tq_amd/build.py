@@ -28,6 +28,9 @@ DEVICE_SOURCES = ["generic.hip", "fast128.hip"]
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs (the kernels read them with vector ALU code);
+    # AGPRs stay free for operands that are pinned there on purpose
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include",

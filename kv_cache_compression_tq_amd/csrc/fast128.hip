@@ -75,35 +75,52 @@ __device__ __forceinline__ void split8(const float *f, u32x4 &hi, u32x4 &lo) {
 }
 
 struct QuantParams {
-  float pos_bnd[8];   // positive boundaries t_{L/2}, ..., t_{L-2}
-  float pos_cent[8];  // positive centroids c_{L/2}, ..., c_{L-1}
+  float cell_scale;  // cells per unit of the normalised coordinate, times 2^-22
+  int cell_words;    // words of the cell table: 2 (2 kCellRadius + 1)
 };
 
-// #{k : T_k < a} over the L/2 - 1 positive scaled boundaries (sorted), by a
-// branch-free binary search.  Each comparison is consumed at once (one mask
-// live at a time) and the count is built bit by bit.
+constexpr uint32_t kCellCap = 2048;  // LDS bytes reserved for the cell table
+// Adding 2 + kCellRadius 2^-22 to u * scale 2^-22 lands in [2, 4), where one
+// float step is 2^-22: the float bits are those of 2.0 plus the cell number
+// r + kCellRadius.  Shifted left by 3 the bits of 2.0 wrap to zero, so the
+// bits times 8 plus the table offset are the entry's LDS address.
+constexpr float kCellStep = 0x1p-22f;
+constexpr float kCellMagic = 2.f + kCellRadius * kCellStep;
+constexpr uint32_t kCellFirst = 0x40000000u;
+constexpr uint32_t kCellLast = kCellFirst + 2 * kCellRadius;
+static_assert((kCellFirst << 3) == 0u, "cell base must vanish in the address");
+
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) const float lds_f32;
+
+// LDS byte address of a shared array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+// Index #{k : t_k < u} of the rotated coordinate y = nu u by the cell table
+// at LDS byte address `tab` (sv = scale 2^-22 / nu): round u * scale to a
+// cell, read that cell's (boundary, count below) pair, and add one when
+// y > nu t.  The clamp keeps any input, even a non-finite one, in the table.
+__device__ __forceinline__ uint32_t cell_index(uint32_t tab, float y, float nu, float sv) {
+  uint32_t g = __float_as_uint(fmaf(y, sv, kCellMagic));
+  g = min(max(g, kCellFirst), kCellLast);  // one v_med3_u32
+  const u32x2 e = *(lds_u32x2 *)(uintptr_t)((g << 3) + tab);
+  const float dd = fmaf(nu, __uint_as_float(e[0]), -y);
+  return e[1] + (__float_as_uint(dd) >> 31);
+}
+
+// Codebook entry c[idx] staged in LDS at byte address `cent`.
+__device__ __forceinline__ float lds_centroid(uint32_t cent, uint32_t idx) {
+  return *(lds_f32 *)(uintptr_t)(cent + 4 * idx);
+}
+
+// OR the MB-bit field of coordinate j (0..31) into the lane's code words.
 template <int MB>
-__device__ __forceinline__ uint32_t count_below(float a, const float *T) {
-  if constexpr (MB <= 1) {
-    return 0u;
-  } else if constexpr (MB == 2) {
-    return T[0] < a ? 1u : 0u;
-  } else if constexpr (MB == 3) {
-    const bool c1 = T[1] < a;
-    uint32_t cnt = c1 ? 1u : 0u;
-    const float t = c1 ? T[2] : T[0];
-    return 2u * cnt + (t < a ? 1u : 0u);
-  } else {
-    const bool c2 = T[3] < a;
-    uint32_t cnt = c2 ? 1u : 0u;
-    const float t2 = c2 ? T[5] : T[1];
-    const float tl = c2 ? T[4] : T[0];
-    const float th = c2 ? T[6] : T[2];
-    const bool c1 = t2 < a;
-    cnt = 2u * cnt + (c1 ? 1u : 0u);
-    const float t3 = c1 ? th : tl;
-    return 2u * cnt + (t3 < a ? 1u : 0u);
-  }
+__device__ __forceinline__ void put_field(uint32_t *w, int j, uint32_t idx) {
+  const int bit = j * MB, wi = bit >> 5, sh = bit & 31;
+  w[wi] |= idx << sh;
+  if (sh + MB > 32) w[wi + 1] |= idx >> (32 - sh);
 }
 
 // Bitwise select m ? a : b for an all-ones / all-zeros mask m as one
@@ -112,119 +129,6 @@ __device__ __forceinline__ uint32_t count_below(float a, const float *T) {
 __device__ __forceinline__ float fsel(int32_t m, float a, float b) {
   return __uint_as_float(
       __builtin_amdgcn_bitop3_b32((uint32_t)m, __float_as_uint(a), __float_as_uint(b), 0xCA));
-}
-// (w << 1) | signbit(x)
-__device__ __forceinline__ uint32_t push_sign(uint32_t w, float x) {
-  return __builtin_amdgcn_alignbit(w, __float_as_uint(x), 31);
-}
-__device__ __forceinline__ uint32_t push_bit(uint32_t w, uint32_t x) {
-  return __builtin_amdgcn_alignbit(w, x, 31);
-}
-__device__ __forceinline__ int32_t sign_mask(float d) { return __float_as_int(d) >> 31; }
-
-// Stored word i of a lane's 32 fields when every field holds L/2 - 1 (the
-// index of y = 0): the zero vector.
-template <int MB>
-__host__ __device__ constexpr uint32_t zero_word(int i) {
-  uint32_t w = 0;
-  for (int b = 0; b < 32; ++b) {
-    const int p = 32 * i + b, bit = p % MB;
-    const uint32_t v = (1u << (MB - 1)) - 1u;
-    w |= ((v >> bit) & 1u) << b;
-  }
-  return w;
-}
-// Mask of the field MSBs inside stored word i.
-template <int MB>
-__host__ __device__ constexpr uint32_t msb_word(int i) {
-  uint32_t w = 0;
-  for (int b = 0; b < 32; ++b)
-    if ((32 * i + b) % MB == MB - 1) w |= 1u << b;
-  return w;
-}
-
-// Quantize and pack the lane's 32 rotated coordinates y[j] (j = 4 m + q,
-// coordinate 32 grp + j of its vector) against the scaled positive boundaries
-// T.  Symmetric codebook: the index is L/2 + c for y > 0 and L/2 - 1 - c
-// otherwise, c = #{k : T_k < |y|}.  Each comparison is a subtraction whose
-// sign bit is the answer; sign bits are shifted straight into the code words
-// (fields are written from the highest bit of the lane's chunk down), and the
-// flip for negative y is applied afterwards on whole words.  y = +0 takes the
-// positive branch: it lies on the middle boundary, where either neighbour is
-// within any boundary tolerance.
-template <int MB>
-__device__ __forceinline__ void quantize_pack(const f32x4 (&acc)[8], const float *T, bool zero,
-                                              uint32_t *w) {
-  if constexpr (MB == 4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t raw = 0;
-#pragma unroll
-      for (int jj = 7; jj >= 0; --jj) {
-        const int j = 8 * i + jj;
-        const float y = acc[j >> 2][j & 3];
-        const float a = fabsf(y);
-        const float d2 = T[3] - a;
-        const int32_t m2 = sign_mask(d2);
-        const float t2 = fsel(m2, T[5], T[1]);
-        const float tl = fsel(m2, T[4], T[0]), th = fsel(m2, T[6], T[2]);
-        const float d1 = t2 - a;
-        const float t3 = fsel(sign_mask(d1), th, tl);
-        const float d0 = t3 - a;
-        raw = push_sign(raw, y);
-        raw = push_sign(raw, d2);
-        raw = push_sign(raw, d1);
-        raw = push_sign(raw, d0);
-      }
-      // nibble [s_y, c2, c1, c0] -> [~s_y, c2^s_y, c1^s_y, c0^s_y]
-      const uint32_t sy = (raw >> 3) & 0x11111111u;
-      const uint32_t sy7 = sy | (sy << 1) | (sy << 2);
-      const uint32_t v = raw ^ sy7 ^ 0x88888888u;
-      w[i] = zero ? 0x77777777u : v;
-    }
-  } else if constexpr (MB >= 1) {
-    uint32_t ww[MB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i) ww[i] = 0;
-    // stream bits p = MB j + k; pushed from p = 32 MB - 1 down to 0
-#pragma unroll
-    for (int j = 31; j >= 0; --j) {
-      const float y = acc[j >> 2][j & 3];
-      const float a = fabsf(y);
-      const uint32_t sy = __float_as_uint(y);
-      const int top = MB * j + MB - 1;
-      ww[top >> 5] = push_sign(ww[top >> 5], y);  // field MSB: flipped below
-      if constexpr (MB == 2) {
-        const float d0 = T[0] - a;
-        ww[(top - 1) >> 5] = push_bit(ww[(top - 1) >> 5], __float_as_uint(d0) ^ sy);
-      } else if constexpr (MB == 3) {
-        const float d1 = T[1] - a;
-        const float t = fsel(sign_mask(d1), T[2], T[0]);
-        const float d0 = t - a;
-        ww[(top - 1) >> 5] = push_bit(ww[(top - 1) >> 5], __float_as_uint(d1) ^ sy);
-        ww[(top - 2) >> 5] = push_bit(ww[(top - 2) >> 5], __float_as_uint(d0) ^ sy);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < MB; ++i) w[i] = zero ? zero_word<MB>(i) : (ww[i] ^ msb_word<MB>(i));
-  }
-}
-
-template <int MB>
-__device__ __forceinline__ float pos_centroid(uint32_t cnt, const float *C) {
-  if constexpr (MB <= 1) {
-    return C[0];
-  } else if constexpr (MB == 2) {
-    return cnt ? C[1] : C[0];
-  } else if constexpr (MB == 3) {
-    const float lo = (cnt & 1) ? C[1] : C[0], hi = (cnt & 1) ? C[3] : C[2];
-    return (cnt & 2) ? hi : lo;
-  } else {
-    const float a = (cnt & 1) ? C[1] : C[0], b = (cnt & 1) ? C[3] : C[2];
-    const float c = (cnt & 1) ? C[5] : C[4], d = (cnt & 1) ? C[7] : C[6];
-    const float ab = (cnt & 2) ? b : a, cd = (cnt & 2) ? d : c;
-    return (cnt & 4) ? cd : ab;
-  }
 }
 
 template <int MB>
@@ -340,12 +244,15 @@ constexpr int quant_threads() { return 512; }
 template <int MB, bool PROD, bool F32IN>
 __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
     const void *__restrict__ xin, int64_t n, int groups, const uint32_t *__restrict__ pi_img,
-    const uint32_t *__restrict__ m_img, QuantParams qp, uint8_t *__restrict__ codes,
-    uint8_t *__restrict__ signs, float *__restrict__ norms, float *__restrict__ rnorms) {
+    const uint32_t *__restrict__ m_img, const uint32_t *__restrict__ cells,
+    const float *__restrict__ cent, QuantParams qp,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ signs, float *__restrict__ norms,
+    float *__restrict__ rnorms) {
   extern __shared__ u32x4 lds[];
-  constexpr int L = 1 << MB;
-  constexpr int NB = MB > 0 ? L / 2 - 1 : 0;  // positive boundaries
   constexpr int kQuantThreads = quant_threads<PROD>();
+  // LDS: rotation image, [QJL image], cell table, [codebook]
+  constexpr uint32_t kTab = (PROD ? 2 : 1) * kImageVec * 16;
+  const uint32_t tab_addr = lds_addr(lds) + kTab, cent_addr = tab_addr + kCellCap;
   const int s = blockIdx.y;
   const int g = s % groups;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -358,6 +265,12 @@ __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
     if constexpr (PROD) {
       const u32x4 *srcm = (const u32x4 *)(m_img + (size_t)g * kImageWords);
       for (int i = tid; i < kImageVec; i += kQuantThreads) lds[kImageVec + i] = srcm[i];
+    }
+    uint32_t *tab = (uint32_t *)((char *)lds + kTab);
+    for (int i = tid; i < qp.cell_words; i += kQuantThreads) tab[i] = cells[i];
+    if constexpr (PROD && MB > 0) {
+      float *cl = (float *)((char *)lds + kTab + kCellCap);
+      if (tid < (1 << MB)) cl[tid] = cent[tid];
     }
   }
   __syncthreads();
@@ -384,42 +297,25 @@ __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
     for (int t = 0; t < 2; ++t) {
       const f32x4(&acc)[8] = acc2[t];
       const int64_t v = v0 + 16 * t + col;
-      const float nu = sqrtf(nsq2[t]);
-      const float nthr = nu > 0.f ? nu : 1.f;  // a zero vector has y = 0
-      float T[NB > 0 ? NB : 1];
-#pragma unroll
-      for (int k = 0; k < NB; ++k) T[k] = nthr * qp.pos_bnd[k];
+      const float nu = __builtin_amdgcn_sqrtf(nsq2[t]);
+      // a zero vector has y = 0, which every cell scale maps to the middle
+      const float sv = qp.cell_scale * __builtin_amdgcn_rcpf(nu > 0.f ? nu : 1.f);
       uint32_t w[MB > 0 ? MB : 1];
 #pragma unroll
       for (int i = 0; i < (MB > 0 ? MB : 1); ++i) w[i] = 0;
       float res[32];
       float rs = 0.f;
-      if constexpr (!PROD) quantize_pack<MB>(acc, T, nu == 0.f, w);
 #pragma unroll
-      for (int m = 0; m < 8 && PROD; ++m) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = 4 * m + q;  // coordinate 32 grp + j of the lane's vector
-          const float y = acc[m][q];
-          if constexpr (MB > 0) {
-            // an exact tie with a boundary may round either way (it lies on
-            // the boundary, within any boundary tolerance)
-            const float a = fabsf(y);
-            const bool pos = y > 0.f;
-            const uint32_t cnt = count_below<MB>(a, T);
-            const uint32_t idx = cnt ^ (pos ? (uint32_t)(L / 2) : (uint32_t)(L / 2 - 1));
-            const int bit = j * MB, wi = bit >> 5, sh = bit & 31;
-            w[wi] |= idx << sh;
-            if (sh + MB > 32) w[wi + 1] |= idx >> (32 - sh);
-            if constexpr (PROD) {
-              const float cv = pos_centroid<MB>(cnt, qp.pos_cent);
-              res[j] = y - nu * (pos ? cv : -cv);
-            }
-          } else {
-            res[j] = y;
-          }
-          if constexpr (PROD) rs = fmaf(res[j], res[j], rs);
+      for (int j = 0; j < 32; ++j) {  // coordinate 32 grp + j of the lane's vector
+        const float y = acc[j >> 2][j & 3];
+        if constexpr (MB > 0) {
+          const uint32_t idx = cell_index(tab_addr, y, nu, sv);
+          put_field<MB>(w, j, idx);
+          if constexpr (PROD) res[j] = fmaf(-nu, lds_centroid(cent_addr, idx), y);
+        } else {
+          res[j] = y;
         }
+        if constexpr (PROD) rs = fmaf(res[j], res[j], rs);
       }
       if (v < n) {
         const int64_t row = set_row0 + v;
@@ -490,6 +386,177 @@ __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
       process(xb, tile * 32);
       tile = nxt;
       if (!more) break;
+    }
+  }
+}
+
+// TurboQuant_mse of bfloat16 input with the rotation held in registers.  One
+// wave per SIMD (a 256-thread workgroup per CU) leaves each wave 512
+// registers: all 64 hi/lo fragments of Pi live in its 256 AGPRs, which the
+// MFMAs read directly, so LDS carries only the 2 KB cell table.  Each wave
+// runs a software pipeline over 16-vector stages: while the MFMAs rotate
+// stage i+1, the vector ALU searches and packs stage i, and the inputs of
+// stages i+2 .. i+kMseDepth-1 are in flight.
+constexpr int kMseThreads = 256;
+constexpr int kMseDepth = 4;  // input stages held in registers
+
+// Input fragments of one 16-vector stage: lane (col, grp) holds vector col,
+// elements 32 k + 8 grp .. + 8 (bf16 pairs) for K steps k.
+struct XStage {
+  u32x4 v[4];
+};
+
+__device__ __forceinline__ void load_stage(XStage &r, const uint16_t *xin, int64_t set_row0, int64_t n,
+                                           int64_t v0, int col, int grp) {
+  int64_t v = v0 + col;
+  v = v < n ? v : n - 1;  // ragged tail or a padding stage: a valid row, results discarded
+  const uint16_t *p = xin + (set_row0 + v) * D + 8 * grp;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r.v[k] = *(const u32x4 *)(p + 32 * k);
+}
+
+// acc[m] = rows 16 m .. 16 m + 15 of the permuted Pi times the stage; nsq =
+// ||x||^2 of the lane's vector from the Gram diagonal.
+__device__ __forceinline__ void rotate_stage(const XStage &x, const u32x4 (&im)[64], f32x4 (&acc)[8],
+                                             float &nsq, int col) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      acc[m] = mfma_bf16(im[(m * 4 + k) * 2], x.v[k], acc[m]);
+      acc[m] = mfma_bf16(im[(m * 4 + k) * 2 + 1], x.v[k], acc[m]);
+    }
+  f32x4 gm = {0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) gm = mfma_bf16(x.v[k], x.v[k], gm);
+  const int32_t m0 = -(col & 1), m1 = -((col >> 1) & 1);
+  const float mine = fsel(m1, fsel(m0, gm[3], gm[2]), fsel(m0, gm[1], gm[0]));
+  nsq = __shfl(mine, ((col >> 2) << 4) + col);
+}
+
+// Buffer resources over one set's codes and norms: stores at byte offsets at
+// or past num_records are dropped by the hardware, which masks the ragged
+// tail without a branch (a branch would split the MFMA / search overlap).
+constexpr uint32_t kBufferFlags = 0x00020000u;  // gfx9 raw buffer, 32-bit data
+constexpr uint32_t kDropped = 0x80000000u;      // offset past every set (host-checked)
+
+// The search of one stage in two halves, so that the MFMAs of the next stage
+// run between them and cover the LDS latency: first the 32 cell reads, then
+// the comparisons, packing and stores.
+struct StageCells {
+  u32x2 e[32];
+  float nu, sv;
+};
+
+__device__ __forceinline__ void lookup_stage(const f32x4 (&acc)[8], float nsq, uint32_t tab_addr,
+                                             float cell_scale, StageCells &c) {
+  c.nu = __builtin_amdgcn_sqrtf(nsq);
+  c.sv = cell_scale * __builtin_amdgcn_rcpf(c.nu > 0.f ? c.nu : 1.f);
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    uint32_t g = __float_as_uint(fmaf(acc[j >> 2][j & 3], c.sv, kCellMagic));
+    g = min(max(g, kCellFirst), kCellLast);
+    c.e[j] = *(lds_u32x2 *)(uintptr_t)((g << 3) + tab_addr);
+  }
+}
+
+template <int MB>
+__device__ __forceinline__ void pack_stage(const f32x4 (&acc)[8], const StageCells &c, int64_t v,
+                                           int64_t n, int grp, __amdgpu_buffer_rsrc_t rc,
+                                           __amdgpu_buffer_rsrc_t rn) {
+  uint32_t w[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) w[i] = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float y = acc[j >> 2][j & 3];
+    const float dd = fmaf(c.nu, __uint_as_float(c.e[j][0]), -y);
+    put_field<MB>(w, j, c.e[j][1] + (__float_as_uint(dd) >> 31));
+  }
+  const uint32_t off = v < n ? (uint32_t)v * (16 * MB) + grp * (4 * MB) : kDropped;
+  if constexpr (MB == 1) {
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], rc, off, 0, 0);
+  } else if constexpr (MB == 2) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rc, off, 0, 0);
+  } else if constexpr (MB == 3) {
+    __builtin_amdgcn_raw_buffer_store_b96(u32x3{w[0], w[1], w[2]}, rc, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rc, off, 0, 0);
+  }
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c.nu), rn,
+                                        v < n && grp == 0 ? (uint32_t)v * 4 : kDropped, 0, 0);
+}
+
+template <int MB>
+__global__ __launch_bounds__(kMseThreads, 1) void k_quant128_mse(
+    const uint16_t *__restrict__ xin, int64_t n, int groups, const u32x4 *__restrict__ pi_img,
+    const uint32_t *__restrict__ cells, float cell_scale, uint8_t *__restrict__ codes,
+    float *__restrict__ norms) {
+  constexpr int kCellWords = 2 * (2 * kCellRadius + 1);
+  __shared__ uint32_t tab[kCellWords];
+  __shared__ u32x4 img[kImageVec];  // staging: each CU reads the image from L2 once
+  const int s = blockIdx.y;
+  const int g = s % groups;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  for (int i = tid; i < kCellWords; i += kMseThreads) tab[i] = cells[i];
+
+  // stages of this wave: tile0 + k stride, k = 0 .. count - 1 (32-bit: the
+  // host guarantees n_sets n < 2^31); all of it is wave-uniform scalar work
+  const int ntiles = (int)((n + 15) / 16);
+  const int64_t set_row0 = (int64_t)s * n;
+  constexpr int kWaves = kMseThreads / 64;
+  const int stride = (int)gridDim.x * kWaves;
+  const int tile0 = (int)blockIdx.x * kWaves + wave;
+  const int count = __builtin_amdgcn_readfirstlane(tile0 < ntiles ? (ntiles - tile0 + stride - 1) / stride : 0);
+  // first row of stage k; stages past the end read the last stage again and
+  // store nothing
+  auto row0 = [&](int k) { return (int64_t)(tile0 + min(k, count - 1) * stride) * 16; };
+  auto valid_row0 = [&](int k) { return k < count ? (int64_t)(tile0 + k * stride) * 16 : n; };
+
+  // the image first (every stage needs all of it), then the first inputs
+  {
+    const u32x4 *src = pi_img + (size_t)g * kImageVec;
+    u32x4 t[kImageVec / kMseThreads];
+#pragma unroll
+    for (int i = 0; i < kImageVec / kMseThreads; ++i) t[i] = src[i * kMseThreads + tid];
+#pragma unroll
+    for (int i = 0; i < kImageVec / kMseThreads; ++i) img[i * kMseThreads + tid] = t[i];
+  }
+  XStage xs[kMseDepth];
+#pragma unroll
+  for (int j = 0; j + 1 < kMseDepth; ++j) load_stage(xs[j], xin, set_row0, n, row0(j), col, grp);
+  __syncthreads();
+  u32x4 im[64];
+#pragma unroll
+  for (int f = 0; f < 64; ++f) {
+    im[f] = img[f * kFragVec + lane];
+    asm volatile("" : "+a"(im[f]));  // keep the fragment in an AGPR
+  }
+  if (count == 0) return;  // no barrier follows
+  const uint32_t tab_addr = lds_addr(tab);
+
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc(codes + set_row0 * (16 * MB), 0, (int)(n * (16 * MB)), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rn =
+      __builtin_amdgcn_make_buffer_rsrc(norms + set_row0, 0, (int)(n * 4), kBufferFlags);
+  f32x4 acc[2][8];
+  float nsq[2];
+  rotate_stage(xs[0], im, acc[0], nsq[0], col);
+  for (int k0 = 0; k0 < count; k0 += kMseDepth) {
+#pragma unroll
+    for (int j = 0; j < kMseDepth; ++j) {
+      const int k = k0 + j;
+      // refill the buffer that stage k used; look up stage k's cells; rotate
+      // stage k + 1; finish stage k
+      load_stage(xs[(j + kMseDepth - 1) % kMseDepth], xin, set_row0, n, row0(k + kMseDepth - 1), col, grp);
+      StageCells cells;
+      lookup_stage(acc[j & 1], nsq[j & 1], tab_addr, cell_scale, cells);
+      rotate_stage(xs[(j + 1) % kMseDepth], im, acc[(j + 1) & 1], nsq[(j + 1) & 1], col);
+      pack_stage<MB>(acc[j & 1], cells, valid_row0(k) + col, n, grp, rc, rn);
     }
   }
 }
@@ -758,15 +825,33 @@ __global__ __launch_bounds__(kLogitThreads, 2) void k_logits128(
   }
 }
 
+template <int MB>
+hipError_t run_quant_mse(const DeviceTables &t, const void *x, int64_t n_sets, int64_t n,
+                         uint8_t *codes, float *norms, hipStream_t st) {
+  // per-set byte offsets of codes and norms stay below the dropped-store offset
+  if (t.cell_radius != kCellRadius || n * (16 * MB) >= (int64_t)kDropped) return hipErrorNotSupported;
+  const int64_t ntiles = (n + 15) / 16;
+  constexpr int waves = kMseThreads / 64;
+  const int64_t per_set_max = (ntiles + waves - 1) / waves;  // >= 1 stage per wave
+  const int64_t target = 256;                               // one workgroup per CU
+  int64_t gx = (target + n_sets - 1) / n_sets;
+  if (gx > per_set_max) gx = per_set_max;
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL((k_quant128_mse<MB>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kMseThreads), 0,
+                     st, (const uint16_t *)x, n, t.groups, (const u32x4 *)t.pi_frag, t.cells,
+                     t.cell_scale * kCellStep, codes, norms);
+  return hipGetLastError();
+}
+
 template <int MB, bool PROD, bool F32IN>
 hipError_t run_quant(const DeviceTables &t, const void *x, int64_t n_sets, int64_t n, uint8_t *codes,
                      uint8_t *signs, float *norms, float *rnorms, hipStream_t st) {
   QuantParams qp;
-  for (int k = 0; k < 8; ++k) {
-    qp.pos_bnd[k] = t.pos_bnd[k];
-    qp.pos_cent[k] = t.pos_cent[k];
-  }
-  const size_t lds = (PROD ? 2 : 1) * (size_t)kImageVec * sizeof(u32x4);
+  if (MB > 0 && t.cell_radius != kCellRadius) return hipErrorNotSupported;
+  qp.cell_scale = t.cell_scale * kCellStep;
+  qp.cell_words = MB > 0 ? 2 * (2 * kCellRadius + 1) : 0;
+  static_assert(2 * (2 * kCellRadius + 1) * 4 <= kCellCap, "cell table exceeds its LDS slot");
+  const size_t lds = (PROD ? 2 : 1) * (size_t)kImageVec * sizeof(u32x4) + kCellCap + 64;
   hipError_t e = hipFuncSetAttribute((const void *)k_quant128<MB, PROD, F32IN>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -778,7 +863,8 @@ hipError_t run_quant(const DeviceTables &t, const void *x, int64_t n_sets, int64
   if (gx > per_set_max) gx = per_set_max;
   if (gx < 1) gx = 1;
   hipLaunchKernelGGL((k_quant128<MB, PROD, F32IN>), dim3((unsigned)gx, (unsigned)n_sets), dim3(threads),
-                     lds, st, x, n, t.groups, t.pi_frag, t.m_frag, qp, codes, signs, norms, rnorms);
+                     lds, st, x, n, t.groups, t.pi_frag, t.m_frag, t.cells, t.cent, qp, codes, signs, norms,
+                     rnorms);
   return hipGetLastError();
 }
 
@@ -916,6 +1002,14 @@ hipError_t launch_quant128(const DeviceTables &t, const void *x, int dtype, int6
                            hipStream_t st) {
   if (t.d != D || !t.pi_frag || t.mse_bits > 4 || ((uintptr_t)x & 15u)) return hipErrorNotSupported;
   const bool prod = t.variant == 1, f32 = dtype == 0;
+  if (!prod && !f32 && t.mse_bits >= 1) {
+    switch (t.mse_bits) {
+      case 1: return run_quant_mse<1>(t, x, n_sets, n, codes, norms, st);
+      case 2: return run_quant_mse<2>(t, x, n_sets, n, codes, norms, st);
+      case 3: return run_quant_mse<3>(t, x, n_sets, n, codes, norms, st);
+      case 4: return run_quant_mse<4>(t, x, n_sets, n, codes, norms, st);
+    }
+  }
 #define TQ_Q(MB, P, F) \
   if (t.mse_bits == MB && prod == P && f32 == F) \
     return run_quant<MB, P, F>(t, x, n_sets, n, codes, signs, norms, rnorms, st);

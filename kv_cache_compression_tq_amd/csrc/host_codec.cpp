@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <stdexcept>
 #include <thread>
 
@@ -223,6 +224,42 @@ Codebook lloyd_max(int d, int bits) {
   cb.distortion = 1.0 - d * e;
   cb.iterations = it;
   return cb;
+}
+
+bool build_cell_table(const std::vector<float> &bounds, int min_radius, CellTable &out) {
+  const double margin = 1.0 / 16.0;
+  double gap = 2.0;
+  for (size_t k = 0; k + 1 < bounds.size(); ++k) {
+    const double g = (double)bounds[k + 1] - (double)bounds[k];
+    if (!(g > 0.0)) return false;
+    gap = std::min(gap, g);
+  }
+  // a widened cell spans (1 + 2 margin) / scale < gap
+  const float scale = (float)((1.0 + 2.0 * margin) / gap * 1.01);
+  const int radius = std::max((int)std::ceil((double)scale) + 2, min_radius);
+  std::vector<uint32_t> words(2 * (2 * radius + 1));
+  for (int r = -radius; r <= radius; ++r) {
+    const double lo = (r - 0.5 - margin) / (double)scale, hi = (r + 0.5 + margin) / (double)scale;
+    float t = 1e30f;
+    uint32_t below = 0;
+    int inside = 0;
+    for (size_t k = 0; k < bounds.size(); ++k) {
+      const double b = bounds[k];
+      if (b < lo) {
+        ++below;
+      } else if (b <= hi) {
+        t = bounds[k];
+        ++inside;
+      }
+    }
+    if (inside > 1) return false;
+    std::memcpy(&words[2 * (r + radius)], &t, 4);
+    words[2 * (r + radius) + 1] = below;
+  }
+  out.scale = scale;
+  out.radius = radius;
+  out.words.swap(words);
+  return true;
 }
 
 }  // namespace tq

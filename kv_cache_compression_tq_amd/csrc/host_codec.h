@@ -35,4 +35,21 @@ struct Codebook {
 // f_d(x) ∝ (1 - x^2)^((d-3)/2) on [-1, 1] with 2^bits levels.
 Codebook lloyd_max(int d, int bits);
 
+// Table for a branch-free boundary search over a normalised coordinate u in
+// [-1, 1].  Cell r (r = round(u * scale), |r| <= radius) covers
+// u in [(r - 0.5 - m) / scale, (r + 0.5 + m) / scale] with a margin m = 1/16;
+// scale is chosen so that no cell holds more than one boundary.  Entry
+// r + radius is two words: the float bits of the boundary inside the cell
+// (1e30f if none) and the number of boundaries below it.  The index of u is
+// then that count, plus one when u is above the cell's boundary.
+struct CellTable {
+  float scale = 1.f;
+  int radius = 0;
+  std::vector<uint32_t> words;
+};
+
+// Builds the table for ascending float32 boundaries with a radius of at least
+// min_radius cells; false if the boundaries are not strictly ascending.
+bool build_cell_table(const std::vector<float> &bounds, int min_radius, CellTable &out);
+
 }  // namespace tq

@@ -18,6 +18,10 @@ struct DeviceTables {
   const float *MT = nullptr;   // [G][d][d] = (S Pi^T)^T (prod)
   const float *cent = nullptr; // [2^mse_bits]
   const float *bnd = nullptr;  // [2^mse_bits - 1]
+  // boundary-search cell table (host_codec.h CellTable): 2 words per cell
+  const uint32_t *cells = nullptr;
+  int cell_radius = 0;
+  float cell_scale = 1.f;
   // d == 128 fast path: MFMA operand images (see quant128.hip)
   const uint32_t *pi_frag = nullptr;  // [G][...] bf16 hi/lo pairs, permuted rows
   const uint32_t *m_frag = nullptr;   // [G][...] same for M (prod)
@@ -29,6 +33,9 @@ struct DeviceTables {
 };
 
 constexpr float kQjlScale = 1.2533141373155003f;  // sqrt(pi/2)
+// Radius of the boundary-search cell table the d = 128 kernels are built for
+// (255 cells; wider tables send a shape to the generic kernels).
+constexpr int kCellRadius = 127;
 
 hipError_t launch_quant_generic(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
                                 int64_t n, uint8_t *codes, uint8_t *signs, float *norms,

@@ -113,6 +113,11 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     for (double c : cb.centroids) h->h_c.push_back((float)c);
     for (double t : cb.boundaries) h->h_t.push_back((float)t);
   }
+  tq::CellTable cells;
+  if (mse_bits > 0 && !tq::build_cell_table(h->h_t, tq::kCellRadius, cells)) {
+    delete h;
+    return fail(TQ_EINVAL, "codebook boundaries are not strictly ascending");
+  }
   const bool fast = tq::fast128_supported(d, mse_bits, variant);
   const size_t rot_words = fast ? tq::fast128_rotation_words(d) : 0;
   const size_t lut_words = fast ? tq::fast128_lut_words(mse_bits) : 0;
@@ -169,6 +174,7 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     }
     h->dev.cent = carve<float>(base, off, L ? L : 1);
     h->dev.bnd = carve<float>(base, off, L > 1 ? L - 1 : 1);
+    h->dev.cells = carve<uint32_t>(base, off, cells.words.empty() ? 2 : cells.words.size());
     if (fast) {
       h->dev.pi_frag = carve<uint32_t>(base, off, groups * rot_words);
       if (prod) h->dev.m_frag = carve<uint32_t>(base, off, groups * rot_words);
@@ -207,6 +213,7 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
   }
   up(h->dev.cent, h->h_c.data(), h->h_c.size() * 4);
   up(h->dev.bnd, h->h_t.data(), h->h_t.size() * 4);
+  up(h->dev.cells, cells.words.data(), cells.words.size() * 4);
   if (fast) {
     up(h->dev.pi_frag, pi_img.data(), pi_img.size() * 4);
     if (prod) up(h->dev.m_frag, m_img.data(), m_img.size() * 4);
@@ -222,6 +229,8 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     for (int k = 0; k + 1 < L / 2; ++k) h->dev.pos_bnd[k] = h->h_t[L / 2 + k];
   }
   h->dev.lut_inv_scale = lut_inv_scale;
+  h->dev.cell_radius = cells.radius;
+  h->dev.cell_scale = cells.scale;
   h->dev.d = d;
   h->dev.groups = groups;
   h->dev.variant = variant;
