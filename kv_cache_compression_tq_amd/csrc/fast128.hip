@@ -563,7 +563,7 @@ __global__ __launch_bounds__(kMseThreads, 1) void k_quant128_mse(
 
 // ---------------------------------------------------------------- logits --
 constexpr int kLogitTiles = 4;     // 16-key tiles per wave iteration
-constexpr int kLogitThreads = 512;  // 8 waves share one set of decode tables
+constexpr int kLogitThreads = 1024;  // 16 waves share one set of decode tables
 constexpr int kLogitWaves = kLogitThreads / 64;
 
 // Per-wave registers of KT 16-key tiles: lane (col, grp) holds key col of each
@@ -627,16 +627,27 @@ __device__ __forceinline__ void load_tail(KeyRegs<CW> &r, int64_t t0, int64_t ke
   }
 }
 
-// Decode-table geometry (must match the host builder): G codes per lookup.
+// Decode tables (the host builds one copy): one u32 per pair of codes (two
+// f16 values alpha c[i0], alpha c[i1]) and one u32x4 per sign byte (eight f16
+// +1 / -1).  In LDS every entry is replicated so that each lane reads its own
+// copy: the copy index is the low lane bits, which puts the lanes served in
+// one LDS cycle on distinct banks whatever codes they hold.
 template <int MB>
 struct LutGeom {
-  static constexpr int G = MB == 1 ? 8 : (MB == 4 ? 2 : 4);
-  static constexpr int W = G * MB;                       // index bits
+  static constexpr int W = 2 * MB;                       // index bits (two codes)
   static constexpr int ENTRIES = MB > 0 ? 1 << W : 1;
-  static constexpr int WORDS = MB > 0 ? ENTRIES * G / 2 : 1;
+  static constexpr int COPIES = MB == 4 ? 32 : 64;        // u32 entries
+  static constexpr int SHIFT = MB == 4 ? 7 : 8;           // log2(4 COPIES): entry stride in bytes
+  static constexpr int WORDS = MB > 0 ? ENTRIES : 1;      // host table
+  // dynamic LDS: replicated code table at byte 0 (so an entry address is the
+  // index shifted left by SHIFT, OR the lane's copy), sign table, query buffers
+  static constexpr uint32_t CODE_BYTES = MB > 0 ? ENTRIES * COPIES * 4 : 0;
 };
+constexpr int kSignCopies = 8;                     // u32x4 entries
+constexpr uint32_t kSignBytes = 256 * kSignCopies * 16;
+constexpr uint32_t kQueryBytes = 3 * 8 * D * 4;    // qs, qt, pp
 
-// Score one 16-key tile.  Each LDS lookup decodes G codes (or 8 signs)
+// Score one 16-key tile.  Each LDS lookup decodes two codes (or eight signs)
 // straight into f16 operand registers of the lane's key; the queries are the
 // A operand (row 2h + part: head h, hi or lo f16 part) and the decoded keys the
 // B operand (column = key), one MFMA per 32 coordinates of codes and one per
@@ -646,33 +657,29 @@ struct LutGeom {
 // folded into the projected query.
 template <int MB, bool PROD>
 __device__ __forceinline__ void score_tile(const KeyRegs<MB> &r, int u, const u32x4 *bq,
-                                           const u32x4 *bp, const uint32_t *t_code,
-                                           const u32x4 *t_sg, float &o0, float &o1) {
+                                           const u32x4 *bp, uint32_t code_base, uint32_t sign_base,
+                                           float &o0, float &o1) {
   using GM = LutGeom<MB>;
-  constexpr int G = GM::G, W = GM::W;
+  constexpr int W = GM::W;
   f32x4 cm = {0, 0, 0, 0}, cq = {0, 0, 0, 0};
   if constexpr (MB > 0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       u32x4 bk;
 #pragma unroll
-      for (int jj = 0; jj < 8 / G; ++jj) {
-        const int j = k * (8 / G) + jj;  // group j of the lane's 32 coordinates
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * k + jj;  // code pair j of the lane's 32 coordinates
         const int bit = j * W, wi = bit >> 5, sh = bit & 31;
-        uint32_t fld;
-        if (sh + W <= 32)
-          fld = (r.cw[u][wi] >> sh) & (uint32_t)((1 << W) - 1);
+        // the field moved to bit SHIFT: the entry's byte offset
+        uint32_t x;
+        if (sh + W > 32)
+          x = __builtin_amdgcn_alignbit(r.cw[u][wi + 1], r.cw[u][wi], sh - GM::SHIFT);
+        else if (sh >= GM::SHIFT)
+          x = r.cw[u][wi] >> (sh - GM::SHIFT);
         else
-          fld = __builtin_amdgcn_alignbit(r.cw[u][wi + 1], r.cw[u][wi], sh) & (uint32_t)((1 << W) - 1);
-        if constexpr (G == 2) {
-          bk[jj] = t_code[fld];
-        } else if constexpr (G == 4) {
-          const u32x2 v = ((const u32x2 *)t_code)[fld];
-          bk[2 * jj] = v[0];
-          bk[2 * jj + 1] = v[1];
-        } else {
-          bk = ((const u32x4 *)t_code)[fld];
-        }
+          x = r.cw[u][wi] << (GM::SHIFT - sh);
+        const uint32_t addr = (x & (uint32_t)(((1 << W) - 1) << GM::SHIFT)) | code_base;
+        bk[jj] = *(__attribute__((address_space(3))) const uint32_t *)(uintptr_t)addr;
       }
       cm = mfma_f16(bq[k], bk, cm);
     }
@@ -680,8 +687,11 @@ __device__ __forceinline__ void score_tile(const KeyRegs<MB> &r, int u, const u3
   if constexpr (PROD) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t byte = (r.sw[u] >> (8 * k)) & 0xffu;
-      cq = mfma_f16(bp[k], t_sg[byte], cq);
+      // sign byte k times the entry stride (128 bytes), OR the lane's copy
+      const uint32_t x = k == 0 ? r.sw[u] << 7 : r.sw[u] >> (8 * k - 7);
+      const uint32_t addr = (x & 0x7F80u) | sign_base;
+      const u32x4 sg = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(addr + GM::CODE_BYTES);
+      cq = mfma_f16(bp[k], sg, cq);
     }
   }
   float v0 = cm[0] + cm[1], v1 = cm[2] + cm[3];
@@ -693,54 +703,91 @@ __device__ __forceinline__ void score_tile(const KeyRegs<MB> &r, int u, const u3
   o1 = v1 * r.nv[u];
 }
 
+// Workgroup layout: one 1024-thread workgroup per CU (16 waves, 4 per SIMD)
+// scores one contiguous key range of one set.  Waves take 64-key blocks from
+// a counter in LDS, so faster waves (the scheduler favours older ones) take
+// more blocks and every wave finishes at about the same time.
 template <int MB, bool PROD>
-__global__ __launch_bounds__(kLogitThreads, 2) void k_logits128(
+__global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
     const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ signs, const float *__restrict__ norms,
     const float *__restrict__ rnorms, int64_t n_keys, int groups, const float *__restrict__ PiT,
     const float *__restrict__ ST, const uint32_t *__restrict__ lut, float lut_inv_scale,
     int64_t keys_per_wg, float *__restrict__ out) {
   constexpr int CW = MB;  // code words per lane (32 coordinates)
-  constexpr int LW = LutGeom<MB>::WORDS;
-  __shared__ float qs[8 * D];
-  __shared__ float qt[8 * D];
-  __shared__ float pp[8 * D];
-  __shared__ __attribute__((aligned(16))) uint32_t t_code[LW];
-  __shared__ u32x4 t_sg[256];
+  using GM = LutGeom<MB>;
+  extern __shared__ u32x4 dyn_lds[];  // the kernel's only LDS: starts at address 0
+  uint32_t *t_code = (uint32_t *)dyn_lds;
+  u32x4 *t_sg = (u32x4 *)((char *)dyn_lds + GM::CODE_BYTES);
+  float *qs = (float *)((char *)dyn_lds + GM::CODE_BYTES + kSignBytes);
+  float *qt = qs + 8 * D;
+  float *pp = qt + 8 * D;
+  float *scratch = pp + 8 * D;                 // [2][4][8][D] partial sums
+  uint32_t *counter = (uint32_t *)(scratch + 2 * 4 * 8 * D);
 
   const int s = blockIdx.y;
   const int g = s % groups;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar loop control
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
+  const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
+  const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
+  const int64_t srow = (int64_t)s * n_keys;
+  const uint8_t *cbase = MB > 0 ? codes + srow * (16 * CW) + grp * (4 * CW) : nullptr;
+  const uint8_t *sbase = PROD ? signs + srow * 16 + grp * 4 : nullptr;
+  const float *nbase = norms + srow;
+  const float *gbase = PROD ? rnorms + srow : nullptr;
+  constexpr int KT = kLogitTiles;
+  constexpr int W = 16 * KT;  // keys per block
+  const int nfull = (int)((kend - kbeg) / W);
+  const bool ragged = kbeg + (int64_t)nfull * W < kend;
 
-  for (int e = tid; e < 8 * D; e += kLogitThreads) {
-    const int h = e / D;
-    qs[e] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + (e % D)] : 0.f;
+  // 1. every global load of the set-up at once: this wave's first key block
+  // (wave w starts with block w; later blocks come from the counter), the
+  // query, the columns of Pi^T / S^T this thread contracts, the tables
+  KeyRegs<CW> ra, rb;  // ping-pong: one block is scored while the next loads
+  int b = wave;
+  if (b < nfull) load_full<CW, PROD, KT>(ra, kbeg + (int64_t)b * W, col, cbase, sbase, nbase, gbase);
+  const int mat = tid >> 9, slice = (tid >> 7) & 3, jj = tid & 127;
+  float w[32];
+  {
+    const float *Wm = (mat == 0 ? PiT : (PROD ? ST : PiT)) + (size_t)g * D * D + (size_t)(32 * slice) * D + jj;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) w[k] = Wm[(size_t)k * D];
+  }
+  {
+    const int h = tid / D;
+    qs[tid] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + (tid % D)] : 0.f;  // 8 D == threads
   }
   if constexpr (MB > 0)
-    for (int e = tid; e < LW / 4; e += kLogitThreads) ((u32x4 *)t_code)[e] = ((const u32x4 *)lut)[e];
-  if (PROD && tid < 256) t_sg[tid] = ((const u32x4 *)(lut + (MB > 0 ? LW : 0)))[tid];
+    for (int e = tid; e < GM::ENTRIES * GM::COPIES; e += kLogitThreads) t_code[e] = lut[e / GM::COPIES];
+  if constexpr (PROD)
+    for (int e = tid; e < 256 * kSignCopies; e += kLogitThreads)
+      t_sg[e] = ((const u32x4 *)(lut + (MB > 0 ? GM::WORDS : 0)))[e / kSignCopies];
+  if (tid == 0) *counter = kLogitWaves;
   __syncthreads();
-  {
-    // rotate (threads 0..127) and project (threads 128..255) every head once
-    const int j = tid & 127;
-    const float *W = tid < 128 ? PiT + (size_t)g * D * D
-                               : (PROD && tid < 256 ? ST + (size_t)g * D * D : nullptr);
-    if (W) {
-      float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int k = 0; k < D; ++k) {
-        const float w = W[(size_t)k * D + j];
+  // 2. rotate (Pi q) and project (S q) every head: thread (mat, slice, j)
+  // sums 32 contraction steps for output coordinate j
+  if (mat == 0 || PROD) {
+    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int h = 0; h < 8; ++h) a[h] = fmaf(w, qs[h * D + k], a[h]);
-      }
-      float *dst = tid < 128 ? qt : pp;
+    for (int k = 0; k < 32; ++k)
 #pragma unroll
-      for (int h = 0; h < 8; ++h) dst[h * D + j] = a[h];
-    }
+      for (int h = 0; h < 8; ++h) a[h] = fmaf(w[k], qs[h * D + 32 * slice + k], a[h]);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) scratch[((mat * 4 + slice) * 8 + h) * D + jj] = a[h];
   }
   __syncthreads();
-  // Query operands (MFMA A): row col = (head col >> 1, part col & 1);
+  // 3. reduce the four slices
+  for (int e = tid; e < (PROD ? 2 : 1) * 8 * D; e += kLogitThreads) {
+    const int m = e / (8 * D), hj = e % (8 * D);
+    float v = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) v += scratch[(m * 4 + sl) * 8 * D + hj];
+    (m == 0 ? qt : pp)[hj] = v;
+  }
+  __syncthreads();
+  // 4. query operands (MFMA A): row col = (head col >> 1, part col & 1);
   // contraction element e of K step k is coordinate 32 grp + 8 k + e.
   u32x4 bq[4], bp[4];
   {
@@ -765,62 +812,62 @@ __global__ __launch_bounds__(kLogitThreads, 2) void k_logits128(
       }
     }
   }
-  const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
-  const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
-  const int64_t srow = (int64_t)s * n_keys;
-  const int hA = 2 * grp, hB = 2 * grp + 1;  // heads held by this lane
-  float *outA = out + ((int64_t)s * nq + h0 + hA) * n_keys;
-  float *outB = out + ((int64_t)s * nq + h0 + hB) * n_keys;
-  const bool wA = hA < hc, wB = hB < hc;
-  const uint8_t *cbase = MB > 0 ? codes + srow * (16 * CW) + grp * (4 * CW) : nullptr;
-  const uint8_t *sbase = PROD ? signs + srow * 16 + grp * 4 : nullptr;
-  const float *nbase = norms + srow;
-  const float *gbase = PROD ? rnorms + srow : nullptr;
 
-  constexpr int KT = kLogitTiles;
-  constexpr int W = 16 * KT;  // keys per wave iteration
-  KeyRegs<CW> ra, rb;  // ping-pong: one set is scored while the other loads
-  int64_t t0 = kbeg + (int64_t)wave * W;
+  const int hA = 2 * grp, hB = 2 * grp + 1;  // heads held by this lane
+  // logits of this set through a buffer resource: lanes without a head, and
+  // keys past the end, get an offset past num_records and store nothing
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)s * nq * n_keys, 0, (int)(nq * n_keys * 4), kBufferFlags);
+  const uint32_t rowA = hA < hc ? (uint32_t)((h0 + hA) * n_keys) * 4 : kDropped;
+  const uint32_t rowB = hB < hc ? (uint32_t)((h0 + hB) * n_keys) * 4 : kDropped;
+  // each lane reads its own copy of every table entry (the tables start at
+  // LDS address 0 and CODE_BYTES, so the copy offset is OR-ed in)
+  const uint32_t code_base = 4 * (lane & (GM::COPIES - 1));
+  const uint32_t sign_base = 16 * (lane & (kSignCopies - 1));
+  auto grab = [&]() {  // next block of this workgroup's range (wave-uniform)
+    uint32_t b = 0;
+    if (lane == 0) b = atomicAdd(counter, 1u);
+    return (int)__builtin_amdgcn_readfirstlane(__shfl(b, 0));
+  };
   auto score_store = [&](const KeyRegs<CW> &r, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
       float o0, o1;
-      score_tile<MB, PROD>(r, u, bq, bp, t_code, t_sg, o0, o1);
-      const int64_t key = tb + 16 * u + col;
-      if (wA) outA[key] = o0;
-      if (wB) outB[key] = o1;
+      score_tile<MB, PROD>(r, u, bq, bp, code_base, sign_base, o0, o1);
+      const uint32_t key4 = (uint32_t)(tb + 16 * u + col) * 4;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o0), ro, rowA + key4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o1), ro, rowB + key4, 0, 0);
     }
   };
-  if (t0 + W <= kend) {
-    load_full<CW, PROD, KT>(ra, t0, col, cbase, sbase, nbase, gbase);
+  if (b < nfull) {  // ra holds block b
     while (true) {
       // The prefetch is unconditional (a branch around it would make the
-      // wait-count pass wait for it): past the end it re-reads tile t0.
-      int64_t t1 = t0 + kLogitWaves * W;
-      bool more = t1 + W <= kend;
-      load_full<CW, PROD, KT>(rb, more ? t1 : t0, col, cbase, sbase, nbase, gbase);
-      score_store(ra, t0);
-      t0 = t1;
+      // wait-count pass wait for it): past the end it re-reads block b.
+      int b2 = grab();
+      bool more = b2 < nfull;
+      load_full<CW, PROD, KT>(rb, kbeg + (int64_t)(more ? b2 : b) * W, col, cbase, sbase, nbase, gbase);
+      score_store(ra, kbeg + (int64_t)b * W);
+      b = b2;
       if (!more) break;
-      t1 = t0 + kLogitWaves * W;
-      more = t1 + W <= kend;
-      load_full<CW, PROD, KT>(ra, more ? t1 : t0, col, cbase, sbase, nbase, gbase);
-      score_store(rb, t0);
-      t0 = t1;
+      b2 = grab();
+      more = b2 < nfull;
+      load_full<CW, PROD, KT>(ra, kbeg + (int64_t)(more ? b2 : b) * W, col, cbase, sbase, nbase, gbase);
+      score_store(rb, kbeg + (int64_t)b * W);
+      b = b2;
       if (!more) break;
     }
   }
-  if (t0 < kend) {  // ragged tail of this workgroup's range: guarded loads and stores
+  if (b == nfull && ragged) {  // the one wave that holds the partial block: guarded loads and stores
+    const int64_t t0 = kbeg + (int64_t)nfull * W;
     load_tail<CW, PROD, KT>(ra, t0, kend, col, cbase, sbase, nbase, gbase);
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
       float o0, o1;
-      score_tile<MB, PROD>(ra, u, bq, bp, t_code, t_sg, o0, o1);
+      score_tile<MB, PROD>(ra, u, bq, bp, code_base, sign_base, o0, o1);
       const int64_t key = t0 + 16 * u + col;
-      if (key < kend) {
-        if (wA) outA[key] = o0;
-        if (wB) outB[key] = o1;
-      }
+      const uint32_t key4 = (uint32_t)key * 4;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o0), ro, key < kend ? rowA + key4 : kDropped, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o1), ro, key < kend ? rowB + key4 : kDropped, 0, 0);
     }
   }
 }
@@ -873,16 +920,22 @@ hipError_t run_logits(const DeviceTables &t, const float *q, int64_t nq, const u
                       const uint8_t *signs, const float *norms, const float *rnorms, int64_t n_sets,
                       int64_t n_keys, float *out, hipStream_t st) {
   const int64_t unit = kLogitWaves * 16 * kLogitTiles;  // keys per workgroup iteration
-  int64_t gx = (512 + n_sets - 1) / n_sets;             // about one round of workgroups
+  int64_t gx = (256 + n_sets - 1) / n_sets;             // about one workgroup per CU
   const int64_t max_gx = (n_keys + unit - 1) / unit;
   if (gx > max_gx) gx = max_gx;
   if (gx < 1) gx = 1;
   int64_t kpw = (n_keys + gx - 1) / gx;
   kpw = (kpw + unit - 1) / unit * unit;
   gx = (n_keys + kpw - 1) / kpw;
+  // a set's logits are addressed with 32-bit byte offsets below the dropped-store offset
+  if (nq * n_keys * 4 >= (int64_t)kDropped) return hipErrorNotSupported;
+  const size_t lds = LutGeom<MB>::CODE_BYTES + kSignBytes + kQueryBytes + 2 * 4 * 8 * D * 4 + 16;
+  hipError_t e0 = hipFuncSetAttribute((const void *)k_logits128<MB, PROD>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e0 != hipSuccess) return e0;
   for (int64_t h0 = 0; h0 < nq; h0 += 8) {
     const int hc = (int)(nq - h0 < 8 ? nq - h0 : 8);
-    hipLaunchKernelGGL((k_logits128<MB, PROD>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kLogitThreads), 0,
+    hipLaunchKernelGGL((k_logits128<MB, PROD>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kLogitThreads), lds,
                        st, q, (int)nq, (int)h0, hc, codes, signs, norms, rnorms, n_keys, t.groups,
                        t.PiT, t.ST, t.logit_lut, t.lut_inv_scale, kpw, out);
     const hipError_t e = hipGetLastError();
@@ -936,14 +989,8 @@ void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out)
 
 // Decode-table geometry: one lookup turns G codes of `mse_bits` bits (one
 // index of G * mse_bits <= 12 bits) into G f16 values.
-static int lut_group(int mse_bits) { return mse_bits == 1 ? 8 : (mse_bits == 4 ? 2 : 4); }
-
 size_t fast128_lut_words(int mse_bits) {
-  size_t code_words = 0;
-  if (mse_bits > 0) {
-    const int G = lut_group(mse_bits);
-    code_words = ((size_t)1 << (G * mse_bits)) * (size_t)G / 2;
-  }
+  const size_t code_words = mse_bits > 0 ? (size_t)1 << (2 * mse_bits) : 0;  // code pair -> 2 x f16
   return code_words + 256 * 4;  // + sign table: byte -> 8 x (+1 / -1)
 }
 
@@ -976,14 +1023,10 @@ float fast128_build_logit_lut(const float *cent, int mse_bits, uint32_t *out) {
   }
   size_t w = 0;
   if (mse_bits > 0) {
-    const int G = lut_group(mse_bits);
-    const int entries = 1 << (G * mse_bits);
-    for (int e = 0; e < entries; ++e)
-      for (int h = 0; h < G; h += 2) {
-        const int i0 = (e >> (h * mse_bits)) & (L - 1);
-        const int i1 = (e >> ((h + 1) * mse_bits)) & (L - 1);
-        out[w++] = (uint32_t)h16(alpha * cent[i0]) | ((uint32_t)h16(alpha * cent[i1]) << 16);
-      }
+    for (int e = 0; e < (1 << (2 * mse_bits)); ++e) {
+      const int i0 = e & (L - 1), i1 = (e >> mse_bits) & (L - 1);
+      out[w++] = (uint32_t)h16(alpha * cent[i0]) | ((uint32_t)h16(alpha * cent[i1]) << 16);
+    }
   }
   for (int byte = 0; byte < 256; ++byte)
     for (int h = 0; h < 8; h += 2) {
