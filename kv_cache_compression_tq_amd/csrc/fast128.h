@@ -17,8 +17,9 @@ size_t fast128_rotation_words(int d);
 // holding 32 consecutive output coordinates.  k_order 0: the contraction index
 // follows the input-vector load order (rotation of x); k_order 1: it follows
 // the lane-chunk order of register-resident rotated coordinates (QJL
-// projection of the residual).
-void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out);
+// projection of the residual, dequantization).  f16: split into f16 hi/lo
+// parts instead of bf16 (operands multiplied with f16 decode tables).
+void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out, bool f16 = false);
 
 // Words of the logits decode tables for `mse_bits` (pair LUT + sign LUT).
 // The pair LUT holds f16 values of alpha * c, with alpha > 0 chosen so that

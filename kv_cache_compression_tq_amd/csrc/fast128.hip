@@ -627,6 +627,176 @@ __device__ __forceinline__ void load_tail(KeyRegs<CW> &r, int64_t t0, int64_t ke
   }
 }
 
+// ---------------------------------------------------------- dequantize --
+// x = nu Pi^T c[idx] (mse) and x = nu (Pi^T c[idx] + sqrt(pi/2)/d gamma S^T z)
+// (prod) as f16 MFMAs: the A operands are f16 hi/lo images of Pi^T and S^T
+// staged in LDS (output coordinates permuted as in the rotation, contraction
+// in lane-chunk order), the B operands the decoded codes (alpha c, two per
+// table read) and signs (+1/-1, eight per read) of 16 vectors.  Each lane
+// ends with 32 consecutive output coordinates of one vector and writes them
+// as eight 16-byte stores.  [tqnet] 实现步骤草图 (dequant: inverse rotation of
+// the centroids); [ttakun] TurboQuant_prod (residual reconstruction).
+constexpr int kDqThreads = 512;
+constexpr int kDqCodeCopies = 16;  // u32 entries; the copy is the low lane bits
+constexpr int kDqSignCopies = 4;   // u32x4 entries
+
+template <int MB>
+struct DqGeom {
+  static constexpr int W = 2 * MB;                               // two codes per read
+  static constexpr int SHIFT = 6;                                // log2(4 kDqCodeCopies)
+  static constexpr uint32_t CODE_BYTES = MB > 0 ? (1u << W) * kDqCodeCopies * 4 : 0;
+  static constexpr uint32_t SIGN_OFF = CODE_BYTES;
+  static constexpr uint32_t SIGN_BYTES = 256 * kDqSignCopies * 16;
+  static constexpr uint32_t IMG_OFF = SIGN_OFF + SIGN_BYTES;
+};
+
+template <int MB, bool PROD>
+__global__ __launch_bounds__(kDqThreads, 1) void k_dequant128(
+    const uint8_t *__restrict__ codes, const uint8_t *__restrict__ signs, const float *__restrict__ norms,
+    const float *__restrict__ rnorms, int64_t n, int groups, const u32x4 *__restrict__ pi_img,
+    const u32x4 *__restrict__ s_img, const uint32_t *__restrict__ lut, float inv_alpha, float *__restrict__ out) {
+  using GQ = DqGeom<MB>;
+  constexpr int CW = MB;
+  extern __shared__ u32x4 dyn_lds[];  // the kernel's only LDS: starts at address 0
+  uint32_t *t_code = (uint32_t *)dyn_lds;
+  u32x4 *t_sg = (u32x4 *)((char *)dyn_lds + GQ::SIGN_OFF);
+  u32x4 *img = (u32x4 *)((char *)dyn_lds + GQ::IMG_OFF);
+  const int s = blockIdx.y;
+  const int g = s % groups;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+
+  if constexpr (MB > 0)
+    for (int e = tid; e < (1 << GQ::W) * kDqCodeCopies; e += kDqThreads) t_code[e] = lut[e / kDqCodeCopies];
+  if constexpr (PROD)
+    for (int e = tid; e < 256 * kDqSignCopies; e += kDqThreads)
+      t_sg[e] = ((const u32x4 *)(lut + (MB > 0 ? (1 << GQ::W) : 0)))[e / kDqSignCopies];
+  if constexpr (MB > 0)
+    for (int i = tid; i < kImageVec; i += kDqThreads) img[i] = pi_img[(size_t)g * kImageVec + i];
+  if constexpr (PROD)
+    for (int i = tid; i < kImageVec; i += kDqThreads)
+      img[(MB > 0 ? kImageVec : 0) + i] = s_img[(size_t)g * kImageVec + i];
+  __syncthreads();
+
+  const int64_t ntiles = (n + 31) / 32;
+  const int64_t set_row0 = (int64_t)s * n;
+  constexpr int kWaves = kDqThreads / 64;
+  const int64_t stride = (int64_t)gridDim.x * kWaves;
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(out + set_row0 * D, 0, (int)(n * D * 4), kBufferFlags);
+  const uint32_t code_base = 4 * (lane & (kDqCodeCopies - 1));
+  const uint32_t sign_base = 16 * (lane & (kDqSignCopies - 1));
+  const float qjl = kQjlScale / (float)D;
+
+  for (int64_t tile = (int64_t)blockIdx.x * kWaves + wave; tile < ntiles; tile += stride) {
+    // an opaque offset keeps the image reads inside the loop (hoisted, 64 KB
+    // of fragments would not fit in registers)
+    int frag_lane = lane;
+    asm volatile("" : "+v"(frag_lane));
+    f32x4 acc[2][8];
+    float scale_c[2], scale_s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
+    }
+    uint32_t cw[2][CW > 0 ? CW : 1], sw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      int64_t v = tile * 32 + 16 * t + col;
+      v = v < n ? v : n - 1;  // ragged tail: a valid row, the store is dropped
+      const int64_t row = set_row0 + v;
+      if constexpr (MB > 0) load_codes<CW>(cw[t], codes + row * (16 * CW) + grp * (4 * CW));
+      if constexpr (PROD) sw[t] = *(const uint32_t *)(signs + row * 16 + grp * 4);
+      const float nu = norms[row];
+      scale_c[t] = nu * inv_alpha;
+      scale_s[t] = PROD ? nu * qjl * rnorms[row] : 0.f;
+    }
+    if constexpr (MB > 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u32x4 bc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int j = 4 * k + jj;  // code pair j of the lane's 32 coordinates
+            const int bit = j * GQ::W, wi = bit >> 5, sh = bit & 31;
+            uint32_t x;
+            if (sh + GQ::W > 32)
+              x = __builtin_amdgcn_alignbit(cw[t][wi + 1], cw[t][wi], sh - GQ::SHIFT);
+            else if (sh >= GQ::SHIFT)
+              x = cw[t][wi] >> (sh - GQ::SHIFT);
+            else
+              x = cw[t][wi] << (GQ::SHIFT - sh);
+            const uint32_t addr = (x & (uint32_t)(((1 << GQ::W) - 1) << GQ::SHIFT)) | code_base;
+            bc[t][jj] = *(__attribute__((address_space(3))) const uint32_t *)(uintptr_t)addr;
+          }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int f = (m * 4 + k) * 2;
+          const u32x4 ah = img[f * kFragVec + frag_lane];
+          const u32x4 al = img[(f + 1) * kFragVec + frag_lane];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            acc[t][m] = mfma_f16(ah, bc[t], acc[t][m]);
+            acc[t][m] = mfma_f16(al, bc[t], acc[t][m]);
+          }
+        }
+      }
+    }
+    // the code part is scaled now, so the sign part accumulates on top of it
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[t][m] *= scale_c[t];
+    if constexpr (PROD) {
+      f32x4 as[2][8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) as[t][m] = f32x4{0, 0, 0, 0};
+      constexpr int SIMG = MB > 0 ? kImageVec : 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        u32x4 bs[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          // sign byte k times the entry stride (64 bytes), OR the lane's copy
+          const uint32_t x = k == 0 ? sw[t] << 6 : sw[t] >> (8 * k - 6);
+          const uint32_t addr = (x & 0x3FC0u) | sign_base;
+          bs[t] = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(addr + GQ::SIGN_OFF);
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int f = (m * 4 + k) * 2;
+          const u32x4 ah = img[SIMG + f * kFragVec + frag_lane];
+          const u32x4 al = img[SIMG + (f + 1) * kFragVec + frag_lane];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            as[t][m] = mfma_f16(ah, bs[t], as[t][m]);
+            as[t][m] = mfma_f16(al, bs[t], as[t][m]);
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[t][m] += as[t][m] * scale_s[t];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t v = tile * 32 + 16 * t + col;
+      // coordinates 32 grp + 4 m + q of vector v are acc[t][m][q]
+      const uint32_t base = v < n ? (uint32_t)(v * D + 32 * grp) * 4 : kDropped;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t][m]), ro, base + 16 * m, 0, 0);
+    }
+  }
+}
+
 // Decode tables (the host builds one copy): one u32 per pair of codes (two
 // f16 values alpha c[i0], alpha c[i1]) and one u32x4 per sign byte (eight f16
 // +1 / -1).  In LDS every entry is replicated so that each lane reads its own
@@ -872,6 +1042,27 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   }
 }
 
+template <int MB, bool PROD>
+hipError_t run_dequant(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs, const float *norms,
+                       const float *rnorms, int64_t n_sets, int64_t n, float *out, hipStream_t st) {
+  using GQ = DqGeom<MB>;
+  if (n * D * 4 >= (int64_t)kDropped) return hipErrorNotSupported;
+  const size_t lds = GQ::IMG_OFF + ((MB > 0 ? 1 : 0) + (PROD ? 1 : 0)) * (size_t)kImageVec * 16;
+  hipError_t e = hipFuncSetAttribute((const void *)k_dequant128<MB, PROD>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t ntiles = (n + 31) / 32;
+  constexpr int waves = kDqThreads / 64;
+  const int64_t per_set_max = (ntiles + waves - 1) / waves;
+  int64_t gx = (256 + n_sets - 1) / n_sets;  // one workgroup per CU
+  if (gx > per_set_max) gx = per_set_max;
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL((k_dequant128<MB, PROD>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kDqThreads), lds, st,
+                     codes, signs, norms, rnorms, n, t.groups, (const u32x4 *)t.dq_pi_frag,
+                     (const u32x4 *)t.dq_s_frag, t.logit_lut, t.lut_inv_scale, out);
+  return hipGetLastError();
+}
+
 template <int MB>
 hipError_t run_quant_mse(const DeviceTables &t, const void *x, int64_t n_sets, int64_t n,
                          uint8_t *codes, float *norms, hipStream_t st) {
@@ -967,7 +1158,14 @@ static float host_bf16_to_f(uint16_t h) {
   return f;
 }
 
-void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out) {
+static uint16_t host_f16(float f) {
+  const _Float16 h = (_Float16)f;
+  uint16_t u;
+  memcpy(&u, &h, 2);
+  return u;
+}
+
+void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out, bool f16) {
   memset(out, 0, (size_t)kImageWords * 4);
   for (int m = 0; m < 8; ++m)
     for (int k = 0; k < 4; ++k)
@@ -979,8 +1177,14 @@ void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out)
           for (int e = 0; e < 8; ++e) {
             const int kin = k_order == 0 ? 32 * k + 8 * grp + e : 32 * grp + 8 * k + e;
             const float v = (float)mat[(size_t)orow * D + kin];
-            const uint16_t hi = host_bf16(v);
-            const uint16_t val = part == 0 ? hi : host_bf16(v - host_bf16_to_f(hi));
+            uint16_t val;
+            if (f16) {
+              const uint16_t hi = host_f16(v);
+              val = part == 0 ? hi : host_f16(v - (float)(_Float16)v);
+            } else {
+              const uint16_t hi = host_bf16(v);
+              val = part == 0 ? hi : host_bf16(v - host_bf16_to_f(hi));
+            }
             out[((size_t)f * 64 + lane) * 4 + e / 2] |= (uint32_t)val << (16 * (e & 1));
           }
         }
@@ -1062,6 +1266,19 @@ hipError_t launch_quant128(const DeviceTables &t, const void *x, int dtype, int6
   TQ_Q(3, false, false) TQ_Q(3, false, true) TQ_Q(3, true, false) TQ_Q(3, true, true)
   TQ_Q(4, false, false) TQ_Q(4, false, true) TQ_Q(4, true, false) TQ_Q(4, true, true)
 #undef TQ_Q
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_dequant128(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs,
+                             const float *norms, const float *rnorms, int64_t n_sets, int64_t n,
+                             float *out, hipStream_t st) {
+  if (t.d != D || !t.dq_pi_frag || t.mse_bits > 4 || ((uintptr_t)out & 15u)) return hipErrorNotSupported;
+  const bool prod = t.variant == 1;
+#define TQ_DQ(MB, P) \
+  if (t.mse_bits == MB && prod == P) return run_dequant<MB, P>(t, codes, signs, norms, rnorms, n_sets, n, out, st);
+  TQ_DQ(0, true) TQ_DQ(1, false) TQ_DQ(1, true) TQ_DQ(2, false) TQ_DQ(2, true)
+  TQ_DQ(3, false) TQ_DQ(3, true) TQ_DQ(4, false) TQ_DQ(4, true)
+#undef TQ_DQ
   return hipErrorNotSupported;
 }
 

@@ -25,6 +25,8 @@ struct DeviceTables {
   // d == 128 fast path: MFMA operand images (see quant128.hip)
   const uint32_t *pi_frag = nullptr;  // [G][...] bf16 hi/lo pairs, permuted rows
   const uint32_t *m_frag = nullptr;   // [G][...] same for M (prod)
+  const uint32_t *dq_pi_frag = nullptr;  // [G][...] f16 hi/lo image of Pi^T (dequantize)
+  const uint32_t *dq_s_frag = nullptr;   // [G][...] f16 hi/lo image of S^T (dequantize, prod)
   const uint32_t *logit_lut = nullptr; // packed f16 decode tables for logits128
   float lut_inv_scale = 1.f;           // 1 / alpha of the f16 centroid table
   // positive halves of the codebook (host values, passed as launch arguments)
@@ -57,6 +59,9 @@ hipError_t launch_unpack(const uint8_t *in, int bits, int64_t rows, int count, i
 hipError_t launch_quant128(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
                            int64_t n, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
                            hipStream_t st);
+hipError_t launch_dequant128(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs,
+                             const float *norms, const float *rnorms, int64_t n_sets, int64_t n,
+                             float *out, hipStream_t st);
 hipError_t launch_logits128(const DeviceTables &t, const float *q, int64_t nq,
                             const uint8_t *codes, const uint8_t *signs, const float *norms,
                             const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,

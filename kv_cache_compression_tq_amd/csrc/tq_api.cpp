@@ -82,6 +82,13 @@ void group_matrices(int d, uint64_t seed, int g, bool prod, std::vector<double> 
     }
 }
 
+// out = transpose of the d x d row-major matrix a
+void transpose(int d, const std::vector<double> &a, std::vector<double> &out) {
+  out.resize((size_t)d * d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) out[(size_t)j * d + i] = a[(size_t)i * d + j];
+}
+
 template <class T>
 T *carve(char *base, size_t &off, size_t count) {
   off = (off + 255) / 256 * 256;
@@ -126,6 +133,8 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
   std::vector<float> pi_all(groups * dd), pit_all(groups * dd);
   std::vector<float> s_all, st_all, mt_all;
   std::vector<uint32_t> pi_img(groups * rot_words), m_img(prod ? groups * rot_words : 0);
+  std::vector<uint32_t> dq_pi_img(groups * rot_words), dq_s_img(prod ? groups * rot_words : 0);
+  std::vector<double> trans;
   if (prod) {
     s_all.resize(groups * dd);
     st_all.resize(groups * dd);
@@ -140,7 +149,11 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
         P[(size_t)i * d + j] = (float)pi[(size_t)i * d + j];
         PT[(size_t)j * d + i] = (float)pi[(size_t)i * d + j];
       }
-    if (fast) tq::fast128_build_rotation_image(pi.data(), 0, &pi_img[g * rot_words]);
+    if (fast) {
+      tq::fast128_build_rotation_image(pi.data(), 0, &pi_img[g * rot_words]);
+      transpose(d, pi, trans);
+      tq::fast128_build_rotation_image(trans.data(), 1, &dq_pi_img[g * rot_words], true);
+    }
     if (prod) {
       float *S = &s_all[g * dd], *ST = &st_all[g * dd], *MT = &mt_all[g * dd];
       for (int i = 0; i < d; ++i)
@@ -149,7 +162,11 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
           ST[(size_t)j * d + i] = (float)s[(size_t)i * d + j];
           MT[(size_t)j * d + i] = (float)m[(size_t)i * d + j];
         }
-      if (fast) tq::fast128_build_rotation_image(m.data(), 1, &m_img[g * rot_words]);
+      if (fast) {
+        tq::fast128_build_rotation_image(m.data(), 1, &m_img[g * rot_words]);
+        transpose(d, s, trans);
+        tq::fast128_build_rotation_image(trans.data(), 1, &dq_s_img[g * rot_words], true);
+      }
     }
     if (g == 0) {
       h->h_pi.assign(P, P + dd);
@@ -178,6 +195,8 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     if (fast) {
       h->dev.pi_frag = carve<uint32_t>(base, off, groups * rot_words);
       if (prod) h->dev.m_frag = carve<uint32_t>(base, off, groups * rot_words);
+      h->dev.dq_pi_frag = carve<uint32_t>(base, off, groups * rot_words);
+      if (prod) h->dev.dq_s_frag = carve<uint32_t>(base, off, groups * rot_words);
       if (lut_words) h->dev.logit_lut = carve<uint32_t>(base, off, lut_words);
     }
     return off;
@@ -217,6 +236,8 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
   if (fast) {
     up(h->dev.pi_frag, pi_img.data(), pi_img.size() * 4);
     if (prod) up(h->dev.m_frag, m_img.data(), m_img.size() * 4);
+    up(h->dev.dq_pi_frag, dq_pi_img.data(), dq_pi_img.size() * 4);
+    if (prod) up(h->dev.dq_s_frag, dq_s_img.data(), dq_s_img.size() * 4);
     up(h->dev.logit_lut, lut.data(), lut.size() * 4);
   }
   if (e != hipSuccess) {
@@ -337,8 +358,11 @@ int tq_dequantize(tq_handle h, const void *codes, const void *signs, const float
   if (n_sets == 0 || n == 0) return TQ_OK;
   if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, false))) return st;
   if (!x_out || ((uintptr_t)x_out & 3u)) return fail(TQ_EINVAL, "x_out NULL or misaligned");
-  hipError_t e = tq::launch_dequant_generic(h->dev, (const uint8_t *)codes, (const uint8_t *)signs,
-                                            norms, rnorms, n_sets, n, x_out, (hipStream_t)stream);
+  hipError_t e = tq::launch_dequant128(h->dev, (const uint8_t *)codes, (const uint8_t *)signs, norms,
+                                       rnorms, n_sets, n, x_out, (hipStream_t)stream);
+  if (e == hipErrorNotSupported)
+    e = tq::launch_dequant_generic(h->dev, (const uint8_t *)codes, (const uint8_t *)signs, norms, rnorms,
+                                   n_sets, n, x_out, (hipStream_t)stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "dequantize launch");
 }
 

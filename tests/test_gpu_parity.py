@@ -219,7 +219,8 @@ def _stored(cd, keys_per_set):
     return out
 
 
-DEQ_CASES = [(128, 4, O.MSE), (128, 2, O.MSE), (128, 4, O.PROD), (128, 1, O.PROD), (200, 3, O.PROD), (200, 2, O.MSE)]
+DEQ_CASES = [(128, 4, O.MSE), (128, 2, O.MSE), (128, 1, O.MSE), (128, 3, O.MSE), (128, 4, O.PROD),
+             (128, 1, O.PROD), (128, 2, O.PROD), (128, 5, O.PROD), (200, 3, O.PROD), (200, 2, O.MSE)]
 
 
 @pytest.mark.parametrize("d,bits,variant", DEQ_CASES)
@@ -237,6 +238,23 @@ def test_dequantize_oracle_codes(d, bits, variant):
         else:
             ref = O.dequantize_prod(cd, k["idx"], k["signs"], k["norms"], k["rnorms"], s)
         check_rows(got[s], ref, f"dequant set {s}")
+
+
+@pytest.mark.parametrize("variant,bits", [(O.MSE, 4), (O.PROD, 4)])
+def test_dequantize_unaligned_output_matches(variant, bits):
+    """An output that is not 16-byte aligned takes the generic kernel; both
+    kernels reconstruct the same codes to the parity tolerance."""
+    d, n = 128, 333
+    x = np.random.default_rng(7).standard_normal((1, n, d))
+    cd = O.make_codec(d, bits, variant, 3)
+    codec = tq.Codec(d, bits, variant, seed=3)
+    stored = _stored(cd, [_oracle_keys(cd, x[0], 0)])
+    fast = codec.dequantize(stored).cpu().numpy()[0]
+    buf = torch.empty(n * d + 1, dtype=torch.float32, device="cuda")
+    view = buf[1:].view(1, n, d)  # 4-byte offset
+    codec.dequantize(stored, out=view)
+    slow = view.cpu().numpy()[0]
+    check_rows(slow, fast.astype(np.float64), "generic vs fast dequantize")
 
 
 LOGIT_CASES = [
