@@ -27,6 +27,10 @@ struct DeviceTables {
   const uint32_t *m_frag = nullptr;   // [G][...] same for M (prod)
   const uint32_t *dq_pi_frag = nullptr;  // [G][...] f16 hi/lo image of Pi^T (dequantize)
   const uint32_t *dq_s_frag = nullptr;   // [G][...] f16 hi/lo image of S^T (dequantize, prod)
+  // any d (multiple of 8) != 128: 128 x 128 blocks of Pi ([G][panel][chunk]) and,
+  // for prod, of S then M ([G][panel][2 chunks]); images as pi_frag
+  const uint32_t *tiled_rot = nullptr;
+  const uint32_t *tiled_sign = nullptr;
   const uint32_t *logit_lut = nullptr; // packed f16 decode tables for logits128
   float lut_inv_scale = 1.f;           // 1 / alpha of the f16 centroid table
   // positive halves of the codebook (host values, passed as launch arguments)
@@ -59,6 +63,8 @@ hipError_t launch_unpack(const uint8_t *in, int bits, int64_t rows, int count, i
 hipError_t launch_quant128(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
                            int64_t n, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
                            hipStream_t st);
+hipError_t launch_quant_tiled(const DeviceTables &t, const void *x, int dtype, int64_t n_sets, int64_t n,
+                              uint8_t *codes, uint8_t *signs, float *norms, float *rnorms, hipStream_t st);
 hipError_t launch_dequant128(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs,
                              const float *norms, const float *rnorms, int64_t n_sets, int64_t n,
                              float *out, hipStream_t st);

@@ -127,6 +127,14 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
   }
   const bool fast = tq::fast128_supported(d, mse_bits, variant);
   const size_t rot_words = fast ? tq::fast128_rotation_words(d) : 0;
+  // other dimensions (multiples of 8): 128 x 128 block images for the tiled
+  // kernels, when all of them fit in 1 GiB
+  const int nblk = (d + 127) / 128;
+  const size_t blk_words = tq::fast128_rotation_words(128);
+  const size_t tiled_rot_words = (size_t)groups * nblk * nblk * blk_words;
+  const size_t tiled_sign_words = prod ? 2 * tiled_rot_words : 0;
+  const bool tiled = !fast && d % 8 == 0 && mse_bits <= 4 && d > 8 &&
+                     (tiled_rot_words + tiled_sign_words) * 4 <= ((size_t)1 << 30);
   const size_t lut_words = fast ? tq::fast128_lut_words(mse_bits) : 0;
 
   // Host images of every device table.
@@ -135,6 +143,15 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
   std::vector<uint32_t> pi_img(groups * rot_words), m_img(prod ? groups * rot_words : 0);
   std::vector<uint32_t> dq_pi_img(groups * rot_words), dq_s_img(prod ? groups * rot_words : 0);
   std::vector<double> trans;
+  std::vector<uint32_t> t_rot(tiled ? tiled_rot_words : 0), t_sign(tiled ? tiled_sign_words : 0);
+  std::vector<double> blk(128 * 128);
+  // image of the 128 x 128 block (rows r0.., cols c0..) of a d x d matrix, zero past d
+  auto block_image = [&](const std::vector<double> &mat, int r0, int c0, int k_order, uint32_t *dst) {
+    for (int i = 0; i < 128; ++i)
+      for (int j = 0; j < 128; ++j)
+        blk[(size_t)i * 128 + j] = (r0 + i < d && c0 + j < d) ? mat[(size_t)(r0 + i) * d + c0 + j] : 0.0;
+    tq::fast128_build_rotation_image(blk.data(), k_order, dst);
+  };
   if (prod) {
     s_all.resize(groups * dd);
     st_all.resize(groups * dd);
@@ -168,6 +185,17 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
         tq::fast128_build_rotation_image(trans.data(), 1, &dq_s_img[g * rot_words], true);
       }
     }
+    if (tiled) {
+      for (int pp = 0; pp < nblk; ++pp)
+        for (int c = 0; c < nblk; ++c) {
+          block_image(pi, 128 * pp, 128 * c, 0, &t_rot[(((size_t)g * nblk + pp) * nblk + c) * blk_words]);
+          if (prod) {
+            const size_t base = ((size_t)g * nblk + pp) * 2 * nblk;
+            block_image(s, 128 * pp, 128 * c, 0, &t_sign[(base + c) * blk_words]);
+            block_image(m, 128 * pp, 128 * c, 1, &t_sign[(base + nblk + c) * blk_words]);
+          }
+        }
+    }
     if (g == 0) {
       h->h_pi.assign(P, P + dd);
       if (prod) h->h_s.assign(&s_all[0], &s_all[0] + dd);
@@ -192,6 +220,10 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     h->dev.cent = carve<float>(base, off, L ? L : 1);
     h->dev.bnd = carve<float>(base, off, L > 1 ? L - 1 : 1);
     h->dev.cells = carve<uint32_t>(base, off, cells.words.empty() ? 2 : cells.words.size());
+    if (tiled) {
+      h->dev.tiled_rot = carve<uint32_t>(base, off, tiled_rot_words);
+      if (prod) h->dev.tiled_sign = carve<uint32_t>(base, off, tiled_sign_words);
+    }
     if (fast) {
       h->dev.pi_frag = carve<uint32_t>(base, off, groups * rot_words);
       if (prod) h->dev.m_frag = carve<uint32_t>(base, off, groups * rot_words);
@@ -233,6 +265,10 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
   up(h->dev.cent, h->h_c.data(), h->h_c.size() * 4);
   up(h->dev.bnd, h->h_t.data(), h->h_t.size() * 4);
   up(h->dev.cells, cells.words.data(), cells.words.size() * 4);
+  if (tiled) {
+    up(h->dev.tiled_rot, t_rot.data(), t_rot.size() * 4);
+    if (prod) up(h->dev.tiled_sign, t_sign.data(), t_sign.size() * 4);
+  }
   if (fast) {
     up(h->dev.pi_frag, pi_img.data(), pi_img.size() * 4);
     if (prod) up(h->dev.m_frag, m_img.data(), m_img.size() * 4);
@@ -344,6 +380,9 @@ int tq_quantize(tq_handle h, const void *x, int dtype, int64_t n_sets, int64_t n
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = tq::launch_quant128(h->dev, x, dtype, n_sets, n, (uint8_t *)codes,
                                      (uint8_t *)signs, norms, rnorms, s);
+  if (e == hipErrorNotSupported)
+    e = tq::launch_quant_tiled(h->dev, x, dtype, n_sets, n, (uint8_t *)codes, (uint8_t *)signs, norms,
+                               rnorms, s);
   if (e == hipErrorNotSupported)
     e = tq::launch_quant_generic(h->dev, x, dtype, n_sets, n, (uint8_t *)codes, (uint8_t *)signs,
                                  norms, rnorms, s);
