@@ -34,6 +34,8 @@ def _parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-logits", action="store_true")
+    p.add_argument("--skip-others", action="store_true",
+                   help="skip the non-headline paths (prod quantize, dequantize, high-d, NN indexing)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (counter calibration)")
     return p.parse_args()
@@ -147,6 +149,70 @@ def logits_phase(torch, tq, workloads, steps, warmup):
                 total_gbs=(packed + written) / (kern * 1e-3) / 1e9)
 
 
+def _mean_launch_ms(torch, fn, reps=5, warm=1):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = _events(torch, 2)
+    ev[0].record()
+    for _ in range(reps):
+        fn()
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def other_paths_phase(torch, tq, workloads, x_kv):
+    """The rest of the hot path, timed once each (not the headline metric):
+    TurboQuant_prod quantize and both dequantizes on the KV workload, the
+    high-dimensional quantize (d = 1536, 1e5 vectors; d = 3072, 5e4) and the
+    nearest-neighbour indexing (d = 200, 1e6 unit vectors).  Inputs are drawn
+    on the device with the workloads' distributions."""
+    res = {}
+    sets, n, d = x_kv.shape
+    xk = x_kv.cuda()
+    for variant, name in ((tq.TQ_MSE, "mse"), (tq.TQ_PROD, "prod")):
+        codec = tq.Codec(d, 4, variant, seed=0, groups=workloads.KV_HEADS)
+        out = codec.empty_codes(sets, n)
+        ms = _mean_launch_ms(torch, lambda: codec.quantize(xk, out=out))
+        if variant == tq.TQ_PROD:
+            res["kv_prod_b4_quantize_ms"] = ms
+        rec = torch.empty((sets, n, d), dtype=torch.float32, device="cuda")
+        ms = _mean_launch_ms(torch, lambda: codec.dequantize(out, out=rec))
+        res[f"kv_{name}_b4_dequantize_ms"] = ms
+        res[f"kv_{name}_b4_dequantize_gbs"] = (sets * n * (d * 4 + codec.code_row + codec.sign_row + 8)) / (ms * 1e-3) / 1e9
+        del rec
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    for dd, nn in ((1536, 100_000), (3072, 50_000)):
+        z = torch.randn((1, nn, dd), generator=gen, device="cuda")
+        rho = torch.empty((1, nn, 1), device="cuda").log_normal_(0.0, 0.5, generator=gen)
+        xh = z / z.norm(dim=2, keepdim=True) * rho
+        del z
+        for variant, name, bits in ((tq.TQ_MSE, "mse", 4), (tq.TQ_PROD, "prod", 4)):
+            codec = tq.Codec(dd, bits, variant, seed=0)
+            out = codec.empty_codes(1, nn)
+            ms = _mean_launch_ms(torch, lambda: codec.quantize(xh, out=out))
+            # f32 input: 3 split-bf16 passes per GEMM; prod adds S x and M c (2 d contraction)
+            gemm = 1 if variant == tq.TQ_MSE else 3
+            flops = 2.0 * nn * dd * dd * 3 * gemm
+            res[f"d{dd}_{name}_b{bits}_quantize_ms"] = ms
+            res[f"d{dd}_{name}_b{bits}_vectors_per_s"] = nn / (ms * 1e-3)
+            res[f"d{dd}_{name}_b{bits}_mfma_frac"] = flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS
+        del xh
+    centres = torch.randn((workloads.NN_CENTRES, workloads.NN_D), generator=gen, device="cuda")
+    centres /= centres.norm(dim=1, keepdim=True)
+    m = torch.randint(0, workloads.NN_CENTRES, (workloads.NN_POINTS,), generator=gen, device="cuda")
+    pts = centres[m] + workloads.NN_STD * torch.randn((workloads.NN_POINTS, workloads.NN_D), generator=gen,
+                                                      device="cuda")
+    pts = (pts / pts.norm(dim=1, keepdim=True)).unsqueeze(0).contiguous()
+    for bits in (2, 4):
+        codec = tq.Codec(workloads.NN_D, bits, tq.TQ_PROD, seed=0)
+        out = codec.empty_codes(1, workloads.NN_POINTS)
+        res[f"nn_index_d200_prod_b{bits}_ms"] = _mean_launch_ms(torch, lambda: codec.quantize(pts, out=out))
+    return res
+
+
 def cpu_baseline(workloads, x_bf16, budget_s=15.0):
     """The oracle (float64 NumPy) quantizing a bounded sample of the same KV
     workload; vectors/s extrapolated from the sample."""
@@ -188,6 +254,7 @@ def main():
     qp = quantize_phase(torch, tq, workloads, args.steps, args.warmup)
     q3 = quantize_b3_phase(torch, tq, workloads, qp["x"], args.steps, args.warmup)
     lp = None if args.skip_logits else logits_phase(torch, tq, workloads, args.steps, args.warmup)
+    other = None if args.skip_others else other_paths_phase(torch, tq, workloads, qp["x"])
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, qp["x"])
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -240,6 +307,8 @@ def main():
                          "frac_incl_logits_written": lp["total_gbs"] / HBM_PEAK_GBS},
             "cache_build_s": lp["cache_build_s"],
         }
+    if other is not None:
+        line["other_paths"] = other
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
