@@ -392,6 +392,25 @@ def logits_plain(cd: Codec, q: np.ndarray, keys: dict, group: int = 0) -> np.nda
     return np.asarray(q, dtype=np.float64) @ kh.T
 
 
+def attention_plain(cd_k: Codec, cd_v: Codec, q: np.ndarray, keys: dict, values: dict, scale: float,
+                    group: int = 0) -> np.ndarray:
+    """Decode attention over quantized keys and values: for every query h,
+    out[h] = sum_t softmax_t(scale * <q_h, k_hat_t>) v_hat_t, with k_hat and
+    v_hat the dequantized keys and values ([tqnet] 实现步骤草图 › 集成到 attention: keys and values
+    both go through the quantizer and the attention stage reads the QJL-coded
+    keys; the softmax of scaled inner products is scaled dot-product
+    attention, Vaswani et al., "Attention Is All You Need", 2017).
+    q: [nq, d]; returns [nq, d]."""
+    logit = scale * logits_plain(cd_k, q, keys, group)
+    w = np.exp(logit - logit.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    if cd_v.variant == MSE:
+        vh = dequantize_mse(cd_v, values["idx"], values["norms"], group)
+    else:
+        vh = dequantize_prod(cd_v, values.get("idx"), values["signs"], values["norms"], values["rnorms"], group)
+    return w @ vh
+
+
 def logits_fast(cd: Codec, q: np.ndarray, keys: dict, group: int = 0) -> np.ndarray:
     """The same quantity evaluated in the rotated/projected domain:
     <q, Pi^T c> = <Pi q, c> and <q, S^T z> = <S q, z> ([admirer] 第二步: the
