@@ -105,6 +105,33 @@ int tq_logits(tq_handle h, const float *q, int64_t nq, const void *codes, const 
               const float *norms, const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
               void *stream);
 
+/* Decode attention over quantized keys and values ([tqnet] 实现步骤草图 ›
+ * 集成到 attention: keys and values are both stored in the quantized format and
+ * attention reads the QJL-coded keys).  For set s and query i:
+ *   out[s][i] = sum_t softmax_t(scale * <q[s][i], k_hat[s][t]>) v_hat[s][t],
+ * with k_hat the tq_dequantize reconstruction of the keys under hk and v_hat
+ * that of the values under hv (same d; any variants and bits).  The softmax
+ * runs over the n_keys keys of set s; scale is the caller's (1/sqrt(d) for
+ * standard attention) and must be finite.  Set s uses group s % groups of
+ * each codec.  q: [n_sets][nq][d] float32, out: [n_sets][nq][d] float32
+ * (4-byte aligned); key and value arrays as in tq_logits / tq_dequantize.
+ * workspace: caller-owned device memory, 256-byte aligned, of at least the
+ * size tq_attention_workspace reports for the same (hk, hv, nq, n_sets,
+ * n_keys); its contents are scratch (undefined before and after), and two
+ * calls in flight at once need two workspaces.  1 <= nq <= 64; n_keys >= 1
+ * unless n_sets == 0 (a no-op).  Errors: TQ_EINVAL (also for a small or
+ * misaligned workspace), TQ_EHIP. */
+int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const void *k_codes,
+                 const void *k_signs, const float *k_norms, const float *k_rnorms, const void *v_codes,
+                 const void *v_signs, const float *v_norms, const float *v_rnorms, int64_t n_sets,
+                 int64_t n_keys, float scale, float *out, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* Workspace bytes tq_attention needs for this shape (0 when n_sets == 0).
+ * Host only; validates as tq_attention does.  Errors: TQ_EINVAL. */
+int tq_attention_workspace(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_sets, int64_t n_keys,
+                           size_t *bytes);
+
 /* Static text for a status code. */
 const char *tq_strerror(int status);
 /* Thread-local detail of the last failure on this thread ("" if none). */

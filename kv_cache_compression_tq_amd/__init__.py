@@ -31,6 +31,9 @@ _SIGS = {
     "tq_quantize": (_INT, [_P, _P, _INT, _I64, _I64, _P, _P, _P, _P, _P]),
     "tq_dequantize": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _P, _P]),
     "tq_logits": (_INT, [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P]),
+    "tq_attention": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P,
+                            ctypes.c_size_t, _P]),
+    "tq_attention_workspace": (_INT, [_P, _P, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
     "tq_strerror": (ctypes.c_char_p, [_INT]),
     "tq_last_error": (ctypes.c_char_p, []),
     "tq_get_tables": (_INT, [_P, _INT, _P, _P, _P, _P]),
@@ -184,6 +187,44 @@ class Codec:
             out = torch.empty((n_sets, nq, n_keys), dtype=torch.float32, device=norms.device)
         _check(lib().tq_logits(self._h, _ptr(q), nq, _ptr(keys.get("codes")), _ptr(keys.get("signs")), _ptr(norms),
                                _ptr(keys.get("rnorms")), n_sets, n_keys, _ptr(out), _stream(stream)), "tq_logits")
+        return out
+
+    def attention_workspace_bytes(self, values_codec: "Codec", nq: int, n_sets: int, n_keys: int) -> int:
+        b = ctypes.c_size_t()
+        _check(lib().tq_attention_workspace(self._h, values_codec.handle, nq, n_sets, n_keys, ctypes.byref(b)),
+               "tq_attention_workspace")
+        return b.value
+
+    def attention(self, q, keys, values_codec: "Codec", values, scale=None, out=None, workspace=None, stream=None):
+        """Decode attention: this codec holds the keys, `values_codec` the
+        values.  q: [n_sets, nq, d] float32.  Returns [n_sets, nq, d] float32
+        sum_t softmax_t(scale <q, k_hat_t>) v_hat_t (scale defaults to
+        1/sqrt(d)).  `workspace` is a uint8 CUDA tensor (allocated here when
+        not given)."""
+        import math
+
+        import torch
+
+        if q.dim() == 2:
+            q = q.unsqueeze(0)
+        if q.dtype != torch.float32 or not q.is_contiguous():
+            raise TypeError("q must be contiguous float32")
+        n_sets, n_keys = keys["norms"].shape
+        nq = q.shape[1]
+        if q.shape[0] != n_sets or q.shape[2] != self.d or values["norms"].shape != keys["norms"].shape:
+            raise ValueError("q, keys and values do not match")
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.d)
+        if out is None:
+            out = torch.empty((n_sets, nq, self.d), dtype=torch.float32, device=q.device)
+        need = self.attention_workspace_bytes(values_codec, nq, n_sets, n_keys)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _check(lib().tq_attention(self._h, values_codec.handle, _ptr(q), nq, _ptr(keys.get("codes")),
+                                  _ptr(keys.get("signs")), _ptr(keys["norms"]), _ptr(keys.get("rnorms")),
+                                  _ptr(values.get("codes")), _ptr(values.get("signs")), _ptr(values["norms"]),
+                                  _ptr(values.get("rnorms")), n_sets, n_keys, float(scale), _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream(stream)), "tq_attention")
         return out
 
     # -- test hooks ----------------------------------------------------------

@@ -209,6 +209,116 @@ __global__ __launch_bounds__(kThreads) void k_logits_generic(
   }
 }
 
+// ------------------------------------------------------------ attention --
+// Decode attention over quantized keys and values, any d: the logits come
+// from the logits kernels; these three kernels turn them into
+// out = sum_t softmax_t(scale l_t) v_hat_t.
+
+// One workgroup per (set, head) row: the row's logits become normalised
+// softmax weights in place (max, sum of exponentials, divide).
+__global__ __launch_bounds__(kThreads) void k_softmax_rows(float *__restrict__ w, int64_t n_keys, float scale) {
+  __shared__ float red[kThreads / 64];
+  float *row = w + (int64_t)blockIdx.x * n_keys;
+  const int tid = threadIdx.x;
+  float m = -INFINITY;
+  for (int64_t t = tid; t < n_keys; t += kThreads) m = fmaxf(m, scale * row[t]);
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = red[0];
+  for (int i = 1; i < kThreads / 64; ++i) m = fmaxf(m, red[i]);
+  float sum = 0.f;
+  for (int64_t t = tid; t < n_keys; t += kThreads) sum += expf(scale * row[t] - m);
+  sum = block_sum(sum, red);
+  const float inv = 1.f / sum;
+  for (int64_t t = tid; t < n_keys; t += kThreads) row[t] = expf(scale * row[t] - m) * inv;
+}
+
+constexpr int kAttnChunk = 256;  // keys per workgroup of the value pass
+
+// Value pass: workgroup (chunk, set) adds, for every head h and coordinate j,
+//   a[h][j] = sum_t w[h][t] nu_t c[idx_tj]        (rotated domain)
+//   b[h][j] = sum_t w[h][t] nu_t gamma_t z_tj     (projected domain, prod)
+// over its chunk of keys, and writes them to part[chunk][set][h][2][d].
+__global__ __launch_bounds__(kThreads) void k_attn_values_generic(
+    const float *__restrict__ w, int nq, const uint8_t *__restrict__ codes, const uint8_t *__restrict__ signs,
+    const float *__restrict__ norms, const float *__restrict__ rnorms, int d, int64_t n_keys, int mse_bits,
+    int prod, const float *__restrict__ cent, int64_t code_row, int64_t sign_row, float *__restrict__ part) {
+  __shared__ float ws[kMaxHeads][kAttnChunk];
+  __shared__ float nv[kAttnChunk], gv[kAttnChunk];
+  const int64_t chunk = blockIdx.x, n_sets = gridDim.y;
+  const int s = blockIdx.y, tid = threadIdx.x;
+  const int64_t t0 = chunk * kAttnChunk;
+  const int tc = (int)(n_keys - t0 < kAttnChunk ? n_keys - t0 : kAttnChunk);
+  const int64_t srow = (int64_t)s * n_keys;
+  for (int i = tid; i < tc; i += kThreads) {
+    nv[i] = norms[srow + t0 + i];
+    gv[i] = prod ? rnorms[srow + t0 + i] : 0.f;
+  }
+  for (int h0 = 0; h0 < nq; h0 += kMaxHeads) {
+    const int hc = nq - h0 < kMaxHeads ? nq - h0 : kMaxHeads;
+    __syncthreads();
+    for (int e = tid; e < hc * kAttnChunk; e += kThreads) {
+      const int h = e / kAttnChunk, i = e % kAttnChunk;
+      ws[h][i] = i < tc ? w[((int64_t)s * nq + h0 + h) * n_keys + t0 + i] * nv[i] : 0.f;
+    }
+    __syncthreads();
+    for (int j = tid; j < d; j += kThreads) {
+      float a[kMaxHeads], b[kMaxHeads];
+      for (int h = 0; h < kMaxHeads; ++h) a[h] = b[h] = 0.f;
+      for (int i = 0; i < tc; ++i) {
+        const int64_t row = srow + t0 + i;
+        const float c = mse_bits > 0 ? cent[read_field(codes + row * code_row, j, mse_bits)] : 0.f;
+        float z = 0.f;
+        if (prod) z = ((signs[row * sign_row + (j >> 3)] >> (j & 7)) & 1) ? gv[i] : -gv[i];
+        for (int h = 0; h < kMaxHeads; ++h)
+          if (h < hc) {
+            a[h] = fmaf(ws[h][i], c, a[h]);
+            b[h] = fmaf(ws[h][i], z, b[h]);
+          }
+      }
+      for (int h = 0; h < hc; ++h) {
+        float *o = part + (((chunk * n_sets + s) * nq + h0 + h) * 2) * (int64_t)d;
+        o[j] = a[h];
+        o[d + j] = b[h];
+      }
+    }
+  }
+}
+
+// Finish: workgroup (set, head) sums the chunks in a fixed order and maps the
+// result back: out = Pi^T a + sqrt(pi/2)/d S^T b.
+__global__ __launch_bounds__(kThreads) void k_attn_finish_generic(
+    const float *__restrict__ part, int64_t chunks, int nq, int d, int groups, int prod,
+    const float *__restrict__ Pi, const float *__restrict__ S, float *__restrict__ out) {
+  extern __shared__ float sm[];
+  float *av = sm, *bv = sm + d;
+  const int64_t n_sets = gridDim.y;
+  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int g = s % groups;
+  for (int j = tid; j < d; j += kThreads) {
+    float a = 0.f, b = 0.f;
+    for (int64_t c = 0; c < chunks; ++c) {
+      const float *o = part + (((c * n_sets + s) * nq + h) * 2) * (int64_t)d;
+      a += o[j];
+      b += o[d + j];
+    }
+    av[j] = a;
+    bv[j] = b;
+  }
+  __syncthreads();
+  const float *P = Pi + (size_t)g * d * d, *Sg = prod ? S + (size_t)g * d * d : nullptr;
+  const float ks = kQjlScale / (float)d;
+  for (int i = tid; i < d; i += kThreads) {
+    float a = 0.f, b = 0.f;
+    for (int j = 0; j < d; ++j) a = fmaf(P[(size_t)j * d + i], av[j], a);
+    if (prod)
+      for (int j = 0; j < d; ++j) b = fmaf(Sg[(size_t)j * d + i], bv[j], b);
+    out[((int64_t)s * nq + h) * d + i] = fmaf(ks, b, a);
+  }
+}
+
 __global__ void k_pack(const uint8_t *__restrict__ idx, int bits, int64_t rows, int count,
                        int64_t row_bytes, uint8_t *__restrict__ out) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -291,6 +401,31 @@ hipError_t launch_logits_generic(const DeviceTables &t, const float *q, int64_t 
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+int64_t attention_generic_chunks(int64_t n_keys) { return (n_keys + kAttnChunk - 1) / kAttnChunk; }
+
+hipError_t launch_attention_generic(const DeviceTables &tk, const DeviceTables &tv, const float *q, int64_t nq,
+                                    const uint8_t *k_codes, const uint8_t *k_signs, const float *k_norms,
+                                    const float *k_rnorms, const uint8_t *v_codes, const uint8_t *v_signs,
+                                    const float *v_norms, const float *v_rnorms, int64_t n_sets, int64_t n_keys,
+                                    float scale, float *logits, float *part, float *out, hipStream_t st) {
+  hipError_t e = launch_logits128(tk, q, nq, k_codes, k_signs, k_norms, k_rnorms, n_sets, n_keys, logits, st);
+  if (e == hipErrorNotSupported)
+    e = launch_logits_generic(tk, q, nq, k_codes, k_signs, k_norms, k_rnorms, n_sets, n_keys, logits, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_softmax_rows, dim3((unsigned)(n_sets * nq)), dim3(kThreads), 0, st, logits, n_keys, scale);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t chunks = attention_generic_chunks(n_keys);
+  const int prod = tv.variant == 1;
+  hipLaunchKernelGGL(k_attn_values_generic, dim3((unsigned)chunks, (unsigned)n_sets), dim3(kThreads), 0, st,
+                     logits, (int)nq, v_codes, v_signs, v_norms, v_rnorms, tv.d, n_keys, tv.mse_bits, prod,
+                     tv.cent, tv.code_row, tv.sign_row, part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_finish_generic, dim3((unsigned)nq, (unsigned)n_sets), dim3(kThreads),
+                     (size_t)2 * tv.d * sizeof(float), st, part, chunks, (int)nq, tv.d, tv.groups, prod, tv.Pi,
+                     tv.S, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(const uint8_t *idx, int bits, int64_t rows, int count, int64_t row_bytes,

@@ -53,6 +53,15 @@ hipError_t launch_logits_generic(const DeviceTables &t, const float *q, int64_t 
                                  const uint8_t *codes, const uint8_t *signs, const float *norms,
                                  const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
                                  hipStream_t st);
+// Decode attention, any d: logits into `logits` [n_sets][nq][n_keys] (then
+// softmax weights in place), value partial sums into `part`
+// [attention_generic_chunks(n_keys)][n_sets][nq][2][d], result into `out`.
+int64_t attention_generic_chunks(int64_t n_keys);
+hipError_t launch_attention_generic(const DeviceTables &tk, const DeviceTables &tv, const float *q, int64_t nq,
+                                    const uint8_t *k_codes, const uint8_t *k_signs, const float *k_norms,
+                                    const float *k_rnorms, const uint8_t *v_codes, const uint8_t *v_signs,
+                                    const float *v_norms, const float *v_rnorms, int64_t n_sets, int64_t n_keys,
+                                    float scale, float *logits, float *part, float *out, hipStream_t st);
 hipError_t launch_pack(const uint8_t *idx, int bits, int64_t rows, int count, int64_t row_bytes,
                        uint8_t *out, hipStream_t st);
 hipError_t launch_unpack(const uint8_t *in, int bits, int64_t rows, int count, int64_t row_bytes,

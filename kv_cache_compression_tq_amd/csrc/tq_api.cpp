@@ -426,6 +426,70 @@ int tq_logits(tq_handle h, const float *q, int64_t nq, const void *codes, const 
   return e == hipSuccess ? TQ_OK : hip_fail(e, "logits launch");
 }
 
+namespace {
+
+// Which kernels serve an attention call, and the workspace they need.
+struct AttnPlan {
+  size_t logits_off = 0, part_off = 0, bytes = 0;
+};
+
+int check_attention(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_sets, int64_t n_keys) {
+  int st = check_handle(hk);
+  if (st) return st;
+  if ((st = check_handle(hv))) return st;
+  if (hk->d != hv->d) return fail(TQ_EINVAL, "key and value codecs must have the same d");
+  if (hk->device != hv->device) return fail(TQ_EINVAL, "key and value codecs live on different devices");
+  if ((st = check_rows(hk, n_sets, n_keys))) return st;
+  if (nq < 1 || nq > 64) return fail(TQ_EINVAL, "nq must be in [1, 64]");
+  if (n_sets > 0 && n_keys < 1) return fail(TQ_EINVAL, "attention needs n_keys >= 1");
+  if (n_sets * nq * n_keys > ((int64_t)1 << 40)) return fail(TQ_EINVAL, "problem too large");
+  return TQ_OK;
+}
+
+AttnPlan plan_attention(tq_handle hk, int64_t nq, int64_t n_sets, int64_t n_keys) {
+  AttnPlan p;
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  p.logits_off = 0;
+  p.part_off = up((size_t)(n_sets * nq * n_keys) * sizeof(float));
+  p.bytes = p.part_off + up((size_t)tq::attention_generic_chunks(n_keys) * n_sets * nq * 2 * hk->d * sizeof(float));
+  return p;
+}
+
+}  // namespace
+
+int tq_attention_workspace(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_sets, int64_t n_keys,
+                           size_t *bytes) {
+  int st = check_attention(hk, hv, nq, n_sets, n_keys);
+  if (st) return st;
+  if (!bytes) return fail(TQ_EINVAL, "bytes is NULL");
+  *bytes = (n_sets == 0) ? 0 : plan_attention(hk, nq, n_sets, n_keys).bytes;
+  return TQ_OK;
+}
+
+int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const void *k_codes,
+                 const void *k_signs, const float *k_norms, const float *k_rnorms, const void *v_codes,
+                 const void *v_signs, const float *v_norms, const float *v_rnorms, int64_t n_sets,
+                 int64_t n_keys, float scale, float *out, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+  int st = check_attention(hk, hv, nq, n_sets, n_keys);
+  if (st) return st;
+  if (n_sets == 0) return TQ_OK;
+  if (!std::isfinite(scale)) return fail(TQ_EINVAL, "scale must be finite");
+  if (!q || ((uintptr_t)q & 3u)) return fail(TQ_EINVAL, "q NULL or misaligned");
+  if (!out || ((uintptr_t)out & 3u)) return fail(TQ_EINVAL, "out NULL or misaligned");
+  if ((st = check_code_ptrs(hk, k_codes, k_signs, k_norms, k_rnorms, false))) return st;
+  if ((st = check_code_ptrs(hv, v_codes, v_signs, v_norms, v_rnorms, false))) return st;
+  const AttnPlan p = plan_attention(hk, nq, n_sets, n_keys);
+  if (!workspace || ((uintptr_t)workspace & 255u)) return fail(TQ_EINVAL, "workspace NULL or not 256-byte aligned");
+  if (workspace_bytes < p.bytes) return fail(TQ_EINVAL, "workspace smaller than tq_attention_workspace reports");
+  char *ws = (char *)workspace;
+  hipError_t e = tq::launch_attention_generic(
+      hk->dev, hv->dev, q, nq, (const uint8_t *)k_codes, (const uint8_t *)k_signs, k_norms, k_rnorms,
+      (const uint8_t *)v_codes, (const uint8_t *)v_signs, v_norms, v_rnorms, n_sets, n_keys, scale,
+      (float *)(ws + p.logits_off), (float *)(ws + p.part_off), out, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "attention launch");
+}
+
 const char *tq_strerror(int status) {
   switch (status) {
     case TQ_OK: return "ok";

@@ -41,6 +41,10 @@ def test_strerror_and_validation_without_device():
     # calls on a NULL handle are rejected before touching the device
     assert L.tq_quantize(None, None, 0, 1, 1, None, None, None, None, None) == tq.TQ_EINVAL
     assert L.tq_logits(None, None, 1, None, None, None, None, 1, 1, None, None) == tq.TQ_EINVAL
+    assert L.tq_attention(None, None, None, 1, None, None, None, None, None, None, None, None, 1, 1,
+                          ctypes.c_float(1.0), None, None, 0, None) == tq.TQ_EINVAL
+    n = ctypes.c_size_t()
+    assert L.tq_attention_workspace(None, None, 1, 1, 1, ctypes.byref(n)) == tq.TQ_EINVAL
     assert L.tq_destroy(None) == tq.TQ_OK
 
 
