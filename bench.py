@@ -9,7 +9,9 @@ copies to defeat the 256 MB Infinity Cache.
 
 The same JSON line also carries the decode-attention-logits phase: 16 batch x
 8 KV heads x 131072 cached tokens stored as TurboQuant_prod b = 4 (3-bit mse +
-1-bit QJL), 4 query heads per KV head, float32 logits -- timed the same way.
+1-bit QJL), 4 query heads per KV head, float32 logits -- timed the same way --
+and the fused decode attention over that key cache plus a TurboQuant_mse b = 4
+value cache of the same shape.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -34,6 +36,7 @@ def _parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--skip-logits", action="store_true")
+    p.add_argument("--skip-attention", action="store_true")
     p.add_argument("--skip-others", action="store_true",
                    help="skip the non-headline paths (prod quantize, dequantize, high-d, NN indexing)")
     p.add_argument("--copy-probe", action="store_true",
@@ -143,10 +146,40 @@ def logits_phase(torch, tq, workloads, steps, warmup):
     keys = sets * T
     packed = keys * (codec.code_row + codec.sign_row + 8)
     written = sets * QH * T * 4
+    del out
     return dict(keys=keys, wall_ms=wall, kernel_ms=kern, kernel_ms_median=kmed, cache_build_s=build_s,
                 packed_bytes=packed, logits_bytes=written,
                 packed_gbs=packed / (kern * 1e-3) / 1e9,
-                total_gbs=(packed + written) / (kern * 1e-3) / 1e9)
+                total_gbs=(packed + written) / (kern * 1e-3) / 1e9, codec=codec, cache=cache, q=q)
+
+
+def attention_phase(torch, tq, workloads, lp, steps, warmup):
+    """Decode attention on the logits phase's key cache plus a value cache of
+    the same shape (TurboQuant_mse b = 4 of float32 N(0,1) draws): one fused
+    tq_attention call per step, softmax scale 1/sqrt(128)."""
+    H, T, d = workloads.DEC_KV_HEADS, workloads.DEC_TOKENS, workloads.DEC_DIM
+    kc, cache, q = lp["codec"], lp["cache"], lp["q"]
+    sets, QH = q.shape[0], q.shape[1]
+    vc = tq.Codec(d, 4, tq.TQ_MSE, seed=1, groups=H)
+    vals = vc.empty_codes(sets, T)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8)
+    chunk = 8
+    vbuf = torch.empty((chunk, T, d), dtype=torch.float32, device="cuda")
+    for s0 in range(0, sets, chunk):
+        vbuf.normal_(generator=gen)
+        vc.quantize(vbuf, out={k: (None if v is None else v[s0:s0 + chunk]) for k, v in vals.items()})
+    torch.cuda.synchronize()
+    del vbuf
+    ws = torch.empty(max(kc.attention_workspace_bytes(vc, QH, sets, T), 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((sets, QH, d), dtype=torch.float32, device="cuda")
+    scale = 1.0 / d ** 0.5
+    wall, kern, kmed = time_launches(
+        torch, lambda i: kc.attention(q, cache, vc, vals, scale=scale, out=out, workspace=ws), steps, warmup, 1)
+    keys = sets * T
+    packed = keys * (kc.code_row + kc.sign_row + 8 + vc.code_row + 4)
+    return dict(keys=keys, wall_ms=wall, kernel_ms=kern, kernel_ms_median=kmed, packed_bytes=packed,
+                packed_gbs=packed / (kern * 1e-3) / 1e9, workspace_bytes=ws.numel())
 
 
 def _mean_launch_ms(torch, fn, reps=5, warm=1):
@@ -254,6 +287,10 @@ def main():
     qp = quantize_phase(torch, tq, workloads, args.steps, args.warmup)
     q3 = quantize_b3_phase(torch, tq, workloads, qp["x"], args.steps, args.warmup)
     lp = None if args.skip_logits else logits_phase(torch, tq, workloads, args.steps, args.warmup)
+    ap = None if (lp is None or args.skip_attention) else attention_phase(torch, tq, workloads, lp, args.steps,
+                                                                          args.warmup)
+    if lp is not None:
+        del lp["cache"], lp["codec"], lp["q"]
     other = None if args.skip_others else other_paths_phase(torch, tq, workloads, qp["x"])
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, qp["x"])
     if args.copy_probe:
@@ -306,6 +343,19 @@ def main():
                          "achieved_incl_logits_written": lp["total_gbs"],
                          "frac_incl_logits_written": lp["total_gbs"] / HBM_PEAK_GBS},
             "cache_build_s": lp["cache_build_s"],
+        }
+    if ap is not None:
+        line["attention"] = {
+            "metric": "softmax(q·K̂)·V̂ GB/s on packed K and V bytes",
+            "value": ap["packed_gbs"], "unit": "GB/s", "ms_per_step": ap["wall_ms"],
+            "config": {"workload": "decode attention: 16 batch x 8 KV heads x 131072 cached tokens, keys "
+                                   "TurboQuant_prod b=4, values TurboQuant_mse b=4, 32 query heads (4 per KV "
+                                   "head), fp32 queries and outputs, scale 1/sqrt(128)", "keys": ap["keys"]},
+            "roofline": {"bound": "hbm", "kernel": "k_attn128<3,prod,4>", "achieved": ap["packed_gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ap["packed_gbs"] / HBM_PEAK_GBS,
+                         "traffic": counted_traffic("attn128_decode_prod4_mse4.md"),
+                         "kernel_ms": ap["kernel_ms"], "bytes_per_key": ap["packed_bytes"] / ap["keys"]},
+            "workspace_bytes": ap["workspace_bytes"],
         }
     if other is not None:
         line["other_paths"] = other

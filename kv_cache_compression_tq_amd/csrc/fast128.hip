@@ -954,6 +954,491 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   }
 }
 
+// ------------------------------------------------------------ attention --
+// Fused decode attention over quantized keys and values, d = 128: for every
+// query head h of a set, out_h = sum_t softmax_t(scale <q_h, k_hat_t>) v_hat_t
+// with v_hat_t = nu_t Pi^T c[idx_t] (TurboQuant_mse values).  [tqnet]
+// 实现步骤草图 › 集成到 attention (K and V both stored quantized, attention on
+// the QJL-coded keys); the softmax of scaled scores is scaled dot-product
+// attention, kept online (running maximum and sum) so that every key is read
+// once.
+//
+// Each workgroup takes one key range of one set and up to four heads.  Per
+// 16-key tile a wave (1) scores the keys exactly as k_logits128 does (keys are
+// the MFMA B operand: lane (key, grp) gets heads 2 grp and 2 grp + 1),
+// (2) turns the scores into weights w = exp(s - m) nu_V (f16 hi + lo parts)
+// and passes them through a small per-wave LDS buffer into the A operand of
+// (3) a second f16 MFMA that adds w alpha c[idx] in the rotated domain.  Its
+// rows are (head, coordinate parity, hi/lo part): a lane's value-code pair
+// lookup yields the two coordinates 2p, 2p + 1 of one key, and the parity row
+// picks one of them, so the decoded pairs go into the B operand as they are.
+// Lane (col, grp) of the accumulators ends with head grp, coordinates
+// 8 col .. 8 col + 7.  A per-set combine kernel merges the workgroups'
+// (max, sum, vector) partials and applies Pi^T once per head.
+constexpr int kAttnThreads = 512;
+constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kAttnTiles = 4;                // 16-key tiles per block
+constexpr int kAttnHeads = 4;                // query heads per pass
+constexpr int kAttnPart = 132;               // floats per partial: m, l, pad, pad, a[128]
+constexpr uint32_t kAttnVTab = 65536;        // LDS byte offset of the value decode table
+constexpr uint32_t kAttnQOff = 98304;        // query buffers, later the wave merge
+constexpr uint32_t kAttnScratch = kAttnQOff + 3 * kAttnHeads * D * 4;
+constexpr uint32_t kAttnWBuf = kAttnScratch + 2 * 4 * kAttnHeads * D * 4;
+constexpr uint32_t kAttnWBytes = 8 * 64 * 4;  // per wave: 8 head rows x 64 keys (u32 hi|lo)
+constexpr uint32_t kAttnCounter = kAttnWBuf + kAttnWaves * kAttnWBytes;
+constexpr uint32_t kAttnLds = kAttnCounter + 16;
+static_assert(kAttnWaves * kAttnHeads * (D + 2) * 4 <= kAttnWBuf - kAttnQOff, "merge buffer");
+static_assert(kAttnLds <= 160 * 1024, "LDS budget");
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Value codes of one block: lane (col, grp) holds, for keys 4 grp + j of each
+// tile, the MBV-bit codes of coordinates 8 col .. 8 col + 7 (3-bit codes: the
+// two words holding them, aligned when decoded); and the value norm of key col.
+template <int MBV>
+struct VRegs {
+  static constexpr int VW = MBV == 3 ? 2 : 1;
+  uint32_t w[kAttnTiles][4][VW];
+  float n[kAttnTiles];
+};
+
+// Lane offsets (bytes) of the attention loads, fixed for the kernel.
+struct AttnOffsets {
+  uint32_t kc, ks, kn, v;  // key codes / signs / norms of key col; value codes of key 4 grp
+};
+
+// One block of keys t0 .. t0 + 63 (wave-uniform t0): the key data in the
+// logits layout (lane (col, grp): key col of each tile) and the value codes
+// in the layout of the value MFMA (lane (col, grp): keys 4 grp + j).  Every
+// address is a wave-uniform base plus the lane's fixed offset plus a
+// constant, so no per-lane address arithmetic runs per block.  TAIL: keys at
+// or past kend are replaced by key t0 (always valid).
+template <int CW, bool PROD, int MBV, bool TAIL>
+__device__ __forceinline__ void attn_load(KeyRegs<CW> &rk, VRegs<MBV> &rv, int64_t t0, int64_t kend, int col,
+                                          int grp, const AttnOffsets &o, const uint8_t *kcodes,
+                                          const uint8_t *ksigns, const float *knorms, const float *krnorms,
+                                          const uint8_t *vcodes, const float *vnorms) {
+  constexpr int ROWV = 16 * MBV;
+  const uint8_t *kc = CW > 0 ? kcodes + t0 * (16 * CW) : nullptr;
+  const uint8_t *ks = PROD ? ksigns + t0 * 16 : nullptr;
+  const uint8_t *kn = (const uint8_t *)(knorms + t0);
+  const uint8_t *kg = PROD ? (const uint8_t *)(krnorms + t0) : nullptr;
+  const uint8_t *vc = vcodes + t0 * ROWV;
+  const uint8_t *vn = (const uint8_t *)(vnorms + t0);
+  const int lim = TAIL ? (int)(kend - t0) : 64;  // keys of this block that exist
+#pragma unroll
+  for (int u = 0; u < kAttnTiles; ++u) {
+    // key col of tile u (logits layout)
+    const bool ok = !TAIL || 16 * u + col < lim;
+    const uint32_t du = ok ? (uint32_t)(16 * u) : 0u, cu = ok ? 0u : (uint32_t)col;  // back to key t0
+    if constexpr (CW > 0) load_codes<CW>(rk.cw[u], kc + o.kc + du * (16 * CW) - cu * (16 * CW));
+    if constexpr (PROD) rk.sw[u] = *(const uint32_t *)(ks + o.ks + du * 16 - cu * 16);
+    rk.nv[u] = *(const float *)(kn + o.kn + du * 4 - cu * 4);
+    if constexpr (PROD) rk.gv[u] = *(const float *)(kg + o.kn + du * 4 - cu * 4);
+    rv.n[u] = *(const float *)(vn + o.kn + du * 4 - cu * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // key 4 grp + j of tile u (value layout)
+      const bool okv = !TAIL || 16 * u + 4 * grp + j < lim;
+      const uint32_t off = okv ? o.v + (uint32_t)((16 * u + j) * ROWV) : o.v - (uint32_t)(4 * grp * ROWV);
+      const uint8_t *row = vc + off;  // the lane's chunk of this key's row
+      if constexpr (MBV == 1) {
+        rv.w[u][j][0] = *row;
+      } else if constexpr (MBV == 2) {
+        rv.w[u][j][0] = *(const uint16_t *)row;
+      } else if constexpr (MBV == 4) {
+        rv.w[u][j][0] = *(const uint32_t *)row;
+      } else {
+        // 3-bit codes: the chunk starts at byte 3 col; o.v points at its
+        // aligned word, the second word is clamped to the row's last
+        rv.w[u][j][0] = *(const uint32_t *)row;
+        rv.w[u][j][1] = *(const uint32_t *)(row + (col == 15 ? 0 : 4));
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float dpp_f(float x, int ctrl) {
+  switch (ctrl) {  // the control must be a constant: one instantiation per use
+    case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));
+    case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));
+    case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true));
+  }
+}
+// Maximum / sum over the 16 lanes of a row (pairs, quads, half rows, rows).
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp_f(x, 0xB1));
+  x = fmaxf(x, dpp_f(x, 0x4E));
+  x = fmaxf(x, dpp_f(x, 0x141));
+  return fmaxf(x, dpp_f(x, 0x140));
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f(x, 0xB1);
+  x += dpp_f(x, 0x4E);
+  x += dpp_f(x, 0x141);
+  return x + dpp_f(x, 0x140);
+}
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ float sel4(int i, float a, float b, float c, float d) {
+  return i == 0 ? a : i == 1 ? b : i == 2 ? c : d;
+}
+
+// Online-softmax state of one wave: running maximum of the (log2-scaled)
+// scores of each head (wave-uniform), the lane's partial sums of the weights
+// of heads 2 grp, 2 grp + 1, and the value accumulators (head grp).
+struct AttnState {
+  float m[kAttnHeads];
+  float lA, lB;
+  f32x4 acc[4];
+};
+
+template <int MBK, bool PRODK, int MBV>
+__device__ __forceinline__ void attn_block(AttnState &st, const KeyRegs<MBK> &rk, const VRegs<MBV> &rv,
+                                           int64_t tb, int64_t kend, bool tail, const u32x4 *bq,
+                                           const u32x4 *bp, uint32_t code_base, uint32_t sign_base,
+                                           uint32_t vbase, float sl2e, uint32_t wrow, uint32_t wread,
+                                           uint32_t psel, int col, int grp) {
+  using GV = LutGeom<MBV>;
+  constexpr int KT = kAttnTiles;
+  // 1. scores (log2 domain) of heads 2 grp, 2 grp + 1 for key col of each tile
+  float s0[KT], s1[KT];
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+    float o0, o1;
+    score_tile<MBK, PRODK>(rk, u, bq, bp, code_base, sign_base, o0, o1);
+    s0[u] = o0 * sl2e;
+    s1[u] = o1 * sl2e;
+    if (tail && tb + 16 * u + col >= kend) s0[u] = s1[u] = -INFINITY;
+  }
+  // 2. new running maxima: row maxima, then the four heads as uniform values
+  float x0 = s0[0], x1 = s1[0];
+#pragma unroll
+  for (int u = 1; u < KT; ++u) {
+    x0 = fmaxf(x0, s0[u]);
+    x1 = fmaxf(x1, s1[u]);
+  }
+  x0 = row_max(x0);
+  x1 = row_max(x1);
+  float alpha[kAttnHeads];
+  {
+    const float bm[kAttnHeads] = {lane_f(x0, 0), lane_f(x1, 0), lane_f(x0, 16), lane_f(x1, 16)};
+#pragma unroll
+    for (int h = 0; h < kAttnHeads; ++h) {
+      const float mn = fmaxf(st.m[h], bm[h]);
+      alpha[h] = __builtin_amdgcn_exp2f(st.m[h] - mn);
+      st.m[h] = mn;
+    }
+  }
+  const bool lo_rows = grp < 2;
+  const float mA = lo_rows ? (grp == 0 ? st.m[0] : st.m[2]) : 0.f;
+  const float mB = lo_rows ? (grp == 0 ? st.m[1] : st.m[3]) : 0.f;
+  const float aA = lo_rows ? (grp == 0 ? alpha[0] : alpha[2]) : 1.f;
+  const float aB = lo_rows ? (grp == 0 ? alpha[1] : alpha[3]) : 1.f;
+  // 3. weights: p = 2^(s - m), the running sums, and w = p nu_V as f16 hi|lo
+  // into this wave's buffer (row = head, column = key of the block)
+  float lA = st.lA * aA, lB = st.lB * aB;
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+    const float pA = __builtin_amdgcn_exp2f(s0[u] - mA), pB = __builtin_amdgcn_exp2f(s1[u] - mB);
+    lA += pA;
+    lB += pB;
+    const float wA = pA * rv.n[u], wB = pB * rv.n[u];
+    const _Float16 hA = (_Float16)wA, hB = (_Float16)wB;
+    const uint32_t vA = f16x2((float)hA, wA - (float)hA), vB = f16x2((float)hB, wB - (float)hB);
+    *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(wrow + 4 * (16 * u)) = vA;
+    *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(wrow + 256 + 4 * (16 * u)) = vB;
+  }
+  st.lA = lA;
+  st.lB = lB;
+  // 4. rescale the value accumulators (head grp) when a maximum moved
+  if (alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f) {
+    const float a = sel4(grp, alpha[0], alpha[1], alpha[2], alpha[3]);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) st.acc[nt] *= a;
+  }
+  // 5. value MFMAs: A = this lane's weight part of keys 4 grp + j at parity
+  // p, B = decoded code pairs 4 col + nt of the same keys
+#pragma unroll
+  for (int u = 0; u < KT; ++u) {
+    const u32x4 wv = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(wread + 4 * (16 * u));
+    u32x4 a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = __builtin_amdgcn_perm(wv[j], wv[j], psel);
+    uint32_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (MBV == 3)
+        c[j] = __builtin_amdgcn_alignbit(rv.w[u][j][1], rv.w[u][j][0], 8 * ((3 * col) & 3));
+      else
+        c[j] = rv.w[u][j][0];
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      constexpr int W = GV::W;
+      u32x4 b;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sh = W * nt;
+        const uint32_t x = sh >= GV::SHIFT ? c[j] >> (sh - GV::SHIFT) : c[j] << (GV::SHIFT - sh);
+        const uint32_t addr = (x & (uint32_t)(((1 << W) - 1) << GV::SHIFT)) | vbase;
+        b[j] = *(__attribute__((address_space(3))) const uint32_t *)(uintptr_t)addr;
+      }
+      st.acc[nt] = mfma_f16(a, b, st.acc[nt]);
+    }
+  }
+}
+
+template <int MBK, bool PRODK, int MBV>
+__global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
+    const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ kcodes,
+    const uint8_t *__restrict__ ksigns, const float *__restrict__ knorms, const float *__restrict__ krnorms,
+    const uint8_t *__restrict__ vcodes, const float *__restrict__ vnorms, int64_t n_keys, int kgroups,
+    const float *__restrict__ PiT, const float *__restrict__ ST, const uint32_t *__restrict__ klut,
+    float k_inv_scale, const uint32_t *__restrict__ vlut, float sl2e, int64_t keys_per_wg,
+    float *__restrict__ part) {
+  constexpr int CW = MBK;
+  using GK = LutGeom<MBK>;
+  using GV = LutGeom<MBV>;
+  static_assert(GK::CODE_BYTES + kSignBytes <= kAttnVTab && GV::CODE_BYTES <= kAttnQOff - kAttnVTab, "LDS map");
+  extern __shared__ u32x4 dyn_lds[];  // the kernel's only LDS: starts at address 0
+  char *lds = (char *)dyn_lds;
+  uint32_t *t_code = (uint32_t *)lds;
+  u32x4 *t_sg = (u32x4 *)(lds + GK::CODE_BYTES);
+  uint32_t *t_val = (uint32_t *)(lds + kAttnVTab);
+  float *qs = (float *)(lds + kAttnQOff);
+  float *qt = qs + kAttnHeads * D;
+  float *pp = qt + kAttnHeads * D;
+  float *scratch = (float *)(lds + kAttnScratch);
+  uint32_t *counter = (uint32_t *)(lds + kAttnCounter);
+
+  const int s = blockIdx.y;
+  const int g = s % kgroups;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
+  const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
+  const int64_t srow = (int64_t)s * n_keys;
+  // set bases (wave-uniform) and the lane's fixed offsets
+  const uint8_t *kcs = MBK > 0 ? kcodes + srow * (16 * CW) : nullptr;
+  const uint8_t *kss = PRODK ? ksigns + srow * 16 : nullptr;
+  const float *kns = knorms + srow;
+  const float *kgs = PRODK ? krnorms + srow : nullptr;
+  const uint8_t *vcs = vcodes + srow * (16 * MBV);
+  const float *vns = vnorms + srow;
+  AttnOffsets ofs;
+  ofs.kc = (uint32_t)(col * (16 * CW) + grp * (4 * CW));
+  ofs.ks = (uint32_t)(col * 16 + grp * 4);
+  ofs.kn = (uint32_t)(col * 4);
+  ofs.v = (uint32_t)(4 * grp * (16 * MBV) + (MBV == 3 ? 4 * ((3 * col) >> 2) : col * MBV));
+  constexpr int KT = kAttnTiles;
+  constexpr int W = 16 * KT;  // keys per block
+  const int nfull = (int)((kend - kbeg) / W);
+  const bool ragged = kbeg + (int64_t)nfull * W < kend;
+
+  // 1. set-up loads: this wave's first block, the query, the columns of Pi^T /
+  // S^T this thread contracts, the decode tables
+  KeyRegs<CW> ka, kb;
+  VRegs<MBV> va, vb;
+  int b = wave;
+  if (b < nfull)
+    attn_load<CW, PRODK, MBV, false>(ka, va, kbeg + (int64_t)b * W, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs,
+                                     vns);
+  const int slice = tid >> 7, jj = tid & 127;
+  {
+    const int h = tid >> 7;
+    qs[tid] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + jj] : 0.f;  // kAttnHeads * D == threads
+  }
+  if constexpr (MBK > 0)
+    for (int e = tid; e < GK::ENTRIES * GK::COPIES; e += kAttnThreads) t_code[e] = klut[e / GK::COPIES];
+  if constexpr (PRODK)
+    for (int e = tid; e < 256 * kSignCopies; e += kAttnThreads)
+      t_sg[e] = ((const u32x4 *)(klut + (MBK > 0 ? GK::WORDS : 0)))[e / kSignCopies];
+  for (int e = tid; e < GV::ENTRIES * GV::COPIES; e += kAttnThreads) t_val[e] = vlut[e / GV::COPIES];
+  if (tid == 0) *counter = kAttnWaves;
+  __syncthreads();
+  // 2. rotate (Pi q) and project (S q) the heads: thread (slice, j) sums 32
+  // contraction steps of output coordinate j
+#pragma unroll
+  for (int mat = 0; mat < (PRODK ? 2 : 1); ++mat) {
+    const float *Wm = (mat == 0 ? PiT : ST) + (size_t)g * D * D + (size_t)(32 * slice) * D + jj;
+    float a[kAttnHeads] = {0, 0, 0, 0};
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const float wk = Wm[(size_t)k * D];
+#pragma unroll
+      for (int h = 0; h < kAttnHeads; ++h) a[h] = fmaf(wk, qs[h * D + 32 * slice + k], a[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < kAttnHeads; ++h) scratch[((mat * 4 + slice) * kAttnHeads + h) * D + jj] = a[h];
+  }
+  __syncthreads();
+  for (int e = tid; e < (PRODK ? 2 : 1) * kAttnHeads * D; e += kAttnThreads) {
+    const int m = e / (kAttnHeads * D), hj = e % (kAttnHeads * D);
+    float v = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) v += scratch[(m * 4 + sl) * kAttnHeads * D + hj];
+    (m == 0 ? qt : pp)[hj] = v;
+  }
+  __syncthreads();
+  // 3. query operands (MFMA A of the scores): row col = (head col >> 1, part col & 1)
+  u32x4 bq[4], bp[4];
+  {
+    const int h = col >> 1, part = col & 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 32 * grp + 8 * k + 2 * i;
+        float a0 = 0.f, a1 = 0.f, p0 = 0.f, p1 = 0.f;
+        if (h < kAttnHeads) {
+          a0 = qt[h * D + c] * k_inv_scale;
+          a1 = qt[h * D + c + 1] * k_inv_scale;
+          p0 = pp[h * D + c] * kQjlScale / (float)D;
+          p1 = pp[h * D + c + 1] * kQjlScale / (float)D;
+        }
+        if (part) {
+          a0 -= (float)(_Float16)a0;
+          a1 -= (float)(_Float16)a1;
+          p0 -= (float)(_Float16)p0;
+          p1 -= (float)(_Float16)p1;
+        }
+        bq[k][i] = f16x2(a0, a1);
+        bp[k][i] = f16x2(p0, p1);
+      }
+    }
+  }
+
+  const uint32_t code_base = 4 * (lane & (GK::COPIES - 1));
+  const uint32_t sign_base = 16 * (lane & (kSignCopies - 1));
+  const uint32_t vbase = kAttnVTab | (4 * (lane & (GV::COPIES - 1)));
+  // weight buffer of this wave: writer lane (col, grp) owns rows 2 grp, 2 grp + 1
+  // (heads), column col of each tile; reader lane (n = col, grp) takes head
+  // n >> 2, keys 4 grp .. 4 grp + 3 of each tile, half n & 1 at parity (n >> 1) & 1
+  const uint32_t wb = kAttnWBuf + wave * kAttnWBytes;
+  const uint32_t wrow = wb + (2 * grp) * 256 + 4 * col;
+  const uint32_t wread = wb + (col >> 2) * 256 + 16 * grp;
+  const int wpart = col & 1, wpar = (col >> 1) & 1;
+  const uint32_t psel = wpart == 0 ? (wpar == 0 ? 0x0C0C0100u : 0x01000C0Cu) : (wpar == 0 ? 0x0C0C0302u : 0x03020C0Cu);
+
+  AttnState stt;
+#pragma unroll
+  for (int h = 0; h < kAttnHeads; ++h) stt.m[h] = -1e30f;
+  stt.lA = stt.lB = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) stt.acc[nt] = f32x4{0, 0, 0, 0};
+
+  auto grab = [&]() {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(counter, 1u);
+    return (int)__builtin_amdgcn_readfirstlane(__shfl(v, 0));
+  };
+  if (b < nfull) {
+    while (true) {
+      int b2 = grab();
+      bool more = b2 < nfull;
+      int64_t nb = kbeg + (int64_t)(more ? b2 : b) * W;
+      attn_load<CW, PRODK, MBV, false>(kb, vb, nb, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs, vns);
+      attn_block<MBK, PRODK, MBV>(stt, ka, va, kbeg + (int64_t)b * W, kend, false, bq, bp, code_base, sign_base,
+                                  vbase, sl2e, wrow, wread, psel, col, grp);
+      b = b2;
+      if (!more) break;
+      b2 = grab();
+      more = b2 < nfull;
+      nb = kbeg + (int64_t)(more ? b2 : b) * W;
+      attn_load<CW, PRODK, MBV, false>(ka, va, nb, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs, vns);
+      attn_block<MBK, PRODK, MBV>(stt, kb, vb, kbeg + (int64_t)b * W, kend, false, bq, bp, code_base, sign_base,
+                                  vbase, sl2e, wrow, wread, psel, col, grp);
+      b = b2;
+      if (!more) break;
+    }
+  }
+  if (b == nfull && ragged) {  // the one wave that holds the partial block
+    const int64_t t0 = kbeg + (int64_t)nfull * W;
+    attn_load<CW, PRODK, MBV, true>(ka, va, t0, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs, vns);
+    attn_block<MBK, PRODK, MBV>(stt, ka, va, t0, kend, true, bq, bp, code_base, sign_base, vbase, sl2e, wrow,
+                                wread, psel, col, grp);
+  }
+
+  // 4. merge the waves: each writes its maxima, sums and vectors; then thread
+  // (head, coordinate) combines them and writes the workgroup's partial
+  __syncthreads();  // the query buffers are free from here on
+  float *mv = (float *)(lds + kAttnQOff);                       // [wave][head][D]
+  float *ml = mv + kAttnWaves * kAttnHeads * D;                 // [wave][head][2]
+  {
+    const float lA = row_sum(stt.lA), lB = row_sum(stt.lB);
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < kAttnHeads; ++h) ml[(wave * kAttnHeads + h) * 2] = stt.m[h];
+      ml[(wave * kAttnHeads + 0) * 2 + 1] = lA;
+      ml[(wave * kAttnHeads + 1) * 2 + 1] = lB;
+    }
+    if (lane == 16) {
+      ml[(wave * kAttnHeads + 2) * 2 + 1] = lA;
+      ml[(wave * kAttnHeads + 3) * 2 + 1] = lB;
+    }
+    float v[8];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      v[2 * nt] = stt.acc[nt][0] + stt.acc[nt][1];
+      v[2 * nt + 1] = stt.acc[nt][2] + stt.acc[nt][3];
+    }
+    float *dst = mv + (wave * kAttnHeads + grp) * D + 8 * col;
+    *(f32x4 *)dst = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4 *)(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+  __syncthreads();
+  {
+    const int h = tid >> 7, j = tid & 127;
+    if (h < hc) {
+      float M = -1e30f;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, ml[(w * kAttnHeads + h) * 2]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(ml[(w * kAttnHeads + h) * 2] - M);
+        L = fmaf(ml[(w * kAttnHeads + h) * 2 + 1], f, L);
+        A = fmaf(mv[(w * kAttnHeads + h) * D + j], f, A);
+      }
+      float *o = part + (((int64_t)s * nq + h0 + h) * gridDim.x + blockIdx.x) * kAttnPart;
+      o[4 + j] = A;
+      if (j == 0) {
+        o[0] = M;
+        o[1] = L;
+      }
+    }
+  }
+}
+
+// Merge the workgroups' partials of one (set, head) and map back to the
+// original coordinates: out = Pi^T (a / (alpha l)).
+__global__ __launch_bounds__(D) void k_attn_combine128(const float *__restrict__ part, int nq, int parts,
+                                                       int vgroups, const float *__restrict__ Pi,
+                                                       float v_inv_scale, float *__restrict__ out) {
+  __shared__ float av[D];
+  const int h = blockIdx.x, s = blockIdx.y, j = threadIdx.x;
+  const float *p = part + ((int64_t)s * nq + h) * parts * kAttnPart;
+  float M = -1e30f;
+  for (int w = 0; w < parts; ++w) M = fmaxf(M, p[w * kAttnPart]);
+  float L = 0.f, A = 0.f;
+  for (int w = 0; w < parts; ++w) {
+    const float f = __builtin_amdgcn_exp2f(p[w * kAttnPart] - M);
+    L = fmaf(p[w * kAttnPart + 1], f, L);
+    A = fmaf(p[w * kAttnPart + 4 + j], f, A);
+  }
+  av[j] = A * (v_inv_scale / L);
+  __syncthreads();
+  const float *P = Pi + (size_t)(s % vgroups) * D * D;
+  float o = 0.f;
+#pragma unroll 8
+  for (int k = 0; k < D; ++k) o = fmaf(P[(size_t)k * D + j], av[k], o);  // (Pi^T a)_j = sum_k Pi[k][j] a_k
+  out[((int64_t)s * nq + h) * D + j] = o;
+}
+
 template <int MB, bool PROD>
 hipError_t run_dequant(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs, const float *norms,
                        const float *rnorms, int64_t n_sets, int64_t n, float *out, hipStream_t st) {
@@ -1045,6 +1530,44 @@ hipError_t run_logits(const DeviceTables &t, const float *q, int64_t nq, const u
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Workgroups per set of the fused attention (about one per CU overall) and
+// the keys each takes (a multiple of one block per wave).
+int64_t attn_grid_x(int64_t n_sets, int64_t n_keys, int64_t *kpw) {
+  const int64_t unit = kAttnWaves * 16 * kAttnTiles;
+  int64_t gx = (256 + n_sets - 1) / n_sets;
+  const int64_t max_gx = (n_keys + unit - 1) / unit;
+  if (gx > max_gx) gx = max_gx;
+  if (gx < 1) gx = 1;
+  int64_t k = (n_keys + gx - 1) / gx;
+  k = (k + unit - 1) / unit * unit;
+  *kpw = k;
+  return (n_keys + k - 1) / k;
+}
+
+template <int MBK, bool PRODK, int MBV>
+hipError_t run_attention(const DeviceTables &tk, const DeviceTables &tv, const float *q, int64_t nq,
+                         const uint8_t *kcodes, const uint8_t *ksigns, const float *knorms, const float *krnorms,
+                         const uint8_t *vcodes, const float *vnorms, int64_t n_sets, int64_t n_keys, float scale,
+                         float *part, float *out, hipStream_t st) {
+  int64_t kpw = 0;
+  const int64_t gx = attn_grid_x(n_sets, n_keys, &kpw);
+  hipError_t e = hipFuncSetAttribute((const void *)k_attn128<MBK, PRODK, MBV>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kAttnLds);
+  if (e != hipSuccess) return e;
+  const float sl2e = scale * kLog2e;
+  for (int64_t h0 = 0; h0 < nq; h0 += kAttnHeads) {
+    const int hc = (int)(nq - h0 < kAttnHeads ? nq - h0 : kAttnHeads);
+    hipLaunchKernelGGL((k_attn128<MBK, PRODK, MBV>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kAttnThreads),
+                       kAttnLds, st, q, (int)nq, (int)h0, hc, kcodes, ksigns, knorms, krnorms, vcodes, vnorms,
+                       n_keys, tk.groups, tk.PiT, tk.ST, tk.logit_lut, tk.lut_inv_scale, tv.logit_lut, sl2e, kpw,
+                       part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_attn_combine128, dim3((unsigned)nq, (unsigned)n_sets), dim3(D), 0, st, part, (int)nq,
+                     (int)gx, tv.groups, tv.Pi, tv.lut_inv_scale, out);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1206,6 +1729,38 @@ hipError_t launch_logits128(const DeviceTables &t, const float *q, int64_t nq,
   TQ_L(0, true) TQ_L(1, false) TQ_L(1, true) TQ_L(2, false) TQ_L(2, true)
   TQ_L(3, false) TQ_L(3, true) TQ_L(4, false) TQ_L(4, true)
 #undef TQ_L
+  return hipErrorNotSupported;
+}
+
+static bool attention128_handles(const DeviceTables &tk, const DeviceTables &tv) {
+  return tk.d == D && tv.d == D && tk.logit_lut && tv.logit_lut && tk.mse_bits <= 4 && tv.variant == 0 &&
+         tv.mse_bits >= 1 && tv.mse_bits <= 4;
+}
+
+size_t attention128_workspace(const DeviceTables &tk, const DeviceTables &tv, int64_t nq, int64_t n_sets,
+                              int64_t n_keys) {
+  if (!attention128_handles(tk, tv) || n_sets < 1 || n_keys < 1) return 0;
+  int64_t kpw = 0;
+  const int64_t gx = attn_grid_x(n_sets, n_keys, &kpw);
+  return (size_t)(n_sets * nq * gx) * kAttnPart * sizeof(float);
+}
+
+hipError_t launch_attention128(const DeviceTables &tk, const DeviceTables &tv, const float *q, int64_t nq,
+                               const uint8_t *kcodes, const uint8_t *ksigns, const float *knorms,
+                               const float *krnorms, const uint8_t *vcodes, const float *vnorms, int64_t n_sets,
+                               int64_t n_keys, float scale, float *part, float *out, hipStream_t st) {
+  if (!attention128_handles(tk, tv)) return hipErrorNotSupported;
+  const bool prod = tk.variant == 1;
+#define TQ_A(MBK, P, MBV)                                                                                 \
+  if (tk.mse_bits == MBK && prod == P && tv.mse_bits == MBV)                                              \
+    return run_attention<MBK, P, MBV>(tk, tv, q, nq, kcodes, ksigns, knorms, krnorms, vcodes, vnorms, n_sets, \
+                                      n_keys, scale, part, out, st);
+#define TQ_AV(MBV) \
+  TQ_A(0, true, MBV) TQ_A(1, false, MBV) TQ_A(1, true, MBV) TQ_A(2, false, MBV) TQ_A(2, true, MBV) \
+  TQ_A(3, false, MBV) TQ_A(3, true, MBV) TQ_A(4, false, MBV) TQ_A(4, true, MBV)
+  TQ_AV(1) TQ_AV(2) TQ_AV(3) TQ_AV(4)
+#undef TQ_AV
+#undef TQ_A
   return hipErrorNotSupported;
 }
 

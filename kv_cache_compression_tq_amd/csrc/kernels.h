@@ -82,4 +82,14 @@ hipError_t launch_logits128(const DeviceTables &t, const float *q, int64_t nq,
                             const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
                             hipStream_t st);
 
+// Fused decode attention, d = 128, keys of any variant with <= 4 mse bits and
+// TurboQuant_mse values with 1..4 bits.  attention128_workspace returns the
+// bytes of `part` it needs (0 when it does not handle the codecs).
+size_t attention128_workspace(const DeviceTables &tk, const DeviceTables &tv, int64_t nq, int64_t n_sets,
+                              int64_t n_keys);
+hipError_t launch_attention128(const DeviceTables &tk, const DeviceTables &tv, const float *q, int64_t nq,
+                               const uint8_t *kcodes, const uint8_t *ksigns, const float *knorms,
+                               const float *krnorms, const uint8_t *vcodes, const float *vnorms, int64_t n_sets,
+                               int64_t n_keys, float scale, float *part, float *out, hipStream_t st);
+
 }  // namespace tq

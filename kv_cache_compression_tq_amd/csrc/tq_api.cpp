@@ -430,6 +430,7 @@ namespace {
 
 // Which kernels serve an attention call, and the workspace they need.
 struct AttnPlan {
+  bool fused = false;  // the d = 128 fused kernel (else the any-d kernels)
   size_t logits_off = 0, part_off = 0, bytes = 0;
 };
 
@@ -446,9 +447,15 @@ int check_attention(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_sets, int6
   return TQ_OK;
 }
 
-AttnPlan plan_attention(tq_handle hk, int64_t nq, int64_t n_sets, int64_t n_keys) {
+AttnPlan plan_attention(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_sets, int64_t n_keys) {
   AttnPlan p;
   auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t fused = tq::attention128_workspace(hk->dev, hv->dev, nq, n_sets, n_keys);
+  if (fused > 0) {
+    p.fused = true;
+    p.bytes = up(fused);
+    return p;
+  }
   p.logits_off = 0;
   p.part_off = up((size_t)(n_sets * nq * n_keys) * sizeof(float));
   p.bytes = p.part_off + up((size_t)tq::attention_generic_chunks(n_keys) * n_sets * nq * 2 * hk->d * sizeof(float));
@@ -462,7 +469,7 @@ int tq_attention_workspace(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_set
   int st = check_attention(hk, hv, nq, n_sets, n_keys);
   if (st) return st;
   if (!bytes) return fail(TQ_EINVAL, "bytes is NULL");
-  *bytes = (n_sets == 0) ? 0 : plan_attention(hk, nq, n_sets, n_keys).bytes;
+  *bytes = (n_sets == 0) ? 0 : plan_attention(hk, hv, nq, n_sets, n_keys).bytes;
   return TQ_OK;
 }
 
@@ -479,11 +486,18 @@ int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const v
   if (!out || ((uintptr_t)out & 3u)) return fail(TQ_EINVAL, "out NULL or misaligned");
   if ((st = check_code_ptrs(hk, k_codes, k_signs, k_norms, k_rnorms, false))) return st;
   if ((st = check_code_ptrs(hv, v_codes, v_signs, v_norms, v_rnorms, false))) return st;
-  const AttnPlan p = plan_attention(hk, nq, n_sets, n_keys);
+  const AttnPlan p = plan_attention(hk, hv, nq, n_sets, n_keys);
   if (!workspace || ((uintptr_t)workspace & 255u)) return fail(TQ_EINVAL, "workspace NULL or not 256-byte aligned");
   if (workspace_bytes < p.bytes) return fail(TQ_EINVAL, "workspace smaller than tq_attention_workspace reports");
   char *ws = (char *)workspace;
-  hipError_t e = tq::launch_attention_generic(
+  hipError_t e;
+  if (p.fused) {
+    e = tq::launch_attention128(hk->dev, hv->dev, q, nq, (const uint8_t *)k_codes, (const uint8_t *)k_signs,
+                                k_norms, k_rnorms, (const uint8_t *)v_codes, v_norms, n_sets, n_keys, scale,
+                                (float *)ws, out, (hipStream_t)stream);
+    return e == hipSuccess ? TQ_OK : hip_fail(e, "attention launch");
+  }
+  e = tq::launch_attention_generic(
       hk->dev, hv->dev, q, nq, (const uint8_t *)k_codes, (const uint8_t *)k_signs, k_norms, k_rnorms,
       (const uint8_t *)v_codes, (const uint8_t *)v_signs, v_norms, v_rnorms, n_sets, n_keys, scale,
       (float *)(ws + p.logits_off), (float *)(ws + p.part_off), out, (hipStream_t)stream);

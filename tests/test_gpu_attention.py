@@ -85,7 +85,7 @@ def test_attention_workspace_checks():
     kcod = tq.Codec(d, 4, tq.TQ_PROD, seed=1)
     vcod = tq.Codec(d, 4, tq.TQ_MSE, seed=2)
     need = kcod.attention_workspace_bytes(vcod, 4, 2, 1000)
-    assert need > 0
+    assert 0 < need < 2 * 4 * 1000 * 4  # the fused kernel's partials, not the unfused logits buffer
     x = torch.randn(2, 1000, d, device="cuda")
     keys, vals = kcod.quantize(x), vcod.quantize(x)
     q = torch.randn(2, 4, d, device="cuda")
