@@ -725,7 +725,12 @@ struct LutGeom {
   // index shifted left by SHIFT, OR the lane's copy), sign table, query buffers
   static constexpr uint32_t CODE_BYTES = MB > 0 ? ENTRIES * COPIES * 4 : 0;
 };
-constexpr int kSignCopies = 8;                     // u32x4 entries
+// Sign table: 16 copies of each 16-byte entry, entries 256 bytes apart.  A
+// 16-byte LDS read serves 16 lanes per cycle from 64 four-byte banks, so the
+// 16 lanes of a group must read 16 distinct 16-byte bank slots: with the copy
+// index lane & 15 they do whatever bytes they look up (8 copies at a 128-byte
+// stride measured about four conflict cycles per read).
+constexpr int kSignCopies = 16;                    // u32x4 entries
 constexpr uint32_t kSignBytes = 256 * kSignCopies * 16;
 constexpr uint32_t kQueryBytes = 3 * 8 * D * 4;    // qs, qt, pp
 
@@ -769,9 +774,9 @@ __device__ __forceinline__ void score_tile(const KeyRegs<MB> &r, int u, const u3
   if constexpr (PROD) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      // sign byte k times the entry stride (128 bytes), OR the lane's copy
-      const uint32_t x = k == 0 ? r.sw[u] << 7 : r.sw[u] >> (8 * k - 7);
-      const uint32_t addr = (x & 0x7F80u) | sign_base;
+      // sign byte k times the entry stride (256 bytes), OR the lane's copy
+      const uint32_t x = k == 0 ? r.sw[u] << 8 : r.sw[u] >> (8 * k - 8);
+      const uint32_t addr = (x & 0xFF00u) | sign_base;
       const u32x4 sg = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(addr + GM::CODE_BYTES);
       cq = mfma_f16(bp[k], sg, cq);
     }
@@ -975,24 +980,33 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
 // Lane (col, grp) of the accumulators ends with head grp, coordinates
 // 8 col .. 8 col + 7.  A per-set combine kernel merges the workgroups'
 // (max, sum, vector) partials and applies Pi^T once per head.
-constexpr int kAttnThreads = 512;
+constexpr int kAttnThreads = 768;            // 12 waves: three per SIMD
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kAttnTiles = 4;                // 16-key tiles per block
+constexpr int kAttnTiles = 2;                // 16-key tiles per block
 constexpr int kAttnHeads = 4;                // query heads per pass
 constexpr int kAttnPart = 132;               // floats per partial: m, l, pad, pad, a[128]
-constexpr uint32_t kAttnVTab = 65536;        // LDS byte offset of the value decode table
-constexpr uint32_t kAttnQOff = 98304;        // query buffers, later the wave merge
-constexpr uint32_t kAttnScratch = kAttnQOff + 3 * kAttnHeads * D * 4;
-constexpr uint32_t kAttnWBuf = kAttnScratch + 2 * 4 * kAttnHeads * D * 4;
-constexpr uint32_t kAttnWBytes = 8 * 64 * 4;  // per wave: 8 head rows x 64 keys (u32 hi|lo)
+constexpr uint32_t kAttnVTab = 98304;        // LDS byte offset of the value decode table
+constexpr uint32_t kAttnQOff = 131072;       // query buffers (qs, qt, pp)
+constexpr uint32_t kAttnWBuf = kAttnQOff + 3 * kAttnHeads * D * 4;
+// per-wave weight buffer: 8 head rows x 16 kAttnTiles keys (u32 hi|lo), rows
+// 40 words apart so that the two rows written at once (heads 2 grp of lanes
+// 0-31) fall on different banks and the four rows read at once (16-byte
+// reads, 16 lanes a cycle) on different 16-byte bank slots
+constexpr uint32_t kAttnWRow = 160;
+static_assert(kAttnWRow >= 16 * kAttnTiles * 4, "weight row");
+constexpr uint32_t kAttnWBytes = 8 * kAttnWRow;
 constexpr uint32_t kAttnCounter = kAttnWBuf + kAttnWaves * kAttnWBytes;
 constexpr uint32_t kAttnLds = kAttnCounter + 16;
-static_assert(kAttnWaves * kAttnHeads * (D + 2) * 4 <= kAttnWBuf - kAttnQOff, "merge buffer");
+// the value-table region is free before the tables are filled (rotation
+// scratch of the prologue) and after the main loop (merge of the waves)
+constexpr uint32_t kAttnScratch = kAttnVTab;
+static_assert(2 * 4 * kAttnHeads * D * 4 <= kAttnQOff - kAttnVTab, "prologue scratch");
+static_assert(kAttnWaves * kAttnHeads * (D + 2) * 4 <= kAttnQOff - kAttnVTab, "merge buffer");
 static_assert(kAttnLds <= 160 * 1024, "LDS budget");
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Value codes of one block: lane (col, grp) holds, for keys 4 grp + j of each
+// Value codes of one block: lane (col, grp) holds, for keys grp + 4 j of each
 // tile, the MBV-bit codes of coordinates 8 col .. 8 col + 7 (3-bit codes: the
 // two words holding them, aligned when decoded); and the value norm of key col.
 template <int MBV>
@@ -1004,12 +1018,13 @@ struct VRegs {
 
 // Lane offsets (bytes) of the attention loads, fixed for the kernel.
 struct AttnOffsets {
-  uint32_t kc, ks, kn, v;  // key codes / signs / norms of key col; value codes of key 4 grp
+  uint32_t kc, ks, kn, v;  // key codes / signs / norms of key col; value codes of key grp
 };
 
 // One block of keys t0 .. t0 + 63 (wave-uniform t0): the key data in the
 // logits layout (lane (col, grp): key col of each tile) and the value codes
-// in the layout of the value MFMA (lane (col, grp): keys 4 grp + j).  Every
+// in the layout of the value MFMA (lane (col, grp): keys grp + 4 j, so that
+// load j of a tile reads four consecutive rows, whole cache lines).  Every
 // address is a wave-uniform base plus the lane's fixed offset plus a
 // constant, so no per-lane address arithmetic runs per block.  TAIL: keys at
 // or past kend are replaced by key t0 (always valid).
@@ -1038,9 +1053,9 @@ __device__ __forceinline__ void attn_load(KeyRegs<CW> &rk, VRegs<MBV> &rv, int64
     rv.n[u] = *(const float *)(vn + o.kn + du * 4 - cu * 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // key 4 grp + j of tile u (value layout)
-      const bool okv = !TAIL || 16 * u + 4 * grp + j < lim;
-      const uint32_t off = okv ? o.v + (uint32_t)((16 * u + j) * ROWV) : o.v - (uint32_t)(4 * grp * ROWV);
+      // key grp + 4 j of tile u (value layout)
+      const bool okv = !TAIL || 16 * u + grp + 4 * j < lim;
+      const uint32_t off = okv ? o.v + (uint32_t)((16 * u + 4 * j) * ROWV) : o.v - (uint32_t)(grp * ROWV);
       const uint8_t *row = vc + off;  // the lane's chunk of this key's row
       if constexpr (MBV == 1) {
         rv.w[u][j][0] = *row;
@@ -1149,7 +1164,7 @@ __device__ __forceinline__ void attn_block(AttnState &st, const KeyRegs<MBK> &rk
     const _Float16 hA = (_Float16)wA, hB = (_Float16)wB;
     const uint32_t vA = f16x2((float)hA, wA - (float)hA), vB = f16x2((float)hB, wB - (float)hB);
     *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(wrow + 4 * (16 * u)) = vA;
-    *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(wrow + 256 + 4 * (16 * u)) = vB;
+    *(__attribute__((address_space(3))) uint32_t *)(uintptr_t)(wrow + kAttnWRow + 4 * (16 * u)) = vB;
   }
   st.lA = lA;
   st.lB = lB;
@@ -1159,7 +1174,7 @@ __device__ __forceinline__ void attn_block(AttnState &st, const KeyRegs<MBK> &rk
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) st.acc[nt] *= a;
   }
-  // 5. value MFMAs: A = this lane's weight part of keys 4 grp + j at parity
+  // 5. value MFMAs: A = this lane's weight part of keys grp + 4 j at parity
   // p, B = decoded code pairs 4 col + nt of the same keys
 #pragma unroll
   for (int u = 0; u < KT; ++u) {
@@ -1202,7 +1217,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
   constexpr int CW = MBK;
   using GK = LutGeom<MBK>;
   using GV = LutGeom<MBV>;
-  static_assert(GK::CODE_BYTES + kSignBytes <= kAttnVTab && GV::CODE_BYTES <= kAttnQOff - kAttnVTab, "LDS map");
+  static_assert(GK::CODE_BYTES + kSignBytes <= kAttnVTab && GV::CODE_BYTES <= kAttnQOff - kAttnVTab &&
+                    (kAttnVTab & (GV::CODE_BYTES - 1)) == 0,
+                "LDS map");
   extern __shared__ u32x4 dyn_lds[];  // the kernel's only LDS: starts at address 0
   char *lds = (char *)dyn_lds;
   uint32_t *t_code = (uint32_t *)lds;
@@ -1233,7 +1250,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
   ofs.kc = (uint32_t)(col * (16 * CW) + grp * (4 * CW));
   ofs.ks = (uint32_t)(col * 16 + grp * 4);
   ofs.kn = (uint32_t)(col * 4);
-  ofs.v = (uint32_t)(4 * grp * (16 * MBV) + (MBV == 3 ? 4 * ((3 * col) >> 2) : col * MBV));
+  ofs.v = (uint32_t)(grp * (16 * MBV) + (MBV == 3 ? 4 * ((3 * col) >> 2) : col * MBV));
   constexpr int KT = kAttnTiles;
   constexpr int W = 16 * KT;  // keys per block
   const int nfull = (int)((kend - kbeg) / W);
@@ -1243,37 +1260,38 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
   // S^T this thread contracts, the decode tables
   KeyRegs<CW> ka, kb;
   VRegs<MBV> va, vb;
+  // Blocks are taken in an order rotated by a per-workgroup amount, so that
+  // workgroups that advance in step do not read the same offsets of their
+  // sets (equal strides) at the same time.
+  const int rot = nfull > 0 ? (int)(((uint32_t)s * 2654435761u + (uint32_t)blockIdx.x * 40503u) % (uint32_t)nfull) : 0;
+  auto rotb = [&](int x) { return x + rot >= nfull ? x + rot - nfull : x + rot; };
   int b = wave;
   if (b < nfull)
-    attn_load<CW, PRODK, MBV, false>(ka, va, kbeg + (int64_t)b * W, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs,
-                                     vns);
-  const int slice = tid >> 7, jj = tid & 127;
-  {
-    const int h = tid >> 7;
-    qs[tid] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + jj] : 0.f;  // kAttnHeads * D == threads
+    attn_load<CW, PRODK, MBV, false>(ka, va, kbeg + (int64_t)rotb(b) * W, kend, col, grp, ofs, kcs, kss, kns, kgs,
+                                     vcs, vns);
+  const int slice = (tid >> 7) & 3, jj = tid & 127;
+  for (int e = tid; e < kAttnHeads * D; e += kAttnThreads) {
+    const int h = e >> 7;
+    qs[e] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + (e & 127)] : 0.f;
   }
-  if constexpr (MBK > 0)
-    for (int e = tid; e < GK::ENTRIES * GK::COPIES; e += kAttnThreads) t_code[e] = klut[e / GK::COPIES];
-  if constexpr (PRODK)
-    for (int e = tid; e < 256 * kSignCopies; e += kAttnThreads)
-      t_sg[e] = ((const u32x4 *)(klut + (MBK > 0 ? GK::WORDS : 0)))[e / kSignCopies];
-  for (int e = tid; e < GV::ENTRIES * GV::COPIES; e += kAttnThreads) t_val[e] = vlut[e / GV::COPIES];
   if (tid == 0) *counter = kAttnWaves;
   __syncthreads();
   // 2. rotate (Pi q) and project (S q) the heads: thread (slice, j) sums 32
-  // contraction steps of output coordinate j
+  // contraction steps of output coordinate j (scratch: the value-table region)
+  if (tid < 4 * D) {
 #pragma unroll
-  for (int mat = 0; mat < (PRODK ? 2 : 1); ++mat) {
-    const float *Wm = (mat == 0 ? PiT : ST) + (size_t)g * D * D + (size_t)(32 * slice) * D + jj;
-    float a[kAttnHeads] = {0, 0, 0, 0};
+    for (int mat = 0; mat < (PRODK ? 2 : 1); ++mat) {
+      const float *Wm = (mat == 0 ? PiT : ST) + (size_t)g * D * D + (size_t)(32 * slice) * D + jj;
+      float a[kAttnHeads] = {0, 0, 0, 0};
 #pragma unroll 8
-    for (int k = 0; k < 32; ++k) {
-      const float wk = Wm[(size_t)k * D];
+      for (int k = 0; k < 32; ++k) {
+        const float wk = Wm[(size_t)k * D];
 #pragma unroll
-      for (int h = 0; h < kAttnHeads; ++h) a[h] = fmaf(wk, qs[h * D + 32 * slice + k], a[h]);
+        for (int h = 0; h < kAttnHeads; ++h) a[h] = fmaf(wk, qs[h * D + 32 * slice + k], a[h]);
+      }
+#pragma unroll
+      for (int h = 0; h < kAttnHeads; ++h) scratch[((mat * 4 + slice) * kAttnHeads + h) * D + jj] = a[h];
     }
-#pragma unroll
-    for (int h = 0; h < kAttnHeads; ++h) scratch[((mat * 4 + slice) * kAttnHeads + h) * D + jj] = a[h];
   }
   __syncthreads();
   for (int e = tid; e < (PRODK ? 2 : 1) * kAttnHeads * D; e += kAttnThreads) {
@@ -1283,6 +1301,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
     for (int sl = 0; sl < 4; ++sl) v += scratch[(m * 4 + sl) * kAttnHeads * D + hj];
     (m == 0 ? qt : pp)[hj] = v;
   }
+  __syncthreads();
+  // the decode tables (the value table overwrites the scratch)
+  if constexpr (MBK > 0)
+    for (int e = tid; e < GK::ENTRIES * GK::COPIES; e += kAttnThreads) t_code[e] = klut[e / GK::COPIES];
+  if constexpr (PRODK)
+    for (int e = tid; e < 256 * kSignCopies; e += kAttnThreads)
+      t_sg[e] = ((const u32x4 *)(klut + (MBK > 0 ? GK::WORDS : 0)))[e / kSignCopies];
+  for (int e = tid; e < GV::ENTRIES * GV::COPIES; e += kAttnThreads) t_val[e] = vlut[e / GV::COPIES];
   __syncthreads();
   // 3. query operands (MFMA A of the scores): row col = (head col >> 1, part col & 1)
   u32x4 bq[4], bp[4];
@@ -1317,10 +1343,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
   const uint32_t vbase = kAttnVTab | (4 * (lane & (GV::COPIES - 1)));
   // weight buffer of this wave: writer lane (col, grp) owns rows 2 grp, 2 grp + 1
   // (heads), column col of each tile; reader lane (n = col, grp) takes head
-  // n >> 2, keys 4 grp .. 4 grp + 3 of each tile, half n & 1 at parity (n >> 1) & 1
+  // n >> 2, keys grp + 4 j of each tile, half n & 1 at parity (n >> 1) & 1
   const uint32_t wb = kAttnWBuf + wave * kAttnWBytes;
-  const uint32_t wrow = wb + (2 * grp) * 256 + 4 * col;
-  const uint32_t wread = wb + (col >> 2) * 256 + 16 * grp;
+  // (key k of a tile is stored at position 4 (k & 3) + (k >> 2): the reader's
+  // four consecutive words are keys grp + 4 j, the keys of its value codes)
+  const uint32_t wrow = wb + (2 * grp) * kAttnWRow + 4 * (4 * (col & 3) + (col >> 2));
+  const uint32_t wread = wb + (col >> 2) * kAttnWRow + 16 * grp;
   const int wpart = col & 1, wpar = (col >> 1) & 1;
   const uint32_t psel = wpart == 0 ? (wpar == 0 ? 0x0C0C0100u : 0x01000C0Cu) : (wpar == 0 ? 0x0C0C0302u : 0x03020C0Cu);
 
@@ -1340,18 +1368,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
     while (true) {
       int b2 = grab();
       bool more = b2 < nfull;
-      int64_t nb = kbeg + (int64_t)(more ? b2 : b) * W;
+      int64_t nb = kbeg + (int64_t)rotb(more ? b2 : b) * W;
       attn_load<CW, PRODK, MBV, false>(kb, vb, nb, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs, vns);
-      attn_block<MBK, PRODK, MBV>(stt, ka, va, kbeg + (int64_t)b * W, kend, false, bq, bp, code_base, sign_base,
-                                  vbase, sl2e, wrow, wread, psel, col, grp);
+      attn_block<MBK, PRODK, MBV>(stt, ka, va, kbeg + (int64_t)rotb(b) * W, kend, false, bq, bp, code_base,
+                                  sign_base, vbase, sl2e, wrow, wread, psel, col, grp);
       b = b2;
       if (!more) break;
       b2 = grab();
       more = b2 < nfull;
-      nb = kbeg + (int64_t)(more ? b2 : b) * W;
+      nb = kbeg + (int64_t)rotb(more ? b2 : b) * W;
       attn_load<CW, PRODK, MBV, false>(ka, va, nb, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs, vns);
-      attn_block<MBK, PRODK, MBV>(stt, kb, vb, kbeg + (int64_t)b * W, kend, false, bq, bp, code_base, sign_base,
-                                  vbase, sl2e, wrow, wread, psel, col, grp);
+      attn_block<MBK, PRODK, MBV>(stt, kb, vb, kbeg + (int64_t)rotb(b) * W, kend, false, bq, bp, code_base,
+                                  sign_base, vbase, sl2e, wrow, wread, psel, col, grp);
       b = b2;
       if (!more) break;
     }
@@ -1365,8 +1393,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
 
   // 4. merge the waves: each writes its maxima, sums and vectors; then thread
   // (head, coordinate) combines them and writes the workgroup's partial
-  __syncthreads();  // the query buffers are free from here on
-  float *mv = (float *)(lds + kAttnQOff);                       // [wave][head][D]
+  __syncthreads();  // the value table is free from here on
+  float *mv = (float *)(lds + kAttnVTab);                       // [wave][head][D]
   float *ml = mv + kAttnWaves * kAttnHeads * D;                 // [wave][head][2]
   {
     const float lA = row_sum(stt.lA), lB = row_sum(stt.lB);
@@ -1414,29 +1442,49 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
   }
 }
 
-// Merge the workgroups' partials of one (set, head) and map back to the
-// original coordinates: out = Pi^T (a / (alpha l)).
-__global__ __launch_bounds__(D) void k_attn_combine128(const float *__restrict__ part, int nq, int parts,
-                                                       int vgroups, const float *__restrict__ Pi,
-                                                       float v_inv_scale, float *__restrict__ out) {
-  __shared__ float av[D];
-  const int h = blockIdx.x, s = blockIdx.y, j = threadIdx.x;
-  const float *p = part + ((int64_t)s * nq + h) * parts * kAttnPart;
-  float M = -1e30f;
-  for (int w = 0; w < parts; ++w) M = fmaxf(M, p[w * kAttnPart]);
-  float L = 0.f, A = 0.f;
-  for (int w = 0; w < parts; ++w) {
-    const float f = __builtin_amdgcn_exp2f(p[w * kAttnPart] - M);
-    L = fmaf(p[w * kAttnPart + 1], f, L);
-    A = fmaf(p[w * kAttnPart + 4 + j], f, A);
-  }
-  av[j] = A * (v_inv_scale / L);
-  __syncthreads();
+// Merge the workgroups' partials of every head of one set and map back to
+// the original coordinates: out_h = Pi^T (a_h / (alpha l_h)).  512 threads:
+// thread (slice, j) sums contraction steps 32 slice .. 32 slice + 31 of
+// output coordinate j for up to 8 heads; Pi is read once per set.
+constexpr int kCombineHeads = 8;
+constexpr int kCombineThreads = 4 * D;
+__global__ __launch_bounds__(kCombineThreads) void k_attn_combine128(const float *__restrict__ part, int nq,
+                                                                     int parts, int vgroups,
+                                                                     const float *__restrict__ Pi,
+                                                                     float v_inv_scale, float *__restrict__ out) {
+  __shared__ float av[kCombineHeads][D];
+  __shared__ float red[4][kCombineHeads][D];
+  const int s = blockIdx.x, tid = threadIdx.x, slice = tid >> 7, j = tid & 127;
   const float *P = Pi + (size_t)(s % vgroups) * D * D;
-  float o = 0.f;
+  for (int h0 = 0; h0 < nq; h0 += kCombineHeads) {
+    const int hc = nq - h0 < kCombineHeads ? nq - h0 : kCombineHeads;
+    for (int h = slice; h < hc; h += 4) {
+      const float *p = part + ((int64_t)s * nq + h0 + h) * parts * kAttnPart;
+      float M = -1e30f;
+      for (int w = 0; w < parts; ++w) M = fmaxf(M, p[w * kAttnPart]);
+      float L = 0.f, A = 0.f;
+      for (int w = 0; w < parts; ++w) {
+        const float f = __builtin_amdgcn_exp2f(p[w * kAttnPart] - M);
+        L = fmaf(p[w * kAttnPart + 1], f, L);
+        A = fmaf(p[w * kAttnPart + 4 + j], f, A);
+      }
+      av[h][j] = A * (v_inv_scale / L);
+    }
+    __syncthreads();
+    float o[kCombineHeads] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll 8
-  for (int k = 0; k < D; ++k) o = fmaf(P[(size_t)k * D + j], av[k], o);  // (Pi^T a)_j = sum_k Pi[k][j] a_k
-  out[((int64_t)s * nq + h) * D + j] = o;
+    for (int k = 32 * slice; k < 32 * slice + 32; ++k) {
+      const float pk = P[(size_t)k * D + j];  // (Pi^T a)_j = sum_k Pi[k][j] a_k
+#pragma unroll
+      for (int h = 0; h < kCombineHeads; ++h) o[h] = fmaf(pk, av[h][k], o[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < kCombineHeads; ++h) red[slice][h][j] = o[h];
+    __syncthreads();
+    for (int h = slice; h < hc; h += 4)
+      out[((int64_t)s * nq + h0 + h) * D + j] = red[0][h][j] + red[1][h][j] + red[2][h][j] + red[3][h][j];
+    __syncthreads();
+  }
 }
 
 template <int MB, bool PROD>
@@ -1565,7 +1613,7 @@ hipError_t run_attention(const DeviceTables &tk, const DeviceTables &tv, const f
                        part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_attn_combine128, dim3((unsigned)nq, (unsigned)n_sets), dim3(D), 0, st, part, (int)nq,
+  hipLaunchKernelGGL(k_attn_combine128, dim3((unsigned)n_sets), dim3(kCombineThreads), 0, st, part, (int)nq,
                      (int)gx, tv.groups, tv.Pi, tv.lut_inv_scale, out);
   return hipGetLastError();
 }
