@@ -296,10 +296,13 @@ def main():
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
+        # write another 1 GiB so that no part of src is still held in the
+        # 256 MB Infinity Cache: every byte the copy reads comes from HBM
+        evict = torch.empty_like(src).fill_(2.0)
         torch.cuda.synchronize()
-        torch.mul(src, 1.0, out=dst)   # plain elementwise kernel: reads and writes 1 GiB
+        torch.neg(src, out=dst)   # plain elementwise kernel (the only neg here): reads and writes 1 GiB
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, evict
 
     value = qp["vectors"] / (qp["wall_ms"] * 1e-3)
     line = {
