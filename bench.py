@@ -178,8 +178,22 @@ def attention_phase(torch, tq, workloads, lp, steps, warmup):
         torch, lambda i: kc.attention(q, cache, vc, vals, scale=scale, out=out, workspace=ws), steps, warmup, 1)
     keys = sets * T
     packed = keys * (kc.code_row + kc.sign_row + 8 + vc.code_row + 4)
+    # online append into the same caches: one new key and value per set, at the
+    # last slot of each set (rows s * T + T - 1 of the flat [sets * T] cache)
+    flat_k = {k: (None if v is None else v.view(sets * T, *v.shape[2:])) for k, v in cache.items()}
+    flat_v = {k: (None if v is None else v.view(sets * T, *v.shape[2:])) for k, v in vals.items()}
+    rows = torch.arange(sets, device="cuda", dtype=torch.int64) * T + (T - 1)
+    xk = torch.randn((sets, d), generator=gen, device="cuda")
+    xv = torch.randn((sets, d), generator=gen, device="cuda")
+
+    def append_step(i):
+        kc.append(xk, rows, flat_k)
+        vc.append(xv, rows, flat_v)
+
+    awall, akern, _ = time_launches(torch, append_step, steps, warmup, 1)
     return dict(keys=keys, wall_ms=wall, kernel_ms=kern, kernel_ms_median=kmed, packed_bytes=packed,
-                packed_gbs=packed / (kern * 1e-3) / 1e9, workspace_bytes=ws.numel())
+                packed_gbs=packed / (kern * 1e-3) / 1e9, workspace_bytes=ws.numel(), append_ms=akern,
+                append_wall_ms=awall, sets=sets)
 
 
 def _mean_launch_ms(torch, fn, reps=5, warm=1):
@@ -359,6 +373,13 @@ def main():
                          "traffic": counted_traffic("attn128_decode_prod4_mse4.md"),
                          "kernel_ms": ap["kernel_ms"], "bytes_per_key": ap["packed_bytes"] / ap["keys"]},
             "workspace_bytes": ap["workspace_bytes"],
+        }
+        line["append"] = {
+            "metric": "online append latency: one new key (prod b=4) and value (mse b=4) per (batch, KV head) "
+                      "written into the paged decode caches",
+            "value": ap["append_ms"] * 1e3, "unit": "us per token step (K + V, 128 sets)",
+            "higher_is_better": False, "wall_us_per_step": ap["append_wall_ms"] * 1e3,
+            "vectors_per_s": 2 * ap["sets"] / (ap["append_ms"] * 1e-3),
         }
     if other is not None:
         line["other_paths"] = other

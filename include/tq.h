@@ -86,6 +86,19 @@ int tq_layout(tq_handle h, int64_t *code_row_bytes, int64_t *sign_row_bytes, int
 int tq_quantize(tq_handle h, const void *x, int dtype, int64_t n_sets, int64_t n,
                 void *codes, void *signs, float *norms, float *rnorms, void *stream);
 
+/* Online append: quantize one vector per set, x[n_sets][d] (dtype TQ_F32 or
+ * TQ_BF16), and write it into row rows[s] of the cache arrays codes / signs /
+ * norms / rnorms, each holding cache_rows rows in the tq_quantize row layout
+ * ([ttakun] TurboQuant_mse: no training or warm-up, so each new token is
+ * quantized on its own as it arrives).  rows: device array of n_sets int64
+ * physical row indices (a paged cache resolves its page table into them);
+ * a row outside [0, cache_rows) is skipped, and two sets naming one row race.
+ * Set s uses codec group s % groups.  The codes are those tq_quantize
+ * produces for the same vector.  Pointer and NULL rules as tq_quantize.
+ * n_sets == 0 is a no-op.  Errors: TQ_EINVAL, TQ_EHIP. */
+int tq_append(tq_handle h, const void *x, int dtype, int64_t n_sets, const int64_t *rows, int64_t cache_rows,
+              void *codes, void *signs, float *norms, float *rnorms, void *stream);
+
 /* Reconstruct x_out[n_sets][n][d] float32.  mse: ||x|| Pi^T c[idx] ([ttakun]
  * inverse rotation and rescale; [tqnet] dequant x = Pi.T @ centroids[idx]).
  * prod: ||x|| (Pi^T c[idx] + sqrt(pi/2)/d * ||r|| S^T z), the unbiased QJL

@@ -30,6 +30,7 @@ _SIGS = {
     "tq_layout": (_INT, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_INT)]),
     "tq_quantize": (_INT, [_P, _P, _INT, _I64, _I64, _P, _P, _P, _P, _P]),
     "tq_dequantize": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _P, _P]),
+    "tq_append": (_INT, [_P, _P, _INT, _I64, _P, _I64, _P, _P, _P, _P, _P]),
     "tq_logits": (_INT, [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P]),
     "tq_attention": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P,
                             ctypes.c_size_t, _P]),
@@ -156,6 +157,26 @@ class Codec:
         _check(lib().tq_quantize(self._h, _ptr(x), dtype, n_sets, n, _ptr(out["codes"]), _ptr(out["signs"]),
                                  _ptr(out["norms"]), _ptr(out["rnorms"]), _stream(stream)), "tq_quantize")
         return out
+
+    def append(self, x, rows, cache, stream=None):
+        """Quantize x[n_sets, d] (float32 or bfloat16) and write set s's vector
+        into row rows[s] (int64 CUDA tensor) of the cache dict (arrays shaped
+        [cache_rows, ...] as empty_codes(1, cache_rows) returns, or any
+        contiguous arrays with cache_rows rows)."""
+        import torch
+
+        if x.dim() != 2 or x.shape[1] != self.d or not x.is_contiguous():
+            raise ValueError("x must be a contiguous [n_sets, d] tensor")
+        dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}.get(x.dtype)
+        if dtype is None:
+            raise TypeError("x must be float32 or bfloat16")
+        if rows.dtype != torch.int64 or rows.numel() != x.shape[0]:
+            raise ValueError("rows must be an int64 tensor with one entry per set")
+        cache_rows = cache["norms"].numel()
+        _check(lib().tq_append(self._h, _ptr(x), dtype, x.shape[0], _ptr(rows), cache_rows, _ptr(cache.get("codes")),
+                               _ptr(cache.get("signs")), _ptr(cache["norms"]), _ptr(cache.get("rnorms")),
+                               _stream(stream)), "tq_append")
+        return cache
 
     def dequantize(self, keys, out=None, stream=None):
         import torch

@@ -116,6 +116,113 @@ __global__ __launch_bounds__(kThreads) void k_quant_generic(
   if (tid == 0) rnorms[row] = nu > 0.f ? rn / nu : 0.f;
 }
 
+// ---------------------------------------------------------------- append --
+// One vector per set written straight into row rows[s] of a (paged) cache:
+// the online path of the pages ([ttakun] TurboQuant_mse: no training, one
+// vector at a time).  One 512-thread workgroup per set, tuned for latency:
+// the d x d contractions run as nsl slices of d/nsl steps per output
+// coordinate (Pi^T and M^T columns read coalesced from L2), reduced in LDS;
+// codes are packed a 32-bit word per thread, signs by ballot.  A row outside
+// [0, cache_rows) is skipped.
+constexpr int kAppendThreads = 512;
+
+template <typename T>
+__global__ __launch_bounds__(kAppendThreads) void k_append(
+    const T *__restrict__ x, int d, int groups, int mse_bits, int prod, const int64_t *__restrict__ rows,
+    int64_t cache_rows, const float *__restrict__ PiT, const float *__restrict__ MT, const float *__restrict__ cent,
+    const float *__restrict__ bnd, uint8_t *__restrict__ codes, int64_t code_row, uint8_t *__restrict__ signs,
+    int64_t sign_row, float *__restrict__ norms, float *__restrict__ rnorms) {
+  extern __shared__ float sm[];  // xs[d], part[kAppendThreads], ys[d], idx[d]
+  __shared__ float red[kAppendThreads / 64];
+  float *xs = sm, *part = sm + d, *ys = part + kAppendThreads;
+  int *is = (int *)(ys + d);
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const int64_t row = rows[s];
+  if (row < 0 || row >= cache_rows) return;  // the whole workgroup leaves together
+  const int g = s % groups;
+  const int nsl = d <= kAppendThreads ? kAppendThreads / d : 1;  // contraction slices per coordinate
+  const int span = (d + nsl - 1) / nsl;
+  const T *xv = x + (int64_t)s * d;
+  float acc = 0.f;
+  for (int j = tid; j < d; j += kAppendThreads) {
+    const float v = load_x(xv, j);
+    xs[j] = v;
+    acc = fmaf(v, v, acc);
+  }
+  const float nu = sqrtf(block_sum(acc, red));  // block_sum syncs before it reads
+  const float nthr = nu > 0.f ? nu : 1.f;
+  // y = Pi x: thread (slice, j) sums its span of k (PiT[k][j] = Pi[j][k])
+  auto contract = [&](const float *Mt, const float *vin, float *vout) {
+    for (int j0 = 0; j0 < d; j0 += kAppendThreads / nsl) {
+      const int j = j0 + tid % (kAppendThreads / nsl), sl = tid / (kAppendThreads / nsl);
+      float a = 0.f;
+      if (j < d && sl < nsl) {
+        const int k0 = sl * span, k1 = min(d, k0 + span);
+        // eight independent partial sums keep eight L2 loads in flight
+        float p8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int k = k0;
+        for (; k + 8 <= k1; k += 8) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) p8[u] = fmaf(Mt[(size_t)(k + u) * d + j], vin[k + u], p8[u]);
+        }
+        for (; k < k1; ++k) p8[0] = fmaf(Mt[(size_t)k * d + j], vin[k], p8[0]);
+        a = ((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]));
+      }
+      __syncthreads();
+      part[tid] = a;
+      __syncthreads();
+      if (tid < kAppendThreads / nsl && j0 + tid < d) {
+        float v = 0.f;
+        for (int q = 0; q < nsl; ++q) v += part[q * (kAppendThreads / nsl) + tid];
+        vout[j0 + tid] = v;
+      }
+    }
+    __syncthreads();
+  };
+  contract(PiT + (size_t)g * d * d, xs, ys);
+  const int L = 1 << mse_bits;
+  for (int j = tid; j < d; j += kAppendThreads) {
+    const float y = ys[j];
+    int idx = 0;
+    if (mse_bits > 0)
+      for (int k = 0; k + 1 < L; ++k) idx += fmaf(nthr, bnd[k], -y) < 0.f ? 1 : 0;  // nu t_k < y
+    is[j] = idx;
+    ys[j] = mse_bits > 0 ? y - nu * cent[idx] : y;  // nu times the rotated residual
+  }
+  __syncthreads();
+  if (mse_bits > 0) {
+    uint32_t *crow = (uint32_t *)(codes + row * code_row);
+    for (int w = tid; w < (int)(code_row / 4); w += kAppendThreads) {
+      uint32_t v = 0;
+      const int b0 = 32 * w;
+      for (int j = b0 / mse_bits; j < d && j * mse_bits < b0 + 32; ++j) {
+        const int sh = j * mse_bits - b0;  // may be negative for the field that straddles in
+        const uint32_t f = (uint32_t)is[j];
+        v |= sh >= 0 ? f << sh : f >> (-sh);
+      }
+      crow[w] = v;
+    }
+  }
+  if (tid == 0) norms[row] = nu;
+  if (!prod) return;
+  float r2 = 0.f;
+  for (int j = tid; j < d; j += kAppendThreads) r2 = fmaf(ys[j], ys[j], r2);
+  const float rn = sqrtf(block_sum(r2, red));
+  // sign(S r) = sign(M (Pi r)) with M = S Pi^T (MT[j][i] = M[i][j]); xs is free now
+  contract(MT + (size_t)g * d * d, ys, xs);
+  uint32_t *srow = (uint32_t *)(signs + row * sign_row);
+  for (int i0 = 0; i0 < (int)(sign_row * 8); i0 += kAppendThreads) {
+    const int i = i0 + tid;
+    const uint64_t m = __ballot(i < d && xs[i] >= 0.f);
+    if ((tid & 63) == 0) {
+      const int w = i >> 5;  // lane 0 of each wave writes its 64 bits
+      if (w < (int)(sign_row / 4)) srow[w] = (uint32_t)m;
+      if (w + 1 < (int)(sign_row / 4)) srow[w + 1] = (uint32_t)(m >> 32);
+    }
+  }
+  if (tid == 0) rnorms[row] = nu > 0.f ? rn / nu : 0.f;
+}
+
 // Reconstruction of one vector per workgroup:
 // out = nu (Pi^T c[idx] + sqrt(pi/2)/d * gamma * S^T z).
 __global__ __launch_bounds__(kThreads) void k_dequant_generic(
@@ -365,6 +472,23 @@ hipError_t launch_quant_generic(const DeviceTables &t, const void *x, int dtype,
   else
     hipLaunchKernelGGL(k_quant_generic<uint16_t>, dim3((unsigned)rows), dim3(kThreads), shmem, st,
                        (const uint16_t *)x, t.d, n, t.groups, t.mse_bits, prod, t.PiT, t.MT,
+                       t.cent, t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const DeviceTables &t, const void *x, int dtype, int64_t n_sets, const int64_t *rows,
+                         int64_t cache_rows, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
+                         hipStream_t st) {
+  if (n_sets == 0) return hipSuccess;
+  const size_t shmem = ((size_t)3 * t.d + kAppendThreads) * sizeof(float);
+  const int prod = t.variant == 1;
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_append<float>, dim3((unsigned)n_sets), dim3(kAppendThreads), shmem, st, (const float *)x,
+                       t.d, t.groups, t.mse_bits, prod, rows, cache_rows, t.PiT, t.MT, t.cent, t.bnd, codes,
+                       t.code_row, signs, t.sign_row, norms, rnorms);
+  else
+    hipLaunchKernelGGL(k_append<uint16_t>, dim3((unsigned)n_sets), dim3(kAppendThreads), shmem, st,
+                       (const uint16_t *)x, t.d, t.groups, t.mse_bits, prod, rows, cache_rows, t.PiT, t.MT,
                        t.cent, t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms);
   return hipGetLastError();
 }

@@ -62,6 +62,11 @@ hipError_t launch_attention_generic(const DeviceTables &tk, const DeviceTables &
                                     const float *k_rnorms, const uint8_t *v_codes, const uint8_t *v_signs,
                                     const float *v_norms, const float *v_rnorms, int64_t n_sets, int64_t n_keys,
                                     float scale, float *logits, float *part, float *out, hipStream_t st);
+// One vector per set into row rows[s] of the cache arrays (rows outside
+// [0, cache_rows) are skipped).
+hipError_t launch_append(const DeviceTables &t, const void *x, int dtype, int64_t n_sets, const int64_t *rows,
+                         int64_t cache_rows, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
+                         hipStream_t st);
 hipError_t launch_pack(const uint8_t *idx, int bits, int64_t rows, int count, int64_t row_bytes,
                        uint8_t *out, hipStream_t st);
 hipError_t launch_unpack(const uint8_t *in, int bits, int64_t rows, int count, int64_t row_bytes,

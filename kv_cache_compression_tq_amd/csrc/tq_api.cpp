@@ -389,6 +389,22 @@ int tq_quantize(tq_handle h, const void *x, int dtype, int64_t n_sets, int64_t n
   return e == hipSuccess ? TQ_OK : hip_fail(e, "quantize launch");
 }
 
+int tq_append(tq_handle h, const void *x, int dtype, int64_t n_sets, const int64_t *rows, int64_t cache_rows,
+              void *codes, void *signs, float *norms, float *rnorms, void *stream) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (n_sets < 0 || n_sets > 65535) return fail(TQ_EINVAL, "n_sets must be in [0, 65535]");
+  if (cache_rows < 0) return fail(TQ_EINVAL, "cache_rows must be >= 0");
+  if (n_sets == 0) return TQ_OK;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_EINVAL, "dtype must be TQ_F32 or TQ_BF16");
+  if (!x || ((uintptr_t)x & (dtype == TQ_F32 ? 3u : 1u))) return fail(TQ_EINVAL, "x NULL or misaligned");
+  if (!rows || ((uintptr_t)rows & 7u)) return fail(TQ_EINVAL, "rows NULL or misaligned");
+  if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, true))) return st;
+  hipError_t e = tq::launch_append(h->dev, x, dtype, n_sets, rows, cache_rows, (uint8_t *)codes, (uint8_t *)signs,
+                                   norms, rnorms, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "append launch");
+}
+
 int tq_dequantize(tq_handle h, const void *codes, const void *signs, const float *norms,
                   const float *rnorms, int64_t n_sets, int64_t n, float *x_out, void *stream) {
   int st = check_handle(h);

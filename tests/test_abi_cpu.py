@@ -45,6 +45,7 @@ def test_strerror_and_validation_without_device():
                           ctypes.c_float(1.0), None, None, 0, None) == tq.TQ_EINVAL
     n = ctypes.c_size_t()
     assert L.tq_attention_workspace(None, None, 1, 1, 1, ctypes.byref(n)) == tq.TQ_EINVAL
+    assert L.tq_append(None, None, 0, 1, None, 1, None, None, None, None, None) == tq.TQ_EINVAL
     assert L.tq_destroy(None) == tq.TQ_OK
 
 
