@@ -427,3 +427,75 @@ def logits_fast(cd: Codec, q: np.ndarray, keys: dict, group: int = 0) -> np.ndar
         z = np.asarray(keys["signs"], dtype=np.float64)
         out += (QJL_SCALE / cd.m) * (p @ z.T) * np.asarray(keys["rnorms"], dtype=np.float64)[None, :]
     return out * nu[None, :]
+
+# ---------------------------------------------------------------------------
+# Outlier-channel mixed precision.
+# ---------------------------------------------------------------------------
+@dataclass
+class Mixed:
+    """Two independent codecs over a channel split ([tmdm]-style pages on KV
+    compression: outlier channels kept apart at a higher precision; the 2.5-
+    and 3.5-bit configurations).  channels[g] lists the outlier channels of
+    group g first (the caller's order), then the other channels ascending.
+    The outlier part (n_out dims) is coded at b + 1 bits with `seed`, the
+    regular part (d - n_out dims) at b bits with `seed + 1`."""
+    d: int
+    n_out: int
+    channels: np.ndarray              # [groups][d] int
+    outlier: Codec | None
+    regular: Codec | None
+
+
+def make_mixed(d: int, bits: int, variant: int, seed: int, out_channels, groups: int = 1) -> Mixed:
+    out_channels = np.asarray(out_channels, dtype=np.int64).reshape(groups, -1)
+    n_out = out_channels.shape[1]
+    perm = np.empty((groups, d), dtype=np.int64)
+    for g in range(groups):
+        rest = np.setdiff1d(np.arange(d), out_channels[g])
+        perm[g] = np.concatenate([out_channels[g], rest])
+        assert len(set(perm[g].tolist())) == d, "outlier channels must be distinct channels of [0, d)"
+    outlier = make_codec(n_out, bits + 1, variant, seed, groups) if n_out > 0 else None
+    regular = make_codec(d - n_out, bits, variant, seed + 1, groups) if n_out < d else None
+    return Mixed(d, n_out, perm, outlier, regular)
+
+
+def _quantize_part(cd: Codec, x: np.ndarray, group: int) -> dict:
+    if cd.variant == MSE:
+        idx, nu, y = quantize_mse(cd, x, group)
+        return dict(idx=idx, norms=nu, y=y)
+    return quantize_prod(cd, x, group)
+
+
+def _dequantize_part(cd: Codec, part: dict, group: int) -> np.ndarray:
+    if cd.variant == MSE:
+        return dequantize_mse(cd, part["idx"], part["norms"], group)
+    return dequantize_prod(cd, part.get("idx"), part["signs"], part["norms"], part["rnorms"], group)
+
+
+def mixed_quantize(mx: Mixed, x: np.ndarray, group: int = 0):
+    """Gather each part's channels and quantize it with its own codec; returns
+    (outlier part, regular part), each a dict as quantize_mse / quantize_prod
+    give (None for an empty part)."""
+    x = np.asarray(x, dtype=np.float64)
+    perm = mx.channels[group]
+    po = _quantize_part(mx.outlier, x[..., perm[:mx.n_out]], group) if mx.outlier else None
+    pr = _quantize_part(mx.regular, x[..., perm[mx.n_out:]], group) if mx.regular else None
+    return po, pr
+
+
+def mixed_dequantize(mx: Mixed, parts, group: int = 0) -> np.ndarray:
+    """Each part's reconstruction, scattered back to its channels."""
+    po, pr = parts
+    ref = po if po is not None else pr
+    out = np.zeros(ref["norms"].shape + (mx.d,))
+    perm = mx.channels[group]
+    if po is not None:
+        out[..., perm[:mx.n_out]] = _dequantize_part(mx.outlier, po, group)
+    if pr is not None:
+        out[..., perm[mx.n_out:]] = _dequantize_part(mx.regular, pr, group)
+    return out
+
+
+def mixed_logits_plain(mx: Mixed, q: np.ndarray, parts, group: int = 0) -> np.ndarray:
+    """<q, x_hat> for every (query, key) with x_hat the mixed reconstruction."""
+    return np.asarray(q, dtype=np.float64) @ mixed_dequantize(mx, parts, group).T
