@@ -145,6 +145,58 @@ int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const v
 int tq_attention_workspace(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_sets, int64_t n_keys,
                            size_t *bytes);
 
+/* ---- outlier-channel mixed precision ----
+ * The pages keep outlier channels apart at a higher precision ([tqnet]
+ * 从工程视角看 TurboQuant 到底改变了什么) and quote 2.5- and 3.5-bit KV
+ * configurations ([tqnet] 数据就是论据 › KV Cache 压缩基准; [ttakun], 3.5 bits
+ * per channel).  No split rule is given; this is the plainest one.  A mixed codec
+ * splits the d channels of every vector into an outlier part (n_out channels
+ * per group, named by the caller) and a regular part (the other d - n_out
+ * channels, ascending).  Each part is an independent TurboQuant codec of its
+ * own dimension: the outlier part at b + 1 bits with `seed`, the regular part
+ * at b bits with `seed + 1`, same variant and groups.  n_out = d / 2 gives
+ * b + 0.5 bits per channel (2.5 at b = 2, 3.5 at b = 3).  Reconstructions
+ * scatter the parts back; inner products are the sum of the parts'. */
+typedef struct tq_mixed_codec *tq_mixed;
+
+/* out_channels: host array [groups][n_out] of distinct channels in [0, d)
+ * per group.  Valid: 6 <= d <= 4096; 3 <= n_out <= d - 3; mse 1 <= b <= 7,
+ * prod 1 <= b <= 4.  Errors: TQ_EINVAL, TQ_ENOMEM, TQ_EHIP. */
+int tq_mixed_init(int d, int b, int variant, uint64_t seed, int groups, int n_out, const int32_t *out_channels,
+                  tq_mixed *out);
+int tq_mixed_destroy(tq_mixed m);
+
+/* The two part codecs (owned by m: do not destroy them).  Their tq_layout
+ * gives each part's row sizes; their tables are the parts' tables. */
+int tq_mixed_parts(tq_mixed m, tq_handle *outlier, tq_handle *regular);
+
+/* Workspace bytes the calls below need for n_sets x n vectors and nq
+ * queries per set (pass nq = 0 when no logits call is planned). */
+int tq_mixed_workspace(tq_mixed m, int64_t n_sets, int64_t n, int64_t nq, size_t *bytes);
+
+/* Quantize x[n_sets][n][d] (TQ_F32 / TQ_BF16): every argument array of two
+ * device pointers holds the outlier part's array at [0] and the regular
+ * part's at [1], each in the layout of tq_quantize for that part's codec.
+ * workspace: caller-owned device memory, 256-byte aligned, at least the
+ * tq_mixed_workspace size; scratch.  Errors: TQ_EINVAL, TQ_EHIP. */
+int tq_mixed_quantize(tq_mixed m, const void *x, int dtype, int64_t n_sets, int64_t n, void *const codes[2],
+                      void *const signs[2], float *const norms[2], float *const rnorms[2], void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Reconstruct x_out[n_sets][n][d] float32 (each part's tq_dequantize,
+ * scattered back to its channels).  Arrays and workspace as above. */
+int tq_mixed_dequantize(tq_mixed m, const void *const codes[2], const void *const signs[2],
+                        const float *const norms[2], const float *const rnorms[2], int64_t n_sets, int64_t n,
+                        float *x_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* out[s][i][t] = <q[s][i], x_hat[s][t]> for the mixed reconstruction: the
+ * outlier part's logits plus the regular part's (queries split the same
+ * way).  q: [n_sets][nq][d] float32, 1 <= nq <= 64.  Arrays and workspace
+ * as above (the workspace also holds one part's logits). */
+int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const codes[2], const void *const signs[2],
+                    const float *const norms[2], const float *const rnorms[2], int64_t n_sets, int64_t n_keys,
+                    float *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *tq_strerror(int status);
 /* Thread-local detail of the last failure on this thread ("" if none). */

@@ -10,7 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Codec", "lib", "library_path", "TQ_MSE", "TQ_PROD", "TQ_F32", "TQ_BF16", "TQError",
+__all__ = ["Codec", "MixedCodec", "lib", "library_path", "TQ_MSE", "TQ_PROD", "TQ_F32", "TQ_BF16", "TQError",
            "EXPORTED_SYMBOLS", "row_bytes"]
 
 TQ_MSE, TQ_PROD = 0, 1
@@ -35,6 +35,13 @@ _SIGS = {
     "tq_attention": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P,
                             ctypes.c_size_t, _P]),
     "tq_attention_workspace": (_INT, [_P, _P, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "tq_mixed_init": (_INT, [_INT, _INT, _INT, ctypes.c_uint64, _INT, _INT, _P, ctypes.POINTER(_P)]),
+    "tq_mixed_destroy": (_INT, [_P]),
+    "tq_mixed_parts": (_INT, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
+    "tq_mixed_workspace": (_INT, [_P, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "tq_mixed_quantize": (_INT, [_P, _P, _INT, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "tq_mixed_dequantize": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "tq_mixed_logits": (_INT, [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
     "tq_strerror": (ctypes.c_char_p, [_INT]),
     "tq_last_error": (ctypes.c_char_p, []),
     "tq_get_tables": (_INT, [_P, _INT, _P, _P, _P, _P]),
@@ -102,10 +109,15 @@ class Codec:
     stream; outputs are allocated here with torch unless given.
     """
 
-    def __init__(self, d: int, bits: int, variant: int = TQ_MSE, seed: int = 0, groups: int = 1):
+    def __init__(self, d: int, bits: int, variant: int = TQ_MSE, seed: int = 0, groups: int = 1, _borrowed=None):
         self.d, self.bits, self.variant, self.seed, self.groups = d, bits, variant, seed, groups
-        h = ctypes.c_void_p()
-        _check(lib().tq_init_groups(d, bits, variant, seed, groups, ctypes.byref(h)), "tq_init_groups")
+        if _borrowed is None:
+            h = ctypes.c_void_p()
+            _check(lib().tq_init_groups(d, bits, variant, seed, groups, ctypes.byref(h)), "tq_init_groups")
+            self._owned = True
+        else:  # a part codec owned by a MixedCodec
+            h = _borrowed
+            self._owned = False
         self._h = h
         cr, sr, mb = _I64(), _I64(), _INT()
         _check(lib().tq_layout(self._h, ctypes.byref(cr), ctypes.byref(sr), ctypes.byref(mb)), "tq_layout")
@@ -113,7 +125,8 @@ class Codec:
 
     def close(self) -> None:
         if getattr(self, "_h", None):
-            lib().tq_destroy(self._h)
+            if getattr(self, "_owned", True):
+                lib().tq_destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -276,6 +289,106 @@ class Codec:
         rows = packed.shape[0]
         out = torch.empty((rows, self.d), dtype=torch.uint8, device=packed.device)
         _check(lib().tq_unpack(self._h, _ptr(packed), bits, rows, _ptr(out), _stream(stream)), "tq_unpack")
+        return out
+
+
+def _ptr_pair(parts, key):
+    arr = (ctypes.c_void_p * 2)()
+    for i, p in enumerate(parts):
+        t = p.get(key)
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+class MixedCodec:
+    """Outlier-channel mixed precision: the channels out_channels[g] of group g
+    are coded at bits + 1 by the `outlier` part codec (seed), the other
+    channels at `bits` by the `regular` part codec (seed + 1).
+    out_channels: [groups, n_out] integers."""
+
+    def __init__(self, d: int, bits: int, variant: int, seed: int, out_channels, groups: int = 1):
+        import numpy as np
+
+        ch = np.ascontiguousarray(np.asarray(out_channels, dtype=np.int32).reshape(groups, -1))
+        self.d, self.bits, self.variant, self.seed, self.groups = d, bits, variant, seed, groups
+        self.n_out = ch.shape[1]
+        h = ctypes.c_void_p()
+        _check(lib().tq_mixed_init(d, bits, variant, seed, groups, self.n_out, ch.ctypes.data, ctypes.byref(h)),
+               "tq_mixed_init")
+        self._h = h
+        ho, hr = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib().tq_mixed_parts(self._h, ctypes.byref(ho), ctypes.byref(hr)), "tq_mixed_parts")
+        self.outlier = Codec(self.n_out, bits + 1, variant, seed, groups, _borrowed=ho)
+        self.regular = Codec(d - self.n_out, bits, variant, seed + 1, groups, _borrowed=hr)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self.outlier.close()
+            self.regular.close()
+            lib().tq_mixed_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, n_sets: int, n: int, nq: int = 0, device="cuda"):
+        import torch
+
+        b = ctypes.c_size_t()
+        _check(lib().tq_mixed_workspace(self._h, n_sets, n, nq, ctypes.byref(b)), "tq_mixed_workspace")
+        return torch.empty(max(b.value, 1), dtype=torch.uint8, device=device)
+
+    def empty_codes(self, n_sets: int, n: int, device="cuda"):
+        return (self.outlier.empty_codes(n_sets, n, device), self.regular.empty_codes(n_sets, n, device))
+
+    def quantize(self, x, out=None, workspace=None, stream=None):
+        """x: [n_sets, n, d] float32 or bfloat16.  Returns (outlier, regular)
+        dicts as Codec.quantize returns for each part."""
+        import torch
+
+        if x.dim() == 2:
+            x = x.unsqueeze(0)
+        dtype = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}.get(x.dtype)
+        if dtype is None or not x.is_contiguous() or x.shape[2] != self.d:
+            raise ValueError("x must be a contiguous [n_sets, n, d] float32 / bfloat16 tensor")
+        n_sets, n, _ = x.shape
+        out = out or self.empty_codes(n_sets, n, x.device)
+        ws = workspace if workspace is not None else self.workspace(n_sets, n, 0, x.device)
+        _check(lib().tq_mixed_quantize(self._h, _ptr(x), dtype, n_sets, n, _ptr_pair(out, "codes"),
+                                       _ptr_pair(out, "signs"), _ptr_pair(out, "norms"), _ptr_pair(out, "rnorms"),
+                                       _ptr(ws), ws.numel(), _stream(stream)), "tq_mixed_quantize")
+        return out
+
+    def dequantize(self, parts, out=None, workspace=None, stream=None):
+        import torch
+
+        n_sets, n = parts[0]["norms"].shape
+        if out is None:
+            out = torch.empty((n_sets, n, self.d), dtype=torch.float32, device=parts[0]["norms"].device)
+        ws = workspace if workspace is not None else self.workspace(n_sets, n, 0, out.device)
+        _check(lib().tq_mixed_dequantize(self._h, _ptr_pair(parts, "codes"), _ptr_pair(parts, "signs"),
+                                         _ptr_pair(parts, "norms"), _ptr_pair(parts, "rnorms"), n_sets, n, _ptr(out),
+                                         _ptr(ws), ws.numel(), _stream(stream)), "tq_mixed_dequantize")
+        return out
+
+    def logits(self, q, parts, out=None, workspace=None, stream=None):
+        import torch
+
+        if q.dim() == 2:
+            q = q.unsqueeze(0)
+        if q.dtype != torch.float32 or not q.is_contiguous():
+            raise TypeError("q must be contiguous float32")
+        n_sets, n_keys = parts[0]["norms"].shape
+        nq = q.shape[1]
+        if out is None:
+            out = torch.empty((n_sets, nq, n_keys), dtype=torch.float32, device=q.device)
+        ws = workspace if workspace is not None else self.workspace(n_sets, n_keys, nq, q.device)
+        _check(lib().tq_mixed_logits(self._h, _ptr(q), nq, _ptr_pair(parts, "codes"), _ptr_pair(parts, "signs"),
+                                     _ptr_pair(parts, "norms"), _ptr_pair(parts, "rnorms"), n_sets, n_keys,
+                                     _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "tq_mixed_logits")
         return out
 
 

@@ -116,6 +116,41 @@ __global__ __launch_bounds__(kThreads) void k_quant_generic(
   if (tid == 0) rnorms[row] = nu > 0.f ? rn / nu : 0.f;
 }
 
+// ------------------------------------------------------- mixed precision --
+// Channel split of an outlier-channel mixed codec: perm[g] lists the outlier
+// channels of group g, then the regular ones.  Row r of a set of n rows uses
+// group (r / n) % groups.  One thread per element.
+template <typename T>
+__global__ void k_gather_parts(const T *__restrict__ x, int64_t rows, int64_t n, int groups, int d, int n_out,
+                               const int32_t *__restrict__ perm, T *__restrict__ xo, T *__restrict__ xr) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= rows * d) return;
+  const int64_t row = e / d;
+  const int c = (int)(e % d);
+  const int g = (int)((row / n) % groups);
+  const T v = x[row * d + perm[(int64_t)g * d + c]];
+  if (c < n_out)
+    xo[row * n_out + c] = v;
+  else
+    xr[row * (d - n_out) + (c - n_out)] = v;
+}
+
+__global__ void k_scatter_parts(const float *__restrict__ xo, const float *__restrict__ xr, int64_t rows, int64_t n,
+                                int groups, int d, int n_out, const int32_t *__restrict__ perm,
+                                float *__restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= rows * d) return;
+  const int64_t row = e / d;
+  const int c = (int)(e % d);
+  const int g = (int)((row / n) % groups);
+  out[row * d + perm[(int64_t)g * d + c]] = c < n_out ? xo[row * n_out + c] : xr[row * (d - n_out) + (c - n_out)];
+}
+
+__global__ void k_add_inplace(float *__restrict__ out, const float *__restrict__ in, int64_t count) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < count) out[e] += in[e];
+}
+
 // ---------------------------------------------------------------- append --
 // One vector per set written straight into row rows[s] of a (paged) cache:
 // the online path of the pages ([ttakun] TurboQuant_mse: no training, one
@@ -490,6 +525,35 @@ hipError_t launch_append(const DeviceTables &t, const void *x, int dtype, int64_
     hipLaunchKernelGGL(k_append<uint16_t>, dim3((unsigned)n_sets), dim3(kAppendThreads), shmem, st,
                        (const uint16_t *)x, t.d, t.groups, t.mse_bits, prod, rows, cache_rows, t.PiT, t.MT,
                        t.cent, t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_parts(const void *x, int dtype, int64_t rows, int64_t n, int groups, int d, int n_out,
+                               const int32_t *perm, void *xo, void *xr, hipStream_t st) {
+  const int64_t total = rows * d;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (dtype == 0)
+    hipLaunchKernelGGL(k_gather_parts<float>, grid, dim3(256), 0, st, (const float *)x, rows, n, groups, d, n_out,
+                       perm, (float *)xo, (float *)xr);
+  else
+    hipLaunchKernelGGL(k_gather_parts<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)x, rows, n, groups, d,
+                       n_out, perm, (uint16_t *)xo, (uint16_t *)xr);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_parts(const float *xo, const float *xr, int64_t rows, int64_t n, int groups, int d,
+                                int n_out, const int32_t *perm, float *out, hipStream_t st) {
+  const int64_t total = rows * d;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_scatter_parts, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, xo, xr, rows, n,
+                     groups, d, n_out, perm, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_inplace(float *out, const float *in, int64_t count, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_add_inplace, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, out, in, count);
   return hipGetLastError();
 }
 

@@ -67,6 +67,13 @@ hipError_t launch_attention_generic(const DeviceTables &tk, const DeviceTables &
 hipError_t launch_append(const DeviceTables &t, const void *x, int dtype, int64_t n_sets, const int64_t *rows,
                          int64_t cache_rows, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
                          hipStream_t st);
+// Outlier-channel split: gather x rows into the two parts (dtype 0 f32, 1
+// bf16), scatter f32 parts back, and out += in.
+hipError_t launch_gather_parts(const void *x, int dtype, int64_t rows, int64_t n, int groups, int d, int n_out,
+                               const int32_t *perm, void *xo, void *xr, hipStream_t st);
+hipError_t launch_scatter_parts(const float *xo, const float *xr, int64_t rows, int64_t n, int groups, int d,
+                                int n_out, const int32_t *perm, float *out, hipStream_t st);
+hipError_t launch_add_inplace(float *out, const float *in, int64_t count, hipStream_t st);
 hipError_t launch_pack(const uint8_t *idx, int bits, int64_t rows, int count, int64_t row_bytes,
                        uint8_t *out, hipStream_t st);
 hipError_t launch_unpack(const uint8_t *in, int bits, int64_t rows, int count, int64_t row_bytes,

@@ -520,6 +520,177 @@ int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const v
   return e == hipSuccess ? TQ_OK : hip_fail(e, "attention launch");
 }
 
+// ------------------------------------------------------- mixed precision --
+struct tq_mixed_codec {
+  int d = 0, n_out = 0, groups = 0, variant = 0;
+  tq_handle parts[2] = {nullptr, nullptr};  // outlier part (n_out dims, b + 1 bits), regular part
+  int32_t *perm = nullptr;                  // device [groups][d]: outlier channels, then the rest ascending
+};
+
+namespace {
+
+int check_mixed(tq_mixed m) { return m ? TQ_OK : fail(TQ_EINVAL, "mixed handle is NULL"); }
+
+size_t up256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+int tq_mixed_init(int d, int b, int variant, uint64_t seed, int groups, int n_out, const int32_t *out_channels,
+                  tq_mixed *out) {
+  g_last_error.clear();
+  return guarded([&]() -> int {
+    if (!out) return fail(TQ_EINVAL, "out is NULL");
+    if (d < 6 || d > 4096) return fail(TQ_EINVAL, "d must be in [6, 4096]");
+    if (groups < 1 || groups > 4096) return fail(TQ_EINVAL, "groups must be in [1, 4096]");
+    if (n_out < 3 || n_out > d - 3) return fail(TQ_EINVAL, "n_out must be in [3, d - 3]");
+    if (variant == TQ_MSE ? (b < 1 || b > 7) : variant == TQ_PROD ? (b < 1 || b > 4) : true)
+      return fail(TQ_EINVAL, "mse needs 1 <= b <= 7, prod 1 <= b <= 4 (the outlier part takes b + 1 bits)");
+    if (!out_channels) return fail(TQ_EINVAL, "out_channels is NULL");
+    std::vector<int32_t> perm((size_t)groups * d);
+    for (int g = 0; g < groups; ++g) {
+      std::vector<char> used(d, 0);
+      int32_t *pg = perm.data() + (size_t)g * d;
+      for (int i = 0; i < n_out; ++i) {
+        const int32_t c = out_channels[(size_t)g * n_out + i];
+        if (c < 0 || c >= d || used[c]) return fail(TQ_EINVAL, "out_channels must be distinct channels of [0, d)");
+        used[c] = 1;
+        pg[i] = c;
+      }
+      int k = n_out;
+      for (int c = 0; c < d; ++c)
+        if (!used[c]) pg[k++] = c;
+    }
+    auto *m = new (std::nothrow) tq_mixed_codec;
+    if (!m) return fail(TQ_ENOMEM, "host allocation failed");
+    m->d = d;
+    m->n_out = n_out;
+    m->groups = groups;
+    m->variant = variant;
+    int st = make_codec(n_out, b + 1, variant, seed, groups, &m->parts[0]);
+    if (st == TQ_OK) st = make_codec(d - n_out, b, variant, seed + 1, groups, &m->parts[1]);
+    if (st == TQ_OK) {
+      hipError_t e = hipMalloc((void **)&m->perm, perm.size() * sizeof(int32_t));
+      if (e == hipSuccess) e = hipMemcpy(m->perm, perm.data(), perm.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+      if (e != hipSuccess) st = hip_fail(e, "channel map upload");
+    }
+    if (st != TQ_OK) {
+      tq_mixed_destroy(m);
+      return st;
+    }
+    *out = m;
+    return TQ_OK;
+  });
+}
+
+int tq_mixed_destroy(tq_mixed m) {
+  if (!m) return TQ_OK;
+  tq_destroy(m->parts[0]);
+  tq_destroy(m->parts[1]);
+  if (m->perm) (void)hipFree(m->perm);
+  delete m;
+  return TQ_OK;
+}
+
+int tq_mixed_parts(tq_mixed m, tq_handle *outlier, tq_handle *regular) {
+  int st = check_mixed(m);
+  if (st) return st;
+  if (outlier) *outlier = m->parts[0];
+  if (regular) *regular = m->parts[1];
+  return TQ_OK;
+}
+
+int tq_mixed_workspace(tq_mixed m, int64_t n_sets, int64_t n, int64_t nq, size_t *bytes) {
+  int st = check_mixed(m);
+  if (st) return st;
+  if (!bytes) return fail(TQ_EINVAL, "bytes is NULL");
+  if (n_sets < 0 || n < 0 || nq < 0) return fail(TQ_EINVAL, "sizes must be >= 0");
+  const size_t vec = up256((size_t)(n_sets * n) * m->d * sizeof(float)) + 256;  // gathered x or parts
+  const size_t lg = up256((size_t)(n_sets * nq) * m->d * sizeof(float)) + up256((size_t)(n_sets * nq * n) * sizeof(float));
+  *bytes = vec > lg ? vec : lg;
+  return TQ_OK;
+}
+
+int tq_mixed_quantize(tq_mixed m, const void *x, int dtype, int64_t n_sets, int64_t n, void *const codes[2],
+                      void *const signs[2], float *const norms[2], float *const rnorms[2], void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  int st = check_mixed(m);
+  if (st) return st;
+  if (!codes || !signs || !norms || !rnorms) return fail(TQ_EINVAL, "part pointer arrays must not be NULL");
+  if ((st = check_rows(m->parts[0], n_sets, n))) return st;
+  if (n_sets == 0 || n == 0) return TQ_OK;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_EINVAL, "dtype must be TQ_F32 or TQ_BF16");
+  if (!x || ((uintptr_t)x & (dtype == TQ_F32 ? 3u : 1u))) return fail(TQ_EINVAL, "x NULL or misaligned");
+  size_t need = 0;
+  tq_mixed_workspace(m, n_sets, n, 0, &need);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_mixed_workspace reports");
+  const size_t es = dtype == TQ_F32 ? 4 : 2;
+  char *xo = (char *)workspace;
+  char *xr = xo + up256((size_t)(n_sets * n) * m->n_out * es);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = tq::launch_gather_parts(x, dtype, n_sets * n, n, m->groups, m->d, m->n_out, m->perm, xo, xr, s);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  for (int p = 0; p < 2; ++p)
+    if ((st = tq_quantize(m->parts[p], p == 0 ? xo : xr, dtype, n_sets, n, codes[p], signs[p], norms[p], rnorms[p],
+                          stream)))
+      return st;
+  return TQ_OK;
+}
+
+int tq_mixed_dequantize(tq_mixed m, const void *const codes[2], const void *const signs[2],
+                        const float *const norms[2], const float *const rnorms[2], int64_t n_sets, int64_t n,
+                        float *x_out, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_mixed(m);
+  if (st) return st;
+  if (!codes || !signs || !norms || !rnorms) return fail(TQ_EINVAL, "part pointer arrays must not be NULL");
+  if ((st = check_rows(m->parts[0], n_sets, n))) return st;
+  if (n_sets == 0 || n == 0) return TQ_OK;
+  if (!x_out || ((uintptr_t)x_out & 3u)) return fail(TQ_EINVAL, "x_out NULL or misaligned");
+  size_t need = 0;
+  tq_mixed_workspace(m, n_sets, n, 0, &need);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_mixed_workspace reports");
+  float *xo = (float *)workspace;
+  float *xr = (float *)((char *)workspace + up256((size_t)(n_sets * n) * m->n_out * 4));
+  for (int p = 0; p < 2; ++p)
+    if ((st = tq_dequantize(m->parts[p], codes[p], signs[p], norms[p], rnorms[p], n_sets, n, p == 0 ? xo : xr,
+                            stream)))
+      return st;
+  hipError_t e = tq::launch_scatter_parts(xo, xr, n_sets * n, n, m->groups, m->d, m->n_out, m->perm, x_out,
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "scatter launch");
+}
+
+int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const codes[2], const void *const signs[2],
+                    const float *const norms[2], const float *const rnorms[2], int64_t n_sets, int64_t n_keys,
+                    float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  int st = check_mixed(m);
+  if (st) return st;
+  if (!codes || !signs || !norms || !rnorms) return fail(TQ_EINVAL, "part pointer arrays must not be NULL");
+  if ((st = check_rows(m->parts[0], n_sets, n_keys))) return st;
+  if (nq < 1 || nq > 64) return fail(TQ_EINVAL, "nq must be in [1, 64]");
+  if (n_sets == 0 || n_keys == 0) return TQ_OK;
+  if (!q || ((uintptr_t)q & 3u)) return fail(TQ_EINVAL, "q NULL or misaligned");
+  if (!out || ((uintptr_t)out & 3u)) return fail(TQ_EINVAL, "out NULL or misaligned");
+  size_t need = 0;
+  tq_mixed_workspace(m, n_sets, n_keys, nq, &need);
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_mixed_workspace reports");
+  char *ws = (char *)workspace;
+  float *qo = (float *)ws;
+  float *qr = (float *)(ws + up256((size_t)(n_sets * nq) * m->n_out * 4));
+  float *lr = (float *)(ws + up256((size_t)(n_sets * nq) * m->d * 4));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = tq::launch_gather_parts(q, TQ_F32, n_sets * nq, nq, m->groups, m->d, m->n_out, m->perm, qo, qr, s);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  if ((st = tq_logits(m->parts[0], qo, nq, codes[0], signs[0], norms[0], rnorms[0], n_sets, n_keys, out, stream)))
+    return st;
+  if ((st = tq_logits(m->parts[1], qr, nq, codes[1], signs[1], norms[1], rnorms[1], n_sets, n_keys, lr, stream)))
+    return st;
+  e = tq::launch_add_inplace(out, lr, n_sets * nq * n_keys, s);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "accumulate launch");
+}
+
 const char *tq_strerror(int status) {
   switch (status) {
     case TQ_OK: return "ok";

@@ -433,9 +433,13 @@ def logits_fast(cd: Codec, q: np.ndarray, keys: dict, group: int = 0) -> np.ndar
 # ---------------------------------------------------------------------------
 @dataclass
 class Mixed:
-    """Two independent codecs over a channel split ([tmdm]-style pages on KV
-    compression: outlier channels kept apart at a higher precision; the 2.5-
-    and 3.5-bit configurations).  channels[g] lists the outlier channels of
+    """Two independent codecs over a channel split: outlier channels kept
+    apart at a higher precision ([tqnet] 从工程视角看 TurboQuant 到底改变了什么),
+    the 2.5- and 3.5-bit KV configurations ([tqnet] 数据就是论据 › KV Cache
+    压缩基准).  The split rule is not on the pages: the outlier part takes one
+    more bit than the rest, which gives b + n_out/d bits per channel.
+    PARITY PINS: reductions to the plain codec, bit budget, part distortions,
+    unbiasedness (tests/test_oracle_mixed.py).  channels[g] lists the outlier channels of
     group g first (the caller's order), then the other channels ascending.
     The outlier part (n_out dims) is coded at b + 1 bits with `seed`, the
     regular part (d - n_out dims) at b bits with `seed + 1`."""

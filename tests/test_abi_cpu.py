@@ -46,6 +46,12 @@ def test_strerror_and_validation_without_device():
     n = ctypes.c_size_t()
     assert L.tq_attention_workspace(None, None, 1, 1, 1, ctypes.byref(n)) == tq.TQ_EINVAL
     assert L.tq_append(None, None, 0, 1, None, 1, None, None, None, None, None) == tq.TQ_EINVAL
+    m = ctypes.c_void_p()
+    ch = (ctypes.c_int32 * 4)(0, 1, 1, 2)  # a repeated channel
+    assert L.tq_mixed_init(128, 2, 0, 0, 1, 4, ch, ctypes.byref(m)) == tq.TQ_EINVAL
+    assert L.tq_mixed_init(128, 8, 0, 0, 1, 4, ch, ctypes.byref(m)) == tq.TQ_EINVAL
+    assert L.tq_mixed_init(128, 2, 0, 0, 1, 2, ch, ctypes.byref(m)) == tq.TQ_EINVAL
+    assert L.tq_mixed_destroy(None) == tq.TQ_OK
     assert L.tq_destroy(None) == tq.TQ_OK
 
 
