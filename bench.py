@@ -247,6 +247,20 @@ def other_paths_phase(torch, tq, workloads, x_kv):
             res[f"d{dd}_{name}_b{bits}_vectors_per_s"] = nn / (ms * 1e-3)
             res[f"d{dd}_{name}_b{bits}_mfma_frac"] = flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS
         del xh
+    # outlier-channel mixed precision on the KV workload: per head the 64
+    # channels of largest RMS at b + 1 bits, the rest at b (2.5 and 3.5 bits)
+    rms = xk.float().pow(2).mean(dim=1).sqrt()           # [16 sets][128]; groups from the key heads
+    chans = torch.argsort(rms[:workloads.KV_HEADS], dim=1, descending=True)[:, :64].cpu().numpy()
+    for bits in (2, 3):
+        mc = tq.MixedCodec(d, bits, tq.TQ_MSE, 0, chans, groups=workloads.KV_HEADS)
+        out = mc.empty_codes(sets, n)
+        ws = mc.workspace(sets, n)
+        ms = _mean_launch_ms(torch, lambda: mc.quantize(xk, out=out, workspace=ws))
+        res[f"kv_mixed_{bits}.5bit_quantize_ms"] = ms
+        res[f"kv_mixed_{bits}.5bit_vectors_per_s"] = sets * n / (ms * 1e-3)
+        byts = sets * n * (d * 2 + mc.outlier.code_row + mc.regular.code_row + 8)
+        res[f"kv_mixed_{bits}.5bit_gbs"] = byts / (ms * 1e-3) / 1e9
+        del mc, out, ws
     centres = torch.randn((workloads.NN_CENTRES, workloads.NN_D), generator=gen, device="cuda")
     centres /= centres.norm(dim=1, keepdim=True)
     m = torch.randint(0, workloads.NN_CENTRES, (workloads.NN_POINTS,), generator=gen, device="cuda")
