@@ -503,3 +503,27 @@ def mixed_dequantize(mx: Mixed, parts, group: int = 0) -> np.ndarray:
 def mixed_logits_plain(mx: Mixed, q: np.ndarray, parts, group: int = 0) -> np.ndarray:
     """<q, x_hat> for every (query, key) with x_hat the mixed reconstruction."""
     return np.asarray(q, dtype=np.float64) @ mixed_dequantize(mx, parts, group).T
+
+
+# ---------------------------------------------------------------------------
+# Inner-product nearest-neighbour search over packed codes.
+# ---------------------------------------------------------------------------
+def topk_plain(cd: Codec, q: np.ndarray, keys: dict, k: int, group: int = 0):
+    """The k keys with the largest estimated inner products <q, k_hat> per
+    query, best first; equal scores are ordered by key index (maximum inner
+    product search on the quantized index: [ttakun] 索引速度 (vector search on
+    TurboQuant codes); scores are logits_plain).  Returns (scores [nq][k],
+    indices [nq][k])."""
+    sc = logits_plain(cd, q, keys, group)
+    n = sc.shape[1]
+    order = np.lexsort((np.broadcast_to(np.arange(n), sc.shape), -sc), axis=1)[:, :k]
+    return np.take_along_axis(sc, order, axis=1), order
+
+
+def recall_at(true_top1: np.ndarray, topk_idx: np.ndarray, ks) -> dict:
+    """recall@1@k: the share of queries whose exact top-1 key is among the
+    first k of the searched list, for each k in ks."""
+    true_top1 = np.asarray(true_top1).reshape(-1, 1)
+    hit = np.asarray(topk_idx) == true_top1
+    first = np.where(hit.any(axis=1), hit.argmax(axis=1), np.iinfo(np.int64).max)
+    return {int(k): float(np.mean(first < k)) for k in ks}
