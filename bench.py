@@ -267,10 +267,27 @@ def other_paths_phase(torch, tq, workloads, x_kv):
     pts = centres[m] + workloads.NN_STD * torch.randn((workloads.NN_POINTS, workloads.NN_D), generator=gen,
                                                       device="cuda")
     pts = (pts / pts.norm(dim=1, keepdim=True)).unsqueeze(0).contiguous()
+    qs = centres[torch.randint(0, workloads.NN_CENTRES, (workloads.NN_QUERIES,), generator=gen, device="cuda")]
+    qs = qs + workloads.NN_STD * torch.randn((workloads.NN_QUERIES, workloads.NN_D), generator=gen, device="cuda")
+    qs = (qs / qs.norm(dim=1, keepdim=True)).contiguous()
+    # exact fp32 top-1 of every query over the unquantized points (queries in chunks)
+    true1 = torch.empty(workloads.NN_QUERIES, dtype=torch.int64, device="cuda")
+    for a in range(0, workloads.NN_QUERIES, 500):
+        true1[a:a + 500] = torch.argmax(qs[a:a + 500] @ pts[0].T, dim=1)
+    ks = (1, 2, 4, 8, 16, 32, 64)
     for bits in (2, 4):
         codec = tq.Codec(workloads.NN_D, bits, tq.TQ_PROD, seed=0)
         out = codec.empty_codes(1, workloads.NN_POINTS)
         res[f"nn_index_d200_prod_b{bits}_ms"] = _mean_launch_ms(torch, lambda: codec.quantize(pts, out=out))
+        keys = {k: (None if v is None else v[0]) for k, v in out.items()}
+        sc, ix = codec.topk(qs, keys, 64)
+        ms = _mean_launch_ms(torch, lambda: codec.topk(qs, keys, 64), reps=3)
+        res[f"nn_search_d200_prod_b{bits}_top64_ms"] = ms
+        res[f"nn_search_d200_prod_b{bits}_pairs_per_s"] = workloads.NN_QUERIES * workloads.NN_POINTS / (ms * 1e-3)
+        hit = ix.long() == true1[:, None]
+        first = torch.where(hit.any(dim=1), hit.float().argmax(dim=1), torch.full_like(true1, 1 << 30))
+        res[f"nn_recall_at_1_at_k_prod_b{bits}"] = {str(k): float((first < k).float().mean()) for k in ks}
+        del out, keys, sc, ix
     return res
 
 

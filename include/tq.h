@@ -145,6 +145,21 @@ int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const v
 int tq_attention_workspace(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_sets, int64_t n_keys,
                            size_t *bytes);
 
+/* Maximum inner product search over one set of n_keys packed keys (group
+ * 0): for each query q[i] (float32 [nq][d]), the k keys with the largest
+ * estimates <q[i], k_hat[t]> (the tq_logits values), best first; equal
+ * scores are ordered by key index.  out_scores: [nq][k] float32, out_idx:
+ * [nq][k] int32.  The scan is fused with the selection: no score matrix is
+ * written.  ([ttakun] 索引速度: the same codes serve vector search; the
+ * inner-product estimator as in tq_logits.)  Handles d <= 256 with at most
+ * 4 mse bits (else TQ_EUNSUPPORTED).  1 <= k <= 64, n_keys >= k.
+ * workspace: caller-owned device memory, 256-byte aligned, of at least the
+ * tq_topk_workspace size; scratch.  Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP. */
+int tq_topk_workspace(tq_handle h, int64_t nq, int64_t n_keys, int k, size_t *bytes);
+int tq_topk(tq_handle h, const float *q, int64_t nq, const void *codes, const void *signs, const float *norms,
+            const float *rnorms, int64_t n_keys, int k, float *out_scores, int32_t *out_idx, void *workspace,
+            size_t workspace_bytes, void *stream);
+
 /* ---- outlier-channel mixed precision ----
  * The pages keep outlier channels apart at a higher precision ([tqnet]
  * 从工程视角看 TurboQuant 到底改变了什么) and quote 2.5- and 3.5-bit KV

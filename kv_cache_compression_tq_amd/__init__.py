@@ -35,6 +35,8 @@ _SIGS = {
     "tq_attention": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P,
                             ctypes.c_size_t, _P]),
     "tq_attention_workspace": (_INT, [_P, _P, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "tq_topk_workspace": (_INT, [_P, _I64, _I64, _INT, ctypes.POINTER(ctypes.c_size_t)]),
+    "tq_topk": (_INT, [_P, _P, _I64, _P, _P, _P, _P, _I64, _INT, _P, _P, _P, ctypes.c_size_t, _P]),
     "tq_mixed_init": (_INT, [_INT, _INT, _INT, ctypes.c_uint64, _INT, _INT, _P, ctypes.POINTER(_P)]),
     "tq_mixed_destroy": (_INT, [_P]),
     "tq_mixed_parts": (_INT, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P)]),
@@ -260,6 +262,27 @@ class Codec:
                                   _ptr(values.get("rnorms")), n_sets, n_keys, float(scale), _ptr(out),
                                   _ptr(workspace), workspace.numel(), _stream(stream)), "tq_attention")
         return out
+
+    def topk(self, q, keys, k: int, workspace=None, stream=None):
+        """Top-k maximum inner product search: q [nq, d] float32 against one
+        set of keys (the dict from quantize, set 0 or unbatched arrays).
+        Returns (scores [nq, k] float32, indices [nq, k] int32), best first."""
+        import torch
+
+        if q.dim() != 2 or q.dtype != torch.float32 or not q.is_contiguous() or q.shape[1] != self.d:
+            raise ValueError("q must be a contiguous [nq, d] float32 tensor")
+        norms = keys["norms"].reshape(-1)
+        n_keys, nq = norms.numel(), q.shape[0]
+        b = ctypes.c_size_t()
+        _check(lib().tq_topk_workspace(self._h, nq, n_keys, k, ctypes.byref(b)), "tq_topk_workspace")
+        if workspace is None:
+            workspace = torch.empty(max(b.value, 1), dtype=torch.uint8, device=q.device)
+        scores = torch.empty((nq, k), dtype=torch.float32, device=q.device)
+        idx = torch.empty((nq, k), dtype=torch.int32, device=q.device)
+        _check(lib().tq_topk(self._h, _ptr(q), nq, _ptr(keys.get("codes")), _ptr(keys.get("signs")), _ptr(norms),
+                             _ptr(keys.get("rnorms")), n_keys, k, _ptr(scores), _ptr(idx), _ptr(workspace),
+                             workspace.numel(), _stream(stream)), "tq_topk")
+        return scores, idx
 
     # -- test hooks ----------------------------------------------------------
     def tables(self, group: int = 0):

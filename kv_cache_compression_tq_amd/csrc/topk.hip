@@ -1,0 +1,425 @@
+// Maximum inner product search over packed codes (d <= 256): for every
+// query, the k keys with the largest estimates <q, k_hat> (the logits), best
+// first, equal scores by key index.  [ttakun] 索引速度 (vector search on the
+// quantized index); [admirer] 第二步 (full-precision query against the
+// codes); [tmdm] 双剑合璧 (QJL inner-product estimator).
+//
+// k_topk_qprep: q~ = Pi q (scaled for the code table) and p = S q
+//   (scaled by sqrt(pi/2)/d) per query, zero-padded to 256 coordinates.
+// k_topk: a workgroup of 8 waves scans one key range; each wave holds 16
+//   queries as f16 hi/lo MFMA A operands (two row tiles of 8 queries) and
+//   streams 16-key tiles: lane (key, grp) decodes the codes of coordinates
+//   64 grp .. 64 grp + 63 of its key through LDS tables (a code pair per
+//   4-byte read, eight signs -- or eight 1-bit codes -- per 16-byte read).
+//   Scores above a query's current k-th best go to a small LDS buffer; a
+//   full buffer is merged into the query's running list, which lives in
+//   registers (lane i holds the i-th best).  Each wave writes its lists.
+// k_topk_merge: one wave per query merges the key ranges' lists.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tq {
+namespace {
+
+constexpr int kTkThreads = 256;           // one wave per SIMD: 512 registers per wave
+constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kTkQ = 16;                  // queries per wave: two row tiles of 8 (hi/lo rows)
+constexpr int kTkPad = 256;               // padded dimension: lane group g holds 64 g .. 64 g + 63
+constexpr int kTkKS = 8;                  // contraction steps of 32 coordinates
+constexpr int kTkRing = 4;                // tiles held in registers (three in flight)
+constexpr int kTkBuf = 48;                // buffered candidates per query
+constexpr int kTkMergeAt = kTkBuf - 16;   // a tile adds at most 16 per query
+constexpr int kTkSignCopies = 16;         // 16-byte entries 256 bytes apart: 16 lanes a cycle, no conflicts
+constexpr uint32_t kTkPairOff = 65536;    // the sign table fills LDS [0, 64 KB)
+constexpr uint32_t kTkBufOff = 98304;
+constexpr uint32_t kTkBufBytes = kTkQ * kTkBuf * 8;
+constexpr uint32_t kTkLds = kTkBufOff + kTkWaves * kTkBufBytes;
+static_assert(kTkLds <= 160 * 1024, "LDS budget");
+
+template <int MB>
+struct TkGeom {  // code-pair table: two codes -> two f16 values (alpha c)
+  static constexpr int W = 2 * MB;
+  static constexpr int ENTRIES = MB >= 2 ? 1 << W : 1;
+  static constexpr int COPIES = MB == 4 ? 32 : 64;
+  static constexpr int SHIFT = MB == 4 ? 7 : 8;
+  static constexpr uint32_t BYTES = MB >= 2 ? ENTRIES * COPIES * 4 : 0;
+  static_assert(BYTES <= kTkBufOff - kTkPairOff, "pair table");
+};
+
+// The key data of one 16-key tile in the lane's registers: its key's code
+// and sign bits of coordinates 64 grp .. 64 grp + 63, norm and residual norm.
+template <int MB, bool PROD>
+struct TkKey {
+  uint32_t c[MB > 0 ? 2 * MB : 1];
+  uint32_t s[2];
+  float nu, ga;
+};
+
+template <int MB, bool PROD>
+__device__ __forceinline__ void tk_load(TkKey<MB, PROD> &r, int64_t key, int64_t klast, int grp,
+                                        __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int64_t code_row,
+                                        int64_t sign_row, const float *norms, const float *rnorms) {
+  // codes and signs through buffer resources: bytes past the arrays read as
+  // zero (the padded coordinates meet zero query operands); keys past the
+  // range are masked by the caller
+  if constexpr (MB > 0) {
+    const uint32_t off = (uint32_t)(key * code_row) + 8 * MB * grp;
+#pragma unroll
+    for (int i = 0; i < 2 * MB; ++i) r.c[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, off + 4 * i, 0, 0);
+  }
+  if constexpr (PROD) {
+    const uint32_t off = (uint32_t)(key * sign_row) + 8 * grp;
+    r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+    r.s[1] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4, 0, 0);
+  }
+  const int64_t kk = key < klast ? key : klast;
+  r.nu = norms[kk];
+  r.ga = PROD ? rnorms[kk] : 0.f;
+}
+
+// Scores of one tile for the wave's 16 queries: lane (key, grp) gets queries
+// 2 grp, 2 grp + 1 of each row tile (rows 4 grp .. 4 grp + 3 = two queries x
+// hi/lo).  MB == 1 decodes the 1-bit codes with the sign table (c[idx] =
+// c1 (2 idx - 1); c1 is folded into the query).
+template <int MB, bool PROD>
+__device__ __forceinline__ void tk_score(const TkKey<MB, PROD> &r, const u32x4 (&qm)[2][kTkKS],
+                                         const u32x4 (&qq)[2][kTkKS], uint32_t sbase, uint32_t pbase,
+                                         float (&sc)[2][2]) {
+  using G = TkGeom<MB>;
+  f32x4 am[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, aq[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+  for (int k = 0; k < kTkKS; ++k) {
+    if constexpr (MB == 1) {
+      const uint32_t byte = (r.c[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      const u32x4 b = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)((byte << 8) | sbase);
+      am[0] = mfma_f16(qm[0][k], b, am[0]);
+      am[1] = mfma_f16(qm[1][k], b, am[1]);
+    } else if constexpr (MB >= 2) {
+      u32x4 b;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int bit = 8 * k * MB + G::W * i, wi = bit >> 5, sh = bit & 31;
+        uint32_t x;
+        if (sh + G::W > 32)
+          x = __builtin_amdgcn_alignbit(r.c[wi + 1], r.c[wi], sh - G::SHIFT);
+        else if (sh >= G::SHIFT)
+          x = r.c[wi] >> (sh - G::SHIFT);
+        else
+          x = r.c[wi] << (G::SHIFT - sh);
+        const uint32_t addr = (x & (uint32_t)(((1 << G::W) - 1) << G::SHIFT)) | pbase;
+        b[i] = *(__attribute__((address_space(3))) const uint32_t *)(uintptr_t)addr;
+      }
+      am[0] = mfma_f16(qm[0][k], b, am[0]);
+      am[1] = mfma_f16(qm[1][k], b, am[1]);
+    }
+    if constexpr (PROD) {
+      const uint32_t byte = (r.s[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      const u32x4 b = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)((byte << 8) | sbase);
+      aq[0] = mfma_f16(qq[0][k], b, aq[0]);
+      aq[1] = mfma_f16(qq[1][k], b, aq[1]);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    float v0 = MB > 0 ? am[rt][0] + am[rt][1] : 0.f, v1 = MB > 0 ? am[rt][2] + am[rt][3] : 0.f;
+    if constexpr (PROD) {
+      v0 = fmaf(r.ga, aq[rt][0] + aq[rt][1], v0);
+      v1 = fmaf(r.ga, aq[rt][2] + aq[rt][3], v1);
+    }
+    sc[rt][0] = v0 * r.nu;
+    sc[rt][1] = v1 * r.nu;
+  }
+}
+
+// (s, i) ranks before (cs, ci): a larger score, or an equal score and a
+// smaller key index.
+__device__ __forceinline__ bool tk_better(float s, int i, float cs, int ci) {
+  return s > cs || (s == cs && i < ci);
+}
+
+// Insert `cnt` buffered candidates into one query's list (lane l holds its
+// l-th best; lanes >= k hold -inf), one candidate at a time.
+__device__ __forceinline__ void tk_insert(float &ls, int &li, const float2 *cand, int cnt, int k, int lane) {
+  for (int c = 0; c < cnt; ++c) {
+    const float2 e = cand[c];
+    const float cs = e.x;
+    const int ci = __float_as_int(e.y);
+    const int pos = __popcll(__ballot(tk_better(ls, li, cs, ci)));
+    if (pos < k) {
+      const float us = __shfl_up(ls, 1);
+      const int ui = __shfl_up(li, 1);
+      if (lane > pos) {
+        ls = us;
+        li = ui;
+      } else if (lane == pos) {
+        ls = cs;
+        li = ci;
+      }
+    }
+  }
+  if (lane >= k) {
+    ls = -INFINITY;
+    li = 0x7fffffff;
+  }
+}
+
+template <int MB, bool PROD>
+__global__ __launch_bounds__(kTkThreads, 1) void k_topk(
+    const float *__restrict__ qprep, int nq, const uint8_t *__restrict__ codes, int64_t code_row,
+    const uint8_t *__restrict__ signs, int64_t sign_row, const float *__restrict__ norms,
+    const float *__restrict__ rnorms, int64_t n_keys, int k, int64_t keys_per_split, const uint32_t *__restrict__ lut,
+    float2 *__restrict__ lists) {
+  using G = TkGeom<MB>;
+  extern __shared__ u32x4 dyn_lds[];  // the kernel's only LDS: starts at address 0
+  char *lds = (char *)dyn_lds;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.y, S = gridDim.y;
+  const int64_t kb = (int64_t)split * keys_per_split;
+  const int64_t ke = kb + keys_per_split < n_keys ? kb + keys_per_split : n_keys;
+  const int qbase = (blockIdx.x * kTkWaves + wave) * kTkQ;
+
+  // tables: sign bytes -> eight f16 +-1 (16 copies); code pairs (MB >= 2)
+  const uint32_t code_words = MB > 0 ? 1u << (2 * MB) : 0u;
+  for (int e = tid; e < 256 * kTkSignCopies; e += kTkThreads)
+    ((u32x4 *)lds)[e] = ((const u32x4 *)(lut + code_words))[e / kTkSignCopies];
+  if constexpr (MB >= 2)
+    for (int e = tid; e < G::ENTRIES * G::COPIES; e += kTkThreads)
+      ((uint32_t *)(lds + kTkPairOff))[e] = lut[e / G::COPIES];
+  // query operands: row col of a row tile = (query col >> 1, part col & 1);
+  // element e of step k is coordinate 64 grp + 8 k + e
+  u32x4 qm[2][kTkKS], qq[2][kTkKS];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int q = qbase + rt * 8 + (col >> 1), part = col & 1;
+#pragma unroll
+    for (int ks = 0; ks < kTkKS; ++ks) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (q < nq && (m == 0 ? MB > 0 : PROD)) {
+          const f32x4 *src = (const f32x4 *)(qprep + ((int64_t)q * 2 + m) * kTkPad + 64 * grp + 8 * ks);
+          const f32x4 a = src[0], b = src[1];
+          v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+          v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+        }
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x0 = v[2 * i], x1 = v[2 * i + 1];
+          if (part) {
+            x0 -= (float)(_Float16)x0;
+            x1 -= (float)(_Float16)x1;
+          }
+          w[i] = f16x2(x0, x1);
+        }
+        (m == 0 ? qm : qq)[rt][ks] = w;
+      }
+    }
+  }
+  __syncthreads();
+
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)codes, 0, MB > 0 ? (int)(n_keys * code_row) : 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)signs, 0, PROD ? (int)(n_keys * sign_row) : 0, kBufferFlags);
+  const uint32_t sbase = 16 * (lane & (kTkSignCopies - 1));
+  const uint32_t pbase = kTkPairOff | (4 * (lane & (G::COPIES - 1)));
+  float2 *buf = (float2 *)(lds + kTkBufOff + wave * kTkBufBytes);  // [kTkQ][kTkBuf]
+
+  // running lists (lane l: the l-th best) and thresholds / buffer counts of
+  // queries 2 grp + h of each row tile (uniform over the lane's row)
+  float ls[kTkQ];
+  int li[kTkQ];
+#pragma unroll
+  for (int i = 0; i < kTkQ; ++i) {
+    ls[i] = -INFINITY;
+    li[i] = 0x7fffffff;
+  }
+  float tau[2][2];
+  int cnt[2][2] = {{0, 0}, {0, 0}};
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)  // queries past nq never take candidates
+      tau[rt][h] = qbase + rt * 8 + 2 * grp + h < nq ? -INFINITY : INFINITY;
+
+  auto merge = [&]() __attribute__((always_inline)) {  // every query with buffered candidates
+#pragma unroll
+    for (int qi = 0; qi < kTkQ; ++qi) {
+      const int rt = qi >> 3, r = qi & 7, gq = r >> 1, h = r & 1;
+      const int c = __builtin_amdgcn_readlane(cnt[rt][h], 16 * gq);
+      if (c > 0) {
+        tk_insert(ls[qi], li[qi], buf + qi * kTkBuf, c, k, lane);
+        const float t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[qi]), k - 1));
+        if (grp == gq) {
+          tau[rt][h] = t;
+          cnt[rt][h] = 0;
+        }
+      }
+    }
+  };
+
+  const int64_t nt = (ke - kb + 15) / 16;
+  // a ring of kTkRing tiles in registers: tile i + kTkRing - 1 loads while tile i is scored
+  TkKey<MB, PROD> ring[kTkRing];
+#pragma unroll
+  for (int j = 0; j + 1 < kTkRing; ++j)
+    if (j < nt) tk_load<MB, PROD>(ring[j], kb + 16 * j + col, ke - 1, grp, rc, rs, code_row, sign_row, norms, rnorms);
+  auto step = [&](const TkKey<MB, PROD> &r, int64_t t0) __attribute__((always_inline)) {
+    float sc[2][2];
+    tk_score<MB, PROD>(r, qm, qq, sbase, pbase, sc);
+    const int64_t key = t0 + col;
+    const bool valid = key < ke;
+    bool cand[2][2];
+    bool anyc = false;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        cand[rt][h] = valid && sc[rt][h] > tau[rt][h];
+        anyc |= cand[rt][h];
+      }
+    if (__ballot(anyc) == 0) return;
+    const uint32_t below = (1u << col) - 1u;
+    bool full = false;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint64_t m = __ballot(cand[rt][h]);
+        const uint32_t row = (uint32_t)(m >> (16 * grp)) & 0xFFFFu;
+        if (cand[rt][h]) {
+          const int qi = rt * 8 + 2 * grp + h;
+          buf[qi * kTkBuf + cnt[rt][h] + __popc(row & below)] = float2{sc[rt][h], __int_as_float((int)key)};
+        }
+        cnt[rt][h] += __popc(row);
+        full |= cnt[rt][h] > kTkMergeAt;
+      }
+    if (__ballot(full) != 0) merge();
+  };
+  for (int64_t i0 = 0; i0 < nt; i0 += kTkRing) {
+#pragma unroll
+    for (int j = 0; j < kTkRing; ++j) {
+      const int64_t i = i0 + j;
+      if (i >= nt) break;
+      const int64_t ip = i + kTkRing - 1;  // the tile that reuses the slot freed last
+      if (ip < nt)
+        tk_load<MB, PROD>(ring[(j + kTkRing - 1) % kTkRing], kb + 16 * ip + col, ke - 1, grp, rc, rs, code_row,
+                          sign_row, norms, rnorms);
+      step(ring[j], kb + 16 * i);
+    }
+  }
+  merge();
+  // this range's lists
+#pragma unroll
+  for (int qi = 0; qi < kTkQ; ++qi) {
+    const int q = qbase + qi;
+    if (q < nq && lane < k) lists[((int64_t)q * S + split) * k + lane] = float2{ls[qi], __int_as_float(li[qi])};
+  }
+}
+
+// One wave per query: merge the ranges' lists into the final top-k.
+__global__ __launch_bounds__(64) void k_topk_merge(const float2 *__restrict__ lists, int S, int k,
+                                                  float *__restrict__ out_scores, int32_t *__restrict__ out_idx) {
+  const int q = blockIdx.x, lane = threadIdx.x;
+  float ls = -INFINITY;
+  int li = 0x7fffffff;
+  for (int s = 0; s < S; ++s) {
+    const float2 *l = lists + ((int64_t)q * S + s) * k;
+    int n = 0;  // entries of this list (lists are sorted; -inf entries are empty slots)
+    while (n < k && l[n].x != -INFINITY) ++n;
+    tk_insert(ls, li, l, n, k, lane);
+  }
+  if (lane < k) {
+    out_scores[(int64_t)q * k + lane] = ls;
+    out_idx[(int64_t)q * k + lane] = li;
+  }
+}
+
+// q~ = Pi q and p = S q per query (one workgroup each), zero-padded to 256;
+// q~ is scaled for the code table (1 / alpha, or c1 for 1-bit codes decoded
+// as signs), p by sqrt(pi/2) / d.
+__global__ __launch_bounds__(kTkPad) void k_topk_qprep(const float *__restrict__ q, int d, int prod, int mse_bits,
+                                                       const float *__restrict__ PiT, const float *__restrict__ ST,
+                                                       float mscale, float *__restrict__ out) {
+  __shared__ float qs[kTkPad];
+  const int r = blockIdx.x, j = threadIdx.x;
+  qs[j] = j < d ? q[(int64_t)r * d + j] : 0.f;
+  __syncthreads();
+  float a = 0.f, b = 0.f;
+  if (j < d) {
+    for (int kk = 0; kk < d; ++kk) {
+      if (mse_bits > 0) a = fmaf(PiT[(size_t)kk * d + j], qs[kk], a);  // (Pi q)_j
+      if (prod) b = fmaf(ST[(size_t)kk * d + j], qs[kk], b);            // (S q)_j
+    }
+  }
+  out[((int64_t)r * 2 + 0) * kTkPad + j] = a * mscale;
+  out[((int64_t)r * 2 + 1) * kTkPad + j] = b * (kQjlScale / (float)d);
+}
+
+}  // namespace
+
+// Splits of the key range for nq queries (about two workgroups per CU, each
+// range at least 1024 keys).
+static int topk_splits(int64_t nq, int64_t n_keys) {
+  const int64_t qg = (nq + kTkWaves * kTkQ - 1) / (kTkWaves * kTkQ);
+  int64_t s = (512 + qg - 1) / qg;
+  const int64_t smax = n_keys / 1024 > 1 ? n_keys / 1024 : 1;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+size_t topk_workspace(const DeviceTables &t, int64_t nq, int64_t n_keys, int k) {
+  if (t.d > kTkPad || t.mse_bits > 4 || !t.logit_lut) return 0;
+  const size_t prep = (size_t)nq * 2 * kTkPad * sizeof(float);
+  const size_t lists = (size_t)nq * topk_splits(nq, n_keys) * k * sizeof(float2);
+  return (prep + 255) / 256 * 256 + lists;
+}
+
+template <int MB, bool PROD>
+static hipError_t run_topk(const DeviceTables &t, const float *q, int64_t nq, const uint8_t *codes,
+                           const uint8_t *signs, const float *norms, const float *rnorms, int64_t n_keys, int k,
+                           float *ws, float *out_scores, int32_t *out_idx, hipStream_t st) {
+  const int S = topk_splits(nq, n_keys);
+  float *prep = ws;
+  float2 *lists = (float2 *)((char *)ws + ((size_t)nq * 2 * kTkPad * sizeof(float) + 255) / 256 * 256);
+  // 1-bit codes are decoded as signs: c[idx] = c1 (2 idx - 1)
+  const float mscale = MB == 1 ? t.pos_cent[0] : t.lut_inv_scale;
+  hipLaunchKernelGGL(k_topk_qprep, dim3((unsigned)nq), dim3(kTkPad), 0, st, q, t.d, PROD ? 1 : 0, MB, t.PiT, t.ST,
+                     mscale, prep);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void *)k_topk<MB, PROD>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTkLds);
+  if (e != hipSuccess) return e;
+  const int64_t kps = (n_keys + S - 1) / S;
+  const dim3 grid((unsigned)((nq + kTkWaves * kTkQ - 1) / (kTkWaves * kTkQ)), (unsigned)S);
+  hipLaunchKernelGGL((k_topk<MB, PROD>), grid, dim3(kTkThreads), kTkLds, st, prep, (int)nq, codes, t.code_row, signs,
+                     t.sign_row, norms, rnorms, n_keys, k, kps, t.logit_lut, lists);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)nq), dim3(64), 0, st, lists, S, k, out_scores, out_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const DeviceTables &t, const float *q, int64_t nq, const uint8_t *codes, const uint8_t *signs,
+                       const float *norms, const float *rnorms, int64_t n_keys, int k, void *ws, float *out_scores,
+                       int32_t *out_idx, hipStream_t st) {
+  if (t.d > kTkPad || t.mse_bits > 4 || !t.logit_lut) return hipErrorNotSupported;
+  // buffer offsets are 32-bit
+  if (n_keys * (t.code_row > t.sign_row ? t.code_row : t.sign_row) >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  const bool prod = t.variant == 1;
+#define TQ_T(MB, P) \
+  if (t.mse_bits == MB && prod == P) \
+    return run_topk<MB, P>(t, q, nq, codes, signs, norms, rnorms, n_keys, k, (float *)ws, out_scores, out_idx, st);
+  TQ_T(0, true) TQ_T(1, false) TQ_T(1, true) TQ_T(2, false) TQ_T(2, true)
+  TQ_T(3, false) TQ_T(3, true) TQ_T(4, false) TQ_T(4, true)
+#undef TQ_T
+  return hipErrorNotSupported;
+}
+
+}  // namespace tq

@@ -135,7 +135,9 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
   const size_t tiled_sign_words = prod ? 2 * tiled_rot_words : 0;
   const bool tiled = !fast && d % 8 == 0 && mse_bits <= 4 && d > 8 &&
                      (tiled_rot_words + tiled_sign_words) * 4 <= ((size_t)1 << 30);
-  const size_t lut_words = fast ? tq::fast128_lut_words(mse_bits) : 0;
+  // decode tables (code pairs, sign bytes) for every codebook of <= 4 bits:
+  // the d = 128 kernels and the top-k search read them
+  const size_t lut_words = mse_bits <= 4 ? tq::fast128_lut_words(mse_bits) : 0;
 
   // Host images of every device table.
   std::vector<float> pi_all(groups * dd), pit_all(groups * dd);
@@ -203,7 +205,7 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
   }
   std::vector<uint32_t> lut(lut_words);
   float lut_inv_scale = 1.f;
-  if (fast && lut_words) lut_inv_scale = tq::fast128_build_logit_lut(h->h_c.data(), mse_bits, lut.data());
+  if (lut_words) lut_inv_scale = tq::fast128_build_logit_lut(h->h_c.data(), mse_bits, lut.data());
 
   // One device arena.
   size_t off = 0;
@@ -229,8 +231,8 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
       if (prod) h->dev.m_frag = carve<uint32_t>(base, off, groups * rot_words);
       h->dev.dq_pi_frag = carve<uint32_t>(base, off, groups * rot_words);
       if (prod) h->dev.dq_s_frag = carve<uint32_t>(base, off, groups * rot_words);
-      if (lut_words) h->dev.logit_lut = carve<uint32_t>(base, off, lut_words);
     }
+    if (lut_words) h->dev.logit_lut = carve<uint32_t>(base, off, lut_words);
     return off;
   };
   const size_t bytes = plan(base0);
@@ -274,8 +276,8 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     if (prod) up(h->dev.m_frag, m_img.data(), m_img.size() * 4);
     up(h->dev.dq_pi_frag, dq_pi_img.data(), dq_pi_img.size() * 4);
     if (prod) up(h->dev.dq_s_frag, dq_s_img.data(), dq_s_img.size() * 4);
-    up(h->dev.logit_lut, lut.data(), lut.size() * 4);
   }
+  if (lut_words) up(h->dev.logit_lut, lut.data(), lut.size() * 4);
   if (e != hipSuccess) {
     (void)hipFree(h->arena);
     delete h;
@@ -518,6 +520,39 @@ int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const v
       (const uint8_t *)v_codes, (const uint8_t *)v_signs, v_norms, v_rnorms, n_sets, n_keys, scale,
       (float *)(ws + p.logits_off), (float *)(ws + p.part_off), out, (hipStream_t)stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "attention launch");
+}
+
+// ------------------------------------------------------------------ top-k --
+int tq_topk_workspace(tq_handle h, int64_t nq, int64_t n_keys, int k, size_t *bytes) {
+  int st = check_handle(h);
+  if (st) return st;
+  if (!bytes) return fail(TQ_EINVAL, "bytes is NULL");
+  if (nq < 0 || nq > 65535 * 128) return fail(TQ_EINVAL, "nq out of range");
+  if (k < 1 || k > 64 || n_keys < k) return fail(TQ_EINVAL, "need 1 <= k <= 64 and n_keys >= k");
+  const size_t b = tq::topk_workspace(h->dev, nq, n_keys, k);
+  if (b == 0) return fail(TQ_EUNSUPPORTED, "top-k search needs d <= 256 and at most 4 mse bits");
+  *bytes = b;
+  return TQ_OK;
+}
+
+int tq_topk(tq_handle h, const float *q, int64_t nq, const void *codes, const void *signs, const float *norms,
+            const float *rnorms, int64_t n_keys, int k, float *out_scores, int32_t *out_idx, void *workspace,
+            size_t workspace_bytes, void *stream) {
+  size_t need = 0;
+  int st = tq_topk_workspace(h, nq, n_keys, k, &need);
+  if (st) return st;
+  if (nq == 0) return TQ_OK;
+  if ((st = check_rows(h, 1, n_keys))) return st;
+  if (!q || ((uintptr_t)q & 3u)) return fail(TQ_EINVAL, "q NULL or misaligned");
+  if (!out_scores || ((uintptr_t)out_scores & 3u) || !out_idx || ((uintptr_t)out_idx & 3u))
+    return fail(TQ_EINVAL, "outputs NULL or misaligned");
+  if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, false))) return st;
+  if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
+    return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_topk_workspace reports");
+  hipError_t e = tq::launch_topk(h->dev, q, nq, (const uint8_t *)codes, (const uint8_t *)signs, norms, rnorms, n_keys,
+                                 k, workspace, out_scores, out_idx, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "index too large for the top-k kernel");
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "top-k launch");
 }
 
 // ------------------------------------------------------- mixed precision --
