@@ -31,12 +31,12 @@ constexpr int kTkQ = 16;                  // queries per wave: two row tiles of 
 constexpr int kTkPad = 256;               // padded dimension: lane group g holds 64 g .. 64 g + 63
 constexpr int kTkKS = 8;                  // contraction steps of 32 coordinates
 constexpr int kTkRing = 4;                // tiles held in registers (three in flight)
-constexpr int kTkBuf = 48;                // buffered candidates per query
+constexpr int kTkBuf = 64;                // buffered candidates per query
 constexpr int kTkMergeAt = kTkBuf - 16;   // a tile adds at most 16 per query
 constexpr int kTkSignCopies = 16;         // 16-byte entries 256 bytes apart: 16 lanes a cycle, no conflicts
 constexpr uint32_t kTkPairOff = 65536;    // the sign table fills LDS [0, 64 KB)
 constexpr uint32_t kTkBufOff = 98304;
-constexpr uint32_t kTkBufBytes = kTkQ * kTkBuf * 8;
+constexpr uint32_t kTkBufBytes = kTkQ * kTkBuf * 8 + 64 * 8;  // buffers + a merge staging row
 constexpr uint32_t kTkLds = kTkBufOff + kTkWaves * kTkBufBytes;
 static_assert(kTkLds <= 160 * 1024, "LDS budget");
 
@@ -85,21 +85,21 @@ __device__ __forceinline__ void tk_load(TkKey<MB, PROD> &r, int64_t key, int64_t
 // 2 grp, 2 grp + 1 of each row tile (rows 4 grp .. 4 grp + 3 = two queries x
 // hi/lo).  MB == 1 decodes the 1-bit codes with the sign table (c[idx] =
 // c1 (2 idx - 1); c1 is folded into the query).
+// The decoded B operands of one tile: code values (or 1-bit codes as
+// signs) and QJL signs of the lane's key for each contraction step.
+struct TkB {
+  u32x4 m[kTkKS], s[kTkKS];
+};
+
 template <int MB, bool PROD>
-__device__ __forceinline__ void tk_score(const TkKey<MB, PROD> &r, const u32x4 (&qm)[2][kTkKS],
-                                         const u32x4 (&qq)[2][kTkKS], uint32_t sbase, uint32_t pbase,
-                                         float (&sc)[2][2]) {
+__device__ __forceinline__ void tk_lookup(const TkKey<MB, PROD> &r, uint32_t sbase, uint32_t pbase, TkB &b) {
   using G = TkGeom<MB>;
-  f32x4 am[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, aq[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
   for (int k = 0; k < kTkKS; ++k) {
     if constexpr (MB == 1) {
       const uint32_t byte = (r.c[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-      const u32x4 b = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)((byte << 8) | sbase);
-      am[0] = mfma_f16(qm[0][k], b, am[0]);
-      am[1] = mfma_f16(qm[1][k], b, am[1]);
+      b.m[k] = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)((byte << 8) | sbase);
     } else if constexpr (MB >= 2) {
-      u32x4 b;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int bit = 8 * k * MB + G::W * i, wi = bit >> 5, sh = bit & 31;
@@ -111,29 +111,53 @@ __device__ __forceinline__ void tk_score(const TkKey<MB, PROD> &r, const u32x4 (
         else
           x = r.c[wi] << (G::SHIFT - sh);
         const uint32_t addr = (x & (uint32_t)(((1 << G::W) - 1) << G::SHIFT)) | pbase;
-        b[i] = *(__attribute__((address_space(3))) const uint32_t *)(uintptr_t)addr;
+        b.m[k][i] = *(__attribute__((address_space(3))) const uint32_t *)(uintptr_t)addr;
       }
-      am[0] = mfma_f16(qm[0][k], b, am[0]);
-      am[1] = mfma_f16(qm[1][k], b, am[1]);
     }
     if constexpr (PROD) {
       const uint32_t byte = (r.s[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-      const u32x4 b = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)((byte << 8) | sbase);
-      aq[0] = mfma_f16(qq[0][k], b, aq[0]);
-      aq[1] = mfma_f16(qq[1][k], b, aq[1]);
+      b.s[k] = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)((byte << 8) | sbase);
+    }
+  }
+}
+
+// Scores of one tile for the wave's 16 queries from its decoded operands:
+// lane (key, grp) gets queries 2 grp, 2 grp + 1 of each row tile (rows 4 grp
+// .. 4 grp + 3 = two queries x hi/lo).  MB == 1 decodes the 1-bit codes with
+// the sign table (c[idx] = c1 (2 idx - 1); c1 is folded into the query).
+template <int MB, bool PROD>
+__device__ __forceinline__ void tk_mma(const TkB &b, float nu, float ga, const u32x4 (&qm)[2][kTkKS],
+                                       const u32x4 (&qq)[2][kTkKS], float (&sc)[2][2]) {
+  f32x4 am[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, aq[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+  for (int k = 0; k < kTkKS; ++k) {
+    if constexpr (MB > 0) {
+      am[0] = mfma_f16(qm[0][k], b.m[k], am[0]);
+      am[1] = mfma_f16(qm[1][k], b.m[k], am[1]);
+    }
+    if constexpr (PROD) {
+      aq[0] = mfma_f16(qq[0][k], b.s[k], aq[0]);
+      aq[1] = mfma_f16(qq[1][k], b.s[k], aq[1]);
     }
   }
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     float v0 = MB > 0 ? am[rt][0] + am[rt][1] : 0.f, v1 = MB > 0 ? am[rt][2] + am[rt][3] : 0.f;
     if constexpr (PROD) {
-      v0 = fmaf(r.ga, aq[rt][0] + aq[rt][1], v0);
-      v1 = fmaf(r.ga, aq[rt][2] + aq[rt][3], v1);
+      v0 = fmaf(ga, aq[rt][0] + aq[rt][1], v0);
+      v1 = fmaf(ga, aq[rt][2] + aq[rt][3], v1);
     }
-    sc[rt][0] = v0 * r.nu;
-    sc[rt][1] = v1 * r.nu;
+    sc[rt][0] = v0 * nu;
+    sc[rt][1] = v1 * nu;
   }
 }
+
+// Float <-> int keys with the same order (for atomicMax on scores).
+__device__ __forceinline__ int tk_key(float f) {
+  const int b = __float_as_int(f);
+  return b ^ ((b >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float tk_unkey(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
 
 // (s, i) ranks before (cs, ci): a larger score, or an equal score and a
 // smaller key index.
@@ -142,7 +166,8 @@ __device__ __forceinline__ bool tk_better(float s, int i, float cs, int ci) {
 }
 
 // Insert `cnt` buffered candidates into one query's list (lane l holds its
-// l-th best; lanes >= k hold -inf), one candidate at a time.
+// l-th best; lanes >= k hold -inf), one candidate at a time.  Used by the
+// final merge of the ranges' lists.
 __device__ __forceinline__ void tk_insert(float &ls, int &li, const float2 *cand, int cnt, int k, int lane) {
   for (int c = 0; c < cnt; ++c) {
     const float2 e = cand[c];
@@ -167,12 +192,51 @@ __device__ __forceinline__ void tk_insert(float &ls, int &li, const float2 *cand
   }
 }
 
+// Merge a buffer of `cnt` <= 64 candidates (LDS, any order) into one query's
+// list in one pass: candidate j lands at (list entries better than it) +
+// (candidates better than it); list entry l moves down by the number of
+// candidates better than it.  Entries that land at k or beyond drop out.
+// `stage` is 64 float2 of LDS that only this wave uses.
+__device__ __forceinline__ void tk_merge_batch(float &ls, int &li, const float2 *cand, int cnt, int k, int lane,
+                                               float2 *stage) {
+  float bs = -INFINITY;
+  int bi = 0x7fffffff;
+  if (lane < cnt) {
+    const float2 e = cand[lane];
+    bs = e.x;
+    bi = __float_as_int(e.y);
+  }
+  int rank_b = 0, rank_l = 0, down = 0;  // candidates above my candidate; list above it; candidates above my entry
+  for (int j = 0; j < cnt; ++j) {
+    const float2 e = cand[j];  // broadcast
+    const float cs = e.x;
+    const int ci = __float_as_int(e.y);
+    rank_b += tk_better(cs, ci, bs, bi) ? 1 : 0;
+    down += tk_better(cs, ci, ls, li) ? 1 : 0;
+    const int above = __popcll(__ballot(tk_better(ls, li, cs, ci)));
+    rank_l = lane == j ? above : rank_l;
+  }
+  const int pl = lane + down, pb = rank_l + rank_b;
+  if (lane < k && pl < k) stage[pl] = float2{ls, __int_as_float(li)};
+  if (lane < cnt && pb < k) stage[pb] = float2{bs, __int_as_float(bi)};
+  __builtin_amdgcn_wave_barrier();
+  if (lane < k) {
+    const float2 e = stage[lane];
+    ls = e.x;
+    li = __float_as_int(e.y);
+  } else {
+    ls = -INFINITY;
+    li = 0x7fffffff;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int MB, bool PROD>
 __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
     const float *__restrict__ qprep, int nq, const uint8_t *__restrict__ codes, int64_t code_row,
     const uint8_t *__restrict__ signs, int64_t sign_row, const float *__restrict__ norms,
     const float *__restrict__ rnorms, int64_t n_keys, int k, int64_t keys_per_split, const uint32_t *__restrict__ lut,
-    float2 *__restrict__ lists) {
+    float2 *__restrict__ lists, int *__restrict__ gtau) {
   using G = TkGeom<MB>;
   extern __shared__ u32x4 dyn_lds[];  // the kernel's only LDS: starts at address 0
   char *lds = (char *)dyn_lds;
@@ -221,6 +285,15 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
       }
     }
   }
+  // the query operands stay in AGPRs (the MFMAs read them from there), which
+  // leaves the VGPRs to the tile's table reads
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < kTkKS; ++ks) {
+      asm volatile("" : "+a"(qm[rt][ks]));
+      asm volatile("" : "+a"(qq[rt][ks]));
+    }
   __syncthreads();
 
   const __amdgpu_buffer_rsrc_t rc =
@@ -247,6 +320,20 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
 #pragma unroll
     for (int h = 0; h < 2; ++h)  // queries past nq never take candidates
       tau[rt][h] = qbase + rt * 8 + 2 * grp + h < nq ? -INFINITY : INFINITY;
+  // shared threshold of each query over all key ranges: the largest k-th
+  // best score any range's full list has reached.  The final k-th best is at
+  // least that, so a key below it cannot make the top k; ties are kept (>=)
+  // because keys of other ranges may carry smaller indices.
+  float tg[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
+  auto refresh = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = qbase + rt * 8 + 2 * grp + h;
+        if (q < nq) tg[rt][h] = tk_unkey(__hip_atomic_load(gtau + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      }
+  };
 
   auto merge = [&]() __attribute__((always_inline)) {  // every query with buffered candidates
 #pragma unroll
@@ -254,25 +341,21 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
       const int rt = qi >> 3, r = qi & 7, gq = r >> 1, h = r & 1;
       const int c = __builtin_amdgcn_readlane(cnt[rt][h], 16 * gq);
       if (c > 0) {
-        tk_insert(ls[qi], li[qi], buf + qi * kTkBuf, c, k, lane);
+        tk_merge_batch(ls[qi], li[qi], buf + qi * kTkBuf, c, k, lane, buf + kTkQ * kTkBuf);
         const float t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls[qi]), k - 1));
         if (grp == gq) {
           tau[rt][h] = t;
           cnt[rt][h] = 0;
         }
+        if (lane == 0 && t != -INFINITY && qbase + qi < nq) atomicMax(gtau + qbase + qi, tk_key(t));
       }
     }
   };
 
-  const int64_t nt = (ke - kb + 15) / 16;
-  // a ring of kTkRing tiles in registers: tile i + kTkRing - 1 loads while tile i is scored
-  TkKey<MB, PROD> ring[kTkRing];
-#pragma unroll
-  for (int j = 0; j + 1 < kTkRing; ++j)
-    if (j < nt) tk_load<MB, PROD>(ring[j], kb + 16 * j + col, ke - 1, grp, rc, rs, code_row, sign_row, norms, rnorms);
-  auto step = [&](const TkKey<MB, PROD> &r, int64_t t0) __attribute__((always_inline)) {
+  // scores of tile t0 (decoded operands b, norms nu, ga) -> candidates
+  auto step = [&](const TkB &b, float nu, float ga, int64_t t0) __attribute__((always_inline)) {
     float sc[2][2];
-    tk_score<MB, PROD>(r, qm, qq, sbase, pbase, sc);
+    tk_mma<MB, PROD>(b, nu, ga, qm, qq, sc);
     const int64_t key = t0 + col;
     const bool valid = key < ke;
     bool cand[2][2];
@@ -281,7 +364,7 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        cand[rt][h] = valid && sc[rt][h] > tau[rt][h];
+        cand[rt][h] = valid && sc[rt][h] > tau[rt][h] && sc[rt][h] >= tg[rt][h];
         anyc |= cand[rt][h];
       }
     if (__ballot(anyc) == 0) return;
@@ -302,16 +385,42 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
       }
     if (__ballot(full) != 0) merge();
   };
+  // a ring of kTkRing tiles in registers (tile i + kTkRing - 1 loads while
+  // tile i is scored) and a software pipeline: while the MFMAs of tile i
+  // run, the table reads of tile i + 1 are in flight (operand sets b0 / b1
+  // alternate)
+  const int64_t nt = (ke - kb + 15) / 16;
+  TkKey<MB, PROD> ring[kTkRing];
+#pragma unroll
+  for (int j = 0; j < kTkRing - 1; ++j)
+    if (j < nt) tk_load<MB, PROD>(ring[j], kb + 16 * j + col, ke - 1, grp, rc, rs, code_row, sign_row, norms, rnorms);
+  TkB b0, b1;
+  float nu0 = 0.f, ga0 = 0.f, nu1 = 0.f, ga1 = 0.f;
+  if (nt > 0) {
+    tk_lookup<MB, PROD>(ring[0], sbase, pbase, b0);
+    nu0 = ring[0].nu;
+    ga0 = ring[0].ga;
+  }
   for (int64_t i0 = 0; i0 < nt; i0 += kTkRing) {
 #pragma unroll
     for (int j = 0; j < kTkRing; ++j) {
       const int64_t i = i0 + j;
       if (i >= nt) break;
-      const int64_t ip = i + kTkRing - 1;  // the tile that reuses the slot freed last
+      if ((i & 7) == 7) refresh();
+      const int64_t ip = i + kTkRing - 1;
       if (ip < nt)
         tk_load<MB, PROD>(ring[(j + kTkRing - 1) % kTkRing], kb + 16 * ip + col, ke - 1, grp, rc, rs, code_row,
                           sign_row, norms, rnorms);
-      step(ring[j], kb + 16 * i);
+      TkB &bc = (j & 1) ? b1 : b0, &bn = (j & 1) ? b0 : b1;
+      float &nuc = (j & 1) ? nu1 : nu0, &gac = (j & 1) ? ga1 : ga0;
+      float &nun = (j & 1) ? nu0 : nu1, &gan = (j & 1) ? ga0 : ga1;
+      if (i + 1 < nt) {
+        const TkKey<MB, PROD> &rn = ring[(j + 1) % kTkRing];
+        tk_lookup<MB, PROD>(rn, sbase, pbase, bn);
+        nun = rn.nu;
+        gan = rn.ga;
+      }
+      step(bc, nuc, gac, kb + 16 * i);
     }
   }
   merge();
@@ -346,7 +455,7 @@ __global__ __launch_bounds__(64) void k_topk_merge(const float2 *__restrict__ li
 // as signs), p by sqrt(pi/2) / d.
 __global__ __launch_bounds__(kTkPad) void k_topk_qprep(const float *__restrict__ q, int d, int prod, int mse_bits,
                                                        const float *__restrict__ PiT, const float *__restrict__ ST,
-                                                       float mscale, float *__restrict__ out) {
+                                                       float mscale, float *__restrict__ out, int *__restrict__ gtau) {
   __shared__ float qs[kTkPad];
   const int r = blockIdx.x, j = threadIdx.x;
   qs[j] = j < d ? q[(int64_t)r * d + j] : 0.f;
@@ -360,26 +469,38 @@ __global__ __launch_bounds__(kTkPad) void k_topk_qprep(const float *__restrict__
   }
   out[((int64_t)r * 2 + 0) * kTkPad + j] = a * mscale;
   out[((int64_t)r * 2 + 1) * kTkPad + j] = b * (kQjlScale / (float)d);
+  if (j == 0) gtau[r] = tk_key(-INFINITY);  // the shared threshold starts empty
 }
 
 }  // namespace
 
-// Splits of the key range for nq queries (about two workgroups per CU, each
-// range at least 1024 keys).
+// Splits of the key range for nq queries: at least about two workgroups per
+// CU, and among up to three times that many the count that fills the last
+// round of 256 CUs best (each range at least 1024 keys).
 static int topk_splits(int64_t nq, int64_t n_keys) {
   const int64_t qg = (nq + kTkWaves * kTkQ - 1) / (kTkWaves * kTkQ);
-  int64_t s = (512 + qg - 1) / qg;
   const int64_t smax = n_keys / 1024 > 1 ? n_keys / 1024 : 1;
-  if (s > smax) s = smax;
-  if (s < 1) s = 1;
-  return (int)s;
+  int64_t s0 = (512 + qg - 1) / qg;
+  if (s0 > smax) s0 = smax;
+  if (s0 < 1) s0 = 1;
+  int64_t best = s0;
+  double best_eff = 0.0;
+  for (int64_t s = s0; s <= 3 * s0 && s <= smax; ++s) {
+    const int64_t wg = qg * s, rounds = (wg + 255) / 256;
+    const double eff = (double)wg / (double)(256 * rounds);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  return (int)best;
 }
 
 size_t topk_workspace(const DeviceTables &t, int64_t nq, int64_t n_keys, int k) {
   if (t.d > kTkPad || t.mse_bits > 4 || !t.logit_lut) return 0;
   const size_t prep = (size_t)nq * 2 * kTkPad * sizeof(float);
   const size_t lists = (size_t)nq * topk_splits(nq, n_keys) * k * sizeof(float2);
-  return (prep + 255) / 256 * 256 + lists;
+  return (prep + 255) / 256 * 256 + (lists + 255) / 256 * 256 + (size_t)nq * sizeof(int);
 }
 
 template <int MB, bool PROD>
@@ -389,10 +510,11 @@ static hipError_t run_topk(const DeviceTables &t, const float *q, int64_t nq, co
   const int S = topk_splits(nq, n_keys);
   float *prep = ws;
   float2 *lists = (float2 *)((char *)ws + ((size_t)nq * 2 * kTkPad * sizeof(float) + 255) / 256 * 256);
+  int *gtau = (int *)((char *)lists + ((size_t)nq * S * k * sizeof(float2) + 255) / 256 * 256);
   // 1-bit codes are decoded as signs: c[idx] = c1 (2 idx - 1)
   const float mscale = MB == 1 ? t.pos_cent[0] : t.lut_inv_scale;
   hipLaunchKernelGGL(k_topk_qprep, dim3((unsigned)nq), dim3(kTkPad), 0, st, q, t.d, PROD ? 1 : 0, MB, t.PiT, t.ST,
-                     mscale, prep);
+                     mscale, prep, gtau);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void *)k_topk<MB, PROD>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTkLds);
@@ -400,7 +522,7 @@ static hipError_t run_topk(const DeviceTables &t, const float *q, int64_t nq, co
   const int64_t kps = (n_keys + S - 1) / S;
   const dim3 grid((unsigned)((nq + kTkWaves * kTkQ - 1) / (kTkWaves * kTkQ)), (unsigned)S);
   hipLaunchKernelGGL((k_topk<MB, PROD>), grid, dim3(kTkThreads), kTkLds, st, prep, (int)nq, codes, t.code_row, signs,
-                     t.sign_row, norms, rnorms, n_keys, k, kps, t.logit_lut, lists);
+                     t.sign_row, norms, rnorms, n_keys, k, kps, t.logit_lut, lists, gtau);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)nq), dim3(64), 0, st, lists, S, k, out_scores, out_idx);
   return hipGetLastError();
