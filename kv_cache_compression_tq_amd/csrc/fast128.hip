@@ -509,33 +509,59 @@ struct KeyRegs {
   float nv[kLogitTiles], gv[kLogitTiles];
 };
 
+// Largest key count the fused kernels address: every per-set byte offset
+// (key index times at most 64 bytes per row) stays below 2^31.
+constexpr int64_t kFusedMaxKeys = int64_t(1) << 25;
 
-template <int CW, bool PROD, int KT>
-__device__ __forceinline__ void load_full(KeyRegs<CW> &r, int64_t t0, int col, const uint8_t *cbase,
-                                          const uint8_t *sbase, const float *nbase,
-                                          const float *gbase) {
-#pragma unroll
-  for (int u = 0; u < KT; ++u) {
-    const int64_t key = t0 + 16 * u + col;
-    if constexpr (CW > 0) load_codes<CW>(r.cw[u], cbase + key * (16 * CW));
-    if constexpr (PROD) r.sw[u] = *(const uint32_t *)(sbase + key * 16);
-    r.nv[u] = nbase[key];
-    if constexpr (PROD) r.gv[u] = gbase[key];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t set_rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFlags);
+}
+
+// Buffer resources of one set's key arrays and the lane's fixed byte offsets
+// (lane (col, grp): codes and signs of key col, coordinates 32 grp .. 32 grp
+// + 31; the norms of key col).
+struct KeyRsrc {
+  __amdgpu_buffer_rsrc_t c, s, n, g;
+  uint32_t oc, os, on;
+};
+
+template <int CW>
+__device__ __forceinline__ void buffer_codes(uint32_t *w, __amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t so) {
+  if constexpr (CW == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, so, 0);
+  } else if constexpr (CW == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, so, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  } else if constexpr (CW == 3) {
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, off, so, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+  } else if constexpr (CW == 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, so, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+    w[3] = v[3];
   }
 }
 
-template <int CW, bool PROD, int KT>
-__device__ __forceinline__ void load_tail(KeyRegs<CW> &r, int64_t t0, int64_t kend, int col,
-                                          const uint8_t *cbase, const uint8_t *sbase,
-                                          const float *nbase, const float *gbase) {
+// Keys t0 + 16 u + col (t0 wave-uniform, an index into the set): the lane's
+// offsets plus constants, t0 times the row size as the scalar offset.  TAIL:
+// keys at or past kend are replaced by key t0 (always valid).
+template <int CW, bool PROD, int KT, bool TAIL>
+__device__ __forceinline__ void load_keys(KeyRegs<CW> &r, int64_t t0, int64_t kend, int col, const KeyRsrc &k) {
+  const uint32_t k0 = (uint32_t)t0;
 #pragma unroll
   for (int u = 0; u < KT; ++u) {
-    const int64_t key = t0 + 16 * u + col;
-    const int64_t k = key < kend ? key : t0;  // t0 < kend: always a valid key
-    if constexpr (CW > 0) load_codes<CW>(r.cw[u], cbase + k * (16 * CW));
-    if constexpr (PROD) r.sw[u] = *(const uint32_t *)(sbase + k * 16);
-    r.nv[u] = nbase[k];
-    if constexpr (PROD) r.gv[u] = gbase[k];
+    const bool ok = !TAIL || t0 + 16 * u + col < kend;
+    const uint32_t du = ok ? (uint32_t)(16 * u) : 0u, cu = ok ? 0u : (uint32_t)col;
+    if constexpr (CW > 0) buffer_codes<CW>(r.cw[u], k.c, k.oc + du * (16 * CW) - cu * (16 * CW), k0 * (16 * CW));
+    if constexpr (PROD) r.sw[u] = __builtin_amdgcn_raw_buffer_load_b32(k.s, k.os + du * 16 - cu * 16, k0 * 16, 0);
+    const uint32_t noff = k.on + du * 4 - cu * 4;
+    r.nv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(k.n, noff, k0 * 4, 0));
+    if constexpr (PROD) r.gv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(k.g, noff, k0 * 4, 0));
   }
 }
 
@@ -820,10 +846,14 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
   const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
   const int64_t srow = (int64_t)s * n_keys;
-  const uint8_t *cbase = MB > 0 ? codes + srow * (16 * CW) + grp * (4 * CW) : nullptr;
-  const uint8_t *sbase = PROD ? signs + srow * 16 + grp * 4 : nullptr;
-  const float *nbase = norms + srow;
-  const float *gbase = PROD ? rnorms + srow : nullptr;
+  KeyRsrc kr;  // the set's arrays and the lane's offsets
+  kr.c = set_rsrc(MB > 0 ? codes + srow * (16 * CW) : codes, MB > 0 ? n_keys * (16 * CW) : 0);
+  kr.s = set_rsrc(PROD ? signs + srow * 16 : signs, PROD ? n_keys * 16 : 0);
+  kr.n = set_rsrc(norms + srow, n_keys * 4);
+  kr.g = set_rsrc(PROD ? rnorms + srow : rnorms, PROD ? n_keys * 4 : 0);
+  kr.oc = (uint32_t)(col * (16 * CW) + grp * (4 * CW));
+  kr.os = (uint32_t)(col * 16 + grp * 4);
+  kr.on = (uint32_t)(col * 4);
   constexpr int KT = kLogitTiles;
   constexpr int W = 16 * KT;  // keys per block
   const int nfull = (int)((kend - kbeg) / W);
@@ -834,7 +864,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   // query, the columns of Pi^T / S^T this thread contracts, the tables
   KeyRegs<CW> ra, rb;  // ping-pong: one block is scored while the next loads
   int b = wave;
-  if (b < nfull) load_full<CW, PROD, KT>(ra, kbeg + (int64_t)b * W, col, cbase, sbase, nbase, gbase);
+  if (b < nfull) load_keys<CW, PROD, KT, false>(ra, kbeg + (int64_t)b * W, kend, col, kr);
   const int mat = tid >> 9, slice = (tid >> 7) & 3, jj = tid & 127;
   float w[32];
   {
@@ -851,7 +881,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   if constexpr (PROD)
     for (int e = tid; e < 256 * kSignCopies; e += kLogitThreads)
       t_sg[e] = ((const u32x4 *)(lut + (MB > 0 ? GM::WORDS : 0)))[e / kSignCopies];
-  if (tid == 0) *counter = kLogitWaves;
+  if (tid < 64) counter[tid] = kLogitWaves;
   __syncthreads();
   // 2. rotate (Pi q) and project (S q) every head: thread (mat, slice, j)
   // sums 32 contraction steps for output coordinate j
@@ -911,10 +941,12 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   // LDS address 0 and CODE_BYTES, so the copy offset is OR-ed in)
   const uint32_t code_base = 4 * (lane & (GM::COPIES - 1));
   const uint32_t sign_base = 16 * (lane & (kSignCopies - 1));
-  auto grab = [&]() {  // next block of this workgroup's range (wave-uniform)
-    uint32_t b = 0;
-    if (lane == 0) b = atomicAdd(counter, 1u);
-    return (int)__builtin_amdgcn_readfirstlane(__shfl(b, 0));
+  // next block of this workgroup's range (wave-uniform): every lane adds one
+  // to its own counter word (distinct banks, no branch on the lane); lane 0's
+  // word is the atomic block counter, the other 63 keep the instruction uniform
+  auto grab = [&]() {
+    const uint32_t v = atomicAdd(counter + lane, 1u);
+    return (int)__builtin_amdgcn_readfirstlane(v);
   };
   auto score_store = [&](const KeyRegs<CW> &r, int64_t tb) {
 #pragma unroll
@@ -932,21 +964,35 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
       // wait-count pass wait for it): past the end it re-reads block b.
       int b2 = grab();
       bool more = b2 < nfull;
-      load_full<CW, PROD, KT>(rb, kbeg + (int64_t)(more ? b2 : b) * W, col, cbase, sbase, nbase, gbase);
+      load_keys<CW, PROD, KT, false>(rb, kbeg + (int64_t)(more ? b2 : b) * W, kend, col, kr);
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch issues before the block's work
       score_store(ra, kbeg + (int64_t)b * W);
       b = b2;
       if (!more) break;
       b2 = grab();
       more = b2 < nfull;
-      load_full<CW, PROD, KT>(ra, kbeg + (int64_t)(more ? b2 : b) * W, col, cbase, sbase, nbase, gbase);
+      load_keys<CW, PROD, KT, false>(ra, kbeg + (int64_t)(more ? b2 : b) * W, kend, col, kr);
+      __builtin_amdgcn_sched_barrier(0);
       score_store(rb, kbeg + (int64_t)b * W);
       b = b2;
       if (!more) break;
     }
+    // both buffers are read on the way out, so that neither prefetch is moved
+    // below the block scored after it (into the one successor that uses it)
+    uint32_t keep = 0;
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
+      if constexpr (CW > 0)
+#pragma unroll
+        for (int i = 0; i < CW; ++i) keep ^= ra.cw[u][i] ^ rb.cw[u][i];
+      if constexpr (PROD) keep ^= ra.sw[u] ^ rb.sw[u] ^ __float_as_uint(ra.gv[u]) ^ __float_as_uint(rb.gv[u]);
+      keep ^= __float_as_uint(ra.nv[u]) ^ __float_as_uint(rb.nv[u]);
+    }
+    asm volatile("" ::"v"(keep));
   }
   if (b == nfull && ragged) {  // the one wave that holds the partial block: guarded loads and stores
     const int64_t t0 = kbeg + (int64_t)nfull * W;
-    load_tail<CW, PROD, KT>(ra, t0, kend, col, cbase, sbase, nbase, gbase);
+    load_keys<CW, PROD, KT, true>(ra, t0, kend, col, kr);
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
       float o0, o1;
@@ -996,7 +1042,7 @@ constexpr uint32_t kAttnWRow = 160;
 static_assert(kAttnWRow >= 16 * kAttnTiles * 4, "weight row");
 constexpr uint32_t kAttnWBytes = 8 * kAttnWRow;
 constexpr uint32_t kAttnCounter = kAttnWBuf + kAttnWaves * kAttnWBytes;
-constexpr uint32_t kAttnLds = kAttnCounter + 16;
+constexpr uint32_t kAttnLds = kAttnCounter + 64 * 4;  // one counter word per lane
 // the value-table region is free before the tables are filled (rotation
 // scratch of the prologue) and after the main loop (merge of the waves)
 constexpr uint32_t kAttnScratch = kAttnVTab;
@@ -1018,56 +1064,77 @@ struct VRegs {
 
 // Lane offsets (bytes) of the attention loads, fixed for the kernel.
 struct AttnOffsets {
-  uint32_t kc, ks, kn, v;  // key codes / signs / norms of key col; value codes of key grp
+  uint32_t kc, ks, kn, v, v2;  // key codes / signs / norms of key col; value codes of key grp (two words)
 };
 
-// One block of keys t0 .. t0 + 63 (wave-uniform t0): the key data in the
-// logits layout (lane (col, grp): key col of each tile) and the value codes
-// in the layout of the value MFMA (lane (col, grp): keys grp + 4 j, so that
-// load j of a tile reads four consecutive rows, whole cache lines).  Every
-// address is a wave-uniform base plus the lane's fixed offset plus a
-// constant, so no per-lane address arithmetic runs per block.  TAIL: keys at
-// or past kend are replaced by key t0 (always valid).
+// Buffer resources of one set's key and value arrays (wave-uniform).
+struct AttnRsrc {
+  __amdgpu_buffer_rsrc_t kc, ks, kn, kg, vc, vn;
+};
+
+// One block of keys t0 .. t0 + 16 kAttnTiles - 1 (wave-uniform t0, an index
+// into the set): the key data in the logits layout (lane (col, grp): key col
+// of each tile) and the value codes in the layout of the value MFMA (lane
+// (col, grp): keys grp + 4 j, so that load j of a tile reads four consecutive
+// rows, whole cache lines).  Every load is a buffer load: the set's resource,
+// the lane's fixed offset (plus a constant) and t0 times the row size as the
+// scalar offset, so no vector address arithmetic runs per block.  TAIL: keys
+// at or past kend are replaced by key t0 (always valid).
 template <int CW, bool PROD, int MBV, bool TAIL>
 __device__ __forceinline__ void attn_load(KeyRegs<CW> &rk, VRegs<MBV> &rv, int64_t t0, int64_t kend, int col,
-                                          int grp, const AttnOffsets &o, const uint8_t *kcodes,
-                                          const uint8_t *ksigns, const float *knorms, const float *krnorms,
-                                          const uint8_t *vcodes, const float *vnorms) {
+                                          int grp, const AttnOffsets &o, const AttnRsrc &r) {
   constexpr int ROWV = 16 * MBV;
-  const uint8_t *kc = CW > 0 ? kcodes + t0 * (16 * CW) : nullptr;
-  const uint8_t *ks = PROD ? ksigns + t0 * 16 : nullptr;
-  const uint8_t *kn = (const uint8_t *)(knorms + t0);
-  const uint8_t *kg = PROD ? (const uint8_t *)(krnorms + t0) : nullptr;
-  const uint8_t *vc = vcodes + t0 * ROWV;
-  const uint8_t *vn = (const uint8_t *)(vnorms + t0);
+  const uint32_t k0 = (uint32_t)t0;
   const int lim = TAIL ? (int)(kend - t0) : 64;  // keys of this block that exist
 #pragma unroll
   for (int u = 0; u < kAttnTiles; ++u) {
     // key col of tile u (logits layout)
     const bool ok = !TAIL || 16 * u + col < lim;
     const uint32_t du = ok ? (uint32_t)(16 * u) : 0u, cu = ok ? 0u : (uint32_t)col;  // back to key t0
-    if constexpr (CW > 0) load_codes<CW>(rk.cw[u], kc + o.kc + du * (16 * CW) - cu * (16 * CW));
-    if constexpr (PROD) rk.sw[u] = *(const uint32_t *)(ks + o.ks + du * 16 - cu * 16);
-    rk.nv[u] = *(const float *)(kn + o.kn + du * 4 - cu * 4);
-    if constexpr (PROD) rk.gv[u] = *(const float *)(kg + o.kn + du * 4 - cu * 4);
-    rv.n[u] = *(const float *)(vn + o.kn + du * 4 - cu * 4);
+    if constexpr (CW > 0) {
+      const uint32_t off = o.kc + du * (16 * CW) - cu * (16 * CW);
+      const uint32_t so = k0 * (16 * CW);
+      if constexpr (CW == 1) {
+        rk.cw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(r.kc, off, so, 0);
+      } else if constexpr (CW == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r.kc, off, so, 0);
+        rk.cw[u][0] = v[0];
+        rk.cw[u][1] = v[1];
+      } else if constexpr (CW == 3) {
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r.kc, off, so, 0);
+        rk.cw[u][0] = v[0];
+        rk.cw[u][1] = v[1];
+        rk.cw[u][2] = v[2];
+      } else {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r.kc, off, so, 0);
+        rk.cw[u][0] = v[0];
+        rk.cw[u][1] = v[1];
+        rk.cw[u][2] = v[2];
+        rk.cw[u][3] = v[3];
+      }
+    }
+    if constexpr (PROD) rk.sw[u] = __builtin_amdgcn_raw_buffer_load_b32(r.ks, o.ks + du * 16 - cu * 16, k0 * 16, 0);
+    const uint32_t noff = o.kn + du * 4 - cu * 4;
+    rk.nv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.kn, noff, k0 * 4, 0));
+    if constexpr (PROD) rk.gv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.kg, noff, k0 * 4, 0));
+    rv.n[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r.vn, noff, k0 * 4, 0));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // key grp + 4 j of tile u (value layout)
       const bool okv = !TAIL || 16 * u + grp + 4 * j < lim;
-      const uint32_t off = okv ? o.v + (uint32_t)((16 * u + 4 * j) * ROWV) : o.v - (uint32_t)(grp * ROWV);
-      const uint8_t *row = vc + off;  // the lane's chunk of this key's row
+      const uint32_t dv = okv ? (uint32_t)((16 * u + 4 * j) * ROWV) : 0u - (uint32_t)(grp * ROWV);
+      const uint32_t so = k0 * ROWV;
       if constexpr (MBV == 1) {
-        rv.w[u][j][0] = *row;
+        rv.w[u][j][0] = __builtin_amdgcn_raw_buffer_load_b8(r.vc, o.v + dv, so, 0);
       } else if constexpr (MBV == 2) {
-        rv.w[u][j][0] = *(const uint16_t *)row;
+        rv.w[u][j][0] = __builtin_amdgcn_raw_buffer_load_b16(r.vc, o.v + dv, so, 0);
       } else if constexpr (MBV == 4) {
-        rv.w[u][j][0] = *(const uint32_t *)row;
+        rv.w[u][j][0] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, o.v + dv, so, 0);
       } else {
         // 3-bit codes: the chunk starts at byte 3 col; o.v points at its
-        // aligned word, the second word is clamped to the row's last
-        rv.w[u][j][0] = *(const uint32_t *)row;
-        rv.w[u][j][1] = *(const uint32_t *)(row + (col == 15 ? 0 : 4));
+        // aligned word, o.v2 at the next one (the row's last word for col 15)
+        rv.w[u][j][0] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, o.v + dv, so, 0);
+        rv.w[u][j][1] = __builtin_amdgcn_raw_buffer_load_b32(r.vc, o.v2 + dv, so, 0);
       }
     }
   }
@@ -1239,18 +1306,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
   const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
   const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
   const int64_t srow = (int64_t)s * n_keys;
-  // set bases (wave-uniform) and the lane's fixed offsets
-  const uint8_t *kcs = MBK > 0 ? kcodes + srow * (16 * CW) : nullptr;
-  const uint8_t *kss = PRODK ? ksigns + srow * 16 : nullptr;
-  const float *kns = knorms + srow;
-  const float *kgs = PRODK ? krnorms + srow : nullptr;
-  const uint8_t *vcs = vcodes + srow * (16 * MBV);
-  const float *vns = vnorms + srow;
+  // the set's arrays (wave-uniform resources) and the lane's fixed offsets
+  AttnRsrc rs;
+  rs.kc = set_rsrc(MBK > 0 ? kcodes + srow * (16 * CW) : kcodes, MBK > 0 ? n_keys * (16 * CW) : 0);
+  rs.ks = set_rsrc(PRODK ? ksigns + srow * 16 : ksigns, PRODK ? n_keys * 16 : 0);
+  rs.kn = set_rsrc(knorms + srow, n_keys * 4);
+  rs.kg = set_rsrc(PRODK ? krnorms + srow : krnorms, PRODK ? n_keys * 4 : 0);
+  rs.vc = set_rsrc(vcodes + srow * (16 * MBV), n_keys * (16 * MBV));
+  rs.vn = set_rsrc(vnorms + srow, n_keys * 4);
   AttnOffsets ofs;
   ofs.kc = (uint32_t)(col * (16 * CW) + grp * (4 * CW));
   ofs.ks = (uint32_t)(col * 16 + grp * 4);
   ofs.kn = (uint32_t)(col * 4);
   ofs.v = (uint32_t)(grp * (16 * MBV) + (MBV == 3 ? 4 * ((3 * col) >> 2) : col * MBV));
+  ofs.v2 = ofs.v + (col == 15 ? 0u : 4u);
   constexpr int KT = kAttnTiles;
   constexpr int W = 16 * KT;  // keys per block
   const int nfull = (int)((kend - kbeg) / W);
@@ -1267,14 +1336,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
   auto rotb = [&](int x) { return x + rot >= nfull ? x + rot - nfull : x + rot; };
   int b = wave;
   if (b < nfull)
-    attn_load<CW, PRODK, MBV, false>(ka, va, kbeg + (int64_t)rotb(b) * W, kend, col, grp, ofs, kcs, kss, kns, kgs,
-                                     vcs, vns);
+    attn_load<CW, PRODK, MBV, false>(ka, va, kbeg + (int64_t)rotb(b) * W, kend, col, grp, ofs, rs);
   const int slice = (tid >> 7) & 3, jj = tid & 127;
   for (int e = tid; e < kAttnHeads * D; e += kAttnThreads) {
     const int h = e >> 7;
     qs[e] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + (e & 127)] : 0.f;
   }
-  if (tid == 0) *counter = kAttnWaves;
+  if (tid < 64) counter[tid] = kAttnWaves;
   __syncthreads();
   // 2. rotate (Pi q) and project (S q) the heads: thread (slice, j) sums 32
   // contraction steps of output coordinate j (scratch: the value-table region)
@@ -1359,17 +1427,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) stt.acc[nt] = f32x4{0, 0, 0, 0};
 
+  // next block of this workgroup's range: every lane adds one to its own
+  // counter word (distinct banks, no branch on the lane); lane 0's word is the
+  // atomic block counter, the other 63 only keep the instruction uniform
   auto grab = [&]() {
-    uint32_t v = 0;
-    if (lane == 0) v = atomicAdd(counter, 1u);
-    return (int)__builtin_amdgcn_readfirstlane(__shfl(v, 0));
+    const uint32_t v = atomicAdd(counter + lane, 1u);
+    return (int)__builtin_amdgcn_readfirstlane(v);
   };
   if (b < nfull) {
     while (true) {
       int b2 = grab();
       bool more = b2 < nfull;
       int64_t nb = kbeg + (int64_t)rotb(more ? b2 : b) * W;
-      attn_load<CW, PRODK, MBV, false>(kb, vb, nb, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs, vns);
+      attn_load<CW, PRODK, MBV, false>(kb, vb, nb, kend, col, grp, ofs, rs);
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch issues before the block's work
       attn_block<MBK, PRODK, MBV>(stt, ka, va, kbeg + (int64_t)rotb(b) * W, kend, false, bq, bp, code_base,
                                   sign_base, vbase, sl2e, wrow, wread, psel, col, grp);
       b = b2;
@@ -1377,16 +1448,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn128(
       b2 = grab();
       more = b2 < nfull;
       nb = kbeg + (int64_t)rotb(more ? b2 : b) * W;
-      attn_load<CW, PRODK, MBV, false>(ka, va, nb, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs, vns);
+      attn_load<CW, PRODK, MBV, false>(ka, va, nb, kend, col, grp, ofs, rs);
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch issues before the block's work
       attn_block<MBK, PRODK, MBV>(stt, kb, vb, kbeg + (int64_t)rotb(b) * W, kend, false, bq, bp, code_base,
                                   sign_base, vbase, sl2e, wrow, wread, psel, col, grp);
       b = b2;
       if (!more) break;
     }
+    // both buffers are read on the way out, so that neither prefetch is moved
+    // below the block scored after it (into the one successor that uses it)
+    uint32_t keep = 0;
+#pragma unroll
+    for (int u = 0; u < kAttnTiles; ++u) {
+      if constexpr (CW > 0)
+#pragma unroll
+        for (int i = 0; i < CW; ++i) keep ^= ka.cw[u][i] ^ kb.cw[u][i];
+      if constexpr (PRODK) keep ^= ka.sw[u] ^ kb.sw[u] ^ __float_as_uint(ka.gv[u]) ^ __float_as_uint(kb.gv[u]);
+      keep ^= __float_as_uint(ka.nv[u]) ^ __float_as_uint(kb.nv[u]) ^ __float_as_uint(va.n[u]) ^
+              __float_as_uint(vb.n[u]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < VRegs<MBV>::VW; ++i) keep ^= va.w[u][j][i] ^ vb.w[u][j][i];
+    }
+    asm volatile("" ::"v"(keep));
   }
   if (b == nfull && ragged) {  // the one wave that holds the partial block
     const int64_t t0 = kbeg + (int64_t)nfull * W;
-    attn_load<CW, PRODK, MBV, true>(ka, va, t0, kend, col, grp, ofs, kcs, kss, kns, kgs, vcs, vns);
+    attn_load<CW, PRODK, MBV, true>(ka, va, t0, kend, col, grp, ofs, rs);
     attn_block<MBK, PRODK, MBV>(stt, ka, va, t0, kend, true, bq, bp, code_base, sign_base, vbase, sl2e, wrow,
                                 wread, psel, col, grp);
   }
@@ -1564,8 +1653,8 @@ hipError_t run_logits(const DeviceTables &t, const float *q, int64_t nq, const u
   kpw = (kpw + unit - 1) / unit * unit;
   gx = (n_keys + kpw - 1) / kpw;
   // a set's logits are addressed with 32-bit byte offsets below the dropped-store offset
-  if (nq * n_keys * 4 >= (int64_t)kDropped) return hipErrorNotSupported;
-  const size_t lds = LutGeom<MB>::CODE_BYTES + kSignBytes + kQueryBytes + 2 * 4 * 8 * D * 4 + 16;
+  if (nq * n_keys * 4 >= (int64_t)kDropped || n_keys > kFusedMaxKeys) return hipErrorNotSupported;
+  const size_t lds = LutGeom<MB>::CODE_BYTES + kSignBytes + kQueryBytes + 2 * 4 * 8 * D * 4 + 64 * 4;
   hipError_t e0 = hipFuncSetAttribute((const void *)k_logits128<MB, PROD>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e0 != hipSuccess) return e0;
@@ -1787,7 +1876,7 @@ static bool attention128_handles(const DeviceTables &tk, const DeviceTables &tv)
 
 size_t attention128_workspace(const DeviceTables &tk, const DeviceTables &tv, int64_t nq, int64_t n_sets,
                               int64_t n_keys) {
-  if (!attention128_handles(tk, tv) || n_sets < 1 || n_keys < 1) return 0;
+  if (!attention128_handles(tk, tv) || n_sets < 1 || n_keys < 1 || n_keys > kFusedMaxKeys) return 0;
   int64_t kpw = 0;
   const int64_t gx = attn_grid_x(n_sets, n_keys, &kpw);
   return (size_t)(n_sets * nq * gx) * kAttnPart * sizeof(float);
@@ -1797,7 +1886,7 @@ hipError_t launch_attention128(const DeviceTables &tk, const DeviceTables &tv, c
                                const uint8_t *kcodes, const uint8_t *ksigns, const float *knorms,
                                const float *krnorms, const uint8_t *vcodes, const float *vnorms, int64_t n_sets,
                                int64_t n_keys, float scale, float *part, float *out, hipStream_t st) {
-  if (!attention128_handles(tk, tv)) return hipErrorNotSupported;
+  if (!attention128_handles(tk, tv) || n_keys > kFusedMaxKeys) return hipErrorNotSupported;
   const bool prod = tk.variant == 1;
 #define TQ_A(MBK, P, MBV)                                                                                 \
   if (tk.mse_bits == MBK && prod == P && tv.mse_bits == MBV)                                              \
