@@ -196,6 +196,41 @@ def attention_phase(torch, tq, workloads, lp, steps, warmup):
                 append_wall_ms=awall, sets=sets)
 
 
+def hbm_probes(torch):
+    """Plain torch kernels over 1 GiB streams, each after a 1 GiB fill so that
+    no input is still held in the 256 MB Infinity Cache: a copy (torch.neg,
+    one launch, the calibration of the byte counters; its duration is read from
+    the kernel trace), a three-input one-output elementwise op (torch.addcmul:
+    a quarter of the bytes written, close to the quantize and logits mixes) and
+    a read-only reduction (torch.sum).  Returns GB/s of the last two (events
+    around one launch each, after a small launch that loads the kernel)."""
+    n = 1 << 28
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    evict = torch.empty_like(src).fill_(2.0)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)   # plain elementwise kernel (the only neg here): reads and writes 1 GiB
+    torch.cuda.synchronize()
+    small = torch.ones(4096, dtype=torch.float32, device="cuda")
+    torch.addcmul(small, small, small)
+    torch.sum(small)
+    q = n // 4
+    a, b, c, out = src[:q], src[q:2 * q], src[2 * q:3 * q], dst[:q]
+    ev = _events(torch, 2)
+    res = {}
+    for name, fn, nbytes in (("addcmul_3r1w_gbs", lambda: torch.addcmul(a, b, c, out=out), 16 * q),
+                             ("sum_read_gbs", lambda: torch.sum(src), 4 * n)):
+        evict.fill_(2.0)
+        torch.cuda.synchronize()
+        ev[0].record()
+        fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        res[name] = nbytes / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del src, dst, evict, small
+    return res
+
+
 def _mean_launch_ms(torch, fn, reps=5, warm=1):
     for _ in range(warm):
         fn()
@@ -338,16 +373,7 @@ def main():
         del lp["cache"], lp["codec"], lp["q"]
     other = None if args.skip_others else other_paths_phase(torch, tq, workloads, qp["x"])
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, qp["x"])
-    if args.copy_probe:
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        # write another 1 GiB so that no part of src is still held in the
-        # 256 MB Infinity Cache: every byte the copy reads comes from HBM
-        evict = torch.empty_like(src).fill_(2.0)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)   # plain elementwise kernel (the only neg here): reads and writes 1 GiB
-        torch.cuda.synchronize()
-        del src, dst, evict
+    probes = hbm_probes(torch) if args.copy_probe else None
 
     value = qp["vectors"] / (qp["wall_ms"] * 1e-3)
     line = {
@@ -414,6 +440,8 @@ def main():
         }
     if other is not None:
         line["other_paths"] = other
+    if probes is not None:
+        line["hbm_probes"] = probes
     line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
