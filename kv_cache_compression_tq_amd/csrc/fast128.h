@@ -21,6 +21,15 @@ size_t fast128_rotation_words(int d);
 // parts instead of bf16 (operands multiplied with f16 decode tables).
 void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out, bool f16 = false);
 
+// Image of the fused mixed-precision rotation (d = 128 split 64 + 64): pi_o and
+// pi_r are the parts' 64 x 64 rotations (row-major float64), perm the 128
+// channels (the 64 outlier channels, then the rest).  Output coordinates are
+// ordered so that row tiles 0..3 of the MFMA give each lane group 16
+// coordinates of the outlier part and tiles 4..7 16 of the regular part.
+// mask (4 words): bit c set for the outlier channels.
+void fast128_build_mixed_image(const double *pi_o, const double *pi_r, const int32_t *perm, uint32_t *out,
+                               uint32_t *mask);
+
 // Words of the logits decode tables for `mse_bits` (pair LUT + sign LUT).
 // The pair LUT holds f16 values of alpha * c, with alpha > 0 chosen so that
 // every scaled centroid rounds to f16 with the smallest relative error; the

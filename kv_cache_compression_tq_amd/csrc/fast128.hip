@@ -21,6 +21,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "device_common.h"
 #include "fast128.h"
@@ -490,6 +491,189 @@ __global__ __launch_bounds__(kMseThreads, 1) void k_quant128_mse(
       lookup_stage(acc[j & 1], nsq[j & 1], tab_addr, cell_scale, cells);
       rotate_stage(xs[(j + 1) % kMseDepth], im, acc[(j + 1) & 1], nsq[(j + 1) & 1], col);
       pack_stage<MB>(acc[j & 1], cells, valid_row0(k) + col, n, grp, rc, rn);
+    }
+  }
+}
+
+// ------------------------------------------------ mixed precision, d = 128 --
+// Outlier-channel mixed precision with a 64 + 64 channel split, TurboQuant_mse
+// of bf16 input in one pass.  [tqnet] 从工程视角看 TurboQuant 到底改变了什么
+// (outlier channels kept at a higher bit width); [tqnet] 数据就是论据 › KV
+// Cache 压缩基准 (2.5 and 3.5 bits per channel).  The channel split and both
+// parts' rotations form one 128 x 128 image per group -- rows of Pi_o on the
+// outlier channels and of Pi_r on the others, zero elsewhere -- ordered so
+// that row tiles 0..3 give lane group g the outlier part's coordinates 16 g ..
+// 16 g + 15 and tiles 4..7 the regular part's.  The parts' norms are the
+// diagonals of two Gram products with the input masked to each part's
+// channels; each part is searched in its own cell table and packed at its own
+// width.  The pipeline is that of k_quant128_mse.
+struct MixCells {
+  u32x2 e[32];  // cells of the outlier part's 16 coordinates, then the regular part's
+  float nu[2], sv[2];
+};
+
+// acc[m] = rows 16 m .. 16 m + 15 of the mixed image times the stage; nsq[p]
+// = squared norm of part p of the lane's vector (mo: outlier-channel masks of
+// the B-operand elements).
+__device__ __forceinline__ void rotate_mixed(const XStage &x, const u32x4 (&im)[64], const u32x4 (&mo)[4],
+                                             f32x4 (&acc)[8], float (&nsq)[2], int col) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m] = f32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      acc[m] = mfma_bf16(im[(m * 4 + k) * 2], x.v[k], acc[m]);
+      acc[m] = mfma_bf16(im[(m * 4 + k) * 2 + 1], x.v[k], acc[m]);
+    }
+  f32x4 go = {0, 0, 0, 0}, gr = {0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    go = mfma_bf16(x.v[k] & mo[k], x.v[k], go);
+    gr = mfma_bf16(x.v[k] & ~mo[k], x.v[k], gr);
+  }
+  const int32_t m0 = -(col & 1), m1 = -((col >> 1) & 1);
+  const int src = ((col >> 2) << 4) + col;
+  nsq[0] = __shfl(fsel(m1, fsel(m0, go[3], go[2]), fsel(m0, go[1], go[0])), src);
+  nsq[1] = __shfl(fsel(m1, fsel(m0, gr[3], gr[2]), fsel(m0, gr[1], gr[0])), src);
+}
+
+__device__ __forceinline__ void lookup_mixed(const f32x4 (&acc)[8], const float (&nsq)[2], uint32_t tab_o,
+                                             uint32_t tab_r, float scale_o, float scale_r, MixCells &c) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    c.nu[p] = __builtin_amdgcn_sqrtf(nsq[p]);
+    c.sv[p] = (p == 0 ? scale_o : scale_r) * __builtin_amdgcn_rcpf(c.nu[p] > 0.f ? c.nu[p] : 1.f);
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int p = j >> 4, jj = j & 15;
+    uint32_t g = __float_as_uint(fmaf(acc[4 * p + (jj >> 2)][jj & 3], c.sv[p], kCellMagic));
+    g = min(max(g, kCellFirst), kCellLast);
+    c.e[j] = *(lds_u32x2 *)(uintptr_t)((g << 3) + (p == 0 ? tab_o : tab_r));
+  }
+}
+
+// Part p of the lane's vector: the 16 decisions, packed at MB bits into bytes
+// 2 MB grp .. of the part's row (row bytes per vector; a row longer than 8 MB
+// bytes has 8 bytes of padding, written as zero by lane group 0), and the
+// part's norm.
+template <int MB>
+__device__ __forceinline__ void pack_mixed(const f32x4 (&acc)[8], int p, const MixCells &c, int64_t v, int64_t n,
+                                           int grp, int64_t row, __amdgpu_buffer_rsrc_t rc,
+                                           __amdgpu_buffer_rsrc_t rn) {
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const float y = acc[4 * p + (jj >> 2)][jj & 3];
+    const float dd = fmaf(c.nu[p], __uint_as_float(c.e[16 * p + jj][0]), -y);
+    put_field<MB>(w, jj, c.e[16 * p + jj][1] + (__float_as_uint(dd) >> 31));
+  }
+  const bool ok = v < n;
+  const uint32_t base = ok ? (uint32_t)(v * row) : kDropped;  // kDropped + a few bytes is still past the set
+  const uint32_t at = base + 2 * MB * grp;
+  if constexpr (MB == 1) {
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)w[0], rc, at, 0, 0);
+  } else if constexpr (MB == 2) {
+    __builtin_amdgcn_raw_buffer_store_b32(w[0], rc, at, 0, 0);
+  } else if constexpr (MB == 3) {
+    // 6 bytes at 6 grp: 4 + 2 (grp even) or 2 + 4 (grp odd), so every store is aligned
+    const bool even = (grp & 1) == 0;
+    const uint32_t a = even ? w[0] : (w[0] & 0xFFFFu);
+    const uint32_t b = even ? (w[1] & 0xFFFFu) : ((w[0] >> 16) | (w[1] << 16));
+    if (even) {
+      __builtin_amdgcn_raw_buffer_store_b32(a, rc, at, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)b, rc, at + 4, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)a, rc, at, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(b, rc, at + 2, 0, 0);
+    }
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rc, at, 0, 0);
+  }
+  if (row > 8 * MB)
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rc, ok && grp == 0 ? base + 8 * MB : kDropped, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c.nu[p]), rn, ok && grp == 0 ? (uint32_t)v * 4 : kDropped,
+                                        0, 0);
+}
+
+template <int MBO, int MBR>
+__global__ __launch_bounds__(kMseThreads, 1) void k_quant128_mixed(
+    const uint16_t *__restrict__ xin, int64_t n, int groups, const u32x4 *__restrict__ img_all,
+    const uint32_t *__restrict__ masks, const uint32_t *__restrict__ cells_o, float scale_o,  // scales times 2^-22
+    const uint32_t *__restrict__ cells_r, float scale_r, uint8_t *__restrict__ codes_o, int64_t row_o,
+    uint8_t *__restrict__ codes_r, int64_t row_r, float *__restrict__ norms_o, float *__restrict__ norms_r) {
+  constexpr int kCellWords = 2 * (2 * kCellRadius + 1);
+  __shared__ uint32_t tab[2][kCellWords];
+  __shared__ u32x4 img[kImageVec];  // staging: each CU reads the image from L2 once
+  const int s = blockIdx.y;
+  const int g = s % groups;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  for (int i = tid; i < kCellWords; i += kMseThreads) {
+    tab[0][i] = cells_o[i];
+    tab[1][i] = cells_r[i];
+  }
+  const int ntiles = (int)((n + 15) / 16);
+  const int64_t set_row0 = (int64_t)s * n;
+  constexpr int kWaves = kMseThreads / 64;
+  const int stride = (int)gridDim.x * kWaves;
+  const int tile0 = (int)blockIdx.x * kWaves + wave;
+  const int count = __builtin_amdgcn_readfirstlane(tile0 < ntiles ? (ntiles - tile0 + stride - 1) / stride : 0);
+  auto row0 = [&](int k) { return (int64_t)(tile0 + min(k, count - 1) * stride) * 16; };
+  auto valid_row0 = [&](int k) { return k < count ? (int64_t)(tile0 + k * stride) * 16 : n; };
+  {
+    const u32x4 *src = img_all + (size_t)g * kImageVec;
+    u32x4 t[kImageVec / kMseThreads];
+#pragma unroll
+    for (int i = 0; i < kImageVec / kMseThreads; ++i) t[i] = src[i * kMseThreads + tid];
+#pragma unroll
+    for (int i = 0; i < kImageVec / kMseThreads; ++i) img[i * kMseThreads + tid] = t[i];
+  }
+  XStage xs[kMseDepth];
+#pragma unroll
+  for (int j = 0; j + 1 < kMseDepth; ++j) load_stage(xs[j], xin, set_row0, n, row0(j), col, grp);
+  // outlier-channel masks of the lane's B-operand elements 32 k + 8 grp + e
+  u32x4 mo[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t word = masks[4 * g + k] >> (8 * grp);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      mo[k][i] = ((word >> (2 * i)) & 1u ? 0x0000FFFFu : 0u) | ((word >> (2 * i + 1)) & 1u ? 0xFFFF0000u : 0u);
+  }
+  __syncthreads();
+  u32x4 im[64];
+#pragma unroll
+  for (int f = 0; f < 64; ++f) {
+    im[f] = img[f * kFragVec + lane];
+    asm volatile("" : "+a"(im[f]));  // keep the fragment in an AGPR
+  }
+  if (count == 0) return;  // no barrier follows
+  const uint32_t tab_o = lds_addr(tab[0]), tab_r = lds_addr(tab[1]);
+  const __amdgpu_buffer_rsrc_t rco =
+      __builtin_amdgcn_make_buffer_rsrc(codes_o + set_row0 * row_o, 0, (int)(n * row_o), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rcr =
+      __builtin_amdgcn_make_buffer_rsrc(codes_r + set_row0 * row_r, 0, (int)(n * row_r), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rno =
+      __builtin_amdgcn_make_buffer_rsrc(norms_o + set_row0, 0, (int)(n * 4), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rnr =
+      __builtin_amdgcn_make_buffer_rsrc(norms_r + set_row0, 0, (int)(n * 4), kBufferFlags);
+  f32x4 acc[2][8];
+  float nsq[2][2];
+  rotate_mixed(xs[0], im, mo, acc[0], nsq[0], col);
+  for (int k0 = 0; k0 < count; k0 += kMseDepth) {
+#pragma unroll
+    for (int j = 0; j < kMseDepth; ++j) {
+      const int k = k0 + j;
+      load_stage(xs[(j + kMseDepth - 1) % kMseDepth], xin, set_row0, n, row0(k + kMseDepth - 1), col, grp);
+      MixCells cells;
+      lookup_mixed(acc[j & 1], nsq[j & 1], tab_o, tab_r, scale_o, scale_r, cells);
+      rotate_mixed(xs[(j + 1) % kMseDepth], im, mo, acc[(j + 1) & 1], nsq[(j + 1) & 1], col);
+      const int64_t v = valid_row0(k) + col;
+      pack_mixed<MBO>(acc[j & 1], 0, cells, v, n, grp, row_o, rco, rno);
+      pack_mixed<MBR>(acc[j & 1], 1, cells, v, n, grp, row_r, rcr, rnr);
     }
   }
 }
@@ -1615,6 +1799,23 @@ hipError_t run_quant_mse(const DeviceTables &t, const void *x, int64_t n_sets, i
   return hipGetLastError();
 }
 
+template <int MBO, int MBR>
+hipError_t run_quant_mixed(const DeviceTables &to, const DeviceTables &tr, const uint32_t *img,
+                           const uint32_t *masks, const void *x, int64_t n_sets, int64_t n, int groups,
+                           uint8_t *codes_o, float *norms_o, uint8_t *codes_r, float *norms_r, hipStream_t st) {
+  const int64_t ntiles = (n + 15) / 16;
+  constexpr int waves = kMseThreads / 64;
+  const int64_t per_set_max = (ntiles + waves - 1) / waves;
+  int64_t gx = (256 + n_sets - 1) / n_sets;  // one workgroup per CU
+  if (gx > per_set_max) gx = per_set_max;
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL((k_quant128_mixed<MBO, MBR>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kMseThreads), 0, st,
+                     (const uint16_t *)x, n, groups, (const u32x4 *)img, masks, to.cells,
+                     to.cell_scale * kCellStep, tr.cells, tr.cell_scale * kCellStep, codes_o, to.code_row, codes_r,
+                     tr.code_row, norms_o, norms_r);
+  return hipGetLastError();
+}
+
 template <int MB, bool PROD, bool F32IN>
 hipError_t run_quant(const DeviceTables &t, const void *x, int64_t n_sets, int64_t n, uint8_t *codes,
                      uint8_t *signs, float *norms, float *rnorms, hipStream_t st) {
@@ -1763,6 +1964,21 @@ void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out,
       }
 }
 
+void fast128_build_mixed_image(const double *pi_o, const double *pi_r, const int32_t *perm, uint32_t *out,
+                               uint32_t *mask) {
+  std::vector<double> mat((size_t)D * D, 0.0);
+  for (int orow = 0; orow < D; ++orow) {
+    // the lane group, row tile and row of the MFMA output that holds image row orow
+    const int grp = orow / 32, m = (orow % 32) / 4, q = orow % 4;
+    const int part = m / 4, coord = 16 * grp + 4 * (m % 4) + q;
+    const double *src = (part == 0 ? pi_o : pi_r) + (size_t)coord * 64;
+    for (int j = 0; j < 64; ++j) mat[(size_t)orow * D + perm[64 * part + j]] = src[j];
+  }
+  fast128_build_rotation_image(mat.data(), 0, out);
+  for (int w = 0; w < 4; ++w) mask[w] = 0;
+  for (int j = 0; j < 64; ++j) mask[perm[j] >> 5] |= 1u << (perm[j] & 31);
+}
+
 // Decode-table geometry: one lookup turns G codes of `mse_bits` bits (one
 // index of G * mse_bits <= 12 bits) into G f16 values.
 size_t fast128_lut_words(int mse_bits) {
@@ -1838,6 +2054,23 @@ hipError_t launch_quant128(const DeviceTables &t, const void *x, int dtype, int6
   TQ_Q(3, false, false) TQ_Q(3, false, true) TQ_Q(3, true, false) TQ_Q(3, true, true)
   TQ_Q(4, false, false) TQ_Q(4, false, true) TQ_Q(4, true, false) TQ_Q(4, true, true)
 #undef TQ_Q
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_quant128_mixed(const DeviceTables &to, const DeviceTables &tr, const uint32_t *img,
+                                 const uint32_t *masks, const void *x, int64_t n_sets, int64_t n, int groups,
+                                 uint8_t *codes_o, float *norms_o, uint8_t *codes_r, float *norms_r,
+                                 hipStream_t st) {
+  if (to.d != 64 || tr.d != 64 || to.variant != 0 || tr.variant != 0 || !img || !masks ||
+      to.cell_radius != kCellRadius || tr.cell_radius != kCellRadius || ((uintptr_t)x & 15u))
+    return hipErrorNotSupported;
+  // per-set byte offsets of codes and norms stay below the dropped-store offset
+  if (n * (to.code_row > tr.code_row ? to.code_row : tr.code_row) >= (int64_t)kDropped / 2) return hipErrorNotSupported;
+#define TQ_M(O, R) \
+  if (to.mse_bits == O && tr.mse_bits == R) \
+    return run_quant_mixed<O, R>(to, tr, img, masks, x, n_sets, n, groups, codes_o, norms_o, codes_r, norms_r, st);
+  TQ_M(2, 1) TQ_M(3, 2) TQ_M(4, 3)
+#undef TQ_M
   return hipErrorNotSupported;
 }
 

@@ -84,6 +84,13 @@ hipError_t launch_unpack(const uint8_t *in, int bits, int64_t rows, int count, i
 hipError_t launch_quant128(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
                            int64_t n, uint8_t *codes, uint8_t *signs, float *norms, float *rnorms,
                            hipStream_t st);
+// Fused mixed-precision quantize (d = 128, 64 outlier + 64 regular channels,
+// TurboQuant_mse, bf16 input): img / masks from fast128_build_mixed_image per
+// group; `to` / `tr` the part codecs' tables.
+hipError_t launch_quant128_mixed(const DeviceTables &to, const DeviceTables &tr, const uint32_t *img,
+                                 const uint32_t *masks, const void *x, int64_t n_sets, int64_t n, int groups,
+                                 uint8_t *codes_o, float *norms_o, uint8_t *codes_r, float *norms_r,
+                                 hipStream_t st);
 hipError_t launch_quant_tiled(const DeviceTables &t, const void *x, int dtype, int64_t n_sets, int64_t n,
                               uint8_t *codes, uint8_t *signs, float *norms, float *rnorms, hipStream_t st);
 hipError_t launch_dequant128(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs,

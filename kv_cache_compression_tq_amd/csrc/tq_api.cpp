@@ -560,6 +560,9 @@ struct tq_mixed_codec {
   int d = 0, n_out = 0, groups = 0, variant = 0;
   tq_handle parts[2] = {nullptr, nullptr};  // outlier part (n_out dims, b + 1 bits), regular part
   int32_t *perm = nullptr;                  // device [groups][d]: outlier channels, then the rest ascending
+  // fused quantize (d = 128, n_out = 64, TurboQuant_mse, b + 1 <= 4): device
+  // [groups] rotation images, then [groups][4] outlier-channel masks
+  uint32_t *fused = nullptr;
 };
 
 namespace {
@@ -608,6 +611,22 @@ int tq_mixed_init(int d, int b, int variant, uint64_t seed, int groups, int n_ou
       if (e == hipSuccess) e = hipMemcpy(m->perm, perm.data(), perm.size() * sizeof(int32_t), hipMemcpyHostToDevice);
       if (e != hipSuccess) st = hip_fail(e, "channel map upload");
     }
+    if (st == TQ_OK && d == 128 && n_out == 64 && variant == TQ_MSE && b + 1 <= 4) {
+      // one image per group: both parts' rotations on their channels (the
+      // parts' matrices are those of make_codec: seeds seed and seed + 1)
+      const size_t rot_words = tq::fast128_rotation_words(128);
+      std::vector<uint32_t> host((size_t)groups * (rot_words + 4));
+      std::vector<double> pi_o, pi_r, unused_s, unused_m;
+      for (int g = 0; g < groups; ++g) {
+        group_matrices(64, seed, g, false, pi_o, unused_s, unused_m);
+        group_matrices(64, seed + 1, g, false, pi_r, unused_s, unused_m);
+        tq::fast128_build_mixed_image(pi_o.data(), pi_r.data(), perm.data() + (size_t)g * d,
+                                      &host[(size_t)g * rot_words], &host[(size_t)groups * rot_words + 4 * g]);
+      }
+      hipError_t e = hipMalloc((void **)&m->fused, host.size() * sizeof(uint32_t));
+      if (e == hipSuccess) e = hipMemcpy(m->fused, host.data(), host.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+      if (e != hipSuccess) st = hip_fail(e, "mixed rotation image upload");
+    }
     if (st != TQ_OK) {
       tq_mixed_destroy(m);
       return st;
@@ -622,6 +641,7 @@ int tq_mixed_destroy(tq_mixed m) {
   tq_destroy(m->parts[0]);
   tq_destroy(m->parts[1]);
   if (m->perm) (void)hipFree(m->perm);
+  if (m->fused) (void)hipFree(m->fused);
   delete m;
   return TQ_OK;
 }
@@ -659,10 +679,17 @@ int tq_mixed_quantize(tq_mixed m, const void *x, int dtype, int64_t n_sets, int6
   tq_mixed_workspace(m, n_sets, n, 0, &need);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
     return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_mixed_workspace reports");
+  hipStream_t s = (hipStream_t)stream;
+  if (m->fused && dtype == TQ_BF16) {
+    const uint32_t *masks = m->fused + (size_t)m->groups * tq::fast128_rotation_words(128);
+    const hipError_t e = tq::launch_quant128_mixed(m->parts[0]->dev, m->parts[1]->dev, m->fused, masks, x, n_sets, n,
+                                                   m->groups, (uint8_t *)codes[0], norms[0], (uint8_t *)codes[1],
+                                                   norms[1], s);
+    if (e != hipErrorNotSupported) return e == hipSuccess ? TQ_OK : hip_fail(e, "mixed quantize launch");
+  }
   const size_t es = dtype == TQ_F32 ? 4 : 2;
   char *xo = (char *)workspace;
   char *xr = xo + up256((size_t)(n_sets * n) * m->n_out * es);
-  hipStream_t s = (hipStream_t)stream;
   hipError_t e = tq::launch_gather_parts(x, dtype, n_sets * n, n, m->groups, m->d, m->n_out, m->perm, xo, xr, s);
   if (e != hipSuccess) return hip_fail(e, "gather launch");
   for (int p = 0; p < 2; ++p)

@@ -116,3 +116,49 @@ def test_mixed_kv_workload_sampled(bits):
             gidx = codec.unpack(got["codes"][h, t], cd.mse_bits).cpu().numpy()
             check_indices(gidx, ref["idx"], ref["y"], cd.boundaries, f"head {h}")
             assert np.allclose(got["norms"][h, t].cpu().numpy(), ref["norms"], rtol=1e-5)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_mixed_fused_bf16_quantize(bits):
+    """d = 128 with 64 outlier channels, TurboQuant_mse on bfloat16 input: the
+    fused one-pass kernel (both rotations in one image, part norms from masked
+    Gram products).  Indices, norms and the packed rows byte for byte
+    (padding included) against the oracle, ragged n, two groups."""
+    n_sets, n, groups = 3, 1001, 2
+    chans, x = _data(128, n_sets, n, 64, groups, seed=40 + bits)
+    xb = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+    xr = xb.float().numpy().astype(np.float64)
+    mc = tq.MixedCodec(128, bits, tq.TQ_MSE, 29, chans, groups=groups)
+    mx = O.make_mixed(128, bits, O.MSE, 29, chans, groups=groups)
+    po, pr = mc.quantize(xb.cuda())
+    torch.cuda.synchronize()
+    for s in range(n_sets):
+        ro, rr = O.mixed_quantize(mx, xr[s], s % groups)
+        for codec, cd, got, ref, what in ((mc.outlier, mx.outlier, po, ro, "outlier"),
+                                          (mc.regular, mx.regular, pr, rr, "regular")):
+            gidx = codec.unpack(got["codes"][s], cd.mse_bits).cpu().numpy()
+            check_indices(gidx, ref["idx"], ref["y"], cd.boundaries, f"{what} part set {s}")
+            assert np.allclose(got["norms"][s].cpu().numpy(), ref["norms"], rtol=1e-5)
+            same = np.all(gidx == ref["idx"], axis=1)
+            assert same.mean() > 0.99
+            rows = got["codes"][s].cpu().numpy()
+            assert np.array_equal(rows[same], O.pack(ref["idx"][same], cd.mse_bits, rows.shape[1])), what
+
+
+def test_mixed_fused_single_vector_and_zero_part():
+    """One vector per set (a single partial stage) whose regular channels are
+    all zero: the regular part's norm is 0 and its codes are those of y = 0."""
+    chans = np.arange(64)[None, :]
+    x = np.zeros((2, 1, 128), np.float32)
+    x[:, 0, :64] = np.random.default_rng(5).standard_normal((2, 64))
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    mc = tq.MixedCodec(128, 2, tq.TQ_MSE, 3, chans, groups=1)
+    mx = O.make_mixed(128, 2, O.MSE, 3, chans, groups=1)
+    po, pr = mc.quantize(xb.cuda())
+    torch.cuda.synchronize()
+    for s in range(2):
+        ro, rr = O.mixed_quantize(mx, xb[s].float().numpy().astype(np.float64), 0)
+        assert pr["norms"][s].item() == 0.0
+        assert np.array_equal(mc.regular.unpack(pr["codes"][s], 2).cpu().numpy(), rr["idx"])
+        gidx = mc.outlier.unpack(po["codes"][s], 3).cpu().numpy()
+        check_indices(gidx, ro["idx"], ro["y"], mx.outlier.boundaries, f"outlier set {s}")
