@@ -193,7 +193,11 @@ int tq_mixed_workspace(tq_mixed m, int64_t n_sets, int64_t n, int64_t nq, size_t
  * device pointers holds the outlier part's array at [0] and the regular
  * part's at [1], each in the layout of tq_quantize for that part's codec.
  * workspace: caller-owned device memory, 256-byte aligned, at least the
- * tq_mixed_workspace size; scratch.  Errors: TQ_EINVAL, TQ_EHIP. */
+ * tq_mixed_workspace size; scratch.  For d = 128 with 64 outlier channels,
+ * TurboQuant_mse, b <= 3 and 16-byte aligned TQ_BF16 input, one fused pass
+ * does both parts (the workspace is then not touched); otherwise the channels
+ * are gathered into the workspace and each part codec quantizes its share.
+ * Errors: TQ_EINVAL, TQ_EHIP. */
 int tq_mixed_quantize(tq_mixed m, const void *x, int dtype, int64_t n_sets, int64_t n, void *const codes[2],
                       void *const signs[2], float *const norms[2], float *const rnorms[2], void *workspace,
                       size_t workspace_bytes, void *stream);
