@@ -296,6 +296,28 @@ def other_paths_phase(torch, tq, workloads, x_kv):
         byts = sets * n * (d * 2 + mc.outlier.code_row + mc.regular.code_row + 8)
         res[f"kv_mixed_{bits}.5bit_gbs"] = byts / (ms * 1e-3) / 1e9
         del mc, out, ws
+    # decode logits on a 2.5-bit mixed key cache (the decode shape: 16 x 8 KV
+    # heads x 131072 tokens, 4 query heads per KV head), keys N(0,1) in bf16
+    H, T, QH = workloads.DEC_KV_HEADS, workloads.DEC_TOKENS, workloads.DEC_Q_PER_KV
+    dsets = workloads.DEC_BATCH * H
+    mc = tq.MixedCodec(d, 2, tq.TQ_MSE, 0, chans, groups=H)
+    cache = mc.empty_codes(dsets, T)
+    kb = torch.empty((8, T, d), dtype=torch.bfloat16, device="cuda")
+    ws = mc.workspace(8, T)
+    for s0 in range(0, dsets, 8):
+        kb.copy_(torch.randn((8, T, d), generator=gen, device="cuda"))
+        mc.quantize(kb, out=tuple({k: (None if v is None else v[s0:s0 + 8]) for k, v in p.items()} for p in cache),
+                    workspace=ws)
+    del kb, ws
+    qd = torch.randn((dsets, QH, d), generator=gen, device="cuda")
+    lo = torch.empty((dsets, QH, T), device="cuda")
+    wsl = mc.workspace(dsets, T, QH)
+    ms = _mean_launch_ms(torch, lambda: mc.logits(qd, cache, out=lo, workspace=wsl))
+    kbytes = dsets * T * (mc.outlier.code_row + mc.regular.code_row + 8)
+    res["decode_mixed_2.5bit_logits_ms"] = ms
+    res["decode_mixed_2.5bit_logits_packed_gbs"] = kbytes / (ms * 1e-3) / 1e9
+    res["decode_mixed_2.5bit_logits_total_gbs"] = (kbytes + dsets * QH * T * 4) / (ms * 1e-3) / 1e9
+    del mc, cache, qd, lo, wsl
     centres = torch.randn((workloads.NN_CENTRES, workloads.NN_D), generator=gen, device="cuda")
     centres /= centres.norm(dim=1, keepdim=True)
     m = torch.randint(0, workloads.NN_CENTRES, (workloads.NN_POINTS,), generator=gen, device="cuda")

@@ -1189,6 +1189,262 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   }
 }
 
+// Decode logits on mixed-precision keys: d = 128 split 64 + 64, TurboQuant_mse
+// in both parts (the layout tq_mixed_quantize writes).  [tqnet] 实现步骤草图 ›
+// 集成到 attention (logits straight from the codes); [tqnet] 从工程视角看
+// TurboQuant 到底改变了什么 (outlier channels at b + 1 bits).  The kernel is
+// k_logits128's, with one change of layout: lane (key, grp) takes coordinates
+// 16 grp .. 16 grp + 15 of each part, so contraction steps 0, 1 cover the
+// outlier part and 2, 3 the regular part.  Each part decodes through its own
+// code-pair table, accumulates on its own and is scaled by its own norm:
+// <q, x_hat> = nu_o <Pi_o q_o, c_o> + nu_r <Pi_r q_r, c_r>.
+
+// Code words of the lane's 16 codes of one part (2 MB bytes at bit 16 grp MB
+// of the row): the one or two aligned 32-bit words that hold them.
+template <int MB>
+__device__ __forceinline__ void mixed_key_words(uint32_t (&w)[2], __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                uint32_t so) {
+  if constexpr (MB <= 2) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, so, 0);
+    w[1] = 0u;
+  } else {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, so, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  }
+}
+
+struct MixKeyRegs {
+  uint32_t o[kLogitTiles][2], r[kLogitTiles][2];
+  float no[kLogitTiles], nr[kLogitTiles];
+};
+
+struct MixKeyRsrc {
+  __amdgpu_buffer_rsrc_t co, cr, no, nr;
+  uint32_t oo, orr, on;   // lane offsets: outlier / regular code words of key col, norm of key col
+  uint32_t row_o, row_r;  // bytes per key
+};
+
+template <int MBO, int MBR, bool TAIL>
+__device__ __forceinline__ void load_mixed_keys(MixKeyRegs &r, int64_t t0, int64_t kend, int col,
+                                                const MixKeyRsrc &k) {
+  const uint32_t k0 = (uint32_t)t0;
+#pragma unroll
+  for (int u = 0; u < kLogitTiles; ++u) {
+    const bool ok = !TAIL || t0 + 16 * u + col < kend;
+    const uint32_t du = ok ? (uint32_t)(16 * u) : 0u, cu = ok ? 0u : (uint32_t)col;  // back to key t0
+    mixed_key_words<MBO>(r.o[u], k.co, k.oo + (du - cu) * k.row_o, k0 * k.row_o);
+    mixed_key_words<MBR>(r.r[u], k.cr, k.orr + (du - cu) * k.row_r, k0 * k.row_r);
+    const uint32_t noff = k.on + du * 4 - cu * 4;
+    r.no[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(k.no, noff, k0 * 4, 0));
+    r.nr[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(k.nr, noff, k0 * 4, 0));
+  }
+}
+
+// Two contraction steps of one part: the lane's 16 codes (words w, first code
+// at bit sh of w[0]) as 8 code-pair table reads per step pair.
+template <int MB>
+__device__ __forceinline__ f32x4 mixed_part(const uint32_t (&w)[2], uint32_t sh, const u32x4 *bq,
+                                            uint32_t base, uint32_t table) {
+  using GM = LutGeom<MB>;
+  constexpr int W = GM::W;
+  // the 16 codes from bit 0: two words (fields of a pair never straddle the
+  // end of a 32-bit window for W <= 8 once aligned like this)
+  const uint32_t n0 = MB <= 2 ? w[0] >> sh : __builtin_amdgcn_alignbit(w[1], w[0], sh);
+  const uint32_t n1 = MB <= 2 ? 0u : w[1] >> sh;
+  const uint32_t cw[2] = {n0, n1};
+  f32x4 c = {0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    u32x4 bk;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * k + jj, bit = j * W, wi = bit >> 5, sh2 = bit & 31;
+      uint32_t x;
+      if (sh2 + W > 32)
+        x = __builtin_amdgcn_alignbit(cw[wi + 1], cw[wi], sh2 - GM::SHIFT);
+      else if (sh2 >= GM::SHIFT)
+        x = cw[wi] >> (sh2 - GM::SHIFT);
+      else
+        x = cw[wi] << (GM::SHIFT - sh2);
+      const uint32_t addr = ((x & (uint32_t)(((1 << W) - 1) << GM::SHIFT)) | base) + table;
+      bk[jj] = *(__attribute__((address_space(3))) const uint32_t *)(uintptr_t)addr;
+    }
+    c = mfma_f16(bq[k], bk, c);
+  }
+  return c;
+}
+
+template <int MBO, int MBR>
+__global__ __launch_bounds__(kLogitThreads, 1) void k_logits128_mixed(
+    const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ codes_o, int64_t row_o,
+    const uint8_t *__restrict__ codes_r, int64_t row_r, const float *__restrict__ norms_o,
+    const float *__restrict__ norms_r, int64_t n_keys, int groups, const float *__restrict__ RT,
+    const uint32_t *__restrict__ lut_o, float inv_o, const uint32_t *__restrict__ lut_r, float inv_r,
+    int64_t keys_per_wg, float *__restrict__ out) {
+  using GO = LutGeom<MBO>;
+  using GR = LutGeom<MBR>;
+  extern __shared__ u32x4 dyn_lds[];  // the kernel's only LDS: starts at address 0
+  uint32_t *t_o = (uint32_t *)dyn_lds;
+  uint32_t *t_r = (uint32_t *)((char *)dyn_lds + GO::CODE_BYTES);
+  float *qs = (float *)((char *)dyn_lds + GO::CODE_BYTES + GR::CODE_BYTES);
+  float *qt = qs + 8 * D;
+  float *scratch = qt + 8 * D;                 // [4][8][D] partial sums
+  uint32_t *counter = (uint32_t *)(scratch + 4 * 8 * D);
+
+  const int s = blockIdx.y;
+  const int g = s % groups;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
+  const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
+  const int64_t srow = (int64_t)s * n_keys;
+  MixKeyRsrc kr;
+  kr.co = set_rsrc(codes_o + srow * row_o, n_keys * row_o);
+  kr.cr = set_rsrc(codes_r + srow * row_r, n_keys * row_r);
+  kr.no = set_rsrc(norms_o + srow, n_keys * 4);
+  kr.nr = set_rsrc(norms_r + srow, n_keys * 4);
+  kr.row_o = (uint32_t)row_o;
+  kr.row_r = (uint32_t)row_r;
+  kr.oo = (uint32_t)(col * row_o) + 4u * (uint32_t)((16 * grp * MBO) >> 5);
+  kr.orr = (uint32_t)(col * row_r) + 4u * (uint32_t)((16 * grp * MBR) >> 5);
+  kr.on = (uint32_t)(col * 4);
+  const uint32_t sh_o = (uint32_t)((16 * grp * MBO) & 31), sh_r = (uint32_t)((16 * grp * MBR) & 31);
+  constexpr int KT = kLogitTiles;
+  constexpr int W = 16 * KT;  // keys per block
+  const int nfull = (int)((kend - kbeg) / W);
+  const bool ragged = kbeg + (int64_t)nfull * W < kend;
+
+  // 1. set-up loads: this wave's first block, the query, the columns of R^T
+  // this thread contracts, the tables
+  MixKeyRegs ra, rb;
+  int b = wave;
+  if (b < nfull) load_mixed_keys<MBO, MBR, false>(ra, kbeg + (int64_t)b * W, kend, col, kr);
+  const int slice = (tid >> 7) & 3, jj = tid & 127;
+  float w[32];
+  {
+    const float *Wm = RT + (size_t)g * D * D + (size_t)(32 * slice) * D + jj;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) w[k] = Wm[(size_t)k * D];
+  }
+  {
+    const int h = tid / D;
+    qs[tid] = h < hc ? q[((int64_t)s * nq + h0 + h) * D + (tid % D)] : 0.f;  // 8 D == threads
+  }
+  for (int e = tid; e < GO::ENTRIES * GO::COPIES; e += kLogitThreads) t_o[e] = lut_o[e / GO::COPIES];
+  for (int e = tid; e < GR::ENTRIES * GR::COPIES; e += kLogitThreads) t_r[e] = lut_r[e / GR::COPIES];
+  if (tid < 64) counter[tid] = kLogitWaves;
+  __syncthreads();
+  // 2. rotate every head (coordinates 0..63: Pi_o q_o, 64..127: Pi_r q_r):
+  // threads of slices 0..3 (the first 512) sum 32 contraction steps each
+  if (tid < 4 * D) {
+    float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+#pragma unroll
+      for (int h = 0; h < 8; ++h) a[h] = fmaf(w[k], qs[h * D + 32 * slice + k], a[h]);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) scratch[(slice * 8 + h) * D + jj] = a[h];
+  }
+  __syncthreads();
+  for (int e = tid; e < 8 * D; e += kLogitThreads) {
+    float v = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) v += scratch[sl * 8 * D + e];
+    qt[e] = v;
+  }
+  __syncthreads();
+  // 3. query operands: row col = (head col >> 1, part col & 1); element e of
+  // step k is coordinate 16 grp + 8 (k & 1) + e of the outlier part (k < 2) or
+  // of the regular part (k >= 2), divided by that part's table scale
+  u32x4 bq[4];
+  {
+    const int h = col >> 1, part = col & 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c0 = (k < 2 ? 0 : 64) + 16 * grp + 8 * (k & 1);
+      const float sc = k < 2 ? inv_o : inv_r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a0 = qt[h * D + c0 + 2 * i] * sc, a1 = qt[h * D + c0 + 2 * i + 1] * sc;
+        if (part) {
+          a0 -= (float)(_Float16)a0;
+          a1 -= (float)(_Float16)a1;
+        }
+        bq[k][i] = f16x2(a0, a1);
+      }
+    }
+  }
+
+  const int hA = 2 * grp, hB = 2 * grp + 1;  // heads held by this lane
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)s * nq * n_keys, 0, (int)(nq * n_keys * 4), kBufferFlags);
+  const uint32_t rowA = hA < hc ? (uint32_t)((h0 + hA) * n_keys) * 4 : kDropped;
+  const uint32_t rowB = hB < hc ? (uint32_t)((h0 + hB) * n_keys) * 4 : kDropped;
+  const uint32_t base_o = 4 * (lane & (GO::COPIES - 1)), base_r = 4 * (lane & (GR::COPIES - 1));
+  auto grab = [&]() {
+    const uint32_t v = atomicAdd(counter + lane, 1u);  // lane 0's word is the block counter
+    return (int)__builtin_amdgcn_readfirstlane(v);
+  };
+  auto score = [&](const MixKeyRegs &r, int u, float &o0, float &o1) {
+    const f32x4 co = mixed_part<MBO>(r.o[u], sh_o, bq, base_o, 0u);
+    const f32x4 cr = mixed_part<MBR>(r.r[u], sh_r, bq + 2, base_r, GO::CODE_BYTES);
+    o0 = fmaf(co[0] + co[1], r.no[u], (cr[0] + cr[1]) * r.nr[u]);
+    o1 = fmaf(co[2] + co[3], r.no[u], (cr[2] + cr[3]) * r.nr[u]);
+  };
+  auto score_store = [&](const MixKeyRegs &r, int64_t tb) {
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
+      float o0, o1;
+      score(r, u, o0, o1);
+      const uint32_t key4 = (uint32_t)(tb + 16 * u + col) * 4;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o0), ro, rowA + key4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o1), ro, rowB + key4, 0, 0);
+    }
+  };
+  if (b < nfull) {  // ra holds block b
+    while (true) {
+      int b2 = grab();
+      bool more = b2 < nfull;
+      load_mixed_keys<MBO, MBR, false>(rb, kbeg + (int64_t)(more ? b2 : b) * W, kend, col, kr);
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch issues before the block's work
+      score_store(ra, kbeg + (int64_t)b * W);
+      b = b2;
+      if (!more) break;
+      b2 = grab();
+      more = b2 < nfull;
+      load_mixed_keys<MBO, MBR, false>(ra, kbeg + (int64_t)(more ? b2 : b) * W, kend, col, kr);
+      __builtin_amdgcn_sched_barrier(0);
+      score_store(rb, kbeg + (int64_t)b * W);
+      b = b2;
+      if (!more) break;
+    }
+    // both buffers are read on the way out, so that neither prefetch is moved
+    // below the block scored after it
+    uint32_t keep = 0;
+#pragma unroll
+    for (int u = 0; u < KT; ++u)
+      keep ^= ra.o[u][0] ^ ra.o[u][1] ^ ra.r[u][0] ^ ra.r[u][1] ^ rb.o[u][0] ^ rb.o[u][1] ^ rb.r[u][0] ^
+              rb.r[u][1] ^ __float_as_uint(ra.no[u]) ^ __float_as_uint(ra.nr[u]) ^ __float_as_uint(rb.no[u]) ^
+              __float_as_uint(rb.nr[u]);
+    asm volatile("" ::"v"(keep));
+  }
+  if (b == nfull && ragged) {  // the one wave that holds the partial block: guarded loads and stores
+    const int64_t t0 = kbeg + (int64_t)nfull * W;
+    load_mixed_keys<MBO, MBR, true>(ra, t0, kend, col, kr);
+#pragma unroll
+    for (int u = 0; u < KT; ++u) {
+      float o0, o1;
+      score(ra, u, o0, o1);
+      const int64_t key = t0 + 16 * u + col;
+      const uint32_t key4 = (uint32_t)key * 4;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o0), ro, key < kend ? rowA + key4 : kDropped, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o1), ro, key < kend ? rowB + key4 : kDropped, 0, 0);
+    }
+  }
+}
+
 // ------------------------------------------------------------ attention --
 // Fused decode attention over quantized keys and values, d = 128: for every
 // query head h of a set, out_h = sum_t softmax_t(scale <q_h, k_hat_t>) v_hat_t
@@ -1870,6 +2126,37 @@ hipError_t run_logits(const DeviceTables &t, const float *q, int64_t nq, const u
   return hipSuccess;
 }
 
+template <int MBO, int MBR>
+hipError_t run_logits_mixed(const DeviceTables &to, const DeviceTables &tr, const float *RT, const float *q,
+                            int64_t nq, const uint8_t *codes_o, const uint8_t *codes_r, const float *norms_o,
+                            const float *norms_r, int64_t n_sets, int64_t n_keys, int groups, float *out,
+                            hipStream_t st) {
+  const int64_t unit = kLogitWaves * 16 * kLogitTiles;  // keys per workgroup iteration
+  int64_t gx = (256 + n_sets - 1) / n_sets;             // about one workgroup per CU
+  const int64_t max_gx = (n_keys + unit - 1) / unit;
+  if (gx > max_gx) gx = max_gx;
+  if (gx < 1) gx = 1;
+  int64_t kpw = (n_keys + gx - 1) / gx;
+  kpw = (kpw + unit - 1) / unit * unit;
+  gx = (n_keys + kpw - 1) / kpw;
+  const int64_t rmax = to.code_row > tr.code_row ? to.code_row : tr.code_row;
+  if (nq * n_keys * 4 >= (int64_t)kDropped || n_keys * rmax >= (int64_t)kDropped || n_keys > kFusedMaxKeys)
+    return hipErrorNotSupported;
+  const size_t lds = LutGeom<MBO>::CODE_BYTES + LutGeom<MBR>::CODE_BYTES + 2 * 8 * D * 4 + 4 * 8 * D * 4 + 64 * 4;
+  hipError_t e0 = hipFuncSetAttribute((const void *)k_logits128_mixed<MBO, MBR>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e0 != hipSuccess) return e0;
+  for (int64_t h0 = 0; h0 < nq; h0 += 8) {
+    const int hc = (int)(nq - h0 < 8 ? nq - h0 : 8);
+    hipLaunchKernelGGL((k_logits128_mixed<MBO, MBR>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kLogitThreads),
+                       lds, st, q, (int)nq, (int)h0, hc, codes_o, to.code_row, codes_r, tr.code_row, norms_o, norms_r,
+                       n_keys, groups, RT, to.logit_lut, to.lut_inv_scale, tr.logit_lut, tr.lut_inv_scale, kpw, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // Workgroups per set of the fused attention (about one per CU overall) and
 // the keys each takes (a multiple of one block per wave).
 int64_t attn_grid_x(int64_t n_sets, int64_t n_keys, int64_t *kpw) {
@@ -2099,6 +2386,20 @@ hipError_t launch_logits128(const DeviceTables &t, const float *q, int64_t nq,
   TQ_L(0, true) TQ_L(1, false) TQ_L(1, true) TQ_L(2, false) TQ_L(2, true)
   TQ_L(3, false) TQ_L(3, true) TQ_L(4, false) TQ_L(4, true)
 #undef TQ_L
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_logits128_mixed(const DeviceTables &to, const DeviceTables &tr, const float *RT, const float *q,
+                                  int64_t nq, const uint8_t *codes_o, const uint8_t *codes_r, const float *norms_o,
+                                  const float *norms_r, int64_t n_sets, int64_t n_keys, int groups, float *out,
+                                  hipStream_t st) {
+  if (to.d != 64 || tr.d != 64 || to.variant != 0 || tr.variant != 0 || !RT || !to.logit_lut || !tr.logit_lut)
+    return hipErrorNotSupported;
+#define TQ_M(O, R) \
+  if (to.mse_bits == O && tr.mse_bits == R) \
+    return run_logits_mixed<O, R>(to, tr, RT, q, nq, codes_o, codes_r, norms_o, norms_r, n_sets, n_keys, groups, out, st);
+  TQ_M(2, 1) TQ_M(3, 2) TQ_M(4, 3)
+#undef TQ_M
   return hipErrorNotSupported;
 }
 

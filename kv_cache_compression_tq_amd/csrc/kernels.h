@@ -100,6 +100,13 @@ hipError_t launch_logits128(const DeviceTables &t, const float *q, int64_t nq,
                             const uint8_t *codes, const uint8_t *signs, const float *norms,
                             const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
                             hipStream_t st);
+// Logits on mixed-precision keys (d = 128, 64 + 64, TurboQuant_mse parts):
+// RT = [groups][128][128], the transpose of the block matrix whose rows 0..63
+// are Pi_o on the outlier channels and 64..127 Pi_r on the others.
+hipError_t launch_logits128_mixed(const DeviceTables &to, const DeviceTables &tr, const float *RT, const float *q,
+                                  int64_t nq, const uint8_t *codes_o, const uint8_t *codes_r, const float *norms_o,
+                                  const float *norms_r, int64_t n_sets, int64_t n_keys, int groups, float *out,
+                                  hipStream_t st);
 
 // Fused decode attention, d = 128, keys of any variant with <= 4 mse bits and
 // TurboQuant_mse values with 1..4 bits.  attention128_workspace returns the

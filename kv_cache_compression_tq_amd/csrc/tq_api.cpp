@@ -563,6 +563,10 @@ struct tq_mixed_codec {
   // fused quantize (d = 128, n_out = 64, TurboQuant_mse, b + 1 <= 4): device
   // [groups] rotation images, then [groups][4] outlier-channel masks
   uint32_t *fused = nullptr;
+  // fused logits (same configurations): device [groups][128][128], the
+  // transpose of the block matrix (rows 0..63: Pi_o on the outlier channels,
+  // 64..127: Pi_r on the others)
+  float *rt = nullptr;
 };
 
 namespace {
@@ -616,15 +620,25 @@ int tq_mixed_init(int d, int b, int variant, uint64_t seed, int groups, int n_ou
       // parts' matrices are those of make_codec: seeds seed and seed + 1)
       const size_t rot_words = tq::fast128_rotation_words(128);
       std::vector<uint32_t> host((size_t)groups * (rot_words + 4));
+      std::vector<float> rt((size_t)groups * d * d, 0.f);
       std::vector<double> pi_o, pi_r, unused_s, unused_m;
       for (int g = 0; g < groups; ++g) {
         group_matrices(64, seed, g, false, pi_o, unused_s, unused_m);
         group_matrices(64, seed + 1, g, false, pi_r, unused_s, unused_m);
-        tq::fast128_build_mixed_image(pi_o.data(), pi_r.data(), perm.data() + (size_t)g * d,
-                                      &host[(size_t)g * rot_words], &host[(size_t)groups * rot_words + 4 * g]);
+        const int32_t *pg = perm.data() + (size_t)g * d;
+        tq::fast128_build_mixed_image(pi_o.data(), pi_r.data(), pg, &host[(size_t)g * rot_words],
+                                      &host[(size_t)groups * rot_words + 4 * g]);
+        float *R = &rt[(size_t)g * d * d];  // R^T[c][j] = R[j][c]
+        for (int j = 0; j < 64; ++j)
+          for (int i = 0; i < 64; ++i) {
+            R[(size_t)pg[i] * d + j] = (float)pi_o[(size_t)j * 64 + i];
+            R[(size_t)pg[64 + i] * d + 64 + j] = (float)pi_r[(size_t)j * 64 + i];
+          }
       }
       hipError_t e = hipMalloc((void **)&m->fused, host.size() * sizeof(uint32_t));
       if (e == hipSuccess) e = hipMemcpy(m->fused, host.data(), host.size() * sizeof(uint32_t), hipMemcpyHostToDevice);
+      if (e == hipSuccess) e = hipMalloc((void **)&m->rt, rt.size() * sizeof(float));
+      if (e == hipSuccess) e = hipMemcpy(m->rt, rt.data(), rt.size() * sizeof(float), hipMemcpyHostToDevice);
       if (e != hipSuccess) st = hip_fail(e, "mixed rotation image upload");
     }
     if (st != TQ_OK) {
@@ -642,6 +656,7 @@ int tq_mixed_destroy(tq_mixed m) {
   tq_destroy(m->parts[1]);
   if (m->perm) (void)hipFree(m->perm);
   if (m->fused) (void)hipFree(m->fused);
+  if (m->rt) (void)hipFree(m->rt);
   delete m;
   return TQ_OK;
 }
@@ -738,6 +753,12 @@ int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const co
   tq_mixed_workspace(m, n_sets, n_keys, nq, &need);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
     return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_mixed_workspace reports");
+  if (m->rt) {
+    const hipError_t e = tq::launch_logits128_mixed(m->parts[0]->dev, m->parts[1]->dev, m->rt, q, nq,
+                                                    (const uint8_t *)codes[0], (const uint8_t *)codes[1], norms[0],
+                                                    norms[1], n_sets, n_keys, m->groups, out, (hipStream_t)stream);
+    if (e != hipErrorNotSupported) return e == hipSuccess ? TQ_OK : hip_fail(e, "mixed logits launch");
+  }
   char *ws = (char *)workspace;
   float *qo = (float *)ws;
   float *qr = (float *)(ws + up256((size_t)(n_sets * nq) * m->n_out * 4));

@@ -162,3 +162,21 @@ def test_mixed_fused_single_vector_and_zero_part():
         assert np.array_equal(mc.regular.unpack(pr["codes"][s], 2).cpu().numpy(), rr["idx"])
         gidx = mc.outlier.unpack(po["codes"][s], 3).cpu().numpy()
         check_indices(gidx, ro["idx"], ro["y"], mx.outlier.boundaries, f"outlier set {s}")
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_mixed_fused_logits(bits):
+    """d = 128 with 64 outlier channels, TurboQuant_mse: the one-pass logits
+    kernel over both parts' codes (9 heads: two head chunks; 1000 keys: full
+    blocks and a ragged tail) against <q, x_hat> of the oracle's codes."""
+    n_sets, n, groups, nq = 3, 1000, 2, 9
+    chans, x = _data(128, n_sets, n, 64, groups, seed=60 + bits)
+    mc = tq.MixedCodec(128, bits, tq.TQ_MSE, 31, chans, groups=groups)
+    mx = O.make_mixed(128, bits, O.MSE, 31, chans, groups=groups)
+    parts = [O.mixed_quantize(mx, x[s], s % groups) for s in range(n_sets)]
+    parts = [(_f32_parts(po), _f32_parts(pr)) for po, pr in parts]
+    stored = (_stored(mx.outlier, [p[0] for p in parts]), _stored(mx.regular, [p[1] for p in parts]))
+    q = np.random.default_rng(bits).standard_normal((n_sets, nq, 128)).astype(np.float32)
+    lg = mc.logits(_cuda(q), stored).cpu().numpy()
+    for s in range(n_sets):
+        check_rows(lg[s], O.mixed_logits_plain(mx, q[s].astype(np.float64), parts[s], s % groups), f"logits set {s}")
