@@ -211,7 +211,9 @@ int tq_mixed_dequantize(tq_mixed m, const void *const codes[2], const void *cons
 /* out[s][i][t] = <q[s][i], x_hat[s][t]> for the mixed reconstruction: the
  * outlier part's logits plus the regular part's (queries split the same
  * way).  q: [n_sets][nq][d] float32, 1 <= nq <= 64.  Arrays and workspace
- * as above (the workspace also holds one part's logits). */
+ * as above (the workspace also holds one part's logits).  For d = 128 with
+ * 64 outlier channels and TurboQuant_mse parts (b <= 3) one kernel reads both
+ * parts' codes and the workspace is not touched. */
 int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const codes[2], const void *const signs[2],
                     const float *const norms[2], const float *const rnorms[2], int64_t n_sets, int64_t n_keys,
                     float *out, void *workspace, size_t workspace_bytes, void *stream);
