@@ -325,14 +325,24 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
   // least that, so a key below it cannot make the top k; ties are kept (>=)
   // because keys of other ranges may carry smaller indices.
   float tg[2][2] = {{-INFINITY, -INFINITY}, {-INFINITY, -INFINITY}};
+  // the loads are issued two tiles before the values are applied, so that
+  // no wait on them stalls the tile that issues them
+  int tgn[2][2] = {{0, 0}, {0, 0}};
   auto refresh = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int q = qbase + rt * 8 + 2 * grp + h;
-        if (q < nq) tg[rt][h] = tk_unkey(__hip_atomic_load(gtau + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        tgn[rt][h] = __hip_atomic_load(gtau + (q < nq ? q : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+  };
+  auto apply = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (qbase + rt * 8 + 2 * grp + h < nq) tg[rt][h] = tk_unkey(tgn[rt][h]);
   };
 
   auto merge = [&]() __attribute__((always_inline)) {  // every query with buffered candidates
@@ -406,7 +416,8 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
     for (int j = 0; j < kTkRing; ++j) {
       const int64_t i = i0 + j;
       if (i >= nt) break;
-      if ((i & 7) == 7) refresh();
+      if ((i & 7) == 5) refresh();
+      if ((i & 7) == 7) apply();
       const int64_t ip = i + kTkRing - 1;
       if (ip < nt)
         tk_load<MB, PROD>(ring[(j + kTkRing - 1) % kTkRing], kb + 16 * ip + col, ke - 1, grp, rc, rs, code_row,
