@@ -271,12 +271,15 @@ def other_paths_phase(torch, tq, workloads, x_kv):
         rho = torch.empty((1, nn, 1), device="cuda").log_normal_(0.0, 0.5, generator=gen)
         xh = z / z.norm(dim=2, keepdim=True) * rho
         del z
-        for variant, name, bits in ((tq.TQ_MSE, "mse", 4), (tq.TQ_PROD, "prod", 4)):
+        for variant, name, bits in [(v, nm, b) for v, nm in ((tq.TQ_MSE, "mse"), (tq.TQ_PROD, "prod"))
+                                    for b in (1, 2, 3, 4)]:
             codec = tq.Codec(dd, bits, variant, seed=0)
             out = codec.empty_codes(1, nn)
             ms = _mean_launch_ms(torch, lambda: codec.quantize(xh, out=out))
-            # f32 input: 3 split-bf16 passes per GEMM; prod adds S x and M c (2 d contraction)
-            gemm = 1 if variant == tq.TQ_MSE else 3
+            # f32 input: 3 split-bf16 passes per GEMM.  mse: Pi x; prod: Pi x,
+            # S x and M c, or S x alone when the mse stage has 0 bits (b = 1)
+            mse_bits = bits if variant == tq.TQ_MSE else bits - 1
+            gemm = 1 if variant == tq.TQ_MSE else (3 if mse_bits > 0 else 1)
             flops = 2.0 * nn * dd * dd * 3 * gemm
             res[f"d{dd}_{name}_b{bits}_quantize_ms"] = ms
             res[f"d{dd}_{name}_b{bits}_vectors_per_s"] = nn / (ms * 1e-3)

@@ -52,11 +52,7 @@ def _check_sampled(codec, cd, variant, bits, x, out, seed):
 
 
 @pytest.mark.parametrize("d,n,variant,bits", [
-    (1536, 100_000, O.MSE, 4),
-    (1536, 100_000, O.PROD, 4),
-    (1536, 100_000, O.PROD, 1),
-    (3072, 50_000, O.MSE, 2),
-    (3072, 50_000, O.PROD, 3),
+    (d, n, v, b) for d, n in ((1536, 100_000), (3072, 50_000)) for v in (O.MSE, O.PROD) for b in (1, 2, 3, 4)
 ])
 def test_highd_quantize_full_size_sampled(d, n, variant, bits):
     x = workloads.highd_vectors(n, d)
