@@ -60,12 +60,12 @@ struct TkKey {
 };
 
 template <int MB, bool PROD>
-__device__ __forceinline__ void tk_load(TkKey<MB, PROD> &r, int64_t key, int64_t klast, int grp,
+__device__ __forceinline__ void tk_load(TkKey<MB, PROD> &r, int64_t key, int grp,
                                         __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int64_t code_row,
-                                        int64_t sign_row, const float *norms, const float *rnorms) {
-  // codes and signs through buffer resources: bytes past the arrays read as
-  // zero (the padded coordinates meet zero query operands); keys past the
-  // range are masked by the caller
+                                        int64_t sign_row, __amdgpu_buffer_rsrc_t rn, __amdgpu_buffer_rsrc_t rg) {
+  // codes, signs and norms through buffer resources: bytes past the arrays
+  // read as zero (the padded coordinates meet zero query operands); keys past
+  // the range are masked by the caller
   if constexpr (MB > 0) {
     const uint32_t off = (uint32_t)(key * code_row) + 8 * MB * grp;
 #pragma unroll
@@ -76,9 +76,8 @@ __device__ __forceinline__ void tk_load(TkKey<MB, PROD> &r, int64_t key, int64_t
     r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
     r.s[1] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4, 0, 0);
   }
-  const int64_t kk = key < klast ? key : klast;
-  r.nu = norms[kk];
-  r.ga = PROD ? rnorms[kk] : 0.f;
+  r.nu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)key * 4, 0, 0));
+  r.ga = PROD ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)key * 4, 0, 0)) : 0.f;
 }
 
 // Scores of one tile for the wave's 16 queries: lane (key, grp) gets queries
@@ -300,6 +299,9 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
       __builtin_amdgcn_make_buffer_rsrc((void *)codes, 0, MB > 0 ? (int)(n_keys * code_row) : 0, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc((void *)signs, 0, PROD ? (int)(n_keys * sign_row) : 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc((void *)norms, 0, (int)(n_keys * 4), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rg =
+      __builtin_amdgcn_make_buffer_rsrc((void *)rnorms, 0, PROD ? (int)(n_keys * 4) : 0, kBufferFlags);
   const uint32_t sbase = 16 * (lane & (kTkSignCopies - 1));
   const uint32_t pbase = kTkPairOff | (4 * (lane & (G::COPIES - 1)));
   float2 *buf = (float2 *)(lds + kTkBufOff + wave * kTkBufBytes);  // [kTkQ][kTkBuf]
@@ -403,34 +405,29 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
   TkKey<MB, PROD> ring[kTkRing];
 #pragma unroll
   for (int j = 0; j < kTkRing - 1; ++j)
-    if (j < nt) tk_load<MB, PROD>(ring[j], kb + 16 * j + col, ke - 1, grp, rc, rs, code_row, sign_row, norms, rnorms);
+    tk_load<MB, PROD>(ring[j], kb + 16 * j + col, grp, rc, rs, code_row, sign_row, rn, rg);
   TkB b0, b1;
-  float nu0 = 0.f, ga0 = 0.f, nu1 = 0.f, ga1 = 0.f;
-  if (nt > 0) {
-    tk_lookup<MB, PROD>(ring[0], sbase, pbase, b0);
-    nu0 = ring[0].nu;
-    ga0 = ring[0].ga;
-  }
-  for (int64_t i0 = 0; i0 < nt; i0 += kTkRing) {
+  tk_lookup<MB, PROD>(ring[0], sbase, pbase, b0);
+  float nu0 = ring[0].nu, ga0 = ring[0].ga, nu1 = 0.f, ga1 = 0.f;
+  // no branch inside the loop body (a branch there makes the wait-count pass
+  // wait for the newest loads): the scan runs whole groups of 8 tiles, and
+  // tiles past the range hold keys that are never candidates (past the
+  // arrays the buffer loads read zeros)
+  for (int64_t i0 = 0; i0 < nt; i0 += 8) {
 #pragma unroll
-    for (int j = 0; j < kTkRing; ++j) {
+    for (int j = 0; j < 8; ++j) {
       const int64_t i = i0 + j;
-      if (i >= nt) break;
-      if ((i & 7) == 5) refresh();
-      if ((i & 7) == 7) apply();
-      const int64_t ip = i + kTkRing - 1;
-      if (ip < nt)
-        tk_load<MB, PROD>(ring[(j + kTkRing - 1) % kTkRing], kb + 16 * ip + col, ke - 1, grp, rc, rs, code_row,
-                          sign_row, norms, rnorms);
+      if (j == 5) refresh();
+      if (j == 7) apply();
+      tk_load<MB, PROD>(ring[(j + kTkRing - 1) % kTkRing], kb + 16 * (i + kTkRing - 1) + col, grp, rc, rs, code_row,
+                        sign_row, rn, rg);
       TkB &bc = (j & 1) ? b1 : b0, &bn = (j & 1) ? b0 : b1;
       float &nuc = (j & 1) ? nu1 : nu0, &gac = (j & 1) ? ga1 : ga0;
       float &nun = (j & 1) ? nu0 : nu1, &gan = (j & 1) ? ga0 : ga1;
-      if (i + 1 < nt) {
-        const TkKey<MB, PROD> &rn = ring[(j + 1) % kTkRing];
-        tk_lookup<MB, PROD>(rn, sbase, pbase, bn);
-        nun = rn.nu;
-        gan = rn.ga;
-      }
+      const TkKey<MB, PROD> &rk = ring[(j + 1) % kTkRing];
+      tk_lookup<MB, PROD>(rk, sbase, pbase, bn);
+      nun = rk.nu;
+      gan = rk.ga;
       step(bc, nuc, gac, kb + 16 * i);
     }
   }
