@@ -221,7 +221,10 @@ __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
   int64_t tile = (int64_t)blockIdx.x * kWaves + wave;
   if (tile >= ntiles) return;  // no barrier follows
 
-  auto process = [&](const XRegs<F32IN> &xr, int64_t v0) {
+  // guard: some vectors of the tile may lie past n (only the last tile of a
+  // set); full tiles store without a branch, which keeps the wait-count pass
+  // from waiting for every store before the next tile's loads are used
+  auto process = [&](const XRegs<F32IN> &xr, int64_t v0, bool guard) {
     // The images are re-read from LDS for every tile (an opaque offset keeps
     // the reads inside the loop; hoisted, 64 KB of fragments would not fit in
     // registers).
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
         }
         if constexpr (PROD) rs = fmaf(res[j], res[j], rs);
       }
-      if (v < n) {
+      if (!guard || v < n) {
         const int64_t row = set_row0 + v;
         if constexpr (MB > 0) store_codes<MB>(codes + row * (16 * MB) + grp * (4 * MB), w);
         if (grp == 0) norms[row] = nu;
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
 #pragma unroll
           for (int q = 0; q < 4; ++q) bits |= (pa[q] >= 0.f ? 1u : 0u) << (4 * m + q);
         }
-        if (v < n) {
+        if (!guard || v < n) {
           const int64_t row = set_row0 + v;
           ((uint32_t *)(signs + row * 16))[grp] = bits;
           if (grp == 0) rnorms[row] = nus[t] > 0.f ? sqrtf(gam2[t]) / nus[t] : 0.f;
@@ -300,34 +303,41 @@ __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
     }
   };
 
+  const int64_t nfull = n / 32;  // tiles whose 32 vectors all exist
   if constexpr (F32IN) {
     // float32 input (not the bandwidth-critical path): no prefetch
     XRegs<F32IN> xr;
-    for (; tile < ntiles; tile += stride) {
+    for (; tile < nfull; tile += stride) {
       load_x<F32IN>(xr, xin, set_row0, n, tile * 32, col, grp);
-      process(xr, tile * 32);
+      process(xr, tile * 32, false);
     }
-  } else {
-    // the next tile's input is loaded unconditionally (past the end it
-    // re-reads the current one) so no branch sits between load and use
+  } else if (tile < nfull) {
+    // the next tile's input is loaded unconditionally (past the last full
+    // tile it re-reads the current one) so no branch sits between load and use
     XRegs<F32IN> xa, xb;
     load_x<F32IN>(xa, xin, set_row0, n, tile * 32, col, grp);
     while (true) {
       int64_t nxt = tile + stride;
-      bool more = nxt < ntiles;
+      bool more = nxt < nfull;
       load_x<F32IN>(xb, xin, set_row0, n, (more ? nxt : tile) * 32, col, grp);
-      process(xa, tile * 32);
+      process(xa, tile * 32, false);
       tile = nxt;
       if (!more) break;
       nxt = tile + stride;
-      more = nxt < ntiles;
+      more = nxt < nfull;
       load_x<F32IN>(xa, xin, set_row0, n, (more ? nxt : tile) * 32, col, grp);
-      process(xb, tile * 32);
+      process(xb, tile * 32, false);
       tile = nxt;
       if (!more) break;
     }
   }
+  if (tile == nfull && tile < ntiles) {  // the set's partial last tile, if this wave has it
+    XRegs<F32IN> xr;
+    load_x<F32IN>(xr, xin, set_row0, n, tile * 32, col, grp);
+    process(xr, tile * 32, true);
+  }
 }
+
 
 // TurboQuant_mse of bfloat16 input with the rotation held in registers.  One
 // wave per SIMD (a 256-thread workgroup per CU) leaves each wave 512
