@@ -821,29 +821,67 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_dequant128(
   const uint32_t sign_base = 16 * (lane & (kDqSignCopies - 1));
   const float qjl = kQjlScale / (float)D;
 
-  for (int64_t tile = (int64_t)blockIdx.x * kWaves + wave; tile < ntiles; tile += stride) {
-    // an opaque offset keeps the image reads inside the loop (hoisted, 64 KB
-    // of fragments would not fit in registers)
+  // codes, signs and norms through buffer resources (vectors past n read
+  // zeros; their stores are dropped), one tile ahead in a ping-pong pair of
+  // register sets
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(MB > 0 ? codes + set_row0 * (16 * CW) : codes), 0, MB > 0 ? (int)(n * (16 * CW)) : 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(PROD ? signs + set_row0 * 16 : signs), 0, PROD ? (int)(n * 16) : 0, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rn =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(norms + set_row0), 0, (int)(n * 4), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(PROD ? rnorms + set_row0 : rnorms), 0, PROD ? (int)(n * 4) : 0, kBufferFlags);
+  struct DqRegs {
+    uint32_t cw[2][CW > 0 ? CW : 1], sw[2];
+    float nu[2], ga[2];
+  };
+  auto dq_load = [&](DqRegs &r, int64_t tile) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t v = (uint32_t)(tile * 32 + 16 * t + col);
+      if constexpr (MB > 0) {
+        const uint32_t off = v * (16 * CW) + grp * (4 * CW);
+        if constexpr (CW == 1) {
+          r.cw[t][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0);
+        } else if constexpr (CW == 2) {
+          const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
+          r.cw[t][0] = w[0];
+          r.cw[t][1] = w[1];
+        } else if constexpr (CW == 3) {
+          const u32x3 w = __builtin_amdgcn_raw_buffer_load_b96(rc, off, 0, 0);
+          r.cw[t][0] = w[0];
+          r.cw[t][1] = w[1];
+          r.cw[t][2] = w[2];
+        } else {
+          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+          r.cw[t][0] = w[0];
+          r.cw[t][1] = w[1];
+          r.cw[t][2] = w[2];
+          r.cw[t][3] = w[3];
+        }
+      }
+      if constexpr (PROD) r.sw[t] = __builtin_amdgcn_raw_buffer_load_b32(rs, v * 16 + grp * 4, 0, 0);
+      r.nu[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, v * 4, 0, 0));
+      r.ga[t] = PROD ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, v * 4, 0, 0)) : 0.f;
+    }
+  };
+  auto dq_tile = [&](const DqRegs &r, int64_t tile) __attribute__((always_inline)) {
     int frag_lane = lane;
     asm volatile("" : "+v"(frag_lane));
     f32x4 acc[2][8];
     float scale_c[2], scale_s[2];
+    const auto &cw = r.cw;
+    const auto &sw = r.sw;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      scale_c[t] = r.nu[t] * inv_alpha;
+      scale_s[t] = PROD ? r.nu[t] * qjl * r.ga[t] : 0.f;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
-    }
-    uint32_t cw[2][CW > 0 ? CW : 1], sw[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      int64_t v = tile * 32 + 16 * t + col;
-      v = v < n ? v : n - 1;  // ragged tail: a valid row, the store is dropped
-      const int64_t row = set_row0 + v;
-      if constexpr (MB > 0) load_codes<CW>(cw[t], codes + row * (16 * CW) + grp * (4 * CW));
-      if constexpr (PROD) sw[t] = *(const uint32_t *)(signs + row * 16 + grp * 4);
-      const float nu = norms[row];
-      scale_c[t] = nu * inv_alpha;
-      scale_s[t] = PROD ? nu * qjl * rnorms[row] : 0.f;
     }
     if constexpr (MB > 0) {
 #pragma unroll
@@ -926,6 +964,39 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_dequant128(
       for (int m = 0; m < 8; ++m)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t][m]), ro, base + 16 * m, 0, 0);
     }
+  };
+  int64_t tile = (int64_t)blockIdx.x * kWaves + wave;
+  if (tile < ntiles) {
+    DqRegs ra, rb;
+    dq_load(ra, tile);
+    while (true) {
+      int64_t nxt = tile + stride;
+      bool more = nxt < ntiles;
+      dq_load(rb, more ? nxt : tile);
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch issues before the tile's work
+      dq_tile(ra, tile);
+      tile = nxt;
+      if (!more) break;
+      nxt = tile + stride;
+      more = nxt < ntiles;
+      dq_load(ra, more ? nxt : tile);
+      __builtin_amdgcn_sched_barrier(0);
+      dq_tile(rb, tile);
+      tile = nxt;
+      if (!more) break;
+    }
+    // both register sets are read on the way out, so that neither prefetch is
+    // moved below the tile worked on after it
+    uint32_t keep = 0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if constexpr (MB > 0)
+#pragma unroll
+        for (int i = 0; i < CW; ++i) keep ^= ra.cw[t][i] ^ rb.cw[t][i];
+      keep ^= ra.sw[t] ^ rb.sw[t] ^ __float_as_uint(ra.nu[t]) ^ __float_as_uint(rb.nu[t]) ^
+              __float_as_uint(ra.ga[t]) ^ __float_as_uint(rb.ga[t]);
+    }
+    asm volatile("" ::"v"(keep));
   }
 }
 
