@@ -418,7 +418,7 @@ def main():
                                "32768 tokens x 128, bf16, 4 outlier channels/head x10, TurboQuant_mse b=4, "
                                "one rotation per head",
                    "vectors_per_step": qp["vectors"], "d": 128, "bits": 4, "variant": "mse"},
-        "roofline": {"bound": "hbm", "kernel": "k_quant128<4,mse,bf16>", "achieved": qp["achieved_gbs"],
+        "roofline": {"bound": "hbm", "kernel": "k_quant128_mse<4>", "achieved": qp["achieved_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": qp["achieved_gbs"] / HBM_PEAK_GBS,
                      "traffic": counted_traffic("quant128_kv_mse_b4.md"),
                      "bytes_per_vector": qp["bytes_per_vector"],
