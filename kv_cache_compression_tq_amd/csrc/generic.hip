@@ -159,34 +159,81 @@ __global__ void k_add_inplace(float *__restrict__ out, const float *__restrict__
 // coordinate (Pi^T and M^T columns read coalesced from L2), reduced in LDS;
 // codes are packed a 32-bit word per thread, signs by ballot.  A row outside
 // [0, cache_rows) is skipped.
+//
+// DC = 128 is the compile-time form for d = 128 (4 slices of 32 steps): each
+// thread loads its 32 Pi^T (and 32 M^T) entries into registers at entry,
+// together with the row index and x, so the whole kernel waits on global
+// memory once; a skipped row only drops the stores.
 constexpr int kAppendThreads = 512;
+constexpr int kAppendSpan = 32;  // contraction steps per thread for d = 128
 
-template <typename T>
+template <typename T, int DC>
 __global__ __launch_bounds__(kAppendThreads) void k_append(
-    const T *__restrict__ x, int d, int groups, int mse_bits, int prod, const int64_t *__restrict__ rows,
+    const T *__restrict__ x, int d_arg, int groups, int mse_bits, int prod, const int64_t *__restrict__ rows,
     int64_t cache_rows, const float *__restrict__ PiT, const float *__restrict__ MT, const float *__restrict__ cent,
     const float *__restrict__ bnd, uint8_t *__restrict__ codes, int64_t code_row, uint8_t *__restrict__ signs,
     int64_t sign_row, float *__restrict__ norms, float *__restrict__ rnorms) {
+  static_assert(DC == 0 || DC * 4 == kAppendThreads, "the fixed form has 4 slices of d / 4 steps");
   extern __shared__ float sm[];  // xs[d], part[kAppendThreads], ys[d], idx[d]
   __shared__ float red[kAppendThreads / 64];
+  const int d = DC > 0 ? DC : d_arg;
   float *xs = sm, *part = sm + d, *ys = part + kAppendThreads;
   int *is = (int *)(ys + d);
   const int s = blockIdx.x, tid = threadIdx.x;
-  const int64_t row = rows[s];
-  if (row < 0 || row >= cache_rows) return;  // the whole workgroup leaves together
   const int g = s % groups;
+  const int64_t row = rows[s];
+  float pr[DC > 0 ? kAppendSpan : 1], mr[DC > 0 ? kAppendSpan : 1];
+  if constexpr (DC > 0) {
+    // thread (slice, j): Pi^T[k][j] and M^T[k][j] for k in [32 slice, 32 slice + 32)
+    const size_t off = (size_t)g * DC * DC + (size_t)(kAppendSpan * (tid / DC)) * DC + tid % DC;
+#pragma unroll
+    for (int u = 0; u < kAppendSpan; ++u) pr[u] = PiT[off + (size_t)u * DC];
+    if (prod) {
+#pragma unroll
+      for (int u = 0; u < kAppendSpan; ++u) mr[u] = MT[off + (size_t)u * DC];
+    }
+  } else {
+    if (row < 0 || row >= cache_rows) return;  // the whole workgroup leaves together
+  }
+  const bool keep = row >= 0 && row < cache_rows;
   const int nsl = d <= kAppendThreads ? kAppendThreads / d : 1;  // contraction slices per coordinate
   const int span = (d + nsl - 1) / nsl;
   const T *xv = x + (int64_t)s * d;
+  __shared__ float cl[DC > 0 ? 256 : 1];  // the fixed form's codebook copy (at most 8 bits)
   float acc = 0.f;
-  for (int j = tid; j < d; j += kAppendThreads) {
-    const float v = load_x(xv, j);
-    xs[j] = v;
-    acc = fmaf(v, v, acc);
+  if constexpr (DC > 0) {
+    // x and the codebook are loaded before either is stored, so the kernel's
+    // loads all share one wait; the row index is forced into registers there too
+    // (unconditional loads at clamped indices: the table holds at least one entry)
+    const int L = mse_bits > 0 ? 1 << mse_bits : 1;
+    const float cv = cent[tid < L ? tid : L - 1];
+    const float v = load_x(xv, tid < DC ? tid : DC - 1);
+    asm volatile("" ::"s"(row));
+    if (mse_bits > 0 && tid < L) cl[tid] = cv;
+    if (tid < DC) {
+      xs[tid] = v;
+      acc = v * v;
+    }
+  } else {
+    for (int j = tid; j < d; j += kAppendThreads) {
+      const float v = load_x(xv, j);
+      xs[j] = v;
+      acc = fmaf(v, v, acc);
+    }
   }
   const float nu = sqrtf(block_sum(acc, red));  // block_sum syncs before it reads
   const float nthr = nu > 0.f ? nu : 1.f;
   // y = Pi x: thread (slice, j) sums its span of k (PiT[k][j] = Pi[j][k])
+  auto contract_regs = [&](const float (&rg)[DC > 0 ? kAppendSpan : 1], const float *vin, float *vout) {
+    const int k0 = kAppendSpan * (tid / (DC > 0 ? DC : 1));
+    float p4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < kAppendSpan; ++u) p4[u & 3] = fmaf(rg[u], vin[k0 + u], p4[u & 3]);
+    part[tid] = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+    __syncthreads();
+    if (tid < DC) vout[tid] = (part[tid] + part[DC + tid]) + (part[2 * DC + tid] + part[3 * DC + tid]);
+    __syncthreads();
+  };
   auto contract = [&](const float *Mt, const float *vin, float *vout) {
     for (int j0 = 0; j0 < d; j0 += kAppendThreads / nsl) {
       const int j = j0 + tid % (kAppendThreads / nsl), sl = tid / (kAppendThreads / nsl);
@@ -214,7 +261,10 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(
     }
     __syncthreads();
   };
-  contract(PiT + (size_t)g * d * d, xs, ys);
+  if constexpr (DC > 0)
+    contract_regs(pr, xs, ys);
+  else
+    contract(PiT + (size_t)g * d * d, xs, ys);
   const int L = 1 << mse_bits;
   for (int j = tid; j < d; j += kAppendThreads) {
     const float y = ys[j];
@@ -222,10 +272,11 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(
     if (mse_bits > 0)
       for (int k = 0; k + 1 < L; ++k) idx += fmaf(nthr, bnd[k], -y) < 0.f ? 1 : 0;  // nu t_k < y
     is[j] = idx;
-    ys[j] = mse_bits > 0 ? y - nu * cent[idx] : y;  // nu times the rotated residual
+    const float c = mse_bits > 0 ? (DC > 0 ? cl[idx] : cent[idx]) : 0.f;
+    ys[j] = mse_bits > 0 ? y - nu * c : y;  // nu times the rotated residual
   }
   __syncthreads();
-  if (mse_bits > 0) {
+  if (mse_bits > 0 && keep) {
     uint32_t *crow = (uint32_t *)(codes + row * code_row);
     for (int w = tid; w < (int)(code_row / 4); w += kAppendThreads) {
       uint32_t v = 0;
@@ -238,24 +289,27 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(
       crow[w] = v;
     }
   }
-  if (tid == 0) norms[row] = nu;
+  if (tid == 0 && keep) norms[row] = nu;
   if (!prod) return;
   float r2 = 0.f;
   for (int j = tid; j < d; j += kAppendThreads) r2 = fmaf(ys[j], ys[j], r2);
   const float rn = sqrtf(block_sum(r2, red));
   // sign(S r) = sign(M (Pi r)) with M = S Pi^T (MT[j][i] = M[i][j]); xs is free now
-  contract(MT + (size_t)g * d * d, ys, xs);
+  if constexpr (DC > 0)
+    contract_regs(mr, ys, xs);
+  else
+    contract(MT + (size_t)g * d * d, ys, xs);
   uint32_t *srow = (uint32_t *)(signs + row * sign_row);
   for (int i0 = 0; i0 < (int)(sign_row * 8); i0 += kAppendThreads) {
     const int i = i0 + tid;
     const uint64_t m = __ballot(i < d && xs[i] >= 0.f);
-    if ((tid & 63) == 0) {
+    if ((tid & 63) == 0 && keep) {
       const int w = i >> 5;  // lane 0 of each wave writes its 64 bits
       if (w < (int)(sign_row / 4)) srow[w] = (uint32_t)m;
       if (w + 1 < (int)(sign_row / 4)) srow[w + 1] = (uint32_t)(m >> 32);
     }
   }
-  if (tid == 0) rnorms[row] = nu > 0.f ? rn / nu : 0.f;
+  if (tid == 0 && keep) rnorms[row] = nu > 0.f ? rn / nu : 0.f;
 }
 
 // Reconstruction of one vector per workgroup:
@@ -517,14 +571,23 @@ hipError_t launch_append(const DeviceTables &t, const void *x, int dtype, int64_
   if (n_sets == 0) return hipSuccess;
   const size_t shmem = ((size_t)3 * t.d + kAppendThreads) * sizeof(float);
   const int prod = t.variant == 1;
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_append<float>, dim3((unsigned)n_sets), dim3(kAppendThreads), shmem, st, (const float *)x,
-                       t.d, t.groups, t.mse_bits, prod, rows, cache_rows, t.PiT, t.MT, t.cent, t.bnd, codes,
-                       t.code_row, signs, t.sign_row, norms, rnorms);
-  else
-    hipLaunchKernelGGL(k_append<uint16_t>, dim3((unsigned)n_sets), dim3(kAppendThreads), shmem, st,
-                       (const uint16_t *)x, t.d, t.groups, t.mse_bits, prod, rows, cache_rows, t.PiT, t.MT,
-                       t.cent, t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms);
+  const bool fixed = t.d * 4 == kAppendThreads && t.mse_bits <= 8;
+#define TQ_APPEND(T, DC)                                                                                         \
+  hipLaunchKernelGGL((k_append<T, DC>), dim3((unsigned)n_sets), dim3(kAppendThreads), shmem, st, (const T *)x, t.d, \
+                     t.groups, t.mse_bits, prod, rows, cache_rows, t.PiT, t.MT, t.cent, t.bnd, codes, t.code_row,   \
+                     signs, t.sign_row, norms, rnorms)
+  if (dtype == 0) {
+    if (fixed)
+      TQ_APPEND(float, kAppendThreads / 4);
+    else
+      TQ_APPEND(float, 0);
+  } else {
+    if (fixed)
+      TQ_APPEND(uint16_t, kAppendThreads / 4);
+    else
+      TQ_APPEND(uint16_t, 0);
+  }
+#undef TQ_APPEND
   return hipGetLastError();
 }
 

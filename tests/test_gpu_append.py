@@ -30,30 +30,46 @@ def _cache(codec, rows):
 
 
 def _check_rows(codec, cd, cache, before, rows, x64):
+    """Every appended row against the oracle.  The index and sign rules are
+    taken over all coordinates of the appended batch, as for a quantized
+    batch (a single vector holds only d coordinates); norms row by row."""
     n_sets, d = x64.shape
-    written = torch.from_numpy(rows).cuda()
+    n_rows = cache["norms"].shape[0]
+    valid = (rows >= 0) & (rows < n_rows)
+    written = torch.from_numpy(rows[valid]).cuda()
+    gi, oi, oy = [], [], []
+    gb, ob, op, orn = [], [], [], []
     for s in range(n_sets):
+        if not valid[s]:
+            continue
         g = s % cd.groups
         r = int(rows[s])
         if cd.variant == O.MSE:
             idx, nu, y = O.quantize_mse(cd, x64[s:s + 1], g)
             gidx = codec.unpack(cache["codes"][r:r + 1].contiguous(), cd.mse_bits).cpu().numpy()
-            check_indices(gidx, idx, y, cd.boundaries, f"set {s}")
+            gi.append(gidx), oi.append(idx), oy.append(y)
             assert np.allclose(cache["norms"][r].item(), nu[0], rtol=1e-5)
         else:
             res = O.quantize_prod(cd, x64[s:s + 1], g)
             same = True
             if cd.mse_bits:
                 gidx = codec.unpack(cache["codes"][r:r + 1].contiguous(), cd.mse_bits).cpu().numpy()
-                check_indices(gidx, res["idx"], res["y"], cd.boundaries, f"set {s}")
+                gi.append(gidx), oi.append(res["idx"]), oy.append(res["y"])
                 same = bool(np.all(gidx == res["idx"]))
             if same:
-                gb = codec.unpack(cache["signs"][r:r + 1].contiguous(), 1).cpu().numpy()
-                check_signs(gb, O.signs_to_bits(res["signs"]), res["proj"], res["rnorms"], f"set {s}")
+                gb.append(codec.unpack(cache["signs"][r:r + 1].contiguous(), 1).cpu().numpy())
+                ob.append(O.signs_to_bits(res["signs"]))
+                op.append(res["proj"])
+                orn.append(res["rnorms"])
                 assert np.allclose(cache["rnorms"][r].item(), res["rnorms"][0], rtol=1e-4, atol=1e-6)
             assert np.allclose(cache["norms"][r].item(), res["norms"][0], rtol=1e-5)
+    if gi:
+        check_indices(np.concatenate(gi), np.concatenate(oi), np.concatenate(oy), cd.boundaries, "appended rows")
+    if gb:
+        check_signs(np.concatenate(gb), np.concatenate(ob), np.concatenate(op), np.concatenate(orn),
+                    "appended rows")
     # every other row is untouched
-    keep = torch.ones(cache["norms"].shape[0], dtype=torch.bool, device="cuda")
+    keep = torch.ones(n_rows, dtype=torch.bool, device="cuda")
     keep[written] = False
     for k, v in cache.items():
         if v is not None:
@@ -78,6 +94,49 @@ def test_append_matches_oracle(d, bits, variant, dtype):
     rows = rng.choice(cache_rows, n_sets, replace=False).astype(np.int64)
     codec = tq.Codec(d, bits, variant, seed=13, groups=groups)
     cd = O.make_codec(d, bits, variant, 13, groups=groups)
+    cache = _cache(codec, cache_rows)
+    before = {k: (None if v is None else v.clone()) for k, v in cache.items()}
+    codec.append(xt, torch.from_numpy(rows).cuda(), cache)
+    torch.cuda.synchronize()
+    _check_rows(codec, cd, cache, before, rows, x64)
+
+
+@pytest.mark.parametrize("n_sets,groups,variant,bits,dtype", [
+    (700, 2, O.PROD, 4, torch.float32),   # 350 vectors per group: 11 tiles over two workgroups
+    (333, 5, O.MSE, 2, torch.bfloat16),   # ragged: 67 and 66 vectors per group
+    (3, 5, O.PROD, 3, torch.bfloat16),    # more groups than sets
+    (97, 4, O.MSE, 4, torch.float32),
+])
+def test_append_many_vectors_per_group(n_sets, groups, variant, bits, dtype):
+    d, cache_rows = 128, 2 * n_sets + 5
+    rng = np.random.default_rng(n_sets + groups)
+    x = rng.standard_normal((n_sets, d)).astype(np.float32)
+    x[n_sets // 2] = 0.0
+    xt = torch.from_numpy(x).to(dtype).cuda()
+    x64 = xt.float().cpu().numpy().astype(np.float64)
+    rows = rng.choice(cache_rows, n_sets, replace=False).astype(np.int64)
+    rows[::7] = -1                    # skipped
+    rows[3::11] = cache_rows + 4      # skipped
+    codec = tq.Codec(d, bits, variant, seed=21, groups=groups)
+    cd = O.make_codec(d, bits, variant, 21, groups=groups)
+    cache = _cache(codec, cache_rows)
+    before = {k: (None if v is None else v.clone()) for k, v in cache.items()}
+    codec.append(xt, torch.from_numpy(rows).cuda(), cache)
+    torch.cuda.synchronize()
+    _check_rows(codec, cd, cache, before, rows, x64)
+
+
+def test_append_unaligned_input():
+    """An input that is not 16-byte aligned takes the one-workgroup-per-set
+    kernel; both kernels agree with the oracle."""
+    d, n_sets, cache_rows = 128, 9, 20
+    rng = np.random.default_rng(5)
+    base = torch.from_numpy(rng.standard_normal(n_sets * d + 1).astype(np.float32)).to(torch.bfloat16).cuda()
+    xt = base[1:].view(n_sets, d)
+    x64 = xt.float().cpu().numpy().astype(np.float64)
+    rows = rng.choice(cache_rows, n_sets, replace=False).astype(np.int64)
+    codec = tq.Codec(d, 3, O.PROD, seed=4, groups=2)
+    cd = O.make_codec(d, 3, O.PROD, 4, groups=2)
     cache = _cache(codec, cache_rows)
     before = {k: (None if v is None else v.clone()) for k, v in cache.items()}
     codec.append(xt, torch.from_numpy(rows).cuda(), cache)
