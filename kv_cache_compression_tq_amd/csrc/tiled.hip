@@ -5,9 +5,10 @@
 // [128 c, 128 c + 128) (both zero-padded past d).  Every block is stored as
 // the same bf16 hi/lo MFMA operand image the d = 128 kernels use (rows
 // permuted so that each lane ends up with 32 consecutive coordinates of its
-// vector).  A workgroup computes one panel for 256 vectors: the images of the
-// chunks stream through a double buffer in LDS (direct global-to-LDS loads),
-// the inputs through registers, and after the last chunk the panel's codes
+// vector).  A workgroup computes one panel for 128 vectors: the images of the
+// chunks go through one LDS buffer (direct global-to-LDS loads), the inputs
+// through registers; two workgroups share a CU, so one's MFMAs run while the
+// other waits for its next chunk.  After the last chunk the panel's codes
 // are searched and packed exactly as at d = 128.
 //
 // TurboQuant_prod adds a second pass.  The QJL signs need the residual of the
@@ -26,8 +27,9 @@
 namespace tq {
 namespace {
 
-constexpr int kTiledThreads = 512;     // 8 waves x 32 vectors
-constexpr int kTiledVectors = 256;     // vectors per workgroup
+constexpr int kTiledThreads = 256;     // 4 waves x 32 vectors
+constexpr int kTiledVectors = 128;     // vectors per workgroup
+constexpr int kTiledWaves = kTiledThreads / 64;
 constexpr uint32_t kImgBytes = kImageVec * 16;
 constexpr float kFix = 268435456.f;    // 2^28: fixed-point scale of the residual norm squared
 
@@ -51,11 +53,12 @@ __device__ __forceinline__ uint32_t cell_index_rt(uint32_t tab, float y, float n
 }
 
 // Direct global-to-LDS copy of one 64 KB image block by the whole workgroup
-// (each wave moves 8 KB in 1 KB steps; lane data lands in lane order).
+// (each wave moves 16 KB in 1 KB steps; lane data lands in lane order).
 __device__ __forceinline__ void stage_image(const u32x4 *src, u32x4 *dst, int wave, int lane) {
+  constexpr int kSteps = kImageVec / 64 / kTiledWaves;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int off = (wave * 8 + i) * 64;  // u32x4 index of this 1 KB step
+  for (int i = 0; i < kSteps; ++i) {
+    const int off = (wave * kSteps + i) * 64;  // u32x4 index of this 1 KB step
     __builtin_amdgcn_global_load_lds((const void *)(src + off + lane),
                                      (__attribute__((address_space(3))) void *)(dst + off), 16, 0, 0);
   }
@@ -134,15 +137,15 @@ __device__ __forceinline__ void mma_chunk(const XChunk<F32IN> &x, const u32x4 *i
 
 // Pass 1: rotation panel, norms, search and pack; prod: residual norm partials.
 template <int MB, bool PROD, bool F32IN>
-__global__ __launch_bounds__(kTiledThreads, 1) void k_tiled_rot(const void *__restrict__ xin, TiledArgs a,
+__global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_rot(const void *__restrict__ xin, TiledArgs a,
                                                                 const u32x4 *__restrict__ img_all,
                                                                 const uint32_t *__restrict__ cells,
                                                                 const float *__restrict__ cent,
                                                                 uint8_t *__restrict__ codes, float *__restrict__ norms,
                                                                 int *__restrict__ rn_fix) {
   extern __shared__ u32x4 dyn_lds[];
-  u32x4 *buf = dyn_lds;  // 2 image buffers, then the cell table, then the codebook
-  uint32_t *tab = (uint32_t *)((char *)dyn_lds + 2 * kImgBytes);
+  u32x4 *buf = dyn_lds;  // the image buffer, then the cell table, then the codebook
+  uint32_t *tab = (uint32_t *)((char *)dyn_lds + kImgBytes);
   float *cent_lds = (float *)(tab + a.cell_words);
   const int p = blockIdx.x, s = blockIdx.z, g = s % a.groups;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -151,7 +154,6 @@ __global__ __launch_bounds__(kTiledThreads, 1) void k_tiled_rot(const void *__re
   const int panels = a.chunks;  // square blocks: as many output panels as contraction chunks
   const u32x4 *img = img_all + ((size_t)g * panels + p) * (size_t)a.chunks * kImageVec;
 
-  stage_image(img, buf, wave, lane);
   for (int i = tid; i < a.cell_words; i += kTiledThreads) tab[i] = cells[i];
   if (PROD && MB > 0 && tid < (1 << MB)) cent_lds[tid] = cent[tid];
 
@@ -162,28 +164,25 @@ __global__ __launch_bounds__(kTiledThreads, 1) void k_tiled_rot(const void *__re
     v[t] = (int64_t)blockIdx.y * kTiledVectors + 32 * wave + 16 * t + col;
     row[t] = set_row0 + (v[t] < a.n ? v[t] : a.n - 1);  // ragged tail: a valid row, results discarded
   }
-  XChunk<F32IN> xa, xb;
-  load_chunk<F32IN>(xa, xin, row, 0, a.d, grp);
+  XChunk<F32IN> xa;
   f32x4 acc[2][8];
   float nsq[2] = {0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
 
+  // One image buffer per workgroup and two workgroups per CU: while one waits
+  // for its chunk's image and inputs, the other one's MFMAs run.
   for (int c = 0; c < a.chunks; ++c) {
-    // the next chunk's image and inputs are in flight while this one computes
-    const int cn = c + 1 < a.chunks ? c + 1 : c;
-    if (c + 1 < a.chunks) stage_image(img + (size_t)cn * kImageVec, buf + ((c + 1) & 1) * kImageVec, wave, lane);
-    load_chunk<F32IN>(xb, xin, row, cn, a.d, grp);
-    int frag_lane = lane;
-    asm volatile("" : "+v"(frag_lane));
-    mma_chunk<F32IN>(xa, buf + (c & 1) * kImageVec, frag_lane, acc, nsq);
-    xa = xb;
+    if (c > 0) __syncthreads();  // every wave is done with the previous image
+    stage_image(img + (size_t)c * kImageVec, buf, wave, lane);
+    load_chunk<F32IN>(xa, xin, row, c, a.d, grp);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    int frag_lane = lane;
+    asm volatile("" : "+v"(frag_lane));
+    mma_chunk<F32IN>(xa, buf, frag_lane, acc, nsq);
   }
 
   const uint32_t tab_addr = lds_addr(tab);
@@ -240,15 +239,15 @@ __global__ __launch_bounds__(kTiledThreads, 1) void k_tiled_rot(const void *__re
 // Pass 2 (prod): signs of S x - nu M c[idx], K = d (x) then d (codes);
 // panel 0 also turns the fixed-point residual norms into float32.
 template <int MB, bool F32IN>
-__global__ __launch_bounds__(kTiledThreads, 1) void k_tiled_sign(const void *__restrict__ xin, TiledArgs a,
+__global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__restrict__ xin, TiledArgs a,
                                                                  const u32x4 *__restrict__ img_all,
                                                                  const float *__restrict__ cent,
                                                                  const uint8_t *__restrict__ codes,
                                                                  const float *__restrict__ norms,
                                                                  uint8_t *__restrict__ signs, float *__restrict__ rnorms) {
   extern __shared__ u32x4 dyn_lds[];
-  u32x4 *buf = dyn_lds;
-  float *cent_lds = (float *)((char *)dyn_lds + 2 * kImgBytes);
+  u32x4 *buf = dyn_lds;  // the image buffer, then the codebook
+  float *cent_lds = (float *)((char *)dyn_lds + kImgBytes);
   const int p = blockIdx.x, s = blockIdx.z, g = s % a.groups;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -257,7 +256,6 @@ __global__ __launch_bounds__(kTiledThreads, 1) void k_tiled_sign(const void *__r
   const int kchunks = (MB > 0 ? 2 : 1) * a.chunks;
   const u32x4 *img = img_all + ((size_t)g * panels + p) * (size_t)(2 * a.chunks) * kImageVec;
 
-  stage_image(img, buf, wave, lane);
   if (MB > 0 && tid < (1 << MB)) cent_lds[tid] = cent[tid];
 
   const int64_t set_row0 = (int64_t)s * a.n;
@@ -269,37 +267,33 @@ __global__ __launch_bounds__(kTiledThreads, 1) void k_tiled_sign(const void *__r
     row[t] = set_row0 + (v[t] < a.n ? v[t] : a.n - 1);
     nu[t] = norms[row[t]];
   }
-  XChunk<F32IN> xa, xb;
-  load_chunk<F32IN>(xa, xin, row, 0, a.d, grp);
+  XChunk<F32IN> xa;
   f32x4 acc[2][8];
   float dummy[2] = {0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   const uint32_t cent_addr = lds_addr(cent_lds);
 
-  // S x over the input chunks
+  // S x over the input chunks (one image buffer, as in pass 1)
   for (int c = 0; c < a.chunks; ++c) {
-    if (c + 1 < kchunks) stage_image(img + (size_t)(c + 1) * kImageVec, buf + ((c + 1) & 1) * kImageVec, wave, lane);
-    load_chunk<F32IN>(xb, xin, row, c + 1 < a.chunks ? c + 1 : c, a.d, grp);
-    int frag_lane = lane;
-    asm volatile("" : "+v"(frag_lane));
-    mma_chunk<F32IN>(xa, buf + (c & 1) * kImageVec, frag_lane, acc, dummy);
-    xa = xb;
+    if (c > 0) __syncthreads();
+    stage_image(img + (size_t)c * kImageVec, buf, wave, lane);
+    load_chunk<F32IN>(xa, xin, row, c, a.d, grp);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    int frag_lane = lane;
+    asm volatile("" : "+v"(frag_lane));
+    mma_chunk<F32IN>(xa, buf, frag_lane, acc, dummy);
   }
   // - nu M c[idx] over the code chunks: B = -nu c for coordinates
   // 128 cc + 32 grp + 8 k + e (the lane's 32 codes), split into bf16 hi/lo;
   // coordinates past d meet zero columns
-  for (int c = a.chunks; c < kchunks; ++c) {
-    if (c + 1 < kchunks) stage_image(img + (size_t)(c + 1) * kImageVec, buf + ((c + 1) & 1) * kImageVec, wave, lane);
-    int frag_lane = lane;
-    asm volatile("" : "+v"(frag_lane));
-    if constexpr (MB > 0) {
+  if constexpr (MB > 0) {
+    for (int c = a.chunks; c < kchunks; ++c) {
+      __syncthreads();  // every wave is done with the previous image
+      stage_image(img + (size_t)c * kImageVec, buf, wave, lane);
       const int cc = c - a.chunks;
       XChunk<true> cx;
 #pragma unroll
@@ -324,10 +318,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void k_tiled_sign(const void *__r
           cx.v[t][k][1] = __builtin_bit_cast(u32x4, f32x4{f[4], f[5], f[6], f[7]});
         }
       }
-      mma_chunk<true>(cx, buf + (c & 1) * kImageVec, frag_lane, acc, dummy);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      int frag_lane = lane;
+      asm volatile("" : "+v"(frag_lane));
+      mma_chunk<true>(cx, buf, frag_lane, acc, dummy);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
 
 #pragma unroll
@@ -369,7 +365,7 @@ hipError_t run_tiled(const DeviceTables &t, const void *x, int64_t n_sets, int64
   a.cell_words = MB > 0 ? 2 * (2 * t.cell_radius + 1) : 0;
   const int panels = a.chunks;
   const dim3 grid((unsigned)panels, (unsigned)((n + kTiledVectors - 1) / kTiledVectors), (unsigned)n_sets);
-  const size_t lds1 = 2 * kImgBytes + 4 * (size_t)a.cell_words + 64;
+  const size_t lds1 = kImgBytes + 4 * (size_t)a.cell_words + 64;
   hipError_t e = hipFuncSetAttribute((const void *)k_tiled_rot<MB, PROD, F32IN>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   if (e != hipSuccess) return e;
@@ -382,7 +378,7 @@ hipError_t run_tiled(const DeviceTables &t, const void *x, int64_t n_sets, int64
                      (const u32x4 *)t.tiled_rot, t.cells, t.cent, codes, norms, (int *)rnorms);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (PROD) {
-    const size_t lds2 = 2 * kImgBytes + 64;
+    const size_t lds2 = kImgBytes + 64;
     e = hipFuncSetAttribute((const void *)k_tiled_sign<MB, F32IN>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds2);
     if (e != hipSuccess) return e;
