@@ -95,6 +95,9 @@ __device__ __forceinline__ void load_chunk(XChunk<F32IN> &r, const void *xin, co
 }
 
 // acc[t][m] += image block (LDS) x chunk; also ||x||^2 of the chunk's elements.
+// Per K step the 16 A fragments (8 row tiles, hi and lo) are read from LDS
+// together before that step's MFMAs, so one LDS round trip serves 32 or 48
+// MFMAs; the scheduling-group barriers keep the reads in one group.
 template <bool F32IN>
 __device__ __forceinline__ void mma_chunk(const XChunk<F32IN> &x, const u32x4 *img, int frag_lane,
                                           f32x4 (&acc)[2][8], float (&nsq)[2]) {
@@ -120,19 +123,25 @@ __device__ __forceinline__ void mma_chunk(const XChunk<F32IN> &x, const u32x4 *i
       }
     }
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
+  for (int k = 0; k < 4; ++k) {
+    u32x4 ah[8], al[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int f = (m * 4 + k) * 2;
-      const u32x4 ah = img[f * kFragVec + frag_lane];
-      const u32x4 al = img[(f + 1) * kFragVec + frag_lane];
+      ah[m] = img[f * kFragVec + frag_lane];
+      al[m] = img[(f + 1) * kFragVec + frag_lane];
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // the 16 LDS reads
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        acc[t][m] = mfma_bf16(ah, bh[t][k], acc[t][m]);
-        acc[t][m] = mfma_bf16(al, bh[t][k], acc[t][m]);
-        if constexpr (F32IN) acc[t][m] = mfma_bf16(ah, bl[t][k], acc[t][m]);
+        acc[t][m] = mfma_bf16(ah[m], bh[t][k], acc[t][m]);
+        acc[t][m] = mfma_bf16(al[m], bh[t][k], acc[t][m]);
+        if constexpr (F32IN) acc[t][m] = mfma_bf16(ah[m], bl[t][k], acc[t][m]);
       }
-    }
+    __builtin_amdgcn_sched_group_barrier(0x008, F32IN ? 48 : 32, 0);  // then the step's MFMAs
+  }
 }
 
 // Pass 1: rotation panel, norms, search and pack; prod: residual norm partials.
