@@ -19,7 +19,10 @@ size_t fast128_rotation_words(int d);
 // the lane-chunk order of register-resident rotated coordinates (QJL
 // projection of the residual, dequantization).  f16: split into f16 hi/lo
 // parts instead of bf16 (operands multiplied with f16 decode tables).
-void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out, bool f16 = false);
+// natural_rows: output rows in natural order instead (each lane then holds
+// coordinates 16 m + 4 g .. + 3 of row tile m; the dequantize images).
+void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out, bool f16 = false,
+                                  bool natural_rows = false);
 
 // Image of the fused mixed-precision rotation (d = 128 split 64 + 64): pi_o and
 // pi_r are the parts' 64 x 64 rotations (row-major float64), perm the 128

@@ -762,11 +762,12 @@ __device__ __forceinline__ void load_keys(KeyRegs<CW> &r, int64_t t0, int64_t ke
 // ---------------------------------------------------------- dequantize --
 // x = nu Pi^T c[idx] (mse) and x = nu (Pi^T c[idx] + sqrt(pi/2)/d gamma S^T z)
 // (prod) as f16 MFMAs: the A operands are f16 hi/lo images of Pi^T and S^T
-// staged in LDS (output coordinates permuted as in the rotation, contraction
-// in lane-chunk order), the B operands the decoded codes (alpha c, two per
-// table read) and signs (+1/-1, eight per read) of 16 vectors.  Each lane
-// ends with 32 consecutive output coordinates of one vector and writes them
-// as eight 16-byte stores.  [tqnet] 实现步骤草图 (dequant: inverse rotation of
+// staged in LDS (output coordinates in natural order, contraction in
+// lane-chunk order), the B operands the decoded codes (alpha c, two per table
+// read) and signs (+1/-1, eight per read) of 16 vectors.  Lane (vector, g)
+// ends with coordinates 16 m + 4 g .. + 3 of row tiles m = 0..7 and writes
+// them as eight 16-byte stores: per instruction the four lanes of a vector
+// cover one contiguous 64-byte run.  [tqnet] 实现步骤草图 (dequant: inverse rotation of
 // the centroids); [ttakun] TurboQuant_prod (residual reconstruction).
 constexpr int kDqThreads = 512;
 constexpr int kDqCodeCopies = 16;  // u32 entries; the copy is the low lane bits
@@ -958,11 +959,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_dequant128(
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int64_t v = tile * 32 + 16 * t + col;
-      // coordinates 32 grp + 4 m + q of vector v are acc[t][m][q]
-      const uint32_t base = v < n ? (uint32_t)(v * D + 32 * grp) * 4 : kDropped;
+      // coordinates 16 m + 4 grp + q of vector v are acc[t][m][q] (the images'
+      // output rows are in natural order): each store instruction writes one
+      // contiguous 64-byte run per vector
+      const uint32_t base = v < n ? (uint32_t)(v * D + 4 * grp) * 4 : kDropped;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t][m]), ro, base + 16 * m, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t][m]), ro, base + 64 * m, 0, 0);
     }
   };
   int64_t tile = (int64_t)blockIdx.x * kWaves + wave;
@@ -2306,7 +2309,7 @@ static uint16_t host_f16(float f) {
   return u;
 }
 
-void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out, bool f16) {
+void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out, bool f16, bool natural_rows) {
   memset(out, 0, (size_t)kImageWords * 4);
   for (int m = 0; m < 8; ++m)
     for (int k = 0; k < 4; ++k)
@@ -2314,7 +2317,7 @@ void fast128_build_rotation_image(const double *mat, int k_order, uint32_t *out,
         const int f = (m * 4 + k) * 2 + part;
         for (int lane = 0; lane < 64; ++lane) {
           const int rho = lane & 15, grp = lane >> 4;
-          const int orow = 32 * (rho >> 2) + 4 * m + (rho & 3);
+          const int orow = natural_rows ? 16 * m + rho : 32 * (rho >> 2) + 4 * m + (rho & 3);
           for (int e = 0; e < 8; ++e) {
             const int kin = k_order == 0 ? 32 * k + 8 * grp + e : 32 * grp + 8 * k + e;
             const float v = (float)mat[(size_t)orow * D + kin];

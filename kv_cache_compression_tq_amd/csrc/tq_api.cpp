@@ -171,7 +171,7 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     if (fast) {
       tq::fast128_build_rotation_image(pi.data(), 0, &pi_img[g * rot_words]);
       transpose(d, pi, trans);
-      tq::fast128_build_rotation_image(trans.data(), 1, &dq_pi_img[g * rot_words], true);
+      tq::fast128_build_rotation_image(trans.data(), 1, &dq_pi_img[g * rot_words], true, true);
     }
     if (prod) {
       float *S = &s_all[g * dd], *ST = &st_all[g * dd], *MT = &mt_all[g * dd];
@@ -184,7 +184,7 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
       if (fast) {
         tq::fast128_build_rotation_image(m.data(), 1, &m_img[g * rot_words]);
         transpose(d, s, trans);
-        tq::fast128_build_rotation_image(trans.data(), 1, &dq_s_img[g * rot_words], true);
+        tq::fast128_build_rotation_image(trans.data(), 1, &dq_s_img[g * rot_words], true, true);
       }
     }
     if (tiled) {
