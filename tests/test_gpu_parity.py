@@ -262,6 +262,7 @@ LOGIT_CASES = [
     (128, 4, O.PROD, 2, 4, 4096),
     (128, 3, O.PROD, 3, 4, 1000),
     (128, 2, O.PROD, 1, 12, 777),     # n_keys % 4 != 0 and nq > 8
+    (128, 4, O.PROD, 2, 10, 1024),    # 8 heads in one launch, then 2 (16-byte logits stores)
     (128, 1, O.PROD, 2, 4, 512),
     (128, 4, O.MSE, 2, 4, 2048),
     (128, 3, O.MSE, 1, 1, 1200),
