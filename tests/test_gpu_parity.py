@@ -332,6 +332,63 @@ def test_quantize_kv_config_full_size_sampled():
         assert np.allclose(out["norms"][h].cpu().numpy()[sel], nu, rtol=1e-5)
 
 
+def test_quantize_kv_prod_full_size_sampled():
+    """The KV key tensor (8 heads x 32768 tokens x 128 bf16) under
+    TurboQuant_prod b=4 (3-bit mse + QJL), one codec group per head; sampled
+    vectors checked against the oracle (indices, signs, both norms)."""
+    k = workloads.kv_tensor(2)
+    codec = tq.Codec(128, 4, tq.TQ_PROD, seed=0, groups=8)
+    cd = O.make_codec(128, 4, O.PROD, 0, groups=8)
+    out = codec.quantize(k.cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    xf = k.float().numpy()
+    gi, oi, oy, gb, ob, op, orn = [], [], [], [], [], [], []
+    for h in range(8):
+        sel = np.sort(rng.choice(xf.shape[1], 256, replace=False))
+        st = torch.from_numpy(sel).cuda()
+        res = O.quantize_prod(cd, xf[h, sel].astype(np.float64), h)
+        gidx = _gpu_idx(codec, out["codes"][h, st], 3)
+        gi.append(gidx), oi.append(res["idx"]), oy.append(res["y"])
+        same = np.all(gidx == res["idx"], axis=1)
+        gb.append(_gpu_idx(codec, out["signs"][h, st], 1)[same])
+        ob.append(O.signs_to_bits(res["signs"])[same])
+        op.append(res["proj"][same])
+        orn.append(res["rnorms"][same])
+        assert np.allclose(out["norms"][h].cpu().numpy()[sel], res["norms"], rtol=1e-5)
+        assert np.allclose(out["rnorms"][h].cpu().numpy()[sel], res["rnorms"], rtol=1e-4, atol=1e-6)
+    check_indices(np.concatenate(gi), np.concatenate(oi), np.concatenate(oy), cd.boundaries, "kv prod b=4")
+    check_signs(np.concatenate(gb), np.concatenate(ob), np.concatenate(op), np.concatenate(orn), "kv prod b=4")
+
+
+@pytest.mark.parametrize("variant", [O.MSE, O.PROD])
+def test_dequantize_kv_config_full_size_sampled(variant):
+    """K and V of the KV workload (16 sets x 32768 tokens x 128 bf16, the
+    launch the bench times), b=4: the library's reconstruction of its own
+    codes against the oracle's reconstruction of the same codes, on sampled
+    rows of every set."""
+    x = torch.cat([workloads.kv_tensor(2), workloads.kv_tensor(3)], 0).contiguous()
+    codec = tq.Codec(128, 4, variant, seed=0, groups=8)
+    cd = O.make_codec(128, 4, variant, 0, groups=8)
+    stored = codec.quantize(x.cuda())
+    rec = codec.dequantize(stored)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    mb = cd.mse_bits
+    for s in range(x.shape[0]):
+        sel = np.sort(rng.choice(x.shape[1], 128, replace=False))
+        st = torch.from_numpy(sel).cuda()
+        idx = O.unpack(stored["codes"][s, st].cpu().numpy(), mb, 128)
+        nu = stored["norms"][s, st].cpu().numpy().astype(np.float64)
+        if variant == O.MSE:
+            ref = O.dequantize_mse(cd, idx, nu, s % 8)
+        else:
+            z = O.bits_to_signs(O.unpack(stored["signs"][s, st].cpu().numpy(), 1, 128))
+            ga = stored["rnorms"][s, st].cpu().numpy().astype(np.float64)
+            ref = O.dequantize_prod(cd, idx, z, nu, ga, s % 8)
+        check_rows(rec[s, st].cpu().numpy(), ref, f"set {s}")
+
+
 # --------------------------------------------------------- statistics -----
 @pytest.mark.parametrize("bits", [2, 4])
 def test_gpu_mse_distortion_matches_codebook(bits):
