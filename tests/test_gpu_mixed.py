@@ -180,3 +180,31 @@ def test_mixed_fused_logits(bits):
     lg = mc.logits(_cuda(q), stored).cpu().numpy()
     for s in range(n_sets):
         check_rows(lg[s], O.mixed_logits_plain(mx, q[s].astype(np.float64), parts[s], s % groups), f"logits set {s}")
+
+
+def test_mixed_decode_logits_full_size_sampled():
+    """Decode logits on a 2.5-bit mixed key cache at the decode shape (16 batch
+    x 8 KV heads x 131072 tokens, 4 query heads per KV head, the launch the
+    bench times): a synthetic packed cache (random code bytes, norms about 10),
+    sampled keys of 12 sets against the oracle's logits of the same codes."""
+    sets, T, d, qh = workloads.DEC_BATCH * workloads.DEC_KV_HEADS, workloads.DEC_TOKENS, 128, workloads.DEC_Q_PER_KV
+    rng = np.random.default_rng(7)
+    chans = np.stack([rng.permutation(d)[:64] for _ in range(workloads.DEC_KV_HEADS)])
+    mc = tq.MixedCodec(d, 2, tq.TQ_MSE, 0, chans, groups=workloads.DEC_KV_HEADS)
+    mx = O.make_mixed(d, 2, O.MSE, 0, chans, groups=workloads.DEC_KV_HEADS)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9)
+    cache = mc.empty_codes(sets, T)
+    for part in cache:
+        part["codes"].copy_(torch.randint(0, 256, part["codes"].shape, dtype=torch.uint8, device="cuda", generator=gen))
+        part["norms"].copy_(10.0 + torch.randn(part["norms"].shape, device="cuda", generator=gen))
+    q = torch.randn((sets, qh, d), device="cuda", generator=gen)
+    out = mc.logits(q, cache)
+    torch.cuda.synchronize()
+    for s in rng.choice(sets, 12, replace=False):
+        kt = torch.from_numpy(np.sort(rng.choice(T, 300, replace=False))).cuda()
+        parts = tuple(dict(idx=O.unpack(p["codes"][s, kt].cpu().numpy(), cd.mse_bits, 64),
+                           norms=p["norms"][s, kt].cpu().numpy().astype(np.float64))
+                      for cd, p in ((mx.outlier, cache[0]), (mx.regular, cache[1])))
+        ref = O.mixed_logits_plain(mx, q[s].cpu().numpy().astype(np.float64), parts, int(s) % workloads.DEC_KV_HEADS)
+        check_rows(out[s][:, kt].cpu().numpy(), ref, f"set {s}")
