@@ -93,8 +93,10 @@ int tq_quantize(tq_handle h, const void *x, int dtype, int64_t n_sets, int64_t n
  * quantized on its own as it arrives).  rows: device array of n_sets int64
  * physical row indices (a paged cache resolves its page table into them);
  * a row outside [0, cache_rows) is skipped, and two sets naming one row race.
- * Set s uses codec group s % groups.  The codes are those tq_quantize
- * produces for the same vector.  Pointer and NULL rules as tq_quantize.
+ * Set s uses codec group s % groups.  The codes follow the same definition
+ * as tq_quantize's (the contraction is plain fp32 here, split-bf16 MFMA
+ * there, so a coordinate within rounding of a boundary may take the
+ * neighbouring index).  Pointer and NULL rules as tq_quantize.
  * n_sets == 0 is a no-op.  Errors: TQ_EINVAL, TQ_EHIP. */
 int tq_append(tq_handle h, const void *x, int dtype, int64_t n_sets, const int64_t *rows, int64_t cache_rows,
               void *codes, void *signs, float *norms, float *rnorms, void *stream);
