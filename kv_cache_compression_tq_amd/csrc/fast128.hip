@@ -939,15 +939,21 @@ __global__ __launch_bounds__(kDqThreads, 1) void k_dequant128(
           const uint32_t addr = (x & 0x3FC0u) | sign_base;
           bs[t] = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)(addr + GQ::SIGN_OFF);
         }
+        // With at least 2 mse bits, S^T takes one f16 pass (the hi part).
+        // The QJL term is about sqrt(pi/2) gamma of the vector (gamma^2 is
+        // the mse distortion: gamma ~ 0.34 at 2 bits, 0.18 at 3), so the
+        // 2^-11 rounding of S gives each element an error of about 1e-4
+        // gamma of the row RMS (standard deviation), below a few 1e-4 at
+        // the extremes against the 1e-3 tolerance; with 0 or 1 mse bits
+        // (gamma 1 and 0.6) the lo part is added as well.
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const int f = (m * 4 + k) * 2;
           const u32x4 ah = img[SIMG + f * kFragVec + frag_lane];
-          const u32x4 al = img[SIMG + (f + 1) * kFragVec + frag_lane];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             as[t][m] = mfma_f16(ah, bs[t], as[t][m]);
-            as[t][m] = mfma_f16(al, bs[t], as[t][m]);
+            if constexpr (MB <= 1) as[t][m] = mfma_f16(img[SIMG + (f + 1) * kFragVec + frag_lane], bs[t], as[t][m]);
           }
         }
       }
