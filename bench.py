@@ -69,21 +69,32 @@ def _events(torch, n):
 
 
 def time_launches(torch, fn, steps, warmup, copies):
-    """Run fn(i) `warmup` then `steps` times; return (wall ms per step, mean
-    per-launch ms from events recorded on the launch stream)."""
+    """Run fn(i) `warmup` then `steps` times back to back; return (wall ms per
+    step from the host clock, mean ms per step from one pair of events
+    recorded on the launch stream around the timed steps, median ms per step
+    from a separate pass after the timed region with an event pair around
+    each step)."""
     for i in range(warmup):
         fn(i % copies)
     torch.cuda.synchronize()
-    ev = _events(torch, 2 * steps)
+    e0, e1 = _events(torch, 2)
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
+        fn(i % copies)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    mean = e0.elapsed_time(e1) / steps
+    n = min(steps, 10)
+    ev = _events(torch, 2 * n)
+    for i in range(n):
         ev[2 * i].record()
         fn(i % copies)
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
-    return wall, float(np.mean(per)), float(np.median(per))
+    per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]
+    return wall, mean, float(np.median(per))
 
 
 def quantize_phase(torch, tq, workloads, steps, warmup):
