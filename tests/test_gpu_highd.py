@@ -112,3 +112,41 @@ def test_tiled_ragged_dimensions(d, variant, bits):
             check_signs(gbits[same], O.signs_to_bits(res["signs"][same]), res["proj"][same],
                         res["rnorms"][same], f"d={d} set {s}")
             assert np.allclose(out["rnorms"][s].cpu().numpy()[same], res["rnorms"][same], rtol=1e-4, atol=1e-6)
+
+
+@pytest.mark.parametrize("d", [16, 64, 136])
+@pytest.mark.parametrize("variant,bits", [(O.MSE, 4), (O.PROD, 3)])
+def test_tiled_bf16_input(d, variant, bits):
+    """bfloat16 input through the tiled kernels (two split passes instead of
+    three): one chunk (d = 16, 64) and a partial second chunk (d = 136), two
+    sets and groups, a vector count that leaves a partial 128-vector tile;
+    every vector checked against the oracle on the bf16-rounded input."""
+    n_sets, n, groups = 2, 130, 2
+    xt = torch.from_numpy(np.random.default_rng(d + bits).standard_normal((n_sets, n, d)).astype(np.float32))
+    xt = xt.to(torch.bfloat16)
+    x64 = xt.float().numpy().astype(np.float64)
+    codec = tq.Codec(d, bits, variant, seed=6, groups=groups)
+    cd = O.make_codec(d, bits, variant, 6, groups=groups)
+    out = codec.quantize(xt.cuda())
+    torch.cuda.synchronize()
+    mb = bits if variant == O.MSE else bits - 1
+    gi, oi, oy, gb, ob, op, orn = [], [], [], [], [], [], []
+    for s in range(n_sets):
+        if variant == O.MSE:
+            idx, nu, y = O.quantize_mse(cd, x64[s], s % groups)
+            gi.append(codec.unpack(out["codes"][s], mb).cpu().numpy()), oi.append(idx), oy.append(y)
+            assert np.allclose(out["norms"][s].cpu().numpy(), nu, rtol=1e-5)
+        else:
+            res = O.quantize_prod(cd, x64[s], s % groups)
+            gidx = codec.unpack(out["codes"][s], mb).cpu().numpy()
+            gi.append(gidx), oi.append(res["idx"]), oy.append(res["y"])
+            same = np.all(gidx == res["idx"], axis=1)
+            gb.append(codec.unpack(out["signs"][s], 1).cpu().numpy()[same])
+            ob.append(O.signs_to_bits(res["signs"])[same])
+            op.append(res["proj"][same])
+            orn.append(res["rnorms"][same])
+            assert np.allclose(out["norms"][s].cpu().numpy(), res["norms"], rtol=1e-5)
+            assert np.allclose(out["rnorms"][s].cpu().numpy()[same], res["rnorms"][same], rtol=1e-4, atol=1e-6)
+    check_indices(np.concatenate(gi), np.concatenate(oi), np.concatenate(oy), cd.boundaries, f"d={d}")
+    if gb:
+        check_signs(np.concatenate(gb), np.concatenate(ob), np.concatenate(op), np.concatenate(orn), f"d={d}")
