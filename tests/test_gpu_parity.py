@@ -389,6 +389,33 @@ def test_dequantize_kv_config_full_size_sampled(variant):
         check_rows(rec[s, st].cpu().numpy(), ref, f"set {s}")
 
 
+def test_calls_on_a_side_stream_match_the_default_stream():
+    """The data calls enqueued on a side stream (default priority), right
+    after their input is produced on that stream and with no host
+    synchronisation in between, give the same bytes as on the default
+    stream: the library launches on the stream it is given."""
+    codec = tq.Codec(128, 4, tq.TQ_PROD, seed=3, groups=2)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    x_ref = torch.randn((2, 4096, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    q = torch.randn((2, 4, 128), device="cuda", generator=gen)
+    ref = codec.quantize(x_ref)
+    ref_dq = codec.dequantize(ref)
+    ref_lg = codec.logits(q, ref)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        x = (x_ref.float() * 1.0).to(torch.bfloat16)  # produced on the side stream
+        out = codec.quantize(x, stream=side)
+        dq = codec.dequantize(out, stream=side)
+        lg = codec.logits(q, out, stream=side)
+    side.synchronize()
+    for k in ("codes", "signs", "norms", "rnorms"):
+        assert torch.equal(out[k], ref[k]), k
+    assert torch.equal(dq, ref_dq)
+    assert torch.equal(lg, ref_lg)
+
+
 # --------------------------------------------------------- statistics -----
 @pytest.mark.parametrize("bits", [2, 4])
 def test_gpu_mse_distortion_matches_codebook(bits):
