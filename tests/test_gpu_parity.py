@@ -416,6 +416,47 @@ def test_calls_on_a_side_stream_match_the_default_stream():
     assert torch.equal(lg, ref_lg)
 
 
+def test_graph_capture_replays_match_eager():
+    """quantize and logits captured into one HIP graph (outputs allocated
+    before the capture) and replayed four times, with eager work and
+    synchronisations between the replays: every replay gives the eager bytes."""
+    codec = tq.Codec(128, 4, tq.TQ_PROD, seed=5, groups=2)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    x = torch.randn((2, 4096, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    q = torch.randn((2, 4, 128), device="cuda", generator=gen)
+    out = codec.empty_codes(2, 4096)
+    lg = torch.empty((2, 4, 4096), device="cuda")
+    codec.quantize(x, out=out)
+    codec.logits(q, out, out=lg)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items() if v is not None}
+    ref_lg = lg.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            codec.quantize(x, out=out)
+            codec.logits(q, out, out=lg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        codec.quantize(x, out=out)
+        codec.logits(q, out, out=lg)
+    for r in range(4):
+        for v in out.values():
+            if v is not None:
+                v.zero_()
+        lg.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(out[k], v), f"replay {r}: {k}"
+        assert torch.equal(lg, ref_lg), f"replay {r}: logits"
+
+
 # --------------------------------------------------------- statistics -----
 @pytest.mark.parametrize("bits", [2, 4])
 def test_gpu_mse_distortion_matches_codebook(bits):
