@@ -457,6 +457,72 @@ def test_graph_capture_replays_match_eager():
         assert torch.equal(lg, ref_lg), f"replay {r}: logits"
 
 
+def test_graph_capture_covers_the_other_data_calls():
+    """dequantize, the tiled TurboQuant_prod quantize (d = 200: it clears its
+    residual-norm accumulator with a kernel), attention with a caller
+    workspace, append, and the mixed-precision quantize and logits, captured
+    into one HIP graph with every output allocated before the capture and
+    replayed three times: every replay gives the eager bytes."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(14)
+    kc = tq.Codec(128, 4, tq.TQ_PROD, seed=1, groups=2)
+    vc = tq.Codec(128, 4, tq.TQ_MSE, seed=2, groups=2)
+    tc = tq.Codec(200, 3, tq.TQ_PROD, seed=3)
+    chans = np.stack([np.random.default_rng(g).permutation(128)[:64] for g in range(2)])
+    mc = tq.MixedCodec(128, 2, tq.TQ_MSE, 4, chans, groups=2)
+    xk = torch.randn((2, 2048, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    xv = torch.randn((2, 2048, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    xt = torch.randn((1, 3000, 200), device="cuda", generator=gen)
+    q = torch.randn((2, 4, 128), device="cuda", generator=gen)
+    xa = torch.randn((2, 128), device="cuda", generator=gen)
+    rows = torch.tensor([5, 2048 + 7], dtype=torch.int64, device="cuda")
+    keys, vals = kc.quantize(xk), vc.quantize(xv)
+    flat = {k: (None if v is None else v.view(2 * 2048, *v.shape[2:]).clone()) for k, v in keys.items()}
+    rec = torch.empty((2, 2048, 128), device="cuda")
+    tout = tc.empty_codes(1, 3000)
+    ws = torch.empty(max(kc.attention_workspace_bytes(vc, 4, 2, 2048), 1), dtype=torch.uint8, device="cuda")
+    att = torch.empty((2, 4, 128), device="cuda")
+    mout = mc.empty_codes(2, 2048)
+    mws = mc.workspace(2, 2048, 4)
+    mlg = torch.empty((2, 4, 2048), device="cuda")
+
+    def calls():
+        kc.dequantize(keys, out=rec)
+        tc.quantize(xt, out=tout)
+        kc.attention(q, keys, vc, vals, out=att, workspace=ws)
+        kc.append(xa, rows, flat)
+        mc.quantize(xk, out=mout, workspace=mws)
+        mc.logits(q, mout, out=mlg, workspace=mws)
+
+    cache = [v for v in flat.values() if v is not None]  # append writes only its rows
+    outs = [rec, att, mlg] + [v for v in tout.values() if v is not None] + cache + \
+        [v for p in mout for v in p.values() if v is not None]
+    calls()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for r in range(3):
+        for o, e in zip(outs, ref):
+            if any(o is c for c in cache):
+                o.copy_(e)
+                o[rows] = 0
+            else:
+                o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (o, e) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, e), f"replay {r}: output {i}"
+
+
 # --------------------------------------------------------- statistics -----
 @pytest.mark.parametrize("bits", [2, 4])
 def test_gpu_mse_distortion_matches_codebook(bits):
