@@ -314,6 +314,33 @@ def test_logits_decode_config_full_size_sampled():
         check_rows(out[s][:, kt].cpu().numpy(), ref, f"set {s}")
 
 
+@pytest.mark.parametrize("n_keys", [1 << 25, (1 << 25) + 64])
+def test_logits_at_the_fused_key_limit(n_keys):
+    """One set of 2^25 keys (the most the fused logits kernel addresses) and
+    2^25 + 64 (past it: the generic kernel takes over), prod b=4, 4 heads;
+    sampled keys, the last 64 among them, against the oracle."""
+    codec = tq.Codec(128, 4, tq.TQ_PROD, seed=0)
+    cd = O.make_codec(128, 4, O.PROD, 0)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(15)
+    keys = dict(codes=torch.randint(0, 256, (1, n_keys, codec.code_row), dtype=torch.uint8, device="cuda", generator=gen),
+                signs=torch.randint(0, 256, (1, n_keys, codec.sign_row), dtype=torch.uint8, device="cuda", generator=gen),
+                norms=10.0 + torch.randn((1, n_keys), device="cuda", generator=gen),
+                rnorms=torch.rand((1, n_keys), device="cuda", generator=gen) * 0.45 + 0.05)
+    q = torch.randn((1, 4, 128), device="cuda", generator=gen)
+    out = codec.logits(q, keys)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(16)
+    ks = np.unique(np.concatenate([rng.choice(n_keys, 300, replace=False), np.arange(n_keys - 64, n_keys)]))
+    kt = torch.from_numpy(ks).cuda()
+    sk = dict(idx=O.unpack(keys["codes"][0, kt].cpu().numpy(), 3, 128),
+              signs=O.bits_to_signs(O.unpack(keys["signs"][0, kt].cpu().numpy(), 1, 128)),
+              norms=keys["norms"][0, kt].cpu().numpy().astype(np.float64),
+              rnorms=keys["rnorms"][0, kt].cpu().numpy().astype(np.float64))
+    ref = O.logits_fast(cd, q[0].cpu().numpy().astype(np.float64), sk, 0)
+    check_rows(out[0][:, kt].cpu().numpy(), ref, f"n_keys {n_keys}")
+
+
 def test_quantize_kv_config_full_size_sampled():
     """8 KV heads x 32768 tokens x 128 bf16 with outlier channels, mse b=4,
     one codec group per head; sampled vectors checked against the oracle."""
