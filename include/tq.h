@@ -56,7 +56,7 @@ enum { TQ_OK = 0, TQ_EINVAL = -1, TQ_EUNSUPPORTED = -2, TQ_ENOMEM = -3, TQ_EHIP 
  * TQ_PROD, deterministic from `seed`.  Equivalent to tq_init_groups(..., 1).
  * [tqnet] 实现步骤草图 (precompute the Lloyd–Max centroids once, generate the
  * rotation by QR of a Gaussian matrix); [tqnet] 工程风险与应对 (pre-generate
- * and reuse the matrix).  Valid: 3 <= d <= 4096; mse: 1 <= b <= 8;
+ * and reuse the matrix).  Valid: 2 <= d <= 4096; mse: 1 <= b <= 8;
  * prod: 1 <= b <= 5 (b-1 mse bits, b = 1 is QJL only).  *out receives the
  * handle (unchanged on failure).  Errors: TQ_EINVAL, TQ_ENOMEM, TQ_EHIP. */
 int tq_init(int d, int b, int variant, uint64_t seed, tq_handle *out);
@@ -179,7 +179,7 @@ int tq_topk(tq_handle h, const float *q, int64_t nq, const void *codes, const vo
 typedef struct tq_mixed_codec *tq_mixed;
 
 /* out_channels: host array [groups][n_out] of distinct channels in [0, d)
- * per group.  Valid: 6 <= d <= 4096; 3 <= n_out <= d - 3; mse 1 <= b <= 7,
+ * per group.  Valid: 4 <= d <= 4096; 2 <= n_out <= d - 2; mse 1 <= b <= 7,
  * prod 1 <= b <= 4.  Errors: TQ_EINVAL, TQ_ENOMEM, TQ_EHIP. */
 int tq_mixed_init(int d, int b, int variant, uint64_t seed, int groups, int n_out, const int32_t *out_channels,
                   tq_mixed *out);

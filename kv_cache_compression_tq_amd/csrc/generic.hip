@@ -1,4 +1,4 @@
-// Dimension-generic kernels (any 3 <= d <= 4096): one workgroup per vector for
+// Dimension-generic kernels (any 2 <= d <= 4096): one workgroup per vector for
 // quantize/dequantize, one thread per key for logits.  Plain fp32 VALU
 // arithmetic.  They serve every shape the d = 128 MFMA kernels do not.
 #include <hip/hip_runtime.h>

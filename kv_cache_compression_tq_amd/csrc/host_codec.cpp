@@ -143,19 +143,6 @@ double beta_cf(double x, double a, double b) {
   return 1.0 / f;
 }
 
-double normal_quantile(double p) {
-  // bisection on the normal CDF (initial values only)
-  double lo = -40.0, hi = 40.0;
-  for (int i = 0; i < 200; ++i) {
-    const double mid = 0.5 * (lo + hi);
-    if (0.5 * std::erfc(-mid / std::sqrt(2.0)) < p)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  return 0.5 * (lo + hi);
-}
-
 struct CoordLaw {
   int d;
   double log_c;  // log of Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2))
@@ -175,6 +162,24 @@ struct CoordLaw {
     return std::exp(log_c - std::log((double)(d - 1)) + 0.5 * (d - 1) * std::log1p(-x * x));
   }
   double first_moment(double a, double b) const { return moment_term(a) - moment_term(b); }
+  // f(x) = C (1 - x^2)^((d-3)/2) inside (-1, 1)
+  double density(double x) const {
+    if (std::fabs(x) >= 1.0) return 0.0;
+    return std::exp(log_c + 0.5 * (d - 3) * std::log1p(-x * x));
+  }
+  // F^{-1}(p) by bisection on the increasing CDF (start values only)
+  double quantile(double p) const {
+    double lo = -1.0, hi = 1.0;
+    for (int i = 0; i < 200 && lo < hi; ++i) {
+      const double mid = 0.5 * (lo + hi);
+      if (mid <= lo || mid >= hi) break;
+      if (cdf(mid) < p)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return 0.5 * (lo + hi);
+  }
 };
 
 }  // namespace
@@ -189,35 +194,77 @@ double incomplete_beta(double x, double a, double b) {
 }
 
 Codebook lloyd_max(int d, int bits) {
-  if (d < 3 || bits < 1 || bits > 8) throw std::invalid_argument("lloyd_max: bad d or bits");
+  if (d < 2 || bits < 1 || bits > 8) throw std::invalid_argument("lloyd_max: bad d or bits");
   const int L = 1 << bits;
   CoordLaw law(d);
   std::vector<double> c(L), t(L - 1), edge(L + 1), mass(L), next(L);
-  for (int k = 0; k < L; ++k) c[k] = normal_quantile((k + 0.5) / L) / std::sqrt((double)d);
-  const double tol = 1e-12 / std::sqrt((double)d);
-  int it = 0;
-  auto cells = [&]() {
+  // start at the law's own quantiles: inside (-1, 1) for every d and L, and
+  // the answer itself for d = 3 (uniform law); symmetric by construction
+  for (int k = 0; k < L / 2; ++k) {
+    c[L / 2 + k] = law.quantile((L / 2 + k + 0.5) / L);
+    c[L / 2 - 1 - k] = -c[L / 2 + k];
+  }
+  // next = T(c): boundaries at the midpoints, centroids at the cell means
+  auto lloyd_map = [&]() {
     for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
     edge[0] = -1.0;
     edge[L] = 1.0;
     for (int k = 0; k + 1 < L; ++k) edge[k + 1] = t[k];
     for (int k = 0; k < L; ++k) mass[k] = law.cdf(edge[k + 1]) - law.cdf(edge[k]);
-  };
-  for (it = 1; it <= 100000; ++it) {
-    cells();
-    // centroid condition: conditional mean of each cell
     for (int k = 0; k < L; ++k) next[k] = law.first_moment(edge[k], edge[k + 1]) / mass[k];
+  };
+  const double sd = std::sqrt((double)d);
+  int it = 0;
+  // phase 1: Lloyd's iteration until its moves are below 1e-3 / sqrt(d)
+  for (int pass = 0; pass < 100000; ++pass) {
+    lloyd_map();
+    ++it;
     double step = 0.0;
     for (int k = 0; k < L; ++k) {
       const double sym = 0.5 * (next[k] - next[L - 1 - k]);  // f_d is even
       step = std::max(step, std::fabs(sym - c[k]));
       c[k] = sym;
     }
-    if (step < tol) break;
+    if (step < 1e-3 / sd) break;
   }
-  cells();
+  // phase 2: Newton on c = T(c).  c'_k depends on c only through its cell
+  // edges t_{k-1}, t_k: dc'_k/dt_k = f(t_k)(t_k - c'_k)/P_k and
+  // dc'_k/dt_{k-1} = f(t_{k-1})(c'_k - t_{k-1})/P_k, with t_k = (c_k + c_{k+1})/2,
+  // so (J_T - I) delta = c - T(c) is tridiagonal (Thomas algorithm).
+  std::vector<double> lo(L), up(L), sub(L), dia(L), sup(L), rhs(L), delta(L);
+  double prev = HUGE_VAL;
+  for (int pass = 0; pass < 100; ++pass) {
+    lloyd_map();
+    for (int k = 0; k < L; ++k) {
+      up[k] = k + 1 < L ? law.density(t[k]) * (t[k] - next[k]) / mass[k] : 0.0;
+      lo[k] = k > 0 ? law.density(t[k - 1]) * (next[k] - t[k - 1]) / mass[k] : 0.0;
+      sub[k] = 0.5 * lo[k];
+      dia[k] = 0.5 * (lo[k] + up[k]) - 1.0;
+      sup[k] = 0.5 * up[k];
+      rhs[k] = c[k] - next[k];
+    }
+    for (int k = 1; k < L; ++k) {  // forward elimination
+      const double w = sub[k] / dia[k - 1];
+      dia[k] -= w * sup[k - 1];
+      rhs[k] -= w * rhs[k - 1];
+    }
+    delta[L - 1] = rhs[L - 1] / dia[L - 1];
+    for (int k = L - 2; k >= 0; --k) delta[k] = (rhs[k] - sup[k] * delta[k + 1]) / dia[k];
+    double size = 0.0;
+    for (int k = 0; k < L; ++k) size = std::max(size, std::fabs(delta[k]));
+    if (!(size < prev)) break;  // at the rounding floor of T
+    for (int k = 0; k < L; ++k) next[k] = c[k] + delta[k];
+    for (int k = 0; k < L; ++k) c[k] = 0.5 * (next[k] - next[L - 1 - k]);
+    prev = size;
+    ++it;
+    if (size < 1e-13 / sd) break;
+  }
+  for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+  edge[0] = -1.0;
+  edge[L] = 1.0;
+  for (int k = 0; k + 1 < L; ++k) edge[k + 1] = t[k];
   double e = 0.0;
-  for (int k = 0; k < L; ++k) e += c[k] * c[k] * mass[k];
+  for (int k = 0; k < L; ++k) e += c[k] * c[k] * (law.cdf(edge[k + 1]) - law.cdf(edge[k]));
   Codebook cb;
   cb.centroids = c;
   cb.boundaries = t;

@@ -32,7 +32,8 @@ struct Codebook {
 };
 
 // Lloyd–Max quantizer for the post-rotation coordinate density
-// f_d(x) ∝ (1 - x^2)^((d-3)/2) on [-1, 1] with 2^bits levels.
+// f_d(x) ∝ (1 - x^2)^((d-3)/2) on [-1, 1] with 2^bits levels (d >= 2; d = 2
+// is the arcsine law).
 Codebook lloyd_max(int d, int bits);
 
 // Table for a branch-free boundary search over a normalised coordinate u in

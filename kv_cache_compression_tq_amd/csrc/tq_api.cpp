@@ -47,7 +47,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Validate (d, b, variant) and return the number of mse bits.
 int check_config(int d, int b, int variant, int groups, int *mse_bits) {
-  if (d < 3 || d > 4096) return fail(TQ_EINVAL, "d must be in [3, 4096]");
+  if (d < 2 || d > 4096) return fail(TQ_EINVAL, "d must be in [2, 4096]");
   if (groups < 1 || groups > 4096) return fail(TQ_EINVAL, "groups must be in [1, 4096]");
   if (variant == TQ_MSE) {
     if (b < 1 || b > 8) return fail(TQ_EINVAL, "mse needs 1 <= b <= 8");
@@ -575,6 +575,23 @@ int check_mixed(tq_mixed m) { return m ? TQ_OK : fail(TQ_EINVAL, "mixed handle i
 
 size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 
+// Bytes of `rows` vectors split into the two parts, each part's block
+// starting on a 256-byte boundary: [rows][n_out] then [rows][d - n_out].
+size_t mixed_split_bytes(const tq_mixed_codec *m, int64_t rows, size_t elem) {
+  return up256((size_t)rows * m->n_out * elem) + up256((size_t)rows * (m->d - m->n_out) * elem);
+}
+
+// Both parts' arrays, checked as the part codec's own calls check them, before
+// anything is enqueued.
+int check_mixed_ptrs(tq_mixed m, const void *const codes[2], const void *const signs[2], const float *const norms[2],
+                     const float *const rnorms[2], bool writing) {
+  for (int p = 0; p < 2; ++p) {
+    const int st = check_code_ptrs(m->parts[p], codes[p], signs[p], norms[p], rnorms[p], writing);
+    if (st) return fail(st, std::string(p == 0 ? "outlier part: " : "regular part: ") + g_last_error);
+  }
+  return TQ_OK;
+}
+
 }  // namespace
 
 int tq_mixed_init(int d, int b, int variant, uint64_t seed, int groups, int n_out, const int32_t *out_channels,
@@ -582,9 +599,9 @@ int tq_mixed_init(int d, int b, int variant, uint64_t seed, int groups, int n_ou
   g_last_error.clear();
   return guarded([&]() -> int {
     if (!out) return fail(TQ_EINVAL, "out is NULL");
-    if (d < 6 || d > 4096) return fail(TQ_EINVAL, "d must be in [6, 4096]");
+    if (d < 4 || d > 4096) return fail(TQ_EINVAL, "d must be in [4, 4096]");
     if (groups < 1 || groups > 4096) return fail(TQ_EINVAL, "groups must be in [1, 4096]");
-    if (n_out < 3 || n_out > d - 3) return fail(TQ_EINVAL, "n_out must be in [3, d - 3]");
+    if (n_out < 2 || n_out > d - 2) return fail(TQ_EINVAL, "n_out must be in [2, d - 2]");
     if (variant == TQ_MSE ? (b < 1 || b > 7) : variant == TQ_PROD ? (b < 1 || b > 4) : true)
       return fail(TQ_EINVAL, "mse needs 1 <= b <= 7, prod 1 <= b <= 4 (the outlier part takes b + 1 bits)");
     if (!out_channels) return fail(TQ_EINVAL, "out_channels is NULL");
@@ -674,8 +691,10 @@ int tq_mixed_workspace(tq_mixed m, int64_t n_sets, int64_t n, int64_t nq, size_t
   if (st) return st;
   if (!bytes) return fail(TQ_EINVAL, "bytes is NULL");
   if (n_sets < 0 || n < 0 || nq < 0) return fail(TQ_EINVAL, "sizes must be >= 0");
-  const size_t vec = up256((size_t)(n_sets * n) * m->d * sizeof(float)) + 256;  // gathered x or parts
-  const size_t lg = up256((size_t)(n_sets * nq) * m->d * sizeof(float)) + up256((size_t)(n_sets * nq * n) * sizeof(float));
+  // quantize / dequantize: the two parts' gathered inputs or reconstructions
+  const size_t vec = mixed_split_bytes(m, n_sets * n, sizeof(float));
+  // logits: the two parts' gathered queries, then the regular part's logits
+  const size_t lg = mixed_split_bytes(m, n_sets * nq, sizeof(float)) + up256((size_t)(n_sets * nq * n) * sizeof(float));
   *bytes = vec > lg ? vec : lg;
   return TQ_OK;
 }
@@ -690,6 +709,7 @@ int tq_mixed_quantize(tq_mixed m, const void *x, int dtype, int64_t n_sets, int6
   if (n_sets == 0 || n == 0) return TQ_OK;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_EINVAL, "dtype must be TQ_F32 or TQ_BF16");
   if (!x || ((uintptr_t)x & (dtype == TQ_F32 ? 3u : 1u))) return fail(TQ_EINVAL, "x NULL or misaligned");
+  if ((st = check_mixed_ptrs(m, codes, signs, norms, rnorms, true))) return st;
   size_t need = 0;
   tq_mixed_workspace(m, n_sets, n, 0, &need);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
@@ -723,6 +743,7 @@ int tq_mixed_dequantize(tq_mixed m, const void *const codes[2], const void *cons
   if ((st = check_rows(m->parts[0], n_sets, n))) return st;
   if (n_sets == 0 || n == 0) return TQ_OK;
   if (!x_out || ((uintptr_t)x_out & 3u)) return fail(TQ_EINVAL, "x_out NULL or misaligned");
+  if ((st = check_mixed_ptrs(m, codes, signs, norms, rnorms, false))) return st;
   size_t need = 0;
   tq_mixed_workspace(m, n_sets, n, 0, &need);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
@@ -749,6 +770,7 @@ int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const co
   if (n_sets == 0 || n_keys == 0) return TQ_OK;
   if (!q || ((uintptr_t)q & 3u)) return fail(TQ_EINVAL, "q NULL or misaligned");
   if (!out || ((uintptr_t)out & 3u)) return fail(TQ_EINVAL, "out NULL or misaligned");
+  if ((st = check_mixed_ptrs(m, codes, signs, norms, rnorms, false))) return st;
   size_t need = 0;
   tq_mixed_workspace(m, n_sets, n_keys, nq, &need);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
@@ -762,7 +784,7 @@ int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const co
   char *ws = (char *)workspace;
   float *qo = (float *)ws;
   float *qr = (float *)(ws + up256((size_t)(n_sets * nq) * m->n_out * 4));
-  float *lr = (float *)(ws + up256((size_t)(n_sets * nq) * m->d * 4));
+  float *lr = (float *)(ws + mixed_split_bytes(m, n_sets * nq, 4));
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = tq::launch_gather_parts(q, TQ_F32, n_sets * nq, nq, m->groups, m->d, m->n_out, m->perm, qo, qr, s);
   if (e != hipSuccess) return hip_fail(e, "gather launch");

@@ -169,32 +169,73 @@ class LloydMax:
     iterations: int
 
 
+def coord_quantile(p, d: int):
+    """F_d^{-1}(p): invert F_d = 1/2 + sgn(x)/2 I_{x^2}(1/2, (d-1)/2) with the
+    inverse regularised incomplete beta."""
+    p = np.asarray(p, dtype=np.float64)
+    x = np.sqrt(special.betaincinv(0.5, (d - 1) / 2.0, np.abs(2.0 * p - 1.0)))
+    return np.where(p > 0.5, x, -x)
+
+
+def _lloyd_step(c, d: int):
+    """One application of the two optimality conditions: boundaries at the
+    midpoints of neighbouring centroids, then each cell's conditional mean.
+    Returns (new centroids, boundaries, cell masses)."""
+    t = 0.5 * (c[:-1] + c[1:])
+    edges = np.concatenate(([-1.0], t, [1.0]))
+    mass = coord_cdf(edges[1:], d) - coord_cdf(edges[:-1], d)
+    return cell_first_moment(edges[:-1], edges[1:], d) / mass, t, mass
+
+
 def lloyd_max(d: int, bits: int, max_iter: int = 100000) -> LloydMax:
     """Lloyd–Max scalar quantizer for f_d with L = 2^bits levels ([ttakun]
-    "用Lloyd-Max算法预计算的最优标量量化器"; [tqnet] 预计算 Lloyd-Max 质心).
+    "用Lloyd-Max算法预计算的最优标量量化器"; [tqnet] 预计算 Lloyd-Max 质心): the
+    symmetric codebook c that is a fixed point of the Lloyd map T (boundaries
+    at midpoints, centroids at the conditional means of their cells).
 
-    Alternates the two optimality conditions: boundaries at the midpoints of
-    neighbouring centroids, centroids at the conditional means of their cells.
-    Starts from Gaussian quantiles scaled by 1/sqrt(d) (f_d approaches
-    N(0, 1/d)); keeps the codebook symmetric; stops when the largest centroid
-    move is below 1e-12/sqrt(d)."""
-    if d < 3:
-        raise ValueError("the coordinate law needs d >= 3")
+    Starts from the quantiles F_d^{-1}((k + 1/2)/L) of the law itself, which
+    lie inside (-1, 1) for every d >= 2 and every L (for d = 3, where f_d is
+    uniform, they are already the answer).  Lloyd's iteration c <- T(c) runs
+    until its largest move is below 1e-3/sqrt(d); near many levels it
+    contracts very slowly, so Newton's method on c = T(c) then takes it to
+    the fixed point: T's Jacobian is tridiagonal, since c'_k depends on c
+    only through the cell edges t_{k-1}, t_k, with
+        dc'_k/dt_k     = f(t_k) (t_k - c'_k) / P_k,
+        dc'_k/dt_{k-1} = f(t_{k-1}) (c'_k - t_{k-1}) / P_k,
+    and t_k = (c_k + c_{k+1})/2.  Newton stops when its step is below
+    1e-13/sqrt(d) or stops shrinking (the rounding floor of T).  d = 2 is
+    the arcsine law 1/(pi sqrt(1 - x^2)).  `iterations` counts both phases."""
+    if d < 2:
+        raise ValueError("the coordinate law needs d >= 2")
     L = 1 << bits
-    p = (np.arange(L) + 0.5) / L
-    c = special.ndtri(p) / math.sqrt(d)
-    tol = 1e-12 / math.sqrt(d)
+    c = coord_quantile((np.arange(L) + 0.5) / L, d)
     it = 0
     for it in range(1, max_iter + 1):
-        t = 0.5 * (c[:-1] + c[1:])
-        edges = np.concatenate(([-1.0], t, [1.0]))
-        mass = coord_cdf(edges[1:], d) - coord_cdf(edges[:-1], d)
-        m1 = cell_first_moment(edges[:-1], edges[1:], d)
-        new = m1 / mass
+        new = _lloyd_step(c, d)[0]
         new = 0.5 * (new - new[::-1])          # exact symmetry of f_d
         step = np.max(np.abs(new - c))
         c = new
-        if step < tol:
+        if step < 1e-3 / math.sqrt(d):
+            break
+    prev = np.inf
+    for _ in range(100):
+        tc, t, mass = _lloyd_step(c, d)
+        f = coord_density(t, d)
+        up = np.zeros(L)                       # dc'_k / dt_k
+        lo = np.zeros(L)                       # dc'_k / dt_{k-1}
+        up[:-1] = f * (t - tc[:-1]) / mass[:-1]
+        lo[1:] = f * (tc[1:] - t) / mass[1:]
+        # (J_T - I) delta = c - T(c), J_T tridiagonal
+        jac = np.diag(0.5 * (lo + up) - 1.0) + np.diag(0.5 * up[:-1], 1) + np.diag(0.5 * lo[1:], -1)
+        delta = np.linalg.solve(jac, c - tc)
+        size = float(np.max(np.abs(delta)))
+        if not size < prev:
+            break
+        c = c + delta
+        c = 0.5 * (c - c[::-1])
+        prev = size
+        it += 1
+        if size < 1e-13 / math.sqrt(d):
             break
     t = 0.5 * (c[:-1] + c[1:])
     edges = np.concatenate(([-1.0], t, [1.0]))
@@ -354,6 +395,33 @@ def quantize_prod(cd: Codec, x: np.ndarray, group: int = 0):
     proj = np.where(zero[..., None], 0.0, proj)
     signs = np.where(proj >= 0.0, 1, -1).astype(np.int8)
     return dict(idx=idx, signs=signs, norms=nu, rnorms=gamma, proj=proj, y=y)
+
+
+def prod_signs_from_indices(cd: Codec, x: np.ndarray, idx, group: int = 0):
+    """The QJL stage of TurboQuant_prod for (b-1)-bit indices that are given
+    rather than searched ([ttakun] TurboQuant_prod: the 1-bit QJL step acts on
+    the residual of the mse stage; [admirer] 第二步: the residual is reduced to
+    the signs of a random projection, with its norm kept beside them).
+
+    With u = x/||x|| and the reconstruction u_hat = Pi^T c[idx] that the given
+    indices define (u_hat = 0 when the codec has no mse bits), the residual is
+    r = u - u_hat, gamma = ||r|| and z_i = +1 where (S r)_i >= 0, else -1.
+    A zero vector gets gamma = 0, S r = 0 and all signs +1.  The indices need
+    not be the nearest ones: this scores any codes a quantizer produced.
+    x: [n, d]; idx: [n, d] (ignored without mse bits).
+    Returns dict(signs int8 +1/-1, rnorms, proj = S r), each over x's rows."""
+    x = np.asarray(x, dtype=np.float64).reshape(-1, cd.d)
+    norm = np.sqrt(np.sum(x * x, axis=1))
+    live = norm > 0.0
+    unit = np.divide(x, norm[:, None], out=np.zeros_like(x), where=live[:, None])
+    if cd.mse_bits > 0:
+        recon = cd.centroids[np.asarray(idx, dtype=np.int64).reshape(x.shape)] @ cd.pis[group]
+    else:
+        recon = np.zeros_like(unit)
+    resid = np.where(live[:, None], unit - recon, 0.0)
+    gamma = np.sqrt(np.sum(resid * resid, axis=1))
+    proj = resid @ cd.ss[group].T
+    return dict(signs=np.where(proj >= 0.0, 1, -1).astype(np.int8), rnorms=gamma, proj=proj)
 
 
 def dequantize_prod(cd: Codec, idx, signs, norms, rnorms, group: int = 0) -> np.ndarray:

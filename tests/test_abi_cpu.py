@@ -34,7 +34,7 @@ def test_strerror_and_validation_without_device():
     assert L.tq_strerror(0) == b"ok"
     assert L.tq_strerror(-1) == b"invalid argument"
     h = ctypes.c_void_p()
-    for args in [(2, 2, 0), (5000, 2, 0), (128, 0, 0), (128, 9, 0), (128, 6, 1), (128, 2, 7)]:
+    for args in [(1, 2, 0), (5000, 2, 0), (128, 0, 0), (128, 9, 0), (128, 6, 1), (128, 2, 7)]:
         assert L.tq_init(*args, 0, ctypes.byref(h)) == tq.TQ_EINVAL
         assert L.tq_last_error() != b""
     assert L.tq_init_groups(128, 2, 0, 0, 0, ctypes.byref(h)) == tq.TQ_EINVAL
@@ -50,7 +50,8 @@ def test_strerror_and_validation_without_device():
     ch = (ctypes.c_int32 * 4)(0, 1, 1, 2)  # a repeated channel
     assert L.tq_mixed_init(128, 2, 0, 0, 1, 4, ch, ctypes.byref(m)) == tq.TQ_EINVAL
     assert L.tq_mixed_init(128, 8, 0, 0, 1, 4, ch, ctypes.byref(m)) == tq.TQ_EINVAL
-    assert L.tq_mixed_init(128, 2, 0, 0, 1, 2, ch, ctypes.byref(m)) == tq.TQ_EINVAL
+    assert L.tq_mixed_init(128, 2, 0, 0, 1, 1, ch, ctypes.byref(m)) == tq.TQ_EINVAL   # n_out < 2
+    assert L.tq_mixed_init(3, 2, 0, 0, 1, 2, ch, ctypes.byref(m)) == tq.TQ_EINVAL     # d < 4
     assert L.tq_mixed_destroy(None) == tq.TQ_OK
     assert L.tq_destroy(None) == tq.TQ_OK
 
@@ -71,3 +72,25 @@ def test_host_tables_large_d_lloyd_max_converges():
     got = tq.host_tables(1536, 4, O.MSE, seed=0)
     lm = O.lloyd_max(1536, 4)
     assert np.allclose(got["centroids"], lm.centroids, rtol=1e-6)
+
+
+def _ulps(a, b):
+    a = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    b = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return int(np.abs(a - b).max()) if a.size else 0
+
+
+@pytest.mark.parametrize("d", [2, 3, 4, 5, 16, 128, 200])
+def test_host_codebooks_equal_the_oracle_codebooks(d):
+    """The host's Lloyd–Max tables (C++) against the oracle's (NumPy/SciPy),
+    both rounded to float32: equal for 1..6 bits.  With 7 and 8 bits the
+    fixed point is ill-conditioned (the map contracts at about 1 - 1e-4 per
+    step, so the ~1e-14 rounding of its cell masses moves the fixed point by
+    ~1e-10..1e-8): one float32 step apart at most."""
+    for bits in range(1, 9):
+        got = tq.host_tables(d, bits, tq.TQ_MSE, seed=0)
+        lm = O.lloyd_max(d, bits)
+        c32, t32 = lm.centroids.astype(np.float32), lm.boundaries.astype(np.float32)
+        limit = 0 if bits <= 6 else 1
+        assert _ulps(got["centroids"], c32) <= limit, (d, bits)
+        assert _ulps(got["boundaries"], t32) <= limit, (d, bits)

@@ -133,3 +133,67 @@ def test_nearest_index_equals_brute_force_argmin():
     c = cd.centroids64
     far = np.min(np.abs(y[:, None] - cd.boundaries64[None, :]), axis=1) > 1e-8
     assert np.array_equal(got[far], np.argmin(np.abs(y[far, None] - c[None, :]), axis=1))
+
+
+@pytest.mark.parametrize("bits", range(1, 9))
+def test_three_dimensional_law_is_uniform_and_its_quantizer_is_the_uniform_one(bits):
+    """At d = 3 the coordinate of a uniform point on the sphere is uniform on
+    [-1, 1] (Archimedes' hat-box theorem: f_3 = 1/2), whose Lloyd–Max
+    quantizer is the uniform one: c_k = (2k + 1)/L - 1, t_k = 2(k + 1)/L - 1,
+    distortion d (2/L)^2 / 12 = 4^-b."""
+    assert np.allclose(O.coord_density(np.linspace(-0.99, 0.99, 7), 3), 0.5, rtol=1e-14)
+    lm = O.lloyd_max(3, bits)
+    L = 1 << bits
+    k = np.arange(L)
+    assert np.allclose(lm.centroids, (2 * k + 1) / L - 1.0, atol=1e-14)
+    assert np.allclose(lm.boundaries, 2.0 * (k[:-1] + 1) / L - 1.0, atol=1e-14)
+    assert lm.distortion == pytest.approx(4.0 ** -bits, rel=1e-12)
+
+
+def test_two_dimensional_law_is_the_arcsine_law():
+    """d = 2: a uniform point on the circle has coordinates cos(theta), whose
+    law is the arcsine law 1/(pi sqrt(1 - x^2)) with CDF 1/2 + asin(x)/pi; the
+    1-bit centroid is E|cos theta| = 2/pi and its distortion 1 - 8/pi^2."""
+    x = np.linspace(-0.999, 0.999, 41)
+    assert np.allclose(O.coord_density(x, 2), 1.0 / (math.pi * np.sqrt(1.0 - x * x)), rtol=1e-13)
+    assert np.allclose(O.coord_cdf(x, 2), 0.5 + np.arcsin(x) / math.pi, atol=1e-14)
+    lm = O.lloyd_max(2, 1)
+    assert lm.centroids[1] == pytest.approx(2.0 / math.pi, rel=1e-14)
+    assert lm.distortion == pytest.approx(1.0 - 8.0 / math.pi ** 2, rel=1e-12)
+    # the 2-bit quantizer by brute force: minimise the distortion of a
+    # symmetric (-b, -a, a, b) codebook over a fine grid (boundaries at the
+    # midpoints), the mean-square error integrated in closed form
+    F = lambda t: 0.5 + np.arcsin(t) / math.pi                       # noqa: E731
+    M1 = lambda t: -np.sqrt(1.0 - t * t) / math.pi                   # antiderivative of x f(x)
+    M2 = lambda t: (np.arcsin(t) - t * np.sqrt(1.0 - t * t)) / (2 * math.pi)  # of x^2 f(x)
+
+    def mse(a, b):
+        m = 0.5 * (a + b)
+        inner = (M2(m) - M2(0.0)) - 2 * a * (M1(m) - M1(0.0)) + a * a * (F(m) - F(0.0))
+        outer = (M2(1.0) - M2(m)) - 2 * b * (M1(1.0) - M1(m)) + b * b * (F(1.0) - F(m))
+        return 2 * 2 * (inner + outer)                               # both halves, d = 2
+    grid = np.linspace(0.01, 0.99, 981)
+    A, B = np.meshgrid(grid, grid, indexing="ij")
+    ok = A < B
+    vals = np.where(ok, mse(A, B), np.inf)
+    i, j = np.unravel_index(np.argmin(vals), vals.shape)
+    lm2 = O.lloyd_max(2, 2)
+    assert lm2.centroids[2] == pytest.approx(grid[i], abs=2e-3)
+    assert lm2.centroids[3] == pytest.approx(grid[j], abs=2e-3)
+    assert lm2.distortion <= vals[i, j] + 1e-12
+
+
+@pytest.mark.parametrize("d,bits", [(2, 8), (4, 8), (128, 7), (128, 8), (1536, 8)])
+def test_many_level_codebooks_are_fixed_points(d, bits):
+    """With 128 or 256 levels the returned codebook satisfies both Lloyd–Max
+    conditions: applying the map once more moves no centroid by more than
+    1e-10, centroids ascend, and the distortion keeps the 4^-b scaling."""
+    lm = O.lloyd_max(d, bits)
+    c = lm.centroids
+    t = 0.5 * (c[:-1] + c[1:])
+    edges = np.concatenate(([-1.0], t, [1.0]))
+    mass = O.coord_cdf(edges[1:], d) - O.coord_cdf(edges[:-1], d)
+    again = O.cell_first_moment(edges[:-1], edges[1:], d) / mass
+    assert np.max(np.abs(again - c)) < 1e-10
+    assert np.all(np.diff(c) > 0)
+    assert 0.3 < lm.distortion * 4 ** bits < 2.72

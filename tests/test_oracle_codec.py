@@ -196,3 +196,83 @@ def test_eight_bit_mse_logits_are_nearly_exact(parity_x, parity_q):
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert rel < 3.0 * math.sqrt(cd.distortion)
     assert cd.distortion < 1e-4
+
+
+# ------------------------------------------- QJL stage from given indices ---
+def _hand_codec(mse_bits):
+    """d = 4 codec with hand-chosen tables.  Pi is the cyclic shift
+    y_i = u_{(i+1) % 4} (not symmetric, so a transposed Pi changes the
+    answer); S is not symmetric either; the centroids are dyadic, so every
+    step below is exact in float64."""
+    pi = np.zeros((4, 4))
+    for i in range(4):
+        pi[i, (i + 1) % 4] = 1.0
+    s = np.array([[1.0, 0.0, 0.0, 0.0],
+                  [0.0, 1.0, 0.0, 0.0],
+                  [0.0, 0.0, -1.0, 3.0],
+                  [0.0, 1.0, -1.0, 0.0]])
+    cd = O.Codec(4, mse_bits + 1, O.PROD, 0, 1, mse_bits, pis=[pi], ss=[s])
+    if mse_bits:
+        cd.centroids = np.array([-0.75, -0.25, 0.25, 0.75])
+    return cd
+
+
+def test_prod_signs_from_indices_by_hand():
+    cd = _hand_codec(2)
+    # u = (1/2, 1/2, 1/2, 1/2) for the first two rows; the third is zero
+    x = np.array([[2.0, 2.0, 2.0, 2.0], [1e-3, 1e-3, 1e-3, 1e-3], [0.0, 0.0, 0.0, 0.0]])
+    idx = np.array([[3, 1, 2, 0], [3, 1, 2, 0], [0, 3, 0, 3]])
+    out = O.prod_signs_from_indices(cd, x, idx)
+    # c[idx] = (3/4, -1/4, 1/4, -3/4); Pi^T c[idx] = (-3/4, 3/4, -1/4, 1/4)
+    # r = u - Pi^T c[idx] = (5/4, -1/4, 3/4, 1/4), ||r||^2 = 9/4
+    # S r = (5/4, -1/4, -3/4 + 3/4 = 0, -1/4 - 3/4 = -1); sign(0) = +1
+    for row in (0, 1):
+        assert out["rnorms"][row] == 1.5
+        assert out["proj"][row].tolist() == [1.25, -0.25, 0.0, -1.0]
+        assert out["signs"][row].tolist() == [1, -1, 1, -1]
+    assert out["rnorms"][2] == 0.0
+    assert out["proj"][2].tolist() == [0.0] * 4 and out["signs"][2].tolist() == [1] * 4
+
+
+def test_prod_signs_from_indices_without_mse_bits_by_hand():
+    # b = 1: r = u, gamma = 1, signs of S u
+    cd = _hand_codec(0)
+    out = O.prod_signs_from_indices(cd, np.array([[3.0, 3.0, 3.0, 3.0]]), None)
+    assert out["rnorms"][0] == 1.0
+    assert out["proj"][0].tolist() == [0.5, 0.5, 1.0, 0.0]
+    assert out["signs"][0].tolist() == [1, 1, 1, 1]
+
+
+@pytest.mark.parametrize("d,bits", [(128, 4), (128, 2), (200, 3), (64, 1)])
+def test_prod_signs_from_own_indices_equal_quantize_prod(d, bits):
+    cd = O.make_codec(d, bits, O.PROD, 6)
+    x = np.random.default_rng(d + bits).standard_normal((300, d))
+    x[7] = 0.0
+    res = O.quantize_prod(cd, x)
+    got = O.prod_signs_from_indices(cd, x, res["idx"])
+    assert np.array_equal(got["signs"], res["signs"])
+    assert np.allclose(got["rnorms"], res["rnorms"], rtol=1e-13, atol=0)
+    assert np.allclose(got["proj"], res["proj"], rtol=0, atol=1e-12)
+
+
+def test_prod_residual_norm_moves_by_the_flipped_coordinate():
+    """Moving index j one step changes the rotated-domain residual only in
+    coordinate j: ||r'||^2 = ||r||^2 - (y_j - c[i])^2 + (y_j - c[i'])^2,
+    with y = Pi u from the quantizer (Pi orthogonal)."""
+    cd = O.make_codec(128, 3, O.PROD, 8)
+    x = np.random.default_rng(3).standard_normal((64, 128))
+    res = O.quantize_prod(cd, x)
+    rng = np.random.default_rng(4)
+    j = rng.integers(0, 128, 64)
+    rows = np.arange(64)
+    idx2 = res["idx"].copy()
+    up = idx2[rows, j] < 3
+    idx2[rows, j] = np.where(up, idx2[rows, j] + 1, idx2[rows, j] - 1)
+    got = O.prod_signs_from_indices(cd, x, idx2)
+    y = res["y"][rows, j]
+    c = cd.centroids
+    want = res["rnorms"] ** 2 - (y - c[res["idx"][rows, j]]) ** 2 + (y - c[idx2[rows, j]]) ** 2
+    assert np.allclose(got["rnorms"] ** 2, want, rtol=1e-12)
+    # and the projection moves by -(c[i'] - c[i]) S Pi^T e_j
+    delta = (c[idx2[rows, j]] - c[res["idx"][rows, j]])[:, None] * (cd.pis[0][j] @ cd.ss[0].T)
+    assert np.allclose(got["proj"], res["proj"] - delta, atol=1e-12)

@@ -120,3 +120,14 @@ def test_rotated_coordinates_follow_the_pages_density():
     expect = (O.coord_cdf(edges[1:], d) - O.coord_cdf(edges[:-1], d)) * y.size
     mask = expect > 50
     assert np.max(np.abs(hist[mask] - expect[mask]) / np.sqrt(expect[mask])) < 6.0
+
+
+@pytest.mark.parametrize("d", [2, 3])
+def test_rotated_low_dimensional_coordinates_follow_the_law(d):
+    """y = Pi x/||x|| at d = 2 (arcsine law) and d = 3 (uniform law): one
+    coordinate of 5000 seeded Gaussian vectors against F_d."""
+    x = np.random.default_rng(40 + d).standard_normal((5000, d))
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    y = u @ O.rotation(d, 3, 0).T
+    for j in range(d):
+        assert stats.kstest(y[:, j], lambda t: O.coord_cdf(t, d)).pvalue > 1e-3
