@@ -591,6 +591,13 @@ def test_gpu_mse_distortion_matches_codebook(bits):
     assert abs(err.mean() - cd.distortion) < 4 * err.std() / math.sqrt(err.size)
 
 
+def _logits_all_queries(codec, q, keys):
+    """Logits of every query of q ([nq, d], any nq) against one set of keys,
+    in calls of at most 64 queries."""
+    parts = [codec.logits(_cuda(q[i:i + 64])[None], keys)[0] for i in range(0, q.shape[0], 64)]
+    return torch.cat(parts, 0).cpu().numpy().astype(np.float64)
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_gpu_mse_inner_product_shrinkage(bits):
     """The parity workload (4096 vectors, all 256 queries): the least-squares
@@ -602,7 +609,7 @@ def test_gpu_mse_inner_product_shrinkage(bits):
     codec = tq.Codec(128, bits, tq.TQ_MSE, seed=0)
     cd = O.make_codec(128, bits, O.MSE, 0)
     keys = codec.quantize(_cuda(x))
-    lg = codec.logits(_cuda(q)[None], keys)[0].cpu().numpy().astype(np.float64).ravel()
+    lg = _logits_all_queries(codec, q, keys).ravel()
     exact = (q.astype(np.float64) @ x.astype(np.float64).T).ravel()
     slope = float(lg @ exact / (exact @ exact))
     assert slope == pytest.approx(1.0 - cd.distortion, rel=0.015)
@@ -617,7 +624,7 @@ def test_gpu_prod_inner_products_unbiased_over_vectors(bits):
     q = workloads.parity_queries()
     codec = tq.Codec(128, bits, tq.TQ_PROD, seed=0)
     keys = codec.quantize(_cuda(x))
-    lg = codec.logits(_cuda(q)[None], keys)[0].cpu().numpy().astype(np.float64)
+    lg = _logits_all_queries(codec, q, keys)
     err = lg - q.astype(np.float64) @ x.astype(np.float64).T
     # per-query mean error over 4096 keys, compared with its own spread
     z = err.mean(axis=1) / (err.std(axis=1) / math.sqrt(x.shape[0]))
