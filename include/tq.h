@@ -23,7 +23,11 @@
  *   - The handle owns its device tables (rotation, projection, codebook),
  *     allocated on the HIP device current at tq_init and freed by tq_destroy.
  *     A handle is immutable after init: concurrent calls on it are safe.
- *   - Identical inputs give bitwise identical outputs (no atomics).
+ *   - Identical inputs give bitwise identical outputs, with one exception:
+ *     the d = 128 attention kernel (tq_attention, tq_attention_static) hands
+ *     key blocks to its waves from a counter as they finish, so the order of
+ *     its float32 softmax sums varies from run to run and its outputs agree
+ *     to float32 rounding (about 1e-7 relative), not bit for bit.
  *
  * Stored layout (the pages leave it open)
  *   - codes : [n_sets][n][code_row_bytes] uint8.  Coordinate j's index
@@ -148,6 +152,25 @@ int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const v
  * Host only; validates as tq_attention does.  Errors: TQ_EINVAL. */
 int tq_attention_workspace(tq_handle hk, tq_handle hv, int64_t nq, int64_t n_sets, int64_t n_keys,
                            size_t *bytes);
+
+/* tq_attention for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, with the workspace taken from a fixed device
+ * array inside the library instead of an argument.  That array holds
+ * TQ_STATIC_SCRATCH_BYTES (16 MiB) on every GPU the library runs on, from the
+ * library's load until the process ends; its address on a device is looked
+ * up at tq_init on that device (or at this call's first use there).  The call
+ * allocates nothing.  A shape whose tq_attention_workspace size exceeds the
+ * array fails with TQ_EINVAL (the decode shape, 128 sets x 4 heads x 131072
+ * keys at d = 128, needs 0.5 MiB).  All calls on one GPU share its array:
+ * calls that overlap in time on that GPU (two streams, two threads) race and
+ * give undefined results; calls ordered on one stream are safe.  Arguments,
+ * other rules and errors as tq_attention. */
+#define TQ_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int tq_attention_static(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const void *k_codes,
+                        const void *k_signs, const float *k_norms, const float *k_rnorms, const void *v_codes,
+                        const void *v_signs, const float *v_norms, const float *v_rnorms, int64_t n_sets,
+                        int64_t n_keys, float scale, float *out, void *stream);
 
 /* Maximum inner product search over one set of n_keys packed keys (group
  * 0): for each query q[i] (float32 [nq][d]), the k keys with the largest

@@ -35,6 +35,8 @@ _SIGS = {
     "tq_attention": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float, _P, _P,
                             ctypes.c_size_t, _P]),
     "tq_attention_workspace": (_INT, [_P, _P, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "tq_attention_static": (_INT, [_P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, ctypes.c_float,
+                                   _P, _P]),
     "tq_topk_workspace": (_INT, [_P, _I64, _I64, _INT, ctypes.POINTER(ctypes.c_size_t)]),
     "tq_topk": (_INT, [_P, _P, _I64, _P, _P, _P, _P, _I64, _INT, _P, _P, _P, ctypes.c_size_t, _P]),
     "tq_mixed_init": (_INT, [_INT, _INT, _INT, ctypes.c_uint64, _INT, _INT, _P, ctypes.POINTER(_P)]),
@@ -261,6 +263,33 @@ class Codec:
                                   _ptr(values.get("codes")), _ptr(values.get("signs")), _ptr(values["norms"]),
                                   _ptr(values.get("rnorms")), n_sets, n_keys, float(scale), _ptr(out),
                                   _ptr(workspace), workspace.numel(), _stream(stream)), "tq_attention")
+        return out
+
+    def attention_static(self, q, keys, values_codec: "Codec", values, scale=None, out=None, stream=None):
+        """As attention, through tq_attention_static: the workspace is the
+        library's fixed device array, so nothing is allocated when `out` is
+        given (calls that overlap in time on one GPU race)."""
+        import math
+
+        import torch
+
+        if q.dim() == 2:
+            q = q.unsqueeze(0)
+        if q.dtype != torch.float32 or not q.is_contiguous():
+            raise TypeError("q must be contiguous float32")
+        n_sets, n_keys = keys["norms"].shape
+        nq = q.shape[1]
+        if q.shape[0] != n_sets or q.shape[2] != self.d or values["norms"].shape != keys["norms"].shape:
+            raise ValueError("q, keys and values do not match")
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.d)
+        if out is None:
+            out = torch.empty((n_sets, nq, self.d), dtype=torch.float32, device=q.device)
+        _check(lib().tq_attention_static(self._h, values_codec.handle, _ptr(q), nq, _ptr(keys.get("codes")),
+                                         _ptr(keys.get("signs")), _ptr(keys["norms"]), _ptr(keys.get("rnorms")),
+                                         _ptr(values.get("codes")), _ptr(values.get("signs")), _ptr(values["norms"]),
+                                         _ptr(values.get("rnorms")), n_sets, n_keys, float(scale), _ptr(out),
+                                         _stream(stream)), "tq_attention_static")
         return out
 
     def topk(self, q, keys, k: int, workspace=None, stream=None):

@@ -43,6 +43,14 @@ constexpr float kQjlScale = 1.2533141373155003f;  // sqrt(pi/2)
 // (255 cells; wider tables send a shape to the generic kernels).
 constexpr int kCellRadius = 127;
 
+// The library's fixed device workspace (scratch.hip), for the entry points
+// that allocate nothing.  static_scratch_setup(device) looks up the array's
+// address on `device`, which must be current; it is done once per device.
+// static_scratch(device) returns that address (nullptr before the set-up).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch_setup(int device);
+void *static_scratch(int device);
+
 hipError_t launch_quant_generic(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
                                 int64_t n, uint8_t *codes, uint8_t *signs, float *norms,
                                 float *rnorms, hipStream_t st);

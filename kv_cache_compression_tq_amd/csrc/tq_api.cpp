@@ -283,6 +283,9 @@ int make_codec(int d, int b, int variant, uint64_t seed, int groups, tq_handle *
     delete h;
     return hip_fail(e, "hipMemcpy of the codec tables");
   }
+  // address of the fixed workspace on this device (for tq_attention_static);
+  // a failure here is reported by that call, which retries the lookup
+  (void)tq::static_scratch_setup(h->device);
   if (mse_bits > 0 && mse_bits <= 4) {
     for (int k = 0; k < L / 2; ++k) h->dev.pos_cent[k] = h->h_c[L / 2 + k];
     for (int k = 0; k + 1 < L / 2; ++k) h->dev.pos_bnd[k] = h->h_t[L / 2 + k];
@@ -520,6 +523,30 @@ int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const v
       (const uint8_t *)v_codes, (const uint8_t *)v_signs, v_norms, v_rnorms, n_sets, n_keys, scale,
       (float *)(ws + p.logits_off), (float *)(ws + p.part_off), out, (hipStream_t)stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "attention launch");
+}
+
+int tq_attention_static(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const void *k_codes,
+                        const void *k_signs, const float *k_norms, const float *k_rnorms, const void *v_codes,
+                        const void *v_signs, const float *v_norms, const float *v_rnorms, int64_t n_sets,
+                        int64_t n_keys, float scale, float *out, void *stream) {
+  int st = check_attention(hk, hv, nq, n_sets, n_keys);
+  if (st) return st;
+  if (n_sets == 0) return TQ_OK;
+  const size_t need = plan_attention(hk, hv, nq, n_sets, n_keys).bytes;
+  if (need > tq::kStaticScratchBytes)
+    return fail(TQ_EINVAL, "this shape needs " + std::to_string(need) + " bytes of workspace, more than the " +
+                               std::to_string(tq::kStaticScratchBytes) +
+                               "-byte static workspace; call tq_attention with a caller workspace");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  void *ws = tq::static_scratch(dev);
+  if (!ws) {
+    if ((e = tq::static_scratch_setup(dev)) != hipSuccess) return hip_fail(e, "static workspace address");
+    ws = tq::static_scratch(dev);
+  }
+  return tq_attention(hk, hv, q, nq, k_codes, k_signs, k_norms, k_rnorms, v_codes, v_signs, v_norms, v_rnorms,
+                      n_sets, n_keys, scale, out, ws, tq::kStaticScratchBytes, stream);
 }
 
 // ------------------------------------------------------------------ top-k --
