@@ -39,6 +39,8 @@ def _parse():
     p.add_argument("--skip-attention", action="store_true")
     p.add_argument("--skip-others", action="store_true",
                    help="skip the non-headline paths (prod quantize, dequantize, high-d, NN indexing)")
+    p.add_argument("--skip-dense", action="store_true", help="skip the unquantized-key logits baseline")
+    p.add_argument("--skip-ceilings", action="store_true", help="skip the in-tree stream and MFMA probes")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (counter calibration)")
     return p.parse_args()
@@ -111,13 +113,21 @@ def quantize_phase(torch, tq, workloads, steps, warmup):
         codec.quantize(xs[i], out=outs[i])
 
     wall, kern, kmed = time_launches(torch, step, steps, warmup, copies)
+    # warm: the same input every step (128 MiB in + 34 MB out fit the 256 MB
+    # Infinity Cache)
+    _, kern_warm, _ = time_launches(torch, lambda i: codec.quantize(xs[0], out=outs[0]), steps, warmup, 1)
     vectors = sets * n
     bytes_per_vec = d * 2 + codec.code_row + 4      # bf16 in, packed codes, f32 norm
-    flops_per_vec = 2 * 2 * d * d                   # two bf16 passes (Pi hi + lo)
+    algo_flops = 2 * d * d                          # y = Pi x
+    # executed: two bf16 passes (Pi hi, Pi lo) plus the Gram product for the
+    # norm (4 MFMAs of 16 x 16 x 32 per 16 vectors)
+    exec_flops = 2 * 2 * d * d + 4 * 2 * 16 * 16 * 32 // 16
     achieved = vectors * bytes_per_vec / (kern * 1e-3) / 1e9
-    return dict(vectors=vectors, wall_ms=wall, kernel_ms=kern, kernel_ms_median=kmed,
+    return dict(vectors=vectors, wall_ms=wall, kernel_ms=kern, kernel_ms_median=kmed, kernel_ms_warm=kern_warm,
                 bytes_per_vector=bytes_per_vec, achieved_gbs=achieved,
-                mfma_tflops=vectors * flops_per_vec / (kern * 1e-3) / 1e12, codec=codec, x=x)
+                achieved_gbs_warm=vectors * bytes_per_vec / (kern_warm * 1e-3) / 1e9,
+                mfma_algo_tflops=vectors * algo_flops / (kern * 1e-3) / 1e12,
+                mfma_exec_tflops=vectors * exec_flops / (kern * 1e-3) / 1e12, codec=codec, x=x)
 
 
 def quantize_b3_phase(torch, tq, workloads, x, steps, warmup):
@@ -292,9 +302,13 @@ def other_paths_phase(torch, tq, workloads, x_kv):
             mse_bits = bits if variant == tq.TQ_MSE else bits - 1
             gemm = 1 if variant == tq.TQ_MSE else (3 if mse_bits > 0 else 1)
             flops = 2.0 * nn * dd * dd * 3 * gemm
+            # the method's own flops: Pi x, and for prod S r (one GEMM when
+            # there is no mse stage)
+            algo = 2.0 * nn * dd * dd * (1 if variant == tq.TQ_MSE else (2 if mse_bits > 0 else 1))
             res[f"d{dd}_{name}_b{bits}_quantize_ms"] = ms
             res[f"d{dd}_{name}_b{bits}_vectors_per_s"] = nn / (ms * 1e-3)
-            res[f"d{dd}_{name}_b{bits}_mfma_frac"] = flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS
+            res[f"d{dd}_{name}_b{bits}_mfma_frac_executed_bf16"] = flops / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS
+            res[f"d{dd}_{name}_b{bits}_mfma_frac_algorithmic_bf16"] = algo / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS
         del xh
     # outlier-channel mixed precision on the KV workload: per head the 64
     # channels of largest RMS at b + 1 bits, the rest at b (2.5 and 3.5 bits)
@@ -362,30 +376,172 @@ def other_paths_phase(torch, tq, workloads, x_kv):
     return res
 
 
-def cpu_baseline(workloads, x_bf16, budget_s=15.0):
-    """The oracle (float64 NumPy) quantizing a bounded sample of the same KV
-    workload; vectors/s extrapolated from the sample."""
-    from oracle import tq_oracle as O
+def ceilings_phase(torch, tq):
+    """Memory-system and matrix-core ceilings from the library's own probe
+    kernels: streams over 1 GiB of input (each after a 1 GiB fill of another
+    buffer, so no input is still held in the 256 MB Infinity Cache) at the
+    read/write mixes of the hot-path kernels, and a matrix-core loop with no
+    memory traffic.  GB/s count bytes read plus bytes written."""
+    grid = 2048                                   # 8 workgroups of 4 waves per CU
+    n_in = 1 << 30
+    src = torch.empty(n_in // 4, dtype=torch.int32, device="cuda").fill_(0x1234567)
+    dst = torch.empty(n_in // 4, dtype=torch.int32, device="cuda")
+    evict = torch.empty(n_in // 4, dtype=torch.int32, device="cuda")
+    ev = _events(torch, 2)
+    res = {}
+    kinds = (("copy", 0, 1, 1), ("mix_4r1w", 1, 4, 1), ("mix_9r2w", 2, 9, 2), ("read_only", 3, 1, 0),
+             ("mix_9r2w_logits_rows", 4, 9, 2))
+    for name, kind, r, w in kinds:
+        tile_in = r * 64 * 16
+        used = n_in // tile_in * tile_in
+        moved = used + used // r * w
+        times = []
+        for rep in range(4):
+            evict.fill_(rep)
+            torch.cuda.synchronize()
+            ev[0].record()
+            tq.probe_stream(kind, src[:used // 4], dst, grid)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if rep:                                # the first launch loads the kernel
+                times.append(ev[0].elapsed_time(ev[1]))
+        ms = float(np.median(times))
+        res[f"{name}_gbs"] = moved / (ms * 1e-3) / 1e9
+        res[f"{name}_ms"] = ms
+    del src, dst, evict
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    iters = 20000
+    for name, f16 in (("bf16", False), ("f16", True)):
+        tq.probe_mfma(f16, 16, grid, out)          # load the kernel
+        torch.cuda.synchronize()
+        ev[0].record()
+        tq.probe_mfma(f16, iters, grid, out)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1])
+        flops = grid * 4 * iters * 8 * 2.0 * 16 * 16 * 32
+        res[f"mfma_{name}_tflops"] = flops / (ms * 1e-3) / 1e12
+    del out
+    return res
+
+
+def dense_logits_phase(torch, tq, workloads, steps, warmup, q):
+    """The dense baseline at the decode shape: the same 16 x 8 x 131072 keys
+    stored unquantized in float16 (the named comparison) and in float32 (the
+    pages' 32-bit comparison), the same 32 query heads, float32 logits."""
+    B, H, QH, T, d = (workloads.DEC_BATCH, workloads.DEC_KV_HEADS, workloads.DEC_Q_PER_KV,
+                      workloads.DEC_TOKENS, workloads.DEC_DIM)
+    sets = B * H
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    out = torch.empty((sets, QH, T), dtype=torch.float32, device="cuda")
+    res = {}
+    for name, dtype in (("f16", torch.float16), ("f32", torch.float32)):
+        keys = torch.empty((sets, T, d), dtype=dtype, device="cuda")
+        for s0 in range(0, sets, 8):
+            keys[s0:s0 + 8] = torch.randn((8, T, d), generator=gen, device="cuda").to(dtype)
+        wall, kern, kmed = time_launches(torch, lambda i: tq.dense_logits(q, keys, out=out), steps, warmup, 1)
+        kbytes = sets * T * d * keys.element_size()
+        res[name] = dict(kernel_ms=kern, kernel_ms_median=kmed, wall_ms=wall, key_bytes=kbytes,
+                         gbs=kbytes / (kern * 1e-3) / 1e9,
+                         total_gbs=(kbytes + sets * QH * T * 4) / (kern * 1e-3) / 1e9)
+        del keys
+    del out
+    return res
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
-    xf = x_bf16.float().numpy()
-    cd = O.make_codec(128, 4, O.MSE, 0, groups=workloads.KV_HEADS)
+        return os.cpu_count() or 1
+
+
+def _kv_quantize_rate(O, cd, xf, budget_s):
+    """Oracle TurboQuant_mse b = 4 over the KV vectors in 8192-vector chunks
+    (norm, rotate, boundary search, pack) for about budget_s."""
     done, t0, rows = 0, time.perf_counter(), 8192
-    sets = xf.shape[0]
-    while time.perf_counter() - t0 < budget_s and done < sets * xf.shape[1]:
+    sets, n = xf.shape[0], xf.shape[1]
+    while time.perf_counter() - t0 < budget_s and done < sets * n:
         s = (done // rows) % sets
         off = (done // (rows * sets)) * rows
         chunk = xf[s, off:off + rows].astype(np.float64)
         idx, nu, _ = O.quantize_mse(cd, chunk, s % cd.groups)
         O.pack(idx, 4)
         done += chunk.shape[0]
-    el = time.perf_counter() - t0
-    return dict(value=done / el, unit="vectors/s", cores=int(threads), kind="oracle",
-                sample=f"{done} of the {sets * xf.shape[1]} KV vectors (mse b=4: norm, rotate, "
-                       f"boundary search, pack) in {el:.1f} s")
+    return done, time.perf_counter() - t0
+
+
+def _random_prod_keys(rng, n, d, mse_bits):
+    return dict(idx=rng.integers(0, 1 << mse_bits, (n, d)), signs=np.where(rng.random((n, d)) < 0.5, -1, 1),
+                norms=10.0 + rng.standard_normal(n), rnorms=0.05 + 0.45 * rng.random(n))
+
+
+def cpu_baseline(workloads, x_bf16, budget_s=8.0):
+    """The oracle (float64 NumPy, BLAS threads as the host gives them) timed on
+    bounded samples of the workloads, beside the GPU figures of the same run.
+    `value` is the headline leg (the KV quantize, vectors/s); the other legs
+    time the oracle's fast logits form (rotated-domain inner products, equal to
+    the plain form up to rounding) on the decode and nearest-neighbour shapes
+    in 65,536-key chunks, and the d = 1536 quantize.  Inputs are seeded
+    synthetic draws (random codes for the logits legs).  Totals for the full
+    workloads are extrapolated linearly from the samples and labelled so."""
+    from oracle import tq_oracle as O
+
+    threads = _blas_threads()
+    xf = x_bf16.float().numpy()
+    cd = O.make_codec(128, 4, O.MSE, 0, groups=workloads.KV_HEADS)
+    done, el = _kv_quantize_rate(O, cd, xf, budget_s)
+    legs = {}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, e1 = _kv_quantize_rate(O, cd, xf, 3.0)
+        legs["kv_quantize_single_thread_vectors_per_s"] = d1 / e1
+    except Exception:
+        pass
+    rng = np.random.default_rng(11)
+    # decode logits: prod b = 4 keys, 4 query heads per set, 65,536-key chunks
+    kd = O.make_codec(128, 4, O.PROD, 0, groups=workloads.DEC_KV_HEADS)
+    chunk, keys_done, t0 = 65536, 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        s = (keys_done // chunk) % (workloads.DEC_BATCH * workloads.DEC_KV_HEADS)
+        keys = _random_prod_keys(rng, chunk, 128, 3)
+        q = rng.standard_normal((workloads.DEC_Q_PER_KV, 128))
+        O.logits_fast(kd, q, keys, s % kd.groups)
+        keys_done += chunk
+    el_l = time.perf_counter() - t0
+    total_keys = workloads.DEC_BATCH * workloads.DEC_KV_HEADS * workloads.DEC_TOKENS
+    legs["decode_logits"] = dict(keys_per_s=keys_done / el_l, packed_gbs=keys_done * 72 / el_l / 1e9,
+                                 extrapolated_full_ms=total_keys / (keys_done / el_l) * 1e3,
+                                 sample=f"{keys_done} keys (prod b=4, 4 heads) in {el_l:.1f} s")
+    # high-dimensional quantize, d = 1536, mse b = 4
+    hd = O.make_codec(1536, 4, O.MSE, 0)
+    xh = workloads.highd_vectors(2000, 1536)
+    t0 = time.perf_counter()
+    idx, _, _ = O.quantize_mse(hd, xh.astype(np.float64))
+    O.pack(idx, 4)
+    el_h = time.perf_counter() - t0
+    legs["highd_d1536_mse_b4"] = dict(vectors_per_s=2000 / el_h, extrapolated_1e5_s=1e5 / (2000 / el_h),
+                                      sample="2000 of the 100000 vectors")
+    # nearest-neighbour scoring: 100 queries x 1e6 prod b = 4 keys at d = 200
+    nd = O.make_codec(workloads.NN_D, 4, O.PROD, 0)
+    qn = rng.standard_normal((100, workloads.NN_D))
+    t0 = time.perf_counter()
+    for a in range(0, workloads.NN_POINTS, chunk):
+        n = min(chunk, workloads.NN_POINTS - a)
+        O.logits_fast(nd, qn, _random_prod_keys(rng, n, workloads.NN_D, 3))
+    el_n = time.perf_counter() - t0
+    pairs = 100 * workloads.NN_POINTS
+    legs["nn_scoring_d200_prod_b4"] = dict(pairs_per_s=pairs / el_n,
+                                           extrapolated_1e4_queries_s=el_n * workloads.NN_QUERIES / 100,
+                                           sample="100 queries x 1e6 keys, extrapolated linearly to 1e4 queries")
+    return dict(value=done / el, unit="vectors/s", cores=int(threads), host_cpu_count=os.cpu_count(),
+                kind="oracle",
+                sample=f"{done} of the {xf.shape[0] * xf.shape[1]} KV vectors (mse b=4: norm, rotate, "
+                       f"boundary search, pack) in {el:.1f} s",
+                legs=legs)
 
 
 def main():
@@ -406,10 +562,17 @@ def main():
     ap = None if (lp is None or args.skip_attention) else attention_phase(torch, tq, workloads, lp, args.steps,
                                                                           args.warmup)
     if lp is not None:
+        qdec = lp["q"]
         del lp["cache"], lp["codec"], lp["q"]
+        dense = None if args.skip_dense else dense_logits_phase(torch, tq, workloads, args.steps, args.warmup, qdec)
+        del qdec
+    else:
+        dense = None
     other = None if args.skip_others else other_paths_phase(torch, tq, workloads, qp["x"])
+    ceil = None if args.skip_ceilings else ceilings_phase(torch, tq)
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, qp["x"])
     probes = hbm_probes(torch) if args.copy_probe else None
+    peak_meas = ceil["copy_gbs"] if ceil else None
 
     value = qp["vectors"] / (qp["wall_ms"] * 1e-3)
     line = {
@@ -434,8 +597,21 @@ def main():
                      "traffic": counted_traffic("quant128_kv_mse_b4.md"),
                      "bytes_per_vector": qp["bytes_per_vector"],
                      "kernel_ms": qp["kernel_ms"],
-                     "mfma_bf16_tflops": qp["mfma_tflops"],
-                     "mfma_frac": qp["mfma_tflops"] / BF16_MFMA_PEAK_TFLOPS},
+                     "measured_peak": peak_meas,
+                     "measured_peak_kind": "in-tree copy kernel, 1 GiB read + 1 GiB written, cold",
+                     "frac_measured": qp["achieved_gbs"] / peak_meas if peak_meas else None,
+                     "mix_ceiling": ceil["mix_4r1w_gbs"] if ceil else None,
+                     "frac_of_mix_ceiling": qp["achieved_gbs"] / ceil["mix_4r1w_gbs"] if ceil else None,
+                     "warm": {"kernel_ms": qp["kernel_ms_warm"], "achieved": qp["achieved_gbs_warm"],
+                              "note": "one resident input, held in the 256 MB Infinity Cache"},
+                     "mfma": {"dtype": "bf16", "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "measured_peak": ceil["mfma_bf16_tflops"] if ceil else None,
+                              "algorithmic": qp["mfma_algo_tflops"],
+                              "algorithmic_frac": qp["mfma_algo_tflops"] / BF16_MFMA_PEAK_TFLOPS,
+                              "executed": qp["mfma_exec_tflops"],
+                              "executed_frac": qp["mfma_exec_tflops"] / BF16_MFMA_PEAK_TFLOPS,
+                              "note": "algorithmic = 2 d^2 flop per vector (y = Pi x); executed = the two split "
+                                      "passes (Pi hi, Pi lo) plus the Gram product for the norm"}},
         "quantize_b3": {"kernel_ms": q3["kernel_ms"], "vectors_per_s": q3["vectors_per_s"],
                         "achieved_gbs": q3["achieved_gbs"], "frac": q3["achieved_gbs"] / HBM_PEAK_GBS},
     }
@@ -451,9 +627,23 @@ def main():
                          "traffic": counted_traffic("logits128_decode_prod_b4.md"),
                          "kernel_ms": lp["kernel_ms"],
                          "achieved_incl_logits_written": lp["total_gbs"],
-                         "frac_incl_logits_written": lp["total_gbs"] / HBM_PEAK_GBS},
+                         "frac_incl_logits_written": lp["total_gbs"] / HBM_PEAK_GBS,
+                         "measured_peak": peak_meas,
+                         "frac_measured": lp["packed_gbs"] / peak_meas if peak_meas else None,
+                         "mix_ceiling": ceil["mix_9r2w_logits_rows_gbs"] if ceil else None,
+                         "mix_ceiling_kind": "in-tree stream, 72 B read + 16 B written per key, the kernel's "
+                                             "4-byte four-row stores; GB/s on all bytes",
+                         "frac_incl_logits_written_of_mix_ceiling":
+                             lp["total_gbs"] / ceil["mix_9r2w_logits_rows_gbs"] if ceil else None},
             "cache_build_s": lp["cache_build_s"],
         }
+        if dense is not None:
+            line["logits"]["dense_baseline"] = {
+                name: {"kernel": f"k_dense_logits128<{name}>", "kernel_ms": r["kernel_ms"],
+                       "key_gbs": r["gbs"], "total_gbs": r["total_gbs"],
+                       "frac_incl_logits_written": r["total_gbs"] / HBM_PEAK_GBS,
+                       "quantized_speedup": r["kernel_ms"] / lp["kernel_ms"]}
+                for name, r in dense.items()}
     if ap is not None:
         line["attention"] = {
             "metric": "softmax(q·K̂)·V̂ GB/s on packed K and V bytes",
@@ -476,6 +666,9 @@ def main():
         }
     if other is not None:
         line["other_paths"] = other
+    if ceil is not None:
+        line["ceilings"] = dict(ceil, note="in-tree probe kernels (probes.hip): 1 GiB streams, cold, GB/s on "
+                                           "bytes read + written; MFMA loops with no memory traffic")
     if probes is not None:
         line["hbm_probes"] = probes
     line["cpu_baseline"] = cpu

@@ -53,7 +53,7 @@ extern "C" {
 typedef struct tq_codec *tq_handle;
 
 enum { TQ_MSE = 0, TQ_PROD = 1 };
-enum { TQ_F32 = 0, TQ_BF16 = 1 };
+enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 };  /* TQ_F16: dense baseline keys only */
 enum { TQ_OK = 0, TQ_EINVAL = -1, TQ_EUNSUPPORTED = -2, TQ_ENOMEM = -3, TQ_EHIP = -4 };
 
 /* Build a codec: d dimensions, b bits per coordinate, variant TQ_MSE or
@@ -244,6 +244,32 @@ int tq_mixed_dequantize(tq_mixed m, const void *const codes[2], const void *cons
 int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const codes[2], const void *const signs[2],
                     const float *const norms[2], const float *const rnorms[2], int64_t n_sets, int64_t n_keys,
                     float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- dense baseline (unquantized keys; not part of the quantized path) ----
+ * out[s][i][t] = <q[s][i], k[s][t]> for keys stored unquantized as float16
+ * (dtype TQ_F16) or float32 (TQ_F32), keys: [n_sets][n_keys][d] (16-byte
+ * aligned), q: [n_sets][nq][d] float32, out: [n_sets][nq][n_keys] float32,
+ * float32 accumulation.  This is the comparison the pages draw for the
+ * attention logits of 4-bit codes against unquantized keys ([admirer]
+ * 內存價格能下來嗎？; [tmdm] 实测数据), run on the same GPU.  d = 128 only
+ * (else TQ_EUNSUPPORTED); 1 <= nq <= 64; a set's keys must fit 32-bit byte
+ * offsets (else TQ_EUNSUPPORTED).  Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP. */
+int tq_dense_logits(const float *q, int64_t nq, const void *keys, int dtype, int d, int64_t n_sets, int64_t n_keys,
+                    float *out, void *stream);
+
+/* ---- measurement probes (the ceilings the kernels are compared with) ----
+ * tq_probe_stream: one streaming kernel over in[in_bytes] (device, 16-byte
+ * aligned): kind 0 copies (reads and writes the same bytes), 1 reads 4 bytes
+ * per byte written (the d = 128 quantize's mix), 2 reads 9 per 2 written (the
+ * decode logits' mix), 3 only reads, 4 is the mix of kind 2 with the logits
+ * kernel's store pattern (4-byte stores into four rows).  Whole 16 KiB / 36 KiB
+ * tiles only; out must hold what the kind writes (in_bytes, in_bytes / 4,
+ * 2 in_bytes / 9, 1 KiB, 2 in_bytes / 9).  grid: workgroups of 256 threads.
+ * tq_probe_mfma: `grid` workgroups of 4 waves, each running iters x 8 back-
+ * to-back 16x16x32 MFMAs (bf16, or f16 when f16 != 0); out: grid x 256
+ * floats.  Errors: TQ_EINVAL, TQ_EHIP. */
+int tq_probe_stream(int kind, const void *in, int64_t in_bytes, void *out, int64_t out_bytes, int grid, void *stream);
+int tq_probe_mfma(int f16, int64_t iters, int grid, float *out, void *stream);
 
 /* Static text for a status code. */
 const char *tq_strerror(int status);

@@ -10,11 +10,11 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Codec", "MixedCodec", "lib", "library_path", "TQ_MSE", "TQ_PROD", "TQ_F32", "TQ_BF16", "TQError",
-           "EXPORTED_SYMBOLS", "row_bytes"]
+__all__ = ["Codec", "MixedCodec", "lib", "library_path", "TQ_MSE", "TQ_PROD", "TQ_F32", "TQ_BF16", "TQ_F16",
+           "TQError", "EXPORTED_SYMBOLS", "row_bytes", "dense_logits", "probe_stream", "probe_mfma"]
 
 TQ_MSE, TQ_PROD = 0, 1
-TQ_F32, TQ_BF16 = 0, 1
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_ENOMEM, TQ_EHIP = 0, -1, -2, -3, -4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +46,9 @@ _SIGS = {
     "tq_mixed_quantize": (_INT, [_P, _P, _INT, _I64, _I64, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "tq_mixed_dequantize": (_INT, [_P, _P, _P, _P, _P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
     "tq_mixed_logits": (_INT, [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "tq_dense_logits": (_INT, [_P, _I64, _P, _INT, _INT, _I64, _I64, _P, _P]),
+    "tq_probe_stream": (_INT, [_INT, _P, _I64, _P, _I64, _INT, _P]),
+    "tq_probe_mfma": (_INT, [_INT, _I64, _INT, _P, _P]),
     "tq_strerror": (ctypes.c_char_p, [_INT]),
     "tq_last_error": (ctypes.c_char_p, []),
     "tq_get_tables": (_INT, [_P, _INT, _P, _P, _P, _P]),
@@ -442,6 +445,35 @@ class MixedCodec:
                                      _ptr_pair(parts, "norms"), _ptr_pair(parts, "rnorms"), n_sets, n_keys,
                                      _ptr(out), _ptr(ws), ws.numel(), _stream(stream)), "tq_mixed_logits")
         return out
+
+
+def dense_logits(q, keys, out=None, stream=None):
+    """Dense baseline: <q, k> over unquantized float16 / float32 keys.
+    q: [n_sets, nq, d] float32, keys: [n_sets, n_keys, d]; returns
+    [n_sets, nq, n_keys] float32 (tq_dense_logits)."""
+    import torch
+
+    dtype = {torch.float16: TQ_F16, torch.float32: TQ_F32}.get(keys.dtype)
+    if dtype is None or not keys.is_contiguous() or q.dtype != torch.float32 or not q.is_contiguous():
+        raise TypeError("keys must be contiguous float16/float32, q contiguous float32")
+    n_sets, n_keys, d = keys.shape
+    nq = q.shape[1]
+    if out is None:
+        out = torch.empty((n_sets, nq, n_keys), dtype=torch.float32, device=q.device)
+    _check(lib().tq_dense_logits(_ptr(q), nq, _ptr(keys), dtype, d, n_sets, n_keys, _ptr(out), _stream(stream)),
+           "tq_dense_logits")
+    return out
+
+
+def probe_stream(kind: int, src, dst, grid: int, stream=None):
+    """One streaming probe kernel over the bytes of src (tq_probe_stream)."""
+    _check(lib().tq_probe_stream(kind, _ptr(src), src.numel() * src.element_size(), _ptr(dst),
+                                 dst.numel() * dst.element_size(), grid, _stream(stream)), "tq_probe_stream")
+
+
+def probe_mfma(f16: bool, iters: int, grid: int, out, stream=None):
+    """Back-to-back MFMAs with no memory traffic (tq_probe_mfma)."""
+    _check(lib().tq_probe_mfma(int(f16), iters, grid, _ptr(out), _stream(stream)), "tq_probe_mfma")
 
 
 def host_tables(d: int, bits: int, variant: int, seed: int, group: int = 0):

@@ -23,7 +23,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["host_codec.cpp", "tq_api.cpp"]
-DEVICE_SOURCES = ["generic.hip", "fast128.hip", "tiled.hip", "topk.hip", "scratch.hip"]
+DEVICE_SOURCES = ["generic.hip", "fast128.hip", "tiled.hip", "topk.hip", "scratch.hip", "dense.hip", "probes.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -51,6 +51,17 @@ constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
 hipError_t static_scratch_setup(int device);
 void *static_scratch(int device);
 
+// Dense baseline: logits of float16 (f32_keys = 0) or float32 keys stored
+// unquantized, [n_sets][n_keys][128]; hipErrorNotSupported past 32-bit offsets.
+hipError_t launch_dense_logits128(const float *q, int64_t nq, const void *keys, int f32_keys, int64_t n_sets,
+                                  int64_t n_keys, float *out, hipStream_t st);
+// Measurement probes (probes.hip).  kind: 0 copy, 1 read/write 4:1, 2 read/write
+// 9:2, 3 read only, 4 the 9:2 mix with the logits kernel's store pattern.
+int64_t probe_stream_tiles(int kind, int64_t in_bytes);
+int64_t probe_stream_out_bytes(int kind, int64_t tiles);
+hipError_t launch_probe_stream(int kind, const void *in, void *out, int64_t tiles, int grid, hipStream_t st);
+hipError_t launch_probe_mfma(int f16, int64_t iters, int grid, float *out, hipStream_t st);
+
 hipError_t launch_quant_generic(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
                                 int64_t n, uint8_t *codes, uint8_t *signs, float *norms,
                                 float *rnorms, hipStream_t st);

@@ -6,7 +6,7 @@
 //
 // k_topk_qprep: q~ = Pi q (scaled for the code table) and p = S q
 //   (scaled by sqrt(pi/2)/d) per query, zero-padded to 256 coordinates.
-// k_topk: a workgroup of 8 waves scans one key range; each wave holds 16
+// k_topk: a workgroup of 4 waves (one per SIMD) scans one key range; each wave holds 16
 //   queries as f16 hi/lo MFMA A operands (two row tiles of 8 queries) and
 //   streams 16-key tiles: lane (key, grp) decodes the codes of coordinates
 //   64 grp .. 64 grp + 63 of its key through LDS tables (a code pair per

@@ -29,9 +29,36 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// TQ_LOG = 0..3 (read once): 1 logs every failure to stderr, 2 also every
+// data call with its shape.
+int log_level() {
+  static const int level = [] {
+    const char *v = std::getenv("TQ_LOG");
+    return v ? std::atoi(v) : 0;
+  }();
+  return level;
+}
+
 int fail(int code, const std::string &msg) {
   g_last_error = msg;
+  if (log_level() >= 1) std::fprintf(stderr, "tq: error %d: %s\n", code, msg.c_str());
   return code;
+}
+
+void trace_call(const char *fn, int d, int64_t n_sets, int64_t n, int64_t nq) {
+  if (log_level() >= 2)
+    std::fprintf(stderr, "tq: %s d=%d n_sets=%lld n=%lld nq=%lld\n", fn, d, (long long)n_sets, (long long)n,
+                 (long long)nq);
+}
+
+// TQ_FAULT=launch: every data call fails as a kernel launch would, after its
+// validation and before anything is enqueued (a test hook for the TQ_EHIP
+// path).  Read on every call so that a test can switch it.
+int launch_fault(const char *fn) {
+  const char *v = std::getenv("TQ_FAULT");
+  if (v && std::strcmp(v, "launch") == 0)
+    return fail(TQ_EHIP, std::string(fn) + ": kernel launch failed (TQ_FAULT=launch)");
+  return TQ_OK;
 }
 
 int hip_fail(hipError_t e, const char *what) {
@@ -382,6 +409,8 @@ int tq_quantize(tq_handle h, const void *x, int dtype, int64_t n_sets, int64_t n
   if (dtype != TQ_F32 && dtype != TQ_BF16) return fail(TQ_EINVAL, "dtype must be TQ_F32 or TQ_BF16");
   if (!x || ((uintptr_t)x & (dtype == TQ_F32 ? 3u : 1u))) return fail(TQ_EINVAL, "x NULL or misaligned");
   if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, true))) return st;
+  trace_call("tq_quantize", h->d, n_sets, n, 0);
+  if ((st = launch_fault("tq_quantize"))) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = tq::launch_quant128(h->dev, x, dtype, n_sets, n, (uint8_t *)codes,
                                      (uint8_t *)signs, norms, rnorms, s);
@@ -405,6 +434,8 @@ int tq_append(tq_handle h, const void *x, int dtype, int64_t n_sets, const int64
   if (!x || ((uintptr_t)x & (dtype == TQ_F32 ? 3u : 1u))) return fail(TQ_EINVAL, "x NULL or misaligned");
   if (!rows || ((uintptr_t)rows & 7u)) return fail(TQ_EINVAL, "rows NULL or misaligned");
   if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, true))) return st;
+  trace_call("tq_append", h->d, n_sets, 1, 0);
+  if ((st = launch_fault("tq_append"))) return st;
   hipError_t e = tq::launch_append(h->dev, x, dtype, n_sets, rows, cache_rows, (uint8_t *)codes, (uint8_t *)signs,
                                    norms, rnorms, (hipStream_t)stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "append launch");
@@ -418,6 +449,8 @@ int tq_dequantize(tq_handle h, const void *codes, const void *signs, const float
   if (n_sets == 0 || n == 0) return TQ_OK;
   if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, false))) return st;
   if (!x_out || ((uintptr_t)x_out & 3u)) return fail(TQ_EINVAL, "x_out NULL or misaligned");
+  trace_call("tq_dequantize", h->d, n_sets, n, 0);
+  if ((st = launch_fault("tq_dequantize"))) return st;
   hipError_t e = tq::launch_dequant128(h->dev, (const uint8_t *)codes, (const uint8_t *)signs, norms,
                                        rnorms, n_sets, n, x_out, (hipStream_t)stream);
   if (e == hipErrorNotSupported)
@@ -438,6 +471,8 @@ int tq_logits(tq_handle h, const float *q, int64_t nq, const void *codes, const 
   if (!out || ((uintptr_t)out & 3u)) return fail(TQ_EINVAL, "out NULL or misaligned");
   if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, false))) return st;
   if (n_sets * nq * n_keys > ((int64_t)1 << 40)) return fail(TQ_EINVAL, "output too large");
+  trace_call("tq_logits", h->d, n_sets, n_keys, nq);
+  if ((st = launch_fault("tq_logits"))) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = tq::launch_logits128(h->dev, q, nq, (const uint8_t *)codes, (const uint8_t *)signs,
                                       norms, rnorms, n_sets, n_keys, out, s);
@@ -510,6 +545,8 @@ int tq_attention(tq_handle hk, tq_handle hv, const float *q, int64_t nq, const v
   const AttnPlan p = plan_attention(hk, hv, nq, n_sets, n_keys);
   if (!workspace || ((uintptr_t)workspace & 255u)) return fail(TQ_EINVAL, "workspace NULL or not 256-byte aligned");
   if (workspace_bytes < p.bytes) return fail(TQ_EINVAL, "workspace smaller than tq_attention_workspace reports");
+  trace_call("tq_attention", hk->d, n_sets, n_keys, nq);
+  if ((st = launch_fault("tq_attention"))) return st;
   char *ws = (char *)workspace;
   hipError_t e;
   if (p.fused) {
@@ -576,6 +613,8 @@ int tq_topk(tq_handle h, const float *q, int64_t nq, const void *codes, const vo
   if ((st = check_code_ptrs(h, codes, signs, norms, rnorms, false))) return st;
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
     return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_topk_workspace reports");
+  trace_call("tq_topk", h->d, 1, n_keys, nq);
+  if ((st = launch_fault("tq_topk"))) return st;
   hipError_t e = tq::launch_topk(h->dev, q, nq, (const uint8_t *)codes, (const uint8_t *)signs, norms, rnorms, n_keys,
                                  k, workspace, out_scores, out_idx, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "index too large for the top-k kernel");
@@ -741,6 +780,7 @@ int tq_mixed_quantize(tq_mixed m, const void *x, int dtype, int64_t n_sets, int6
   tq_mixed_workspace(m, n_sets, n, 0, &need);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
     return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_mixed_workspace reports");
+  if ((st = launch_fault("tq_mixed_quantize"))) return st;
   hipStream_t s = (hipStream_t)stream;
   if (m->fused && dtype == TQ_BF16) {
     const uint32_t *masks = m->fused + (size_t)m->groups * tq::fast128_rotation_words(128);
@@ -775,6 +815,7 @@ int tq_mixed_dequantize(tq_mixed m, const void *const codes[2], const void *cons
   tq_mixed_workspace(m, n_sets, n, 0, &need);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
     return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_mixed_workspace reports");
+  if ((st = launch_fault("tq_mixed_dequantize"))) return st;
   float *xo = (float *)workspace;
   float *xr = (float *)((char *)workspace + up256((size_t)(n_sets * n) * m->n_out * 4));
   for (int p = 0; p < 2; ++p)
@@ -802,6 +843,7 @@ int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const co
   tq_mixed_workspace(m, n_sets, n_keys, nq, &need);
   if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need)
     return fail(TQ_EINVAL, "workspace NULL, not 256-byte aligned or smaller than tq_mixed_workspace reports");
+  if ((st = launch_fault("tq_mixed_logits"))) return st;
   if (m->rt) {
     const hipError_t e = tq::launch_logits128_mixed(m->parts[0]->dev, m->parts[1]->dev, m->rt, q, nq,
                                                     (const uint8_t *)codes[0], (const uint8_t *)codes[1], norms[0],
@@ -821,6 +863,43 @@ int tq_mixed_logits(tq_mixed m, const float *q, int64_t nq, const void *const co
     return st;
   e = tq::launch_add_inplace(out, lr, n_sets * nq * n_keys, s);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "accumulate launch");
+}
+
+int tq_dense_logits(const float *q, int64_t nq, const void *keys, int dtype, int d, int64_t n_sets, int64_t n_keys,
+                    float *out, void *stream) {
+  if (d != 128) return fail(TQ_EUNSUPPORTED, "the dense baseline handles d = 128");
+  if (dtype != TQ_F16 && dtype != TQ_F32) return fail(TQ_EINVAL, "dtype must be TQ_F16 or TQ_F32");
+  if (n_sets < 0 || n_keys < 0 || n_sets > 65535) return fail(TQ_EINVAL, "n_sets must be in [0, 65535], n_keys >= 0");
+  if (nq < 1 || nq > 64) return fail(TQ_EINVAL, "nq must be in [1, 64]");
+  if (n_sets == 0 || n_keys == 0) return TQ_OK;
+  if (!q || ((uintptr_t)q & 3u)) return fail(TQ_EINVAL, "q NULL or misaligned");
+  if (!keys || !aligned16(keys)) return fail(TQ_EINVAL, "keys NULL or not 16-byte aligned");
+  if (!out || ((uintptr_t)out & 3u)) return fail(TQ_EINVAL, "out NULL or misaligned");
+  if (const int f = launch_fault("tq_dense_logits")) return f;
+  const hipError_t e = tq::launch_dense_logits128(q, nq, keys, dtype == TQ_F32, n_sets, n_keys, out,
+                                                  (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "set too large for 32-bit offsets");
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "dense logits launch");
+}
+
+int tq_probe_stream(int kind, const void *in, int64_t in_bytes, void *out, int64_t out_bytes, int grid, void *stream) {
+  const int64_t tiles = tq::probe_stream_tiles(kind, in_bytes);
+  if (tiles < 0) return fail(TQ_EINVAL, "kind must be in [0, 4]");
+  if (tiles == 0) return TQ_OK;
+  if (!in || !aligned16(in) || !out || !aligned16(out)) return fail(TQ_EINVAL, "in/out NULL or not 16-byte aligned");
+  if (out_bytes < tq::probe_stream_out_bytes(kind, tiles) || out_bytes < 1024)
+    return fail(TQ_EINVAL, "out smaller than the stream writes");
+  if (grid < 1 || grid > (1 << 20)) return fail(TQ_EINVAL, "grid must be in [1, 2^20]");
+  if (kind == 4 && tq::probe_stream_out_bytes(kind, tiles) > 0x7FFFFFFF)
+    return fail(TQ_EINVAL, "kind 4 writes 32-bit offsets: in_bytes too large");
+  const hipError_t e = tq::launch_probe_stream(kind, in, out, tiles, grid, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "probe launch");
+}
+
+int tq_probe_mfma(int f16, int64_t iters, int grid, float *out, void *stream) {
+  if (iters < 0 || grid < 1 || grid > (1 << 20) || !out) return fail(TQ_EINVAL, "bad probe arguments");
+  const hipError_t e = tq::launch_probe_mfma(f16 != 0, iters, grid, out, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "probe launch");
 }
 
 const char *tq_strerror(int status) {

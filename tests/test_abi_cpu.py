@@ -94,3 +94,20 @@ def test_host_codebooks_equal_the_oracle_codebooks(d):
         limit = 0 if bits <= 6 else 1
         assert _ulps(got["centroids"], c32) <= limit, (d, bits)
         assert _ulps(got["boundaries"], t32) <= limit, (d, bits)
+
+
+def test_tq_log_reports_failures_on_stderr():
+    """TQ_LOG=1 (read once at the first failure): a rejected call prints its
+    status and message to stderr; without it nothing is printed."""
+    import subprocess
+    import sys
+
+    code = ("import ctypes, kv_cache_compression_tq_amd as tq; h = ctypes.c_void_p(); "
+            "print(tq.lib().tq_init(1, 2, 0, 0, ctypes.byref(h)))")
+    env = dict(os.environ, TQ_LOG="1", PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
+    assert r.stdout.strip() == str(tq.TQ_EINVAL)
+    assert "tq: error -1: d must be in [2, 4096]" in r.stderr
+    env.pop("TQ_LOG")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT, timeout=120)
+    assert "tq: error" not in r.stderr
