@@ -57,7 +57,7 @@ def counted_traffic(profile):
     fields = dict(line.split(": ", 1) for line in open(path).read().splitlines()
                   if line.startswith(("traffic_bytes_per_launch: ", "kernel_source_sha256_16: ")))
     h = hashlib.sha256()
-    for f in ("fast128.hip", "kernels.h"):
+    for f in ("fast128.hip", "device_common.h"):  # the sources that define the kernel's code
         with open(os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                "kv_cache_compression_tq_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())

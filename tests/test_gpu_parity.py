@@ -92,6 +92,8 @@ MSE_CASES = [
     (2, 1, "f32", 1, 300, 1),
     (2, 4, "bf16", 2, 257, 2),
     (96, 3, "f32", 2, 100, 2),
+    (128, 4, "bf16", 1, 65573, 1),    # several 16-vector stages per wave and a ragged last stage
+    (128, 3, "bf16", 2, 40011, 2),
     # 5..8 mse bits: the dimension-generic kernels
     (128, 5, "f32", 1, 1000, 1),
     (128, 6, "bf16", 2, 300, 2),
@@ -139,6 +141,11 @@ PROD_CASES = [
     (128, 1, "f32", 1, 500, 1),
     (128, 4, "bf16", 2, 600, 2),
     (128, 3, "bf16", 1, 61, 1),
+    (128, 2, "bf16", 3, 257, 2),    # bf16 prod, 1..4 mse bits: the register-resident kernel
+    (128, 5, "bf16", 1, 1000, 1),
+    (128, 4, "bf16", 1, 4096, 1),
+    (128, 4, "bf16", 1, 65573, 1),  # several 16-vector stages per wave and a ragged last stage
+    (128, 3, "bf16", 2, 40011, 2),
     (128, 5, "f32", 1, 300, 1),
     (200, 3, "f32", 1, 400, 1),
     (3, 2, "f32", 1, 64, 1),
@@ -168,13 +175,14 @@ def test_quantize_prod_matches_oracle(d, bits, dtype, n_sets, n, groups):
     qjl.check(f"d={d} prod b={bits}")
 
 
-def test_quantize_zero_and_tiny_vectors():
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_zero_and_tiny_vectors(dtype):
     x = np.zeros((1, 40, 128), np.float32)
-    x[0, 1, 3] = 1e-30
+    x[0, 1, 3] = 1e-30  # representable in bfloat16 too (float32 exponent range)
     x[0, 2, :] = 1.0
-    for variant, bits in ((tq.TQ_MSE, 4), (tq.TQ_PROD, 4), (tq.TQ_PROD, 1)):
+    for variant, bits in ((tq.TQ_MSE, 4), (tq.TQ_PROD, 4), (tq.TQ_PROD, 2), (tq.TQ_PROD, 1)):
         codec = tq.Codec(128, bits, variant, seed=3)
-        out = codec.quantize(_cuda(x))
+        out = codec.quantize(_cuda(x).to(dtype))
         torch.cuda.synchronize()
         mb = codec.mse_bits
         assert out["norms"][0, 0].item() == 0.0
