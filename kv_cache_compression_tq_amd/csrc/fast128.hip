@@ -139,13 +139,32 @@ __device__ __forceinline__ void rotate_tile(const XRegs<F32IN> &xr, const u32x4 
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
+  // Sixteen groups (K step k, row tiles 2 h, 2 h + 1) of four fragments; the
+  // reads of group g + 1 are issued before the MFMAs of group g, so one LDS
+  // round trip hides behind each group's MFMAs.
+  u32x4 fa[2][4];
+  auto read_group = [&](int buf, int g) {
+    const int k = g >> 2, h = g & 3;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+    for (int i = 0; i < 2; ++i) {
+      const int f = ((2 * h + i) * 4 + k) * 2;
+      fa[buf][2 * i] = img[f * kFragVec + frag_lane];
+      fa[buf][2 * i + 1] = img[(f + 1) * kFragVec + frag_lane];
+    }
+  };
+  read_group(0, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int f = (m * 4 + k) * 2;
-      const u32x4 ah = img[f * kFragVec + frag_lane];
-      const u32x4 al = img[(f + 1) * kFragVec + frag_lane];
+  for (int g = 0; g < 16; ++g) {
+    if (g + 1 < 16) {
+      read_group((g + 1) & 1, g + 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    const int k = g >> 2, h = g & 3;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = 2 * h + i;
+      const u32x4 ah = fa[g & 1][2 * i], al = fa[g & 1][2 * i + 1];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         acc[t][m] = mfma_bf16(ah, bh[t][k], acc[t][m]);
@@ -153,6 +172,7 @@ __device__ __forceinline__ void rotate_tile(const XRegs<F32IN> &xr, const u32x4 
         if constexpr (F32IN) acc[t][m] = mfma_bf16(ah, bl[t][k], acc[t][m]);
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, F32IN ? 12 : 8, 0);
   }
   // G[v][v] sits in lane 16 (v/4) + v, register v%4 (selected without branches)
   const int32_t m0 = -(col & 1), m1 = -((col >> 1) & 1);
@@ -274,29 +294,62 @@ __global__ __launch_bounds__(quant_threads<PROD>(), 2) void k_quant128(
       }
     }
     if constexpr (PROD) {
-      // QJL: p = M r (rows permuted like the rotation, K in lane-chunk order)
+      // QJL: p = M r (rows permuted like the rotation, K in lane-chunk order).
+      // Each M fragment is read once for both column tiles; the M image has
+      // its own base so every read's offset fits the instruction's immediate.
+      // Sign bits go into a shift register (one alignbit per projection,
+      // projections 31 .. 0), holding 1 for p < 0.
+      int mfl = lane + kImageVec;
+      asm volatile("" : "+v"(mfl));
+      uint32_t neg[2] = {0u, 0u};
+      u32x4 fm[2][8];
+      f32x4 pa[2][2];
+      auto read_tile = [&](int buf, int m) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int f = (m * 4 + k) * 2;
+          fm[buf][2 * k] = lds[f * kFragVec + mfl];
+          fm[buf][2 * k + 1] = lds[(f + 1) * kFragVec + mfl];
+        }
+      };
+      read_tile(0, 7);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i <= 8; ++i) {
+        if (i < 8) {  // row tile m = 7 - i
+          if (i + 1 < 8) {
+            read_tile((i + 1) & 1, 6 - i);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          }
+          f32x4(&p)[2] = pa[i & 1];
+          p[0] = f32x4{0, 0, 0, 0};
+          p[1] = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const u32x4 ah = fm[i & 1][2 * k], al = fm[i & 1][2 * k + 1];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              p[t] = mfma_bf16(ah, rh[t][k], p[t]);
+              p[t] = mfma_bf16(ah, rl[t][k], p[t]);
+              p[t] = mfma_bf16(al, rh[t][k], p[t]);
+            }
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
+        }
+        if (i > 0) {  // signs of row tile 8 - i, whose MFMAs were issued one step earlier
+          const f32x4(&p)[2] = pa[(i - 1) & 1];
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 3; q >= 0; --q) neg[t] = __builtin_amdgcn_alignbit(neg[t], __float_as_uint(p[t][q]), 31);
+        }
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int64_t v = v0 + 16 * t + col;
-        uint32_t bits = 0;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          f32x4 pa = {0, 0, 0, 0};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int f = (m * 4 + k) * 2;
-            const u32x4 ah = lds[kImageVec + f * kFragVec + frag_lane];
-            const u32x4 al = lds[kImageVec + (f + 1) * kFragVec + frag_lane];
-            pa = mfma_bf16(ah, rh[t][k], pa);
-            pa = mfma_bf16(ah, rl[t][k], pa);
-            pa = mfma_bf16(al, rh[t][k], pa);
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) bits |= (pa[q] >= 0.f ? 1u : 0u) << (4 * m + q);
-        }
         if (!guard || v < n) {
           const int64_t row = set_row0 + v;
-          ((uint32_t *)(signs + row * 16))[grp] = bits;
+          ((uint32_t *)(signs + row * 16))[grp] = ~neg[t];
           if (grp == 0) rnorms[row] = nus[t] > 0.f ? sqrtf(gam2[t]) / nus[t] : 0.f;
         }
       }
