@@ -373,6 +373,57 @@ def other_paths_phase(torch, tq, workloads, x_kv):
         first = torch.where(hit.any(dim=1), hit.float().argmax(dim=1), torch.full_like(true1, 1 << 30))
         res[f"nn_recall_at_1_at_k_prod_b{bits}"] = {str(k): float((first < k).float().mean()) for k in ks}
         del out, keys, sc, ix
+    del pts, qs, true1
+    res.update(generic_paths(torch, tq, gen))
+    return res
+
+
+def generic_paths(torch, tq, gen):
+    """The dimension-generic kernels, on shapes the fast kernels hand over to
+    them: logits of one set of 2^25 + 64 keys (past the fused kernel's 32-bit
+    offsets), logits at d = 200 (NN index keys), and the quantize, dequantize
+    and logits of mse b = 5 at d = 128 (more than 4 bits).  Random codes
+    stand in for quantized keys where only the streaming rate matters."""
+    res = {}
+    nk = (1 << 25) + 64
+    c = tq.Codec(128, 4, tq.TQ_PROD, seed=0)
+    keys = dict(codes=torch.randint(0, 256, (nk, c.code_row), dtype=torch.uint8, device="cuda", generator=gen),
+                signs=torch.randint(0, 256, (nk, c.sign_row), dtype=torch.uint8, device="cuda", generator=gen),
+                norms=torch.rand(nk, device="cuda", generator=gen) + 0.5,
+                rnorms=torch.rand(nk, device="cuda", generator=gen) * 0.2)
+    q = torch.randn((1, 4, 128), device="cuda", generator=gen)
+    lo = torch.empty((1, 4, nk), device="cuda")
+    cache = {k: v.unsqueeze(0) for k, v in keys.items()}
+    ms = _mean_launch_ms(torch, lambda: c.logits(q, cache, out=lo), reps=3)
+    res["generic_logits_2p25_keys_prod_b4_ms"] = ms
+    res["generic_logits_2p25_keys_prod_b4_packed_gbs"] = nk * 72 / (ms * 1e-3) / 1e9
+    del keys, cache, lo
+    # d = 200 keys, prod b = 4: the generic logits kernel (one set of 1e6 keys, 64 queries)
+    c = tq.Codec(200, 4, tq.TQ_PROD, seed=0)
+    x = torch.randn((1, 1_000_000, 200), device="cuda", generator=gen)
+    kc = c.empty_codes(1, 1_000_000)
+    c.quantize(x, out=kc)
+    q = torch.randn((1, 64, 200), device="cuda", generator=gen)
+    lo = torch.empty((1, 64, 1_000_000), device="cuda")
+    ms = _mean_launch_ms(torch, lambda: c.logits(q, kc, out=lo), reps=3)
+    res["generic_logits_d200_prod_b4_64q_ms"] = ms
+    res["generic_logits_d200_prod_b4_64q_packed_gbs"] = 1_000_000 * (c.code_row + c.sign_row + 8) / (ms * 1e-3) / 1e9
+    del x, kc, q, lo
+    # mse b = 5 at d = 128 (KV shape, 16 sets x 32768): generic quantize, dequantize, logits
+    c = tq.Codec(128, 5, tq.TQ_MSE, seed=0, groups=8)
+    x = torch.randn((16, 32768, 128), device="cuda", generator=gen).to(torch.bfloat16)
+    kc = c.empty_codes(16, 32768)
+    ms = _mean_launch_ms(torch, lambda: c.quantize(x, out=kc))
+    res["generic_quant_kv_mse_b5_ms"] = ms
+    res["generic_quant_kv_mse_b5_vectors_per_s"] = 16 * 32768 / (ms * 1e-3)
+    rec = torch.empty((16, 32768, 128), device="cuda")
+    ms = _mean_launch_ms(torch, lambda: c.dequantize(kc, out=rec))
+    res["generic_dequant_kv_mse_b5_ms"] = ms
+    q = torch.randn((16, 4, 128), device="cuda", generator=gen)
+    lo = torch.empty((16, 4, 32768), device="cuda")
+    ms = _mean_launch_ms(torch, lambda: c.logits(q, kc, out=lo))
+    res["generic_logits_kv_mse_b5_ms"] = ms
+    res["generic_logits_kv_mse_b5_packed_gbs"] = 16 * 32768 * (c.code_row + 4) / (ms * 1e-3) / 1e9
     return res
 
 
