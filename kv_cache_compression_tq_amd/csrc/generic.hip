@@ -344,64 +344,91 @@ __global__ __launch_bounds__(kThreads) void k_dequant_generic(
   }
 }
 
-// Logits: each workgroup rotates/projects the queries of its set into LDS
-// (heads in chunks of `hc`), then each thread scores keys one at a time.
+// Logits: each workgroup rotates/projects the queries of its set (heads in
+// chunks of up to HC) into LDS as [coordinate][HC] -- one 16-byte read gives
+// four heads -- beside the codebook; then each thread scores keys one at a
+// time.  A key's code row streams through a 64-bit window filled by aligned
+// 32-bit loads (rows are 16-byte aligned and padded), each field indexes the
+// LDS codebook, and the sign row is read a word per 32 projections.
 constexpr int kMaxHeads = 8;
 constexpr int kKeysPerThread = 8;
 
+template <int HC>
 __global__ __launch_bounds__(kThreads) void k_logits_generic(
     const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ signs, const float *__restrict__ norms,
     const float *__restrict__ rnorms, int d, int64_t n_keys, int groups, int mse_bits, int prod,
     const float *__restrict__ PiT, const float *__restrict__ ST, const float *__restrict__ cent,
     int64_t code_row, int64_t sign_row, float *__restrict__ out) {
-  extern __shared__ float sm[];
-  float *qs = sm, *qt = sm + hc * d, *pp = sm + 2 * hc * d;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  extern __shared__ f4 sm4[];
+  float *qt = (float *)sm4, *pp = qt + HC * d, *cl = pp + HC * d;
   const int s = blockIdx.y;
   const int g = s % groups;
   const int tid = threadIdx.x;
-  for (int e = tid; e < hc * d; e += kThreads) qs[e] = q[((int64_t)s * nq + h0) * d + e];
-  __syncthreads();
+  if (mse_bits > 0)
+    for (int e = tid; e < (1 << mse_bits); e += kThreads) cl[e] = cent[e];
+  // (Pi q)_j and (S q)_j of head h at [j][h]; heads past hc are zero
   const float *P = PiT + (size_t)g * d * d;
   const float *Sg = prod ? ST + (size_t)g * d * d : nullptr;
-  for (int e = tid; e < hc * d; e += kThreads) {
-    const int h = e / d, j = e % d;
+  for (int e = tid; e < HC * d; e += kThreads) {
+    const int h = e / d, j = e % d;  // consecutive threads: consecutive j (coalesced PiT reads)
     float a = 0.f, b = 0.f;
-    for (int k = 0; k < d; ++k) {
-      a = fmaf(P[(size_t)k * d + j], qs[h * d + k], a);            // (Pi q)_j
-      if (prod) b = fmaf(Sg[(size_t)k * d + j], qs[h * d + k], b);  // (S q)_j
+    if (h < hc) {
+      const float *qh = q + ((int64_t)s * nq + h0 + h) * d;
+      for (int k = 0; k < d; ++k) {
+        const float qk = qh[k];
+        a = fmaf(P[(size_t)k * d + j], qk, a);
+        if (prod) b = fmaf(Sg[(size_t)k * d + j], qk, b);
+      }
     }
-    qt[e] = a;
-    pp[e] = b;
+    qt[j * HC + h] = a;
+    pp[j * HC + h] = b;
   }
   __syncthreads();
   const float ks = kQjlScale / (float)d;
+  const uint32_t mask = mse_bits > 0 ? (1u << mse_bits) - 1u : 0u;
   for (int kk = 0; kk < kKeysPerThread; ++kk) {
     const int64_t t = ((int64_t)blockIdx.x * kKeysPerThread + kk) * kThreads + tid;
     if (t >= n_keys) break;
     const int64_t row = (int64_t)s * n_keys + t;
-    float am[kMaxHeads], as[kMaxHeads];
-    for (int h = 0; h < kMaxHeads; ++h) am[h] = as[h] = 0.f;
+    f4 am[HC / 4], as[HC / 4];
+#pragma unroll
+    for (int i = 0; i < HC / 4; ++i) am[i] = as[i] = f4{0.f, 0.f, 0.f, 0.f};
     if (mse_bits > 0) {
-      const uint8_t *crow = codes + row * code_row;
+      const uint32_t *cw = (const uint32_t *)(codes + row * code_row);
+      uint64_t win = 0;
+      int have = 0, wi = 0;
       for (int j = 0; j < d; ++j) {
-        const float c = cent[read_field(crow, j, mse_bits)];
-        for (int h = 0; h < kMaxHeads; ++h)
-          if (h < hc) am[h] = fmaf(qt[h * d + j], c, am[h]);
+        if (have < mse_bits) {  // the field continues in the next word
+          win |= (uint64_t)cw[wi++] << have;
+          have += 32;
+        }
+        const float c = cl[(uint32_t)win & mask];
+        win >>= mse_bits;
+        have -= mse_bits;
+        const f4 *qv = (const f4 *)(qt + j * HC);
+#pragma unroll
+        for (int i = 0; i < HC / 4; ++i) am[i] += qv[i] * c;
       }
     }
     if (prod) {
-      const uint8_t *srow = signs + row * sign_row;
-      for (int i = 0; i < d; ++i) {
-        const bool pos = (srow[i >> 3] >> (i & 7)) & 1;
-        for (int h = 0; h < kMaxHeads; ++h)
-          if (h < hc) as[h] += pos ? pp[h * d + i] : -pp[h * d + i];
+      const uint32_t *sw = (const uint32_t *)(signs + row * sign_row);
+      uint32_t w = 0;
+      for (int j = 0; j < d; ++j) {
+        if ((j & 31) == 0) w = sw[j >> 5];
+        const float z = (w & 1u) ? 1.f : -1.f;
+        w >>= 1;
+        const f4 *pv = (const f4 *)(pp + j * HC);
+#pragma unroll
+        for (int i = 0; i < HC / 4; ++i) as[i] += pv[i] * z;
       }
     }
     const float nu = norms[row];
-    const float w = prod ? ks * rnorms[row] : 0.f;
-    for (int h = 0; h < kMaxHeads; ++h)
-      if (h < hc) out[((int64_t)s * nq + h0 + h) * n_keys + t] = nu * fmaf(w, as[h], am[h]);
+    const float wq = prod ? ks * rnorms[row] : 0.f;
+#pragma unroll
+    for (int h = 0; h < HC; ++h)
+      if (h < hc) out[((int64_t)s * nq + h0 + h) * n_keys + t] = nu * fmaf(wq, as[h / 4][h % 4], am[h / 4][h % 4]);
   }
 }
 
@@ -637,17 +664,27 @@ hipError_t launch_logits_generic(const DeviceTables &t, const float *q, int64_t 
                                  const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
                                  hipStream_t st) {
   if (n_sets == 0 || n_keys == 0) return hipSuccess;
-  int hc_max = 4096 / t.d;  // 3 * hc * d floats of LDS <= 48 KB
-  if (hc_max < 1) hc_max = 1;
-  if (hc_max > kMaxHeads) hc_max = kMaxHeads;
+  // query tables [d][HC] for the rotation and the projection, then the codebook
+  const bool wide = t.d <= 1024;
+  const int hc_max = wide ? 8 : 4;
+  const size_t shmem = (size_t)2 * hc_max * t.d * sizeof(float) + sizeof(float) * (1u << t.mse_bits);
+  const void *fn = wide ? (const void *)k_logits_generic<8> : (const void *)k_logits_generic<4>;
+  if (shmem > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+  }
   const int64_t per_block = (int64_t)kThreads * kKeysPerThread;
   const dim3 grid((unsigned)((n_keys + per_block - 1) / per_block), (unsigned)n_sets);
   for (int h0 = 0; h0 < nq; h0 += hc_max) {
     const int hc = (int)((nq - h0) < hc_max ? (nq - h0) : hc_max);
-    const size_t shmem = (size_t)3 * hc * t.d * sizeof(float);
-    hipLaunchKernelGGL(k_logits_generic, grid, dim3(kThreads), shmem, st, q, (int)nq, h0, hc,
-                       codes, signs, norms, rnorms, t.d, n_keys, t.groups, t.mse_bits,
-                       (int)(t.variant == 1), t.PiT, t.ST, t.cent, t.code_row, t.sign_row, out);
+    if (wide)
+      hipLaunchKernelGGL(k_logits_generic<8>, grid, dim3(kThreads), shmem, st, q, (int)nq, h0, hc, codes, signs,
+                         norms, rnorms, t.d, n_keys, t.groups, t.mse_bits, (int)(t.variant == 1), t.PiT, t.ST, t.cent,
+                         t.code_row, t.sign_row, out);
+    else
+      hipLaunchKernelGGL(k_logits_generic<4>, grid, dim3(kThreads), shmem, st, q, (int)nq, h0, hc, codes, signs,
+                         norms, rnorms, t.d, n_keys, t.groups, t.mse_bits, (int)(t.variant == 1), t.PiT, t.ST, t.cent,
+                         t.code_row, t.sign_row, out);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

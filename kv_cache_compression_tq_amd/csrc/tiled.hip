@@ -164,7 +164,8 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_rot(const void *__re
   const u32x4 *img = img_all + ((size_t)g * panels + p) * (size_t)a.chunks * kImageVec;
 
   for (int i = tid; i < a.cell_words; i += kTiledThreads) tab[i] = cells[i];
-  if (PROD && MB > 0 && tid < (1 << MB)) cent_lds[tid] = cent[tid];
+  if (PROD && MB > 0)
+    for (int i = tid; i < (1 << MB); i += kTiledThreads) cent_lds[i] = cent[i];
 
   const int64_t set_row0 = (int64_t)s * a.n;
   int64_t v[2], row[2];
@@ -265,7 +266,8 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__r
   const int kchunks = (MB > 0 ? 2 : 1) * a.chunks;
   const u32x4 *img = img_all + ((size_t)g * panels + p) * (size_t)(2 * a.chunks) * kImageVec;
 
-  if (MB > 0 && tid < (1 << MB)) cent_lds[tid] = cent[tid];
+  if (MB > 0)
+    for (int i = tid; i < (1 << MB); i += kTiledThreads) cent_lds[i] = cent[i];
 
   const int64_t set_row0 = (int64_t)s * a.n;
   int64_t v[2], row[2];
@@ -374,7 +376,8 @@ hipError_t run_tiled(const DeviceTables &t, const void *x, int64_t n_sets, int64
   a.cell_words = MB > 0 ? 2 * (2 * t.cell_radius + 1) : 0;
   const int panels = a.chunks;
   const dim3 grid((unsigned)panels, (unsigned)((n + kTiledVectors - 1) / kTiledVectors), (unsigned)n_sets);
-  const size_t lds1 = kImgBytes + 4 * (size_t)a.cell_words + 64;
+  const size_t cent_bytes = 4 * (size_t)(1 << MB) > 64 ? 4 * (size_t)(1 << MB) : 64;  // the codebook
+  const size_t lds1 = kImgBytes + 4 * (size_t)a.cell_words + cent_bytes;
   hipError_t e = hipFuncSetAttribute((const void *)k_tiled_rot<MB, PROD, F32IN>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   if (e != hipSuccess) return e;
@@ -387,7 +390,7 @@ hipError_t run_tiled(const DeviceTables &t, const void *x, int64_t n_sets, int64
                      (const u32x4 *)t.tiled_rot, t.cells, t.cent, codes, norms, (int *)rnorms);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (PROD) {
-    const size_t lds2 = kImgBytes + 64;
+    const size_t lds2 = kImgBytes + cent_bytes;
     e = hipFuncSetAttribute((const void *)k_tiled_sign<MB, F32IN>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds2);
     if (e != hipSuccess) return e;

@@ -94,13 +94,16 @@ MSE_CASES = [
     (96, 3, "f32", 2, 100, 2),
     (128, 4, "bf16", 1, 65573, 1),    # several 16-vector stages per wave and a ragged last stage
     (128, 3, "bf16", 2, 40011, 2),
-    # 5..8 mse bits: the dimension-generic kernels
+    # 5..8 mse bits: the dimension-generic kernels (float32 arithmetic)
     (128, 5, "f32", 1, 1000, 1),
     (128, 6, "bf16", 2, 300, 2),
     (128, 7, "f32", 1, 257, 1),
     (128, 8, "f32", 2, 200, 2),
     (200, 6, "f32", 1, 301, 1),
     (200, 8, "bf16", 1, 150, 1),
+    (128, 5, "bf16", 1, 4096, 1),
+    (100, 7, "f32", 1, 200, 1),
+    (100, 5, "bf16", 2, 130, 2),
 ]
 
 
