@@ -41,6 +41,8 @@ def _parse():
                    help="skip the non-headline paths (prod quantize, dequantize, high-d, NN indexing)")
     p.add_argument("--skip-dense", action="store_true", help="skip the unquantized-key logits baseline")
     p.add_argument("--skip-ceilings", action="store_true", help="skip the in-tree stream and MFMA probes")
+    p.add_argument("--kv-only", action="store_true",
+                   help="of the other paths, run only the KV-shape ones (prod quantize, dequantize, mixed)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device-to-device copy (counter calibration)")
     return p.parse_args()
@@ -265,12 +267,13 @@ def _mean_launch_ms(torch, fn, reps=5, warm=1):
     return ev[0].elapsed_time(ev[1]) / reps
 
 
-def other_paths_phase(torch, tq, workloads, x_kv):
+def other_paths_phase(torch, tq, workloads, x_kv, kv_only=False):
     """The rest of the hot path, timed once each (not the headline metric):
     TurboQuant_prod quantize and both dequantizes on the KV workload, the
     high-dimensional quantize (d = 1536, 1e5 vectors; d = 3072, 5e4) and the
     nearest-neighbour indexing (d = 200, 1e6 unit vectors).  Inputs are drawn
-    on the device with the workloads' distributions."""
+    on the device with the workloads' distributions.  kv_only: the KV-shape
+    parts alone (prod quantize, dequantizes, mixed precision)."""
     res = {}
     sets, n, d = x_kv.shape
     xk = x_kv.cuda()
@@ -287,7 +290,7 @@ def other_paths_phase(torch, tq, workloads, x_kv):
         del rec
     gen = torch.Generator(device="cuda")
     gen.manual_seed(9)
-    for dd, nn in ((1536, 100_000), (3072, 50_000)):
+    for dd, nn in (() if kv_only else ((1536, 100_000), (3072, 50_000))):
         z = torch.randn((1, nn, dd), generator=gen, device="cuda")
         rho = torch.empty((1, nn, 1), device="cuda").log_normal_(0.0, 0.5, generator=gen)
         xh = z / z.norm(dim=2, keepdim=True) * rho
@@ -346,6 +349,8 @@ def other_paths_phase(torch, tq, workloads, x_kv):
     res["decode_mixed_2.5bit_logits_packed_gbs"] = kbytes / (ms * 1e-3) / 1e9
     res["decode_mixed_2.5bit_logits_total_gbs"] = (kbytes + dsets * QH * T * 4) / (ms * 1e-3) / 1e9
     del mc, cache, qd, lo, wsl
+    if kv_only:
+        return res
     centres = torch.randn((workloads.NN_CENTRES, workloads.NN_D), generator=gen, device="cuda")
     centres /= centres.norm(dim=1, keepdim=True)
     m = torch.randint(0, workloads.NN_CENTRES, (workloads.NN_POINTS,), generator=gen, device="cuda")
@@ -619,7 +624,7 @@ def main():
         del qdec
     else:
         dense = None
-    other = None if args.skip_others else other_paths_phase(torch, tq, workloads, qp["x"])
+    other = None if args.skip_others else other_paths_phase(torch, tq, workloads, qp["x"], args.kv_only)
     ceil = None if args.skip_ceilings else ceilings_phase(torch, tq)
     cpu = None if args.no_cpu_baseline else cpu_baseline(workloads, qp["x"])
     probes = hbm_probes(torch) if args.copy_probe else None
