@@ -5,11 +5,16 @@
 // [128 c, 128 c + 128) (both zero-padded past d).  Every block is stored as
 // the same bf16 hi/lo MFMA operand image the d = 128 kernels use (rows
 // permuted so that each lane ends up with 32 consecutive coordinates of its
-// vector).  A workgroup computes one panel for 128 vectors: the images of the
-// chunks go through one LDS buffer (direct global-to-LDS loads), the inputs
-// through registers; two workgroups share a CU, so one's MFMAs run while the
-// other waits for its next chunk.  After the last chunk the panel's codes
-// are searched and packed exactly as at d = 128.
+// vector).  A workgroup computes two output panels (256 coordinates) for 128
+// vectors, so that each float32 input element split into bf16 hi/lo on the
+// vector ALU feeds twice the MFMAs of a one-panel workgroup.  The contraction
+// runs in units of 64 elements (two K steps): a unit's fragments of both
+// panels' blocks fill one 64 KB LDS buffer (direct global-to-LDS loads), the
+// inputs come through registers, and two workgroups share a CU, so one's
+// MFMAs run while the other waits for its next unit.  Units wholly past d are
+// skipped.  After the last unit each panel's codes are searched and packed
+// exactly as at d = 128.  Launches too small to fill the chip with pairs keep
+// one panel per workgroup.
 //
 // TurboQuant_prod adds a second pass.  The QJL signs need the residual of the
 // whole vector, so they are taken as sign(S x - nu M c[idx]) = sign(S r)
@@ -30,12 +35,14 @@ namespace {
 constexpr int kTiledThreads = 256;     // 4 waves x 32 vectors
 constexpr int kTiledVectors = 128;     // vectors per workgroup
 constexpr int kTiledWaves = kTiledThreads / 64;
-constexpr uint32_t kImgBytes = kImageVec * 16;
+constexpr int kUnitFrags = 64;         // fragments of one unit: 16 row tiles x 2 K steps x hi/lo
+constexpr uint32_t kUnitBytes = kUnitFrags * kFragVec * 16;  // 64 KB
 constexpr float kFix = 268435456.f;    // 2^28: fixed-point scale of the residual norm squared
 
 struct TiledArgs {
   int64_t n;             // vectors per set
   int d, chunks, groups;
+  int pair;              // output panels per workgroup: 2, or 1 for launches too small to fill the chip
   int64_t code_row, sign_row;
   float cell_scale;      // cells per unit, times 2^-22
   float cell_magic;      // 2 + radius 2^-22
@@ -52,99 +59,174 @@ __device__ __forceinline__ uint32_t cell_index_rt(uint32_t tab, float y, float n
   return e[1] + (__float_as_uint(dd) >> 31);
 }
 
-// Direct global-to-LDS copy of one 64 KB image block by the whole workgroup
-// (each wave moves 16 KB in 1 KB steps; lane data lands in lane order).
-__device__ __forceinline__ void stage_image(const u32x4 *src, u32x4 *dst, int wave, int lane) {
-  constexpr int kSteps = kImageVec / 64 / kTiledWaves;
+// One unit (K steps 2 kh, 2 kh + 1 of contraction chunk c) of the blocks of
+// output panels 2 pp and 2 pp + 1 into LDS by direct global-to-LDS loads:
+// buffer fragment 4 m + 2 kk + hl (row tile m = 0..15; tiles 8..15 are the
+// second panel's) is fragment 2 (4 (m % 8) + 2 kh + kk) + hl of that panel's
+// block.  blk0 / blk1: the two panels' blocks of chunk c (blk1 unused when
+// the pair has one panel).  Each wave moves 16 fragments of 1 KB.
+__device__ __forceinline__ void stage_unit(const u32x4 *blk0, const u32x4 *blk1, bool two, int kh, u32x4 *dst,
+                                           int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
-    const int off = (wave * kSteps + i) * 64;  // u32x4 index of this 1 KB step
-    __builtin_amdgcn_global_load_lds((const void *)(src + off + lane),
-                                     (__attribute__((address_space(3))) void *)(dst + off), 16, 0, 0);
+  for (int i = 0; i < kUnitFrags / kTiledWaves; ++i) {
+    const int fi = wave * (kUnitFrags / kTiledWaves) + i, m = fi >> 2, q = fi & 3;
+    if (m >= 8 && !two) continue;  // wave-uniform
+    const u32x4 *blk = m < 8 ? blk0 : blk1;
+    __builtin_amdgcn_global_load_lds((const void *)(blk + ((m & 7) * 4 + 2 * kh) * 2 * kFragVec + q * kFragVec + lane),
+                                     (__attribute__((address_space(3))) void *)(dst + fi * kFragVec), 16, 0, 0);
   }
 }
 
-// Input fragments of one chunk for the lane's two vectors: elements
-// 128 c + 32 k + 8 grp .. + 8 (bf16 pairs, or raw float32).
+// Input fragments of one unit for the lane's two vectors: elements
+// 128 c + 64 kh + 32 kk + 8 grp .. + 8 (bf16 pairs, or raw float32).
 template <bool F32IN>
-struct XChunk {
-  u32x4 v[2][4][F32IN ? 2 : 1];
+struct XUnit {
+  u32x4 v[2][2][F32IN ? 2 : 1];
 };
 
 template <bool F32IN>
-__device__ __forceinline__ void load_chunk(XChunk<F32IN> &r, const void *xin, const int64_t (&row)[2], int c,
-                                           int d, int grp) {
+__device__ __forceinline__ void load_unit(XUnit<F32IN> &r, const void *xin, const int64_t (&row)[2], int e_unit, int d,
+                                          int grp) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int e0 = 128 * c + 32 * k + 8 * grp;  // d is a multiple of 8: groups are all in or all out
+    for (int kk = 0; kk < 2; ++kk) {
+      const int e0 = e_unit + 32 * kk + 8 * grp;  // d is a multiple of 8: groups are all in or all out
       if (e0 < d) {
         if constexpr (F32IN) {
           const u32x4 *p = (const u32x4 *)((const float *)xin + row[t] * d + e0);
-          r.v[t][k][0] = p[0];
-          r.v[t][k][1] = p[1];
+          r.v[t][kk][0] = p[0];
+          r.v[t][kk][1] = p[1];
         } else {
-          r.v[t][k][0] = *(const u32x4 *)((const uint16_t *)xin + row[t] * d + e0);
+          r.v[t][kk][0] = *(const u32x4 *)((const uint16_t *)xin + row[t] * d + e0);
         }
       } else {
 #pragma unroll
-        for (int h = 0; h < (F32IN ? 2 : 1); ++h) r.v[t][k][h] = u32x4{0, 0, 0, 0};
+        for (int h = 0; h < (F32IN ? 2 : 1); ++h) r.v[t][kk][h] = u32x4{0, 0, 0, 0};
       }
     }
 }
 
-// acc[t][m] += image block (LDS) x chunk; also ||x||^2 of the chunk's elements.
-// Per K step the 16 A fragments (8 row tiles, hi and lo) are read from LDS
-// together before that step's MFMAs, so one LDS round trip serves 32 or 48
-// MFMAs; the scheduling-group barriers keep the reads in one group.
-template <bool F32IN>
-__device__ __forceinline__ void mma_chunk(const XChunk<F32IN> &x, const u32x4 *img, int frag_lane,
-                                          f32x4 (&acc)[2][8], float (&nsq)[2]) {
-  u32x4 bh[2][4], bl[2][4];
+// acc[t][m] += unit (LDS) x the unit's B operands, for row tiles m < 8 (one
+// panel) or m < 16 (two); also ||x||^2 of the unit's elements when NSQ.  Per
+// K step the fragments go in four groups of eight (four row tiles, hi and
+// lo), each group read before its MFMAs.
+template <bool F32IN, bool LO, bool NSQ>
+__device__ __forceinline__ void mma_unit(const XUnit<F32IN> &x, const u32x4 *buf, int frag_lane, bool two,
+                                         f32x4 (&acc)[2][16], float (&nsq)[2]) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int kk = 0; kk < 2; ++kk) {
+    u32x4 bh[2], bl[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int t = 0; t < 2; ++t) {
       if constexpr (F32IN) {
-        const f32x4 a = __builtin_bit_cast(f32x4, x.v[t][k][0]);
-        const f32x4 b = __builtin_bit_cast(f32x4, x.v[t][k][1]);
+        const f32x4 a = __builtin_bit_cast(f32x4, x.v[t][kk][0]);
+        const f32x4 b = __builtin_bit_cast(f32x4, x.v[t][kk][1]);
         const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        split8(f, bh[t][k], bl[t][k]);
+        split8(f, bh[t], bl[t]);
+        if constexpr (NSQ) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) nsq[t] = fmaf(f[i], f[i], nsq[t]);
+          for (int i = 0; i < 8; ++i) nsq[t] = fmaf(f[i], f[i], nsq[t]);
+        }
       } else {
-        bh[t][k] = x.v[t][k][0];
+        bh[t] = x.v[t][kk][0];
+        bl[t] = bh[t];
+        if constexpr (NSQ) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float lo = bf16_lo(bh[t][k][i]), hi = bf16_hi(bh[t][k][i]);
-          nsq[t] = fmaf(lo, lo, fmaf(hi, hi, nsq[t]));
+          for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_lo(bh[t][i]), hi = bf16_hi(bh[t][i]);
+            nsq[t] = fmaf(lo, lo, fmaf(hi, hi, nsq[t]));
+          }
         }
       }
     }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    u32x4 ah[8], al[8];
+    for (int gq = 0; gq < 4; ++gq) {
+      if (gq >= 2 && !two) break;  // wave-uniform: the pair's second panel is absent
+      u32x4 fh[4], fl[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int f = (m * 4 + k) * 2;
-      ah[m] = img[f * kFragVec + frag_lane];
-      al[m] = img[(f + 1) * kFragVec + frag_lane];
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);  // the 16 LDS reads
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        acc[t][m] = mfma_bf16(ah[m], bh[t][k], acc[t][m]);
-        acc[t][m] = mfma_bf16(al[m], bh[t][k], acc[t][m]);
-        if constexpr (F32IN) acc[t][m] = mfma_bf16(ah[m], bl[t][k], acc[t][m]);
+      for (int i = 0; i < 4; ++i) {
+        const int f = (4 * gq + i) * 4 + 2 * kk;
+        fh[i] = buf[f * kFragVec + frag_lane];
+        fl[i] = buf[(f + 1) * kFragVec + frag_lane];
       }
-    __builtin_amdgcn_sched_group_barrier(0x008, F32IN ? 48 : 32, 0);  // then the step's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the group's 8 LDS reads
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x4 &c = acc[t][4 * gq + i];
+          c = mfma_bf16(fh[i], bh[t], c);
+          c = mfma_bf16(fl[i], bh[t], c);
+          if constexpr (LO) c = mfma_bf16(fh[i], bl[t], c);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8 * (LO ? 3 : 2), 0);  // then their MFMAs
+    }
   }
 }
 
-// Pass 1: rotation panel, norms, search and pack; prod: residual norm partials.
+// Rotation (or projection) of the workgroup's 128 vectors for the panel pair,
+// over the input chunks: units of 64 contraction elements stream through one
+// 64 KB LDS buffer (two workgroups share a CU, so one's MFMAs run while the
+// other waits for its unit).  Units wholly past d are skipped.
+template <bool F32IN, bool NSQ>
+__device__ __forceinline__ void rotate_pair(const void *xin, const u32x4 *img0, const u32x4 *img1, bool two,
+                                            u32x4 *buf, const TiledArgs &a, const int64_t (&row)[2], int wave,
+                                            int lane, int grp, f32x4 (&acc)[2][16], float (&nsq)[2]) {
+  XUnit<F32IN> xa;
+  for (int u = 0; 64 * u < a.d; ++u) {
+    const int c = u >> 1, kh = u & 1;
+    if (u > 0) __syncthreads();  // every wave is done with the previous unit
+    stage_unit(img0 + (size_t)c * kImageVec, img1 + (size_t)c * kImageVec, two, kh, buf, wave, lane);
+    load_unit<F32IN>(xa, xin, row, 64 * u, a.d, grp);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int frag_lane = lane;
+    asm volatile("" : "+v"(frag_lane));
+    mma_unit<F32IN, F32IN, NSQ>(xa, buf, frag_lane, two, acc, nsq);
+  }
+}
+
+// Search and pack of one panel's 32 coordinates of column tile t (lane's
+// vector v); prod: the squared residual partial.
+template <int MB, bool PROD>
+__device__ __forceinline__ float search_pack(const f32x4 *acc, int p, int grp, float nu, float inv, float sv,
+                                             uint32_t tab_addr, uint32_t cent_addr, const TiledArgs &a,
+                                             uint8_t *crow, bool live) {
+  uint32_t w[MB > 0 ? MB : 1];
+#pragma unroll
+  for (int i = 0; i < (MB > 0 ? MB : 1); ++i) w[i] = 0;
+  float part = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int coord = 128 * p + 32 * grp + j;  // coordinate of acc[j >> 2][j & 3]
+    const float y = acc[j >> 2][j & 3];
+    if (coord < a.d) {
+      float cv = 0.f;
+      if constexpr (MB > 0) {
+        const uint32_t idx = cell_index_rt(tab_addr, y, nu, sv, a);
+        put_field<MB>(w, j, idx);
+        if constexpr (PROD) cv = *(lds_f32 *)(uintptr_t)(cent_addr + 4 * idx);
+      }
+      if constexpr (PROD) {
+        const float r = fmaf(y, inv, -cv);
+        part = fmaf(r, r, part);
+      }
+    }
+  }
+  if constexpr (MB > 0) {
+    // the lane's 4 MB bytes at offset 16 p MB + 4 grp MB of the code row; whole
+    // words past the row (padding of the last panel) are not stored
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int64_t off = (int64_t)16 * p * MB + 4 * grp * MB + 4 * i;
+      if (live && off < a.code_row) *(uint32_t *)(crow + off) = w[i];
+    }
+  }
+  return part;
+}
+
+// Pass 1: rotation of a panel pair, norms, search and pack; prod: residual norm partials.
 template <int MB, bool PROD, bool F32IN>
 __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_rot(const void *__restrict__ xin, TiledArgs a,
                                                                 const u32x4 *__restrict__ img_all,
@@ -153,15 +235,18 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_rot(const void *__re
                                                                 uint8_t *__restrict__ codes, float *__restrict__ norms,
                                                                 int *__restrict__ rn_fix) {
   extern __shared__ u32x4 dyn_lds[];
-  u32x4 *buf = dyn_lds;  // the image buffer, then the cell table, then the codebook
-  uint32_t *tab = (uint32_t *)((char *)dyn_lds + kImgBytes);
+  u32x4 *buf = dyn_lds;  // the unit buffer, then the cell table, then the codebook
+  uint32_t *tab = (uint32_t *)((char *)dyn_lds + kUnitBytes);
   float *cent_lds = (float *)(tab + a.cell_words);
-  const int p = blockIdx.x, s = blockIdx.z, g = s % a.groups;
+  const int pp = blockIdx.x, s = blockIdx.z, g = s % a.groups;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int panels = a.chunks;  // square blocks: as many output panels as contraction chunks
-  const u32x4 *img = img_all + ((size_t)g * panels + p) * (size_t)a.chunks * kImageVec;
+  const int p0 = a.pair * pp;
+  const bool two = a.pair == 2 && p0 + 1 < panels;
+  const u32x4 *img0 = img_all + ((size_t)g * panels + p0) * (size_t)a.chunks * kImageVec;
+  const u32x4 *img1 = two ? img0 + (size_t)a.chunks * kImageVec : img0;
 
   for (int i = tid; i < a.cell_words; i += kTiledThreads) tab[i] = cells[i];
   if (PROD && MB > 0)
@@ -174,26 +259,13 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_rot(const void *__re
     v[t] = (int64_t)blockIdx.y * kTiledVectors + 32 * wave + 16 * t + col;
     row[t] = set_row0 + (v[t] < a.n ? v[t] : a.n - 1);  // ragged tail: a valid row, results discarded
   }
-  XChunk<F32IN> xa;
-  f32x4 acc[2][8];
+  f32x4 acc[2][16];
   float nsq[2] = {0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
-
-  // One image buffer per workgroup and two workgroups per CU: while one waits
-  // for its chunk's image and inputs, the other one's MFMAs run.
-  for (int c = 0; c < a.chunks; ++c) {
-    if (c > 0) __syncthreads();  // every wave is done with the previous image
-    stage_image(img + (size_t)c * kImageVec, buf, wave, lane);
-    load_chunk<F32IN>(xa, xin, row, c, a.d, grp);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int frag_lane = lane;
-    asm volatile("" : "+v"(frag_lane));
-    mma_chunk<F32IN>(xa, buf, frag_lane, acc, nsq);
-  }
+    for (int m = 0; m < 16; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
+  rotate_pair<F32IN, true>(xin, img0, img1, two, buf, a, row, wave, lane, grp, acc, nsq);
 
   const uint32_t tab_addr = lds_addr(tab);
   const uint32_t cent_addr = lds_addr(cent_lds);
@@ -205,49 +277,25 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_rot(const void *__re
     const float nu = __builtin_amdgcn_sqrtf(q2);
     const float inv = __builtin_amdgcn_rcpf(nu > 0.f ? nu : 1.f);
     const float sv = a.cell_scale * inv;
-    uint32_t w[MB > 0 ? MB : 1];
-#pragma unroll
-    for (int i = 0; i < (MB > 0 ? MB : 1); ++i) w[i] = 0;
-    float part = 0.f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int coord = 128 * p + 32 * grp + j;  // coordinate of acc[t][j >> 2][j & 3]
-      const float y = acc[t][j >> 2][j & 3];
-      if (coord < a.d) {
-        float cv = 0.f;
-        if constexpr (MB > 0) {
-          const uint32_t idx = cell_index_rt(tab_addr, y, nu, sv, a);
-          put_field<MB>(w, j, idx);
-          if constexpr (PROD) cv = *(lds_f32 *)(uintptr_t)(cent_addr + 4 * idx);
-        }
-        if constexpr (PROD) {
-          const float r = fmaf(y, inv, -cv);
-          part = fmaf(r, r, part);
-        }
-      }
-    }
     const bool live = v[t] < a.n;
-    if constexpr (MB > 0) {
-      // the lane's 4 MB bytes at offset 16 p MB + 4 grp MB of the code row; whole
-      // words past the row (padding of the last panel) are not stored
-      uint8_t *crow = codes + (set_row0 + v[t]) * a.code_row;
+    uint8_t *crow = codes + (set_row0 + v[t]) * a.code_row;
+    if (live && pp == 0 && grp == 0) norms[set_row0 + v[t]] = nu;
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        const int64_t off = (int64_t)16 * p * MB + 4 * grp * MB + 4 * i;
-        if (live && off < a.code_row) *(uint32_t *)(crow + off) = w[i];
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && !two) break;
+      float part = search_pack<MB, PROD>(&acc[t][8 * h], p0 + h, grp, nu, inv, sv, tab_addr, cent_addr, a, crow, live);
+      if constexpr (PROD) {  // each panel's share in fixed point, so the sum does not depend on the order
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        if (live && grp == 0 && nu > 0.f) atomicAdd(rn_fix + set_row0 + v[t], (int)rintf(part * kFix));
       }
-    }
-    if (live && p == 0 && grp == 0) norms[set_row0 + v[t]] = nu;
-    if constexpr (PROD) {
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (live && grp == 0 && nu > 0.f) atomicAdd(rn_fix + set_row0 + v[t], (int)rintf(part * kFix));
     }
   }
 }
 
-// Pass 2 (prod): signs of S x - nu M c[idx], K = d (x) then d (codes);
-// panel 0 also turns the fixed-point residual norms into float32.
+// Pass 2 (prod): signs of S x - nu M c[idx] for a pair of projection panels,
+// K = d (x) then d (codes); pair 0 also turns the fixed-point residual norms
+// into float32.
 template <int MB, bool F32IN>
 __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__restrict__ xin, TiledArgs a,
                                                                  const u32x4 *__restrict__ img_all,
@@ -256,15 +304,18 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__r
                                                                  const float *__restrict__ norms,
                                                                  uint8_t *__restrict__ signs, float *__restrict__ rnorms) {
   extern __shared__ u32x4 dyn_lds[];
-  u32x4 *buf = dyn_lds;  // the image buffer, then the codebook
-  float *cent_lds = (float *)((char *)dyn_lds + kImgBytes);
-  const int p = blockIdx.x, s = blockIdx.z, g = s % a.groups;
+  u32x4 *buf = dyn_lds;  // the unit buffer, then the codebook
+  float *cent_lds = (float *)((char *)dyn_lds + kUnitBytes);
+  const int pp = blockIdx.x, s = blockIdx.z, g = s % a.groups;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int panels = a.chunks;
-  const int kchunks = (MB > 0 ? 2 : 1) * a.chunks;
-  const u32x4 *img = img_all + ((size_t)g * panels + p) * (size_t)(2 * a.chunks) * kImageVec;
+  const int p0 = a.pair * pp;
+  const bool two = a.pair == 2 && p0 + 1 < panels;
+  // per panel: the S blocks of the chunks, then the M blocks
+  const u32x4 *img0 = img_all + ((size_t)g * panels + p0) * (size_t)(2 * a.chunks) * kImageVec;
+  const u32x4 *img1 = two ? img0 + (size_t)(2 * a.chunks) * kImageVec : img0;
 
   if (MB > 0)
     for (int i = tid; i < (1 << MB); i += kTiledThreads) cent_lds[i] = cent[i];
@@ -278,35 +329,27 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__r
     row[t] = set_row0 + (v[t] < a.n ? v[t] : a.n - 1);
     nu[t] = norms[row[t]];
   }
-  XChunk<F32IN> xa;
-  f32x4 acc[2][8];
+  f32x4 acc[2][16];
   float dummy[2] = {0.f, 0.f};
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int m = 0; m < 8; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
-  const uint32_t cent_addr = lds_addr(cent_lds);
+    for (int m = 0; m < 16; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
+  // S x over the input chunks
+  rotate_pair<F32IN, false>(xin, img0, img1, two, buf, a, row, wave, lane, grp, acc, dummy);
 
-  // S x over the input chunks (one image buffer, as in pass 1)
-  for (int c = 0; c < a.chunks; ++c) {
-    if (c > 0) __syncthreads();
-    stage_image(img + (size_t)c * kImageVec, buf, wave, lane);
-    load_chunk<F32IN>(xa, xin, row, c, a.d, grp);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int frag_lane = lane;
-    asm volatile("" : "+v"(frag_lane));
-    mma_chunk<F32IN>(xa, buf, frag_lane, acc, dummy);
-  }
   // - nu M c[idx] over the code chunks: B = -nu c for coordinates
-  // 128 cc + 32 grp + 8 k + e (the lane's 32 codes), split into bf16 hi/lo;
-  // coordinates past d meet zero columns
+  // 128 cc + 32 grp + 8 k + e (the lane's 32 codes of the chunk), split into
+  // bf16 hi/lo; coordinates past d meet zero columns.  Every K step of a code
+  // chunk holds coordinates of all four lane groups, so no unit is skipped.
   if constexpr (MB > 0) {
-    for (int c = a.chunks; c < kchunks; ++c) {
-      __syncthreads();  // every wave is done with the previous image
-      stage_image(img + (size_t)c * kImageVec, buf, wave, lane);
-      const int cc = c - a.chunks;
-      XChunk<true> cx;
+    const uint32_t cent_addr = lds_addr(cent_lds);
+    const u32x4 *cimg0 = img0 + (size_t)a.chunks * kImageVec, *cimg1 = img1 + (size_t)a.chunks * kImageVec;
+    for (int u = 0; u < 2 * a.chunks; ++u) {
+      const int cc = u >> 1, kh = u & 1;
+      __syncthreads();  // every wave is done with the previous unit
+      stage_unit(cimg0 + (size_t)cc * kImageVec, cimg1 + (size_t)cc * kImageVec, two, kh, buf, wave, lane);
+      XUnit<true> cx;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         uint32_t cw[MB];
@@ -315,7 +358,8 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__r
 #pragma unroll
         for (int i = 0; i < MB; ++i) cw[i] = off + 4 * i < a.code_row ? *(const uint32_t *)(crow + off + 4 * i) : 0u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int kk = 0; kk < 2; ++kk) {
+          const int k = 2 * kh + kk;
           float f[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -325,30 +369,35 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__r
             idx &= (1u << MB) - 1;
             f[e] = -nu[t] * *(lds_f32 *)(uintptr_t)(cent_addr + 4 * idx);
           }
-          cx.v[t][k][0] = __builtin_bit_cast(u32x4, f32x4{f[0], f[1], f[2], f[3]});
-          cx.v[t][k][1] = __builtin_bit_cast(u32x4, f32x4{f[4], f[5], f[6], f[7]});
+          cx.v[t][kk][0] = __builtin_bit_cast(u32x4, f32x4{f[0], f[1], f[2], f[3]});
+          cx.v[t][kk][1] = __builtin_bit_cast(u32x4, f32x4{f[4], f[5], f[6], f[7]});
         }
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       int frag_lane = lane;
       asm volatile("" : "+v"(frag_lane));
-      mma_chunk<true>(cx, buf, frag_lane, acc, dummy);
+      mma_unit<true, true, false>(cx, buf, frag_lane, two, acc, dummy);
     }
   }
 
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int proj = 128 * p + 32 * grp + j;
-      if (proj < a.d && acc[t][j >> 2][j & 3] >= 0.f) bits |= 1u << j;
-    }
     const bool live = v[t] < a.n;
-    const int64_t off = (int64_t)16 * p + 4 * grp;
-    if (live && off < a.sign_row) *(uint32_t *)(signs + (set_row0 + v[t]) * a.sign_row + off) = bits;
-    if (live && p == 0 && grp == 0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && !two) break;
+      const int p = p0 + h;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int proj = 128 * p + 32 * grp + j;
+        if (proj < a.d && acc[t][8 * h + (j >> 2)][j & 3] >= 0.f) bits |= 1u << j;
+      }
+      const int64_t off = (int64_t)16 * p + 4 * grp;
+      if (live && off < a.sign_row) *(uint32_t *)(signs + (set_row0 + v[t]) * a.sign_row + off) = bits;
+    }
+    if (live && pp == 0 && grp == 0) {
       const int fx = *(volatile int *)(rnorms + set_row0 + v[t]);  // written by pass 1 as fixed point
       rnorms[set_row0 + v[t]] = nu[t] > 0.f ? __builtin_amdgcn_sqrtf((float)fx / kFix) : 0.f;
     }
@@ -375,9 +424,13 @@ hipError_t run_tiled(const DeviceTables &t, const void *x, int64_t n_sets, int64
   a.cell_last = 0x40000000u + 2u * (uint32_t)t.cell_radius;
   a.cell_words = MB > 0 ? 2 * (2 * t.cell_radius + 1) : 0;
   const int panels = a.chunks;
-  const dim3 grid((unsigned)panels, (unsigned)((n + kTiledVectors - 1) / kTiledVectors), (unsigned)n_sets);
+  const int64_t tiles = (n + kTiledVectors - 1) / kTiledVectors;
+  // pairs of panels per workgroup halve the split work per MFMA; a launch with
+  // fewer than about four rounds of workgroups keeps one panel each
+  a.pair = (panels + 1) / 2 * tiles * n_sets >= 2048 ? 2 : 1;
+  const dim3 grid((unsigned)((panels + a.pair - 1) / a.pair), (unsigned)tiles, (unsigned)n_sets);
   const size_t cent_bytes = 4 * (size_t)(1 << MB) > 64 ? 4 * (size_t)(1 << MB) : 64;  // the codebook
-  const size_t lds1 = kImgBytes + 4 * (size_t)a.cell_words + cent_bytes;
+  const size_t lds1 = kUnitBytes + 4 * (size_t)a.cell_words + cent_bytes;
   hipError_t e = hipFuncSetAttribute((const void *)k_tiled_rot<MB, PROD, F32IN>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
   if (e != hipSuccess) return e;
@@ -390,7 +443,7 @@ hipError_t run_tiled(const DeviceTables &t, const void *x, int64_t n_sets, int64
                      (const u32x4 *)t.tiled_rot, t.cells, t.cent, codes, norms, (int *)rnorms);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (PROD) {
-    const size_t lds2 = kImgBytes + cent_bytes;
+    const size_t lds2 = kUnitBytes + cent_bytes;
     e = hipFuncSetAttribute((const void *)k_tiled_sign<MB, F32IN>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds2);
     if (e != hipSuccess) return e;
