@@ -19,9 +19,11 @@
 // TurboQuant_prod adds a second pass.  The QJL signs need the residual of the
 // whole vector, so they are taken as sign(S x - nu M c[idx]) = sign(S r)
 // (nu > 0; M = S Pi^T, c[idx] decoded from the codes the first pass wrote),
-// a GEMM over 2 d contraction elements with images of S and M.  The residual
-// norm is gathered across panels in fixed point (integer atomics, exact and
-// order-independent) and finished by panel 0 of the second pass.
+// a GEMM over 2 d contraction elements with images of S and M: M c[idx]
+// first, its B operands read from a table of code pairs, then each column
+// scaled by -nu and S x added.  The residual norm is gathered across panels
+// in fixed point (integer atomics, exact and order-independent) and finished
+// by panel 0 of the second pass.
 //   [ttakun] TurboQuant_mse / TurboQuant_prod; [tqnet] 实现步骤草图;
 //   [admirer] 第二步 (QJL signs of the residual).
 #include <hip/hip_runtime.h>
@@ -107,39 +109,18 @@ __device__ __forceinline__ void load_unit(XUnit<F32IN> &r, const void *xin, cons
     }
 }
 
-// acc[t][m] += unit (LDS) x the unit's B operands, for row tiles m < 8 (one
-// panel) or m < 16 (two); also ||x||^2 of the unit's elements when NSQ.  Per
-// K step the fragments go in four groups of eight (four row tiles, hi and
-// lo), each group read before its MFMAs.
-template <bool F32IN, bool LO, bool NSQ>
-__device__ __forceinline__ void mma_unit(const XUnit<F32IN> &x, const u32x4 *buf, int frag_lane, bool two,
-                                         f32x4 (&acc)[2][16], float (&nsq)[2]) {
+// acc[t][m] += unit (LDS) x B operands, for row tiles m < 8 (one panel) or
+// m < 16 (two); `operands(kk, bh, bl)` gives the bf16 hi (and lo) B operands
+// of K step kk for the two column tiles.  Per K step the fragments go in four
+// groups of eight (four row tiles, hi and lo), each group read before its
+// MFMAs.
+template <bool LO, typename Operands>
+__device__ __forceinline__ void mma_unit_ops(const u32x4 *buf, int frag_lane, bool two, f32x4 (&acc)[2][16],
+                                             Operands operands) {
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     u32x4 bh[2], bl[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if constexpr (F32IN) {
-        const f32x4 a = __builtin_bit_cast(f32x4, x.v[t][kk][0]);
-        const f32x4 b = __builtin_bit_cast(f32x4, x.v[t][kk][1]);
-        const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        split8(f, bh[t], bl[t]);
-        if constexpr (NSQ) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) nsq[t] = fmaf(f[i], f[i], nsq[t]);
-        }
-      } else {
-        bh[t] = x.v[t][kk][0];
-        bl[t] = bh[t];
-        if constexpr (NSQ) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float lo = bf16_lo(bh[t][i]), hi = bf16_hi(bh[t][i]);
-            nsq[t] = fmaf(lo, lo, fmaf(hi, hi, nsq[t]));
-          }
-        }
-      }
-    }
+    operands(kk, bh, bl);
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       if (gq >= 2 && !two) break;  // wave-uniform: the pair's second panel is absent
@@ -165,6 +146,38 @@ __device__ __forceinline__ void mma_unit(const XUnit<F32IN> &x, const u32x4 *buf
   }
 }
 
+// The same with the unit's input elements as B operands, split into bf16 hi/lo
+// (float32 input) K step by K step; also ||x||^2 of the elements when NSQ.
+template <bool F32IN, bool NSQ>
+__device__ __forceinline__ void mma_unit(const XUnit<F32IN> &x, const u32x4 *buf, int frag_lane, bool two,
+                                         f32x4 (&acc)[2][16], float (&nsq)[2]) {
+  mma_unit_ops<F32IN>(buf, frag_lane, two, acc, [&](int kk, u32x4(&bh)[2], u32x4(&bl)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if constexpr (F32IN) {
+        const f32x4 a = __builtin_bit_cast(f32x4, x.v[t][kk][0]);
+        const f32x4 b = __builtin_bit_cast(f32x4, x.v[t][kk][1]);
+        const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        split8(f, bh[t], bl[t]);
+        if constexpr (NSQ) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) nsq[t] = fmaf(f[i], f[i], nsq[t]);
+        }
+      } else {
+        bh[t] = x.v[t][kk][0];
+        bl[t] = bh[t];
+        if constexpr (NSQ) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = bf16_lo(bh[t][i]), hi = bf16_hi(bh[t][i]);
+            nsq[t] = fmaf(lo, lo, fmaf(hi, hi, nsq[t]));
+          }
+        }
+      }
+    }
+  });
+}
+
 // Rotation (or projection) of the workgroup's 128 vectors for the panel pair,
 // over the input chunks: units of 64 contraction elements stream through one
 // 64 KB LDS buffer (two workgroups share a CU, so one's MFMAs run while the
@@ -183,7 +196,7 @@ __device__ __forceinline__ void rotate_pair(const void *xin, const u32x4 *img0, 
     __syncthreads();
     int frag_lane = lane;
     asm volatile("" : "+v"(frag_lane));
-    mma_unit<F32IN, F32IN, NSQ>(xa, buf, frag_lane, two, acc, nsq);
+    mma_unit<F32IN, NSQ>(xa, buf, frag_lane, two, acc, nsq);
   }
 }
 
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_rot(const void *__re
 }
 
 // Pass 2 (prod): signs of S x - nu M c[idx] for a pair of projection panels,
-// K = d (x) then d (codes); pair 0 also turns the fixed-point residual norms
+// K = d (codes) then d (x); pair 0 also turns the fixed-point residual norms
 // into float32.
 template <int MB, bool F32IN>
 __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__restrict__ xin, TiledArgs a,
@@ -304,8 +317,8 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__r
                                                                  const float *__restrict__ norms,
                                                                  uint8_t *__restrict__ signs, float *__restrict__ rnorms) {
   extern __shared__ u32x4 dyn_lds[];
-  u32x4 *buf = dyn_lds;  // the unit buffer, then the codebook
-  float *cent_lds = (float *)((char *)dyn_lds + kUnitBytes);
+  u32x4 *buf = dyn_lds;  // the unit buffer, then the code-pair table
+  u32x2 *lut = (u32x2 *)((char *)dyn_lds + kUnitBytes);
   const int pp = blockIdx.x, s = blockIdx.z, g = s % a.groups;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -317,8 +330,13 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__r
   const u32x4 *img0 = img_all + ((size_t)g * panels + p0) * (size_t)(2 * a.chunks) * kImageVec;
   const u32x4 *img1 = two ? img0 + (size_t)(2 * a.chunks) * kImageVec : img0;
 
+  // code pair e (codes e % 2^MB, e / 2^MB) -> (bf16 hi parts, bf16 lo parts) of their centroids
   if (MB > 0)
-    for (int i = tid; i < (1 << MB); i += kTiledThreads) cent_lds[i] = cent[i];
+    for (int e = tid; e < (1 << (2 * MB)); e += kTiledThreads) {
+      const float c0 = cent[e & ((1 << MB) - 1)], c1 = cent[e >> MB];
+      const uint32_t h = bf16x2(c0, c1);
+      lut[e] = u32x2{h, bf16x2(c0 - bf16_lo(h), c1 - bf16_hi(h))};
+    }
 
   const int64_t set_row0 = (int64_t)s * a.n;
   int64_t v[2], row[2];
@@ -335,51 +353,59 @@ __global__ __launch_bounds__(kTiledThreads, 2) void k_tiled_sign(const void *__r
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int m = 0; m < 16; ++m) acc[t][m] = f32x4{0, 0, 0, 0};
-  // S x over the input chunks
-  rotate_pair<F32IN, false>(xin, img0, img1, two, buf, a, row, wave, lane, grp, acc, dummy);
 
-  // - nu M c[idx] over the code chunks: B = -nu c for coordinates
-  // 128 cc + 32 grp + 8 k + e (the lane's 32 codes of the chunk), split into
-  // bf16 hi/lo; coordinates past d meet zero columns.  Every K step of a code
-  // chunk holds coordinates of all four lane groups, so no unit is skipped.
+  // M c[idx] over the code chunks, with B = c for coordinates 128 cc + 32 grp
+  // + 8 k + e (the lane's 32 codes of the chunk): a table read per code pair
+  // gives both elements' hi and lo parts.  Coordinates past d meet zero
+  // columns; every K step of a code chunk holds coordinates of all four lane
+  // groups, so no unit is skipped.  Each lane then scales its column (its
+  // vector) by -nu, and S x accumulates on top.
   if constexpr (MB > 0) {
-    const uint32_t cent_addr = lds_addr(cent_lds);
+    const uint32_t lut_addr = lds_addr(lut);
     const u32x4 *cimg0 = img0 + (size_t)a.chunks * kImageVec, *cimg1 = img1 + (size_t)a.chunks * kImageVec;
+    uint32_t cw[2][MB];
     for (int u = 0; u < 2 * a.chunks; ++u) {
       const int cc = u >> 1, kh = u & 1;
-      __syncthreads();  // every wave is done with the previous unit
+      if (u > 0) __syncthreads();  // every wave is done with the previous unit
       stage_unit(cimg0 + (size_t)cc * kImageVec, cimg1 + (size_t)cc * kImageVec, two, kh, buf, wave, lane);
-      XUnit<true> cx;
+      if (kh == 0) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        uint32_t cw[MB];
-        const int64_t off = (int64_t)16 * cc * MB + 4 * grp * MB;
-        const uint8_t *crow = codes + row[t] * a.code_row;
+        for (int t = 0; t < 2; ++t) {
+          const int64_t off = (int64_t)16 * cc * MB + 4 * grp * MB;
+          const uint8_t *crow = codes + row[t] * a.code_row;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) cw[i] = off + 4 * i < a.code_row ? *(const uint32_t *)(crow + off + 4 * i) : 0u;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int k = 2 * kh + kk;
-          float f[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 8 * k + e, bit = j * MB, wi = bit >> 5, sh = bit & 31;
-            uint32_t idx = cw[wi] >> sh;
-            if (sh + MB > 32) idx |= cw[wi + 1] << (32 - sh);
-            idx &= (1u << MB) - 1;
-            f[e] = -nu[t] * *(lds_f32 *)(uintptr_t)(cent_addr + 4 * idx);
-          }
-          cx.v[t][kk][0] = __builtin_bit_cast(u32x4, f32x4{f[0], f[1], f[2], f[3]});
-          cx.v[t][kk][1] = __builtin_bit_cast(u32x4, f32x4{f[4], f[5], f[6], f[7]});
+          for (int i = 0; i < MB; ++i)
+            cw[t][i] = off + 4 * i < a.code_row ? *(const uint32_t *)(crow + off + 4 * i) : 0u;
         }
       }
       __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      __syncthreads();  // also orders the table writes before the first reads
       int frag_lane = lane;
       asm volatile("" : "+v"(frag_lane));
-      mma_unit<true, true, false>(cx, buf, frag_lane, two, acc, dummy);
+      mma_unit_ops<true>(buf, frag_lane, two, acc, [&](int kk, u32x4(&bh)[2], u32x4(&bl)[2]) {
+        const int k = 2 * kh + kk;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {  // elements 2 i, 2 i + 1: codes 8 k + 2 i and 8 k + 2 i + 1
+            const int bit = (8 * k + 2 * i) * MB, wi = bit >> 5, sh = bit & 31;
+            uint32_t pi = cw[t][wi] >> sh;
+            if (sh + 2 * MB > 32) pi |= cw[t][wi + 1] << (32 - sh);
+            pi &= (1u << (2 * MB)) - 1;
+            const u32x2 e = *(lds_u32x2 *)(uintptr_t)(lut_addr + 8 * pi);
+            bh[t][i] = e[0];
+            bl[t][i] = e[1];
+          }
+      });
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int m = 0; m < 16; ++m) acc[t][m] *= -nu[t];
+    __syncthreads();  // every wave is done with the last code unit
   }
+  // S x over the input chunks
+  rotate_pair<F32IN, false>(xin, img0, img1, two, buf, a, row, wave, lane, grp, acc, dummy);
 
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -443,7 +469,7 @@ hipError_t run_tiled(const DeviceTables &t, const void *x, int64_t n_sets, int64
                      (const u32x4 *)t.tiled_rot, t.cells, t.cent, codes, norms, (int *)rnorms);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if constexpr (PROD) {
-    const size_t lds2 = kUnitBytes + cent_bytes;
+    const size_t lds2 = kUnitBytes + (MB > 0 ? ((size_t)8 << (2 * MB)) : 0) + 64;  // the code-pair table
     e = hipFuncSetAttribute((const void *)k_tiled_sign<MB, F32IN>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)lds2);
     if (e != hipSuccess) return e;
