@@ -35,10 +35,14 @@ __device__ inline int read_field(const uint8_t *row, int j, int mb) {
   return (int)((w >> sh) & ((1u << mb) - 1u));
 }
 
-// TurboQuant_mse / _prod quantize of one vector per workgroup.
-// Shared memory: x[d], y[d] (later the residual), idx[d] (int; reused for the
-// sign bits once the codes are packed).
-template <typename T>
+// TurboQuant_mse / _prod quantize of V vectors of one set per workgroup
+// (grid: chunk of V vectors x set), so that every element of Pi^T (and M^T)
+// read from L2 serves V vectors.  Shared memory: x[V][d], y[V][d] (later the
+// residual), idx[V][d] (int; reused for the sign bits once the codes are
+// packed), then the boundaries.  The index of y is the number of k with
+// nu t_k < y, found by halving over the boundaries in LDS (the products
+// nu t_k are monotone in k, so this is the plain count).
+template <typename T, int V>
 __global__ __launch_bounds__(kThreads) void k_quant_generic(
     const T *__restrict__ x, int d, int64_t n, int groups, int mse_bits, int prod,
     const float *__restrict__ PiT, const float *__restrict__ MT, const float *__restrict__ cent,
@@ -47,73 +51,108 @@ __global__ __launch_bounds__(kThreads) void k_quant_generic(
     float *__restrict__ rnorms) {
   extern __shared__ float sm[];
   __shared__ float red[kThreads / 64];
-  float *xs = sm, *ys = sm + d;
-  int *is = (int *)(sm + 2 * d), *bs = is;
-  const int64_t row = blockIdx.x;
-  const int g = (int)((row / n) % groups);
+  float *xs = sm, *ys = sm + V * d;
+  int *is = (int *)(sm + 2 * V * d), *bs = is;
+  float *tb = sm + 3 * V * d;
+  const int s = blockIdx.y;
+  const int g = s % groups;
+  const int64_t i0 = (int64_t)blockIdx.x * V;
+  const int nv = (int)min((int64_t)V, n - i0);  // vectors of this workgroup (the set's last one may hold fewer)
+  const int64_t row0 = (int64_t)s * n + i0;
   const int tid = threadIdx.x;
-  const T *xv = x + row * d;
+  const int L = 1 << mse_bits;
+  for (int k = tid; k + 1 < L; k += kThreads) tb[k] = bnd[k];
 
-  float acc = 0.f;
-  for (int j = tid; j < d; j += kThreads) {
-    const float v = load_x(xv, j);
-    xs[j] = v;
-    acc = fmaf(v, v, acc);
+  float nu[V], nthr[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float acc = 0.f;
+    for (int j = tid; j < d; j += kThreads) {
+      const float e = v < nv ? load_x(x + (row0 + v) * d, j) : 0.f;
+      xs[v * d + j] = e;
+      acc = fmaf(e, e, acc);
+    }
+    nu[v] = sqrtf(block_sum(acc, red));
+    nthr[v] = nu[v] > 0.f ? nu[v] : 1.f;  // a zero vector has y = 0
   }
-  const float nu = sqrtf(block_sum(acc, red));
-  const float nthr = nu > 0.f ? nu : 1.f;  // a zero vector has y = 0
   __syncthreads();
 
   // y = Pi x  (PiT[k][j] = Pi[j][k]; consecutive threads read consecutive j)
   const float *P = PiT + (size_t)g * d * d;
-  const int L = 1 << mse_bits;
   for (int j = tid; j < d; j += kThreads) {
-    float y = 0.f;
-    for (int k = 0; k < d; ++k) y = fmaf(P[(size_t)k * d + j], xs[k], y);
-    int idx = 0;
-    if (mse_bits > 0)
-      for (int k = 0; k + 1 < L; ++k) idx += (nthr * bnd[k] < y) ? 1 : 0;
-    is[j] = idx;
-    // prod residual in the rotated domain: Pi r * ||x|| = y - ||x|| c[idx]
-    ys[j] = mse_bits > 0 ? y - nu * cent[idx] : y;
+    float y[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) y[v] = 0.f;
+    for (int k = 0; k < d; ++k) {
+      const float pk = P[(size_t)k * d + j];
+#pragma unroll
+      for (int v = 0; v < V; ++v) y[v] = fmaf(pk, xs[v * d + k], y[v]);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      int idx = 0;
+      if (mse_bits > 0)
+        for (int step = L >> 1; step > 0; step >>= 1)
+          if (nthr[v] * tb[idx + step - 1] < y[v]) idx += step;
+      is[v * d + j] = idx;
+      // prod residual in the rotated domain: Pi r * ||x|| = y - ||x|| c[idx]
+      ys[v * d + j] = mse_bits > 0 ? y[v] - nu[v] * cent[idx] : y[v];
+    }
   }
   __syncthreads();
 
-  if (mse_bits > 0) {
-    uint8_t *crow = codes + row * code_row;
-    for (int byte = tid; byte < code_row; byte += kThreads) {
-      uint32_t v = 0;
-      for (int p = 0; p < 8; ++p) {
-        const int sb = byte * 8 + p, j = sb / mse_bits, k = sb % mse_bits;
-        if (j < d) v |= (uint32_t)((is[j] >> k) & 1) << p;
+  for (int v = 0; v < nv; ++v) {
+    const int64_t row = row0 + v;
+    if (mse_bits > 0) {
+      uint8_t *crow = codes + row * code_row;
+      for (int byte = tid; byte < code_row; byte += kThreads) {
+        uint32_t w = 0;
+        for (int q = 0; q < 8; ++q) {
+          const int sb = byte * 8 + q, j = sb / mse_bits, k = sb % mse_bits;
+          if (j < d) w |= (uint32_t)((is[v * d + j] >> k) & 1) << q;
+        }
+        crow[byte] = (uint8_t)w;
       }
-      crow[byte] = (uint8_t)v;
     }
+    if (tid == 0) norms[row] = nu[v];
   }
-  if (tid == 0) norms[row] = nu;
   if (!prod) return;
 
-  float r2 = 0.f;
-  for (int j = tid; j < d; j += kThreads) r2 = fmaf(ys[j], ys[j], r2);
-  const float rn = sqrtf(block_sum(r2, red));
+  float rn[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    float r2 = 0.f;
+    for (int j = tid; j < d; j += kThreads) r2 = fmaf(ys[v * d + j], ys[v * d + j], r2);
+    rn[v] = sqrtf(block_sum(r2, red));  // syncs first: the codes above are packed before bs overwrites is
+  }
   // sign(S r) = sign(M (Pi r)), M = S Pi^T
   const float *M = MT + (size_t)g * d * d;
   for (int i = tid; i < d; i += kThreads) {
-    float p = 0.f;
-    for (int j = 0; j < d; ++j) p = fmaf(M[(size_t)j * d + i], ys[j], p);
-    bs[i] = p >= 0.f ? 1 : 0;
+    float pr[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) pr[v] = 0.f;
+    for (int j = 0; j < d; ++j) {
+      const float mj = M[(size_t)j * d + i];
+#pragma unroll
+      for (int v = 0; v < V; ++v) pr[v] = fmaf(mj, ys[v * d + j], pr[v]);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) bs[v * d + i] = pr[v] >= 0.f ? 1 : 0;
   }
   __syncthreads();
-  uint8_t *srow = signs + row * sign_row;
-  for (int byte = tid; byte < sign_row; byte += kThreads) {
-    uint32_t v = 0;
-    for (int p = 0; p < 8; ++p) {
-      const int i = byte * 8 + p;
-      if (i < d) v |= (uint32_t)bs[i] << p;
+  for (int v = 0; v < nv; ++v) {
+    const int64_t row = row0 + v;
+    uint8_t *srow = signs + row * sign_row;
+    for (int byte = tid; byte < sign_row; byte += kThreads) {
+      uint32_t w = 0;
+      for (int q = 0; q < 8; ++q) {
+        const int i = byte * 8 + q;
+        if (i < d) w |= (uint32_t)bs[v * d + i] << q;
+      }
+      srow[byte] = (uint8_t)w;
     }
-    srow[byte] = (uint8_t)v;
+    if (tid == 0) rnorms[row] = nu[v] > 0.f ? rn[v] / nu[v] : 0.f;
   }
-  if (tid == 0) rnorms[row] = nu > 0.f ? rn / nu : 0.f;
 }
 
 // ------------------------------------------------------- mixed precision --
@@ -312,35 +351,61 @@ __global__ __launch_bounds__(kAppendThreads) void k_append(
   if (tid == 0 && keep) rnorms[row] = nu > 0.f ? rn / nu : 0.f;
 }
 
-// Reconstruction of one vector per workgroup:
-// out = nu (Pi^T c[idx] + sqrt(pi/2)/d * gamma * S^T z).
+// Reconstruction of V vectors of one set per workgroup (grid: chunk x set):
+// out = nu (Pi^T c[idx] + sqrt(pi/2)/d * gamma * S^T z), every element of Pi
+// and S read from L2 serving V vectors.
+template <int V>
 __global__ __launch_bounds__(kThreads) void k_dequant_generic(
     const uint8_t *__restrict__ codes, const uint8_t *__restrict__ signs,
     const float *__restrict__ norms, const float *__restrict__ rnorms, int d, int64_t n,
     int groups, int mse_bits, int prod, const float *__restrict__ Pi, const float *__restrict__ S,
     const float *__restrict__ cent, int64_t code_row, int64_t sign_row, float *__restrict__ out) {
   extern __shared__ float sm[];
-  float *cv = sm, *zv = sm + d;
-  const int64_t row = blockIdx.x;
-  const int g = (int)((row / n) % groups);
+  float *cv = sm, *zv = sm + V * d;
+  const int s = blockIdx.y;
+  const int g = s % groups;
+  const int64_t i0 = (int64_t)blockIdx.x * V;
+  const int nv = (int)min((int64_t)V, n - i0);
+  const int64_t row0 = (int64_t)s * n + i0;
   const int tid = threadIdx.x;
-  const uint8_t *crow = codes ? codes + row * code_row : nullptr;
-  const uint8_t *srow = prod ? signs + row * sign_row : nullptr;
-  for (int j = tid; j < d; j += kThreads) {
-    cv[j] = mse_bits > 0 ? cent[read_field(crow, j, mse_bits)] : 0.f;
-    if (prod) zv[j] = ((srow[j >> 3] >> (j & 7)) & 1) ? 1.f : -1.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int64_t row = row0 + (v < nv ? v : 0);  // rows past the set repeat the first (not stored)
+    const uint8_t *crow = codes ? codes + row * code_row : nullptr;
+    const uint8_t *srow = prod ? signs + row * sign_row : nullptr;
+    for (int j = tid; j < d; j += kThreads) {
+      cv[v * d + j] = mse_bits > 0 ? cent[read_field(crow, j, mse_bits)] : 0.f;
+      if (prod) zv[v * d + j] = ((srow[j >> 3] >> (j & 7)) & 1) ? 1.f : -1.f;
+    }
   }
   __syncthreads();
-  const float nu = norms[row];
-  const float w = prod ? kQjlScale / (float)d * rnorms[row] : 0.f;
+  float nu[V], w[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int64_t row = row0 + (v < nv ? v : 0);
+    nu[v] = norms[row];
+    w[v] = prod ? kQjlScale / (float)d * rnorms[row] : 0.f;
+  }
   const float *P = Pi + (size_t)g * d * d, *Sg = S ? S + (size_t)g * d * d : nullptr;
   for (int i = tid; i < d; i += kThreads) {
-    float a = 0.f, b = 0.f;
+    float a[V], b[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) a[v] = b[v] = 0.f;
     if (mse_bits > 0)
-      for (int j = 0; j < d; ++j) a = fmaf(P[(size_t)j * d + i], cv[j], a);
+      for (int j = 0; j < d; ++j) {
+        const float pj = P[(size_t)j * d + i];
+#pragma unroll
+        for (int v = 0; v < V; ++v) a[v] = fmaf(pj, cv[v * d + j], a[v]);
+      }
     if (prod)
-      for (int j = 0; j < d; ++j) b = fmaf(Sg[(size_t)j * d + i], zv[j], b);
-    out[row * d + i] = nu * fmaf(w, b, a);
+      for (int j = 0; j < d; ++j) {
+        const float sj = Sg[(size_t)j * d + i];
+#pragma unroll
+        for (int v = 0; v < V; ++v) b[v] = fmaf(sj, zv[v * d + j], b[v]);
+      }
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (v < nv) out[(row0 + v) * d + i] = nu[v] * fmaf(w[v], b[v], a[v]);
   }
 }
 
@@ -574,21 +639,39 @@ __global__ void k_unpack(const uint8_t *__restrict__ in, int bits, int64_t rows,
 
 }  // namespace
 
+// Vectors per workgroup of the generic quantize and dequantize: 8 when their
+// rows fit 48 KB of LDS, else fewer (1 at d = 4096).
+static int generic_batch(int d, int per_vec_floats) {
+  int v = 8;
+  while (v > 1 && (size_t)v * per_vec_floats * d * sizeof(float) > 48 * 1024) v >>= 1;
+  return v;
+}
+
 hipError_t launch_quant_generic(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,
                                 int64_t n, uint8_t *codes, uint8_t *signs, float *norms,
                                 float *rnorms, hipStream_t st) {
-  const int64_t rows = n_sets * n;
-  if (rows == 0) return hipSuccess;
-  const size_t shmem = (size_t)3 * t.d * sizeof(float);
+  if (n_sets == 0 || n == 0) return hipSuccess;
+  const int V = generic_batch(t.d, 3);
+  const size_t shmem = (size_t)3 * V * t.d * sizeof(float) + sizeof(float) * (1u << t.mse_bits);
   const int prod = t.variant == 1;
-  if (dtype == 0)
-    hipLaunchKernelGGL(k_quant_generic<float>, dim3((unsigned)rows), dim3(kThreads), shmem, st,
-                       (const float *)x, t.d, n, t.groups, t.mse_bits, prod, t.PiT, t.MT, t.cent,
-                       t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms);
-  else
-    hipLaunchKernelGGL(k_quant_generic<uint16_t>, dim3((unsigned)rows), dim3(kThreads), shmem, st,
-                       (const uint16_t *)x, t.d, n, t.groups, t.mse_bits, prod, t.PiT, t.MT,
-                       t.cent, t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms);
+  const dim3 grid((unsigned)((n + V - 1) / V), (unsigned)n_sets);
+#define TQ_QG(T, VV)                                                                                              \
+  hipLaunchKernelGGL((k_quant_generic<T, VV>), grid, dim3(kThreads), shmem, st, (const T *)x, t.d, n, t.groups,   \
+                     t.mse_bits, prod, t.PiT, t.MT, t.cent, t.bnd, codes, t.code_row, signs, t.sign_row, norms, rnorms)
+#define TQ_QGV(T)                \
+  switch (V) {                   \
+    case 8: TQ_QG(T, 8); break;  \
+    case 4: TQ_QG(T, 4); break;  \
+    case 2: TQ_QG(T, 2); break;  \
+    default: TQ_QG(T, 1); break; \
+  }
+  if (dtype == 0) {
+    TQ_QGV(float)
+  } else {
+    TQ_QGV(uint16_t)
+  }
+#undef TQ_QGV
+#undef TQ_QG
   return hipGetLastError();
 }
 
@@ -650,12 +733,20 @@ hipError_t launch_add_inplace(float *out, const float *in, int64_t count, hipStr
 hipError_t launch_dequant_generic(const DeviceTables &t, const uint8_t *codes, const uint8_t *signs,
                                   const float *norms, const float *rnorms, int64_t n_sets, int64_t n,
                                   float *out, hipStream_t st) {
-  const int64_t rows = n_sets * n;
-  if (rows == 0) return hipSuccess;
-  const size_t shmem = (size_t)2 * t.d * sizeof(float);
-  hipLaunchKernelGGL(k_dequant_generic, dim3((unsigned)rows), dim3(kThreads), shmem, st, codes,
-                     signs, norms, rnorms, t.d, n, t.groups, t.mse_bits, (int)(t.variant == 1),
-                     t.Pi, t.S, t.cent, t.code_row, t.sign_row, out);
+  if (n_sets == 0 || n == 0) return hipSuccess;
+  const int V = generic_batch(t.d, 2);
+  const size_t shmem = (size_t)2 * V * t.d * sizeof(float);
+  const dim3 grid((unsigned)((n + V - 1) / V), (unsigned)n_sets);
+#define TQ_DG(VV)                                                                                                  \
+  hipLaunchKernelGGL((k_dequant_generic<VV>), grid, dim3(kThreads), shmem, st, codes, signs, norms, rnorms, t.d, n, \
+                     t.groups, t.mse_bits, (int)(t.variant == 1), t.Pi, t.S, t.cent, t.code_row, t.sign_row, out)
+  switch (V) {
+    case 8: TQ_DG(8); break;
+    case 4: TQ_DG(4); break;
+    case 2: TQ_DG(2); break;
+    default: TQ_DG(1); break;
+  }
+#undef TQ_DG
   return hipGetLastError();
 }
 
