@@ -1271,15 +1271,36 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
     const uint32_t v = atomicAdd(counter + lane, 1u);
     return (int)__builtin_amdgcn_readfirstlane(v);
   };
+  // A full block's logits go through this wave's 2 KB of the (now free)
+  // prologue scratch, [8 heads][64 keys], and leave as 16-byte stores: each
+  // instruction writes 256 contiguous bytes of four head rows.  Only this
+  // wave touches its region; lanes read what other lanes wrote, so
+  // wavefront-scope fences keep the compiler from moving a read above the
+  // writes it needs (or the next block's writes above the reads).
+  static_assert(W == 64 && kLogitWaves * 8 * W <= 2 * 4 * 8 * D, "staging fits the scratch");
+  float *stage = scratch + wave * 8 * W;
+  const int sh = lane >> 4, sk = 4 * (lane & 15);  // store lane: head sh (and sh + 4), keys sk .. sk + 3
+  const uint32_t rowS0 = sh < hc ? (uint32_t)((h0 + sh) * n_keys) * 4 : kDropped;
+  const uint32_t rowS1 = sh + 4 < hc ? (uint32_t)((h0 + sh + 4) * n_keys) * 4 : kDropped;
   auto score_store = [&](const KeyRegs<CW> &r, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
       float o0, o1;
       score_tile<MB, PROD>(r, u, bq, bp, code_base, sign_base, o0, o1);
-      const uint32_t key4 = (uint32_t)(tb + 16 * u + col) * 4;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o0), ro, rowA + key4, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o1), ro, rowB + key4, 0, 0);
+      stage[hA * W + 16 * u + col] = o0;
+      stage[hB * W + 16 * u + col] = o1;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 v0 = *(const u32x4 *)(stage + sh * W + sk);
+    const u32x4 v1 = *(const u32x4 *)(stage + (sh + 4) * W + sk);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t key4 = (uint32_t)(tb + sk) * 4;
+    __builtin_amdgcn_raw_buffer_store_b128(v0, ro, rowS0 + key4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v1, ro, rowS1 + key4, 0, 0);
   };
   if (b < nfull) {  // ra holds block b
     while (true) {
@@ -1428,8 +1449,8 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128_mixed(
   uint32_t *t_r = (uint32_t *)((char *)dyn_lds + GO::CODE_BYTES);
   float *qs = (float *)((char *)dyn_lds + GO::CODE_BYTES + GR::CODE_BYTES);
   float *qt = qs + 8 * D;
-  float *scratch = qt + 8 * D;                 // [4][8][D] partial sums
-  uint32_t *counter = (uint32_t *)(scratch + 4 * 8 * D);
+  float *scratch = qt + 8 * D;                 // [4][8][D] partial sums, later the stores' staging
+  uint32_t *counter = (uint32_t *)(scratch + 8 * 8 * D);
 
   const int s = blockIdx.y;
   const int g = s % groups;
@@ -1532,15 +1553,32 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128_mixed(
     o0 = fmaf(co[0] + co[1], r.no[u], (cr[0] + cr[1]) * r.nr[u]);
     o1 = fmaf(co[2] + co[3], r.no[u], (cr[2] + cr[3]) * r.nr[u]);
   };
+  // full blocks leave through this wave's 2 KB of the scratch as 16-byte
+  // stores, as in k_logits128
+  static_assert(W == 64 && kLogitWaves * 8 * W <= 8 * 8 * D, "staging fits the scratch");
+  float *stage = scratch + wave * 8 * W;
+  const int sh = lane >> 4, sk = 4 * (lane & 15);
+  const uint32_t rowS0 = sh < hc ? (uint32_t)((h0 + sh) * n_keys) * 4 : kDropped;
+  const uint32_t rowS1 = sh + 4 < hc ? (uint32_t)((h0 + sh + 4) * n_keys) * 4 : kDropped;
   auto score_store = [&](const MixKeyRegs &r, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
       float o0, o1;
       score(r, u, o0, o1);
-      const uint32_t key4 = (uint32_t)(tb + 16 * u + col) * 4;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o0), ro, rowA + key4, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o1), ro, rowB + key4, 0, 0);
+      stage[hA * W + 16 * u + col] = o0;
+      stage[hB * W + 16 * u + col] = o1;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const u32x4 v0 = *(const u32x4 *)(stage + sh * W + sk);
+    const u32x4 v1 = *(const u32x4 *)(stage + (sh + 4) * W + sk);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t key4 = (uint32_t)(tb + sk) * 4;
+    __builtin_amdgcn_raw_buffer_store_b128(v0, ro, rowS0 + key4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v1, ro, rowS1 + key4, 0, 0);
   };
   if (b < nfull) {  // ra holds block b
     while (true) {
@@ -2281,7 +2319,7 @@ hipError_t run_logits_mixed(const DeviceTables &to, const DeviceTables &tr, cons
   const int64_t rmax = to.code_row > tr.code_row ? to.code_row : tr.code_row;
   if (nq * n_keys * 4 >= (int64_t)kDropped || n_keys * rmax >= (int64_t)kDropped || n_keys > kFusedMaxKeys)
     return hipErrorNotSupported;
-  const size_t lds = LutGeom<MBO>::CODE_BYTES + LutGeom<MBR>::CODE_BYTES + 2 * 8 * D * 4 + 4 * 8 * D * 4 + 64 * 4;
+  const size_t lds = LutGeom<MBO>::CODE_BYTES + LutGeom<MBR>::CODE_BYTES + 2 * 8 * D * 4 + 8 * 8 * D * 4 + 64 * 4;
   hipError_t e0 = hipFuncSetAttribute((const void *)k_logits128_mixed<MBO, MBR>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e0 != hipSuccess) return e0;

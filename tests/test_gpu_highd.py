@@ -144,3 +144,48 @@ def test_tiled_bf16_input(d, variant, bits):
     check_indices(np.concatenate(gi), np.concatenate(oi), np.concatenate(oy), cd.boundaries, f"d={d}")
     if variant == O.PROD:
         qjl.check(f"d={d}")
+
+
+@pytest.mark.parametrize("d,variant,bits,dtype", [(264, O.MSE, 4, "f32"), (264, O.PROD, 3, "f32"),
+                                                  (520, O.PROD, 4, "bf16"), (520, O.MSE, 2, "bf16")])
+def test_tiled_panel_pairs_odd_panel_count(d, variant, bits, dtype):
+    """A launch large enough for two output panels per workgroup, with an odd
+    number of panels (the last pair holds one), a ragged last tile and two
+    sets of different groups: sampled vectors of both sets against the
+    oracle, and the first vectors of each set bit-identical to a small launch
+    (one panel per workgroup) of the same rows."""
+    n, sets = 90_001, 2
+    rng = np.random.default_rng(d + bits)
+    x = rng.standard_normal((sets, n, d)).astype(np.float32)
+    x[..., 5] *= 8.0  # an outlier channel
+    if dtype == "bf16":
+        xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
+        x = xt.float().cpu().numpy()
+    else:
+        xt = torch.from_numpy(x).cuda()
+    codec = tq.Codec(d, bits, variant, seed=3, groups=2)
+    out = codec.quantize(xt)
+    small = codec.quantize(xt[:, :777].contiguous())
+    torch.cuda.synchronize()
+    for k in ("codes", "signs", "norms", "rnorms"):
+        if out[k] is not None:
+            assert torch.equal(out[k][:, :777], small[k]), k
+    cd = O.make_codec(d, bits, variant, 3, groups=2)
+    mb = bits if variant == O.MSE else bits - 1
+    for s in range(sets):
+        rows = np.sort(np.random.default_rng(s).choice(n, SAMPLE, replace=False))
+        rows_t = torch.from_numpy(rows).cuda()
+        xs = x[s, rows].astype(np.float64)
+        norms = out["norms"][s].cpu().numpy()[rows]
+        if variant == O.MSE:
+            idx, nu, y = O.quantize_mse(cd, xs, s)
+            gidx = codec.unpack(out["codes"][s][rows_t], bits).cpu().numpy()
+            check_indices(gidx, idx, y, cd.boundaries, f"set {s}")
+            assert np.allclose(norms, nu, rtol=1e-5)
+            continue
+        res = O.quantize_prod(cd, xs, s)
+        gidx = codec.unpack(out["codes"][s][rows_t], mb).cpu().numpy()
+        check_indices(gidx, res["idx"], res["y"], cd.boundaries, f"set {s}")
+        gbits = codec.unpack(out["signs"][s][rows_t], 1).cpu().numpy()
+        check_qjl(cd, xs, gidx, gbits, out["rnorms"][s].cpu().numpy()[rows], s, f"set {s}")
+        assert np.allclose(norms, res["norms"], rtol=1e-5)
