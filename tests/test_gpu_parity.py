@@ -154,6 +154,10 @@ PROD_CASES = [
     (3, 2, "f32", 1, 64, 1),
     (2, 3, "f32", 2, 400, 2),
     (2, 1, "f32", 1, 100, 1),
+    # d not a multiple of 8: the generic kernels, 8 vectors per workgroup (ragged last group, two sets)
+    (100, 3, "f32", 2, 203, 2),
+    (100, 5, "bf16", 1, 77, 1),
+    (100, 1, "f32", 1, 9, 1),
 ]
 
 
