@@ -8,9 +8,10 @@
 //   (scaled by sqrt(pi/2)/d) per query, zero-padded to 256 coordinates.
 // k_topk: a workgroup of 4 waves (one per SIMD) scans one key range; each wave holds 16
 //   queries as f16 hi/lo MFMA A operands (two row tiles of 8 queries) and
-//   streams 16-key tiles: lane (key, grp) decodes the codes of coordinates
-//   64 grp .. 64 grp + 63 of its key through LDS tables (a code pair per
-//   4-byte read, eight signs -- or eight 1-bit codes -- per 16-byte read).
+//   streams 16-key tiles: lane (key, grp) decodes the codes of a quarter of
+//   its key's coordinates (d rounded up to 128, 224 or 256) through LDS
+//   tables (a code pair per 4-byte read, eight signs -- or eight 1-bit
+//   codes -- per 16-byte read).
 //   Scores above a query's current k-th best go to a small LDS buffer; a
 //   full buffer is merged into the query's running list, which lives in
 //   registers (lane i holds the i-th best).  Each wave writes its lists.
@@ -28,8 +29,11 @@ namespace {
 constexpr int kTkThreads = 256;           // one wave per SIMD: 512 registers per wave
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kTkQ = 16;                  // queries per wave: two row tiles of 8 (hi/lo rows)
-constexpr int kTkPad = 256;               // padded dimension: lane group g holds 64 g .. 64 g + 63
-constexpr int kTkKS = 8;                  // contraction steps of 32 coordinates
+constexpr int kTkPad = 256;               // largest dimension; the query rows are zero-padded to it
+// A scan with KS contraction steps of 32 coordinates covers 32 KS of them:
+// lane group g holds 8 KS g .. 8 KS g + 8 KS - 1 (the dimension rounded up
+// to 128, 224 or 256; coordinates past d meet zero query operands).
+constexpr int tk_steps(int d) { return d <= 128 ? 4 : d <= 224 ? 7 : 8; }
 constexpr int kTkRing = 4;                // tiles held in registers (three in flight)
 constexpr int kTkBuf = 64;                // buffered candidates per query
 constexpr int kTkMergeAt = kTkBuf - 16;   // a tile adds at most 16 per query
@@ -51,31 +55,46 @@ struct TkGeom {  // code-pair table: two codes -> two f16 values (alpha c)
 };
 
 // The key data of one 16-key tile in the lane's registers: its key's code
-// and sign bits of coordinates 64 grp .. 64 grp + 63, norm and residual norm.
-template <int MB, bool PROD>
+// and sign bits of coordinates 8 KS grp .. 8 KS grp + 8 KS - 1 (bit 0 of
+// word 0 first), norm and residual norm.
+template <int MB, bool PROD, int KS>
 struct TkKey {
-  uint32_t c[MB > 0 ? 2 * MB : 1];
-  uint32_t s[2];
+  static constexpr int CB = KS * MB, SB = KS;  // code and sign bytes of a lane group
+  uint32_t c[MB > 0 ? (CB + 3) / 4 : 1];
+  uint32_t s[(SB + 3) / 4];
   float nu, ga;
 };
 
-template <int MB, bool PROD>
-__device__ __forceinline__ void tk_load(TkKey<MB, PROD> &r, int64_t key, int grp,
+// BYTES bytes from byte offset `at` of a buffer into whole words, bit 0
+// first.  Rows are 16-byte aligned, so `at` is a multiple of 4 whenever BYTES
+// is; otherwise the covering aligned words are read and funnel-shifted.
+template <int BYTES>
+__device__ __forceinline__ void tk_load_run(uint32_t (&dst)[(BYTES + 3) / 4], __amdgpu_buffer_rsrc_t r,
+                                            uint32_t at) {
+  constexpr int NW = (BYTES + 3) / 4;
+  if constexpr (BYTES % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b32(r, at + 4 * i, 0, 0);
+  } else {
+    const uint32_t a0 = at & ~3u, sh = 8 * (at & 3u);
+    uint32_t w[NW + 1];
+#pragma unroll
+    for (int i = 0; i <= NW; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(r, a0 + 4 * i, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) dst[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], sh);
+  }
+}
+
+template <int MB, bool PROD, int KS>
+__device__ __forceinline__ void tk_load(TkKey<MB, PROD, KS> &r, int64_t key, int grp,
                                         __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, int64_t code_row,
                                         int64_t sign_row, __amdgpu_buffer_rsrc_t rn, __amdgpu_buffer_rsrc_t rg) {
   // codes, signs and norms through buffer resources: bytes past the arrays
-  // read as zero (the padded coordinates meet zero query operands); keys past
-  // the range are masked by the caller
-  if constexpr (MB > 0) {
-    const uint32_t off = (uint32_t)(key * code_row) + 8 * MB * grp;
-#pragma unroll
-    for (int i = 0; i < 2 * MB; ++i) r.c[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, off + 4 * i, 0, 0);
-  }
-  if constexpr (PROD) {
-    const uint32_t off = (uint32_t)(key * sign_row) + 8 * grp;
-    r.s[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-    r.s[1] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4, 0, 0);
-  }
+  // read as zero, and code bits past d (padding, or the next key's bytes)
+  // meet zero query operands; keys past the range are masked by the caller
+  using K = TkKey<MB, PROD, KS>;
+  if constexpr (MB > 0) tk_load_run<K::CB>(r.c, rc, (uint32_t)(key * code_row) + K::CB * grp);
+  if constexpr (PROD) tk_load_run<K::SB>(r.s, rs, (uint32_t)(key * sign_row) + K::SB * grp);
   r.nu = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, (uint32_t)key * 4, 0, 0));
   r.ga = PROD ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, (uint32_t)key * 4, 0, 0)) : 0.f;
 }
@@ -86,15 +105,16 @@ __device__ __forceinline__ void tk_load(TkKey<MB, PROD> &r, int64_t key, int grp
 // c1 (2 idx - 1); c1 is folded into the query).
 // The decoded B operands of one tile: code values (or 1-bit codes as
 // signs) and QJL signs of the lane's key for each contraction step.
+template <int KS>
 struct TkB {
-  u32x4 m[kTkKS], s[kTkKS];
+  u32x4 m[KS], s[KS];
 };
 
-template <int MB, bool PROD>
-__device__ __forceinline__ void tk_lookup(const TkKey<MB, PROD> &r, uint32_t sbase, uint32_t pbase, TkB &b) {
+template <int MB, bool PROD, int KS>
+__device__ __forceinline__ void tk_lookup(const TkKey<MB, PROD, KS> &r, uint32_t sbase, uint32_t pbase, TkB<KS> &b) {
   using G = TkGeom<MB>;
 #pragma unroll
-  for (int k = 0; k < kTkKS; ++k) {
+  for (int k = 0; k < KS; ++k) {
     if constexpr (MB == 1) {
       const uint32_t byte = (r.c[k >> 2] >> (8 * (k & 3))) & 0xFFu;
       b.m[k] = *(__attribute__((address_space(3))) const u32x4 *)(uintptr_t)((byte << 8) | sbase);
@@ -124,12 +144,12 @@ __device__ __forceinline__ void tk_lookup(const TkKey<MB, PROD> &r, uint32_t sba
 // lane (key, grp) gets queries 2 grp, 2 grp + 1 of each row tile (rows 4 grp
 // .. 4 grp + 3 = two queries x hi/lo).  MB == 1 decodes the 1-bit codes with
 // the sign table (c[idx] = c1 (2 idx - 1); c1 is folded into the query).
-template <int MB, bool PROD>
-__device__ __forceinline__ void tk_mma(const TkB &b, float nu, float ga, const u32x4 (&qm)[2][kTkKS],
-                                       const u32x4 (&qq)[2][kTkKS], float (&sc)[2][2]) {
+template <int MB, bool PROD, int KS>
+__device__ __forceinline__ void tk_mma(const TkB<KS> &b, float nu, float ga, const u32x4 (&qm)[2][KS],
+                                       const u32x4 (&qq)[2][KS], float (&sc)[2][2]) {
   f32x4 am[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, aq[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
-  for (int k = 0; k < kTkKS; ++k) {
+  for (int k = 0; k < KS; ++k) {
     if constexpr (MB > 0) {
       am[0] = mfma_f16(qm[0][k], b.m[k], am[0]);
       am[1] = mfma_f16(qm[1][k], b.m[k], am[1]);
@@ -230,7 +250,7 @@ __device__ __forceinline__ void tk_merge_batch(float &ls, int &li, const float2 
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int MB, bool PROD>
+template <int MB, bool PROD, int KS>
 __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
     const float *__restrict__ qprep, int nq, const uint8_t *__restrict__ codes, int64_t code_row,
     const uint8_t *__restrict__ signs, int64_t sign_row, const float *__restrict__ norms,
@@ -254,18 +274,18 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
     for (int e = tid; e < G::ENTRIES * G::COPIES; e += kTkThreads)
       ((uint32_t *)(lds + kTkPairOff))[e] = lut[e / G::COPIES];
   // query operands: row col of a row tile = (query col >> 1, part col & 1);
-  // element e of step k is coordinate 64 grp + 8 k + e
-  u32x4 qm[2][kTkKS], qq[2][kTkKS];
+  // element e of step k is coordinate 8 KS grp + 8 k + e
+  u32x4 qm[2][KS], qq[2][KS];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int q = qbase + rt * 8 + (col >> 1), part = col & 1;
 #pragma unroll
-    for (int ks = 0; ks < kTkKS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (q < nq && (m == 0 ? MB > 0 : PROD)) {
-          const f32x4 *src = (const f32x4 *)(qprep + ((int64_t)q * 2 + m) * kTkPad + 64 * grp + 8 * ks);
+          const f32x4 *src = (const f32x4 *)(qprep + ((int64_t)q * 2 + m) * kTkPad + 8 * KS * grp + 8 * ks);
           const f32x4 a = src[0], b = src[1];
           v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
           v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
@@ -289,7 +309,7 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int ks = 0; ks < kTkKS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       asm volatile("" : "+a"(qm[rt][ks]));
       asm volatile("" : "+a"(qq[rt][ks]));
     }
@@ -365,9 +385,9 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
   };
 
   // scores of tile t0 (decoded operands b, norms nu, ga) -> candidates
-  auto step = [&](const TkB &b, float nu, float ga, int64_t t0) __attribute__((always_inline)) {
+  auto step = [&](const TkB<KS> &b, float nu, float ga, int64_t t0) __attribute__((always_inline)) {
     float sc[2][2];
-    tk_mma<MB, PROD>(b, nu, ga, qm, qq, sc);
+    tk_mma<MB, PROD, KS>(b, nu, ga, qm, qq, sc);
     const int64_t key = t0 + col;
     const bool valid = key < ke;
     bool cand[2][2];
@@ -402,12 +422,12 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
   // run, the table reads of tile i + 1 are in flight (operand sets b0 / b1
   // alternate)
   const int64_t nt = (ke - kb + 15) / 16;
-  TkKey<MB, PROD> ring[kTkRing];
+  TkKey<MB, PROD, KS> ring[kTkRing];
 #pragma unroll
   for (int j = 0; j < kTkRing - 1; ++j)
-    tk_load<MB, PROD>(ring[j], kb + 16 * j + col, grp, rc, rs, code_row, sign_row, rn, rg);
-  TkB b0, b1;
-  tk_lookup<MB, PROD>(ring[0], sbase, pbase, b0);
+    tk_load<MB, PROD, KS>(ring[j], kb + 16 * j + col, grp, rc, rs, code_row, sign_row, rn, rg);
+  TkB<KS> b0, b1;
+  tk_lookup<MB, PROD, KS>(ring[0], sbase, pbase, b0);
   float nu0 = ring[0].nu, ga0 = ring[0].ga, nu1 = 0.f, ga1 = 0.f;
   // no branch inside the loop body (a branch there makes the wait-count pass
   // wait for the newest loads): the scan runs whole groups of 8 tiles, and
@@ -419,13 +439,13 @@ __global__ __launch_bounds__(kTkThreads, 1) void k_topk(
       const int64_t i = i0 + j;
       if (j == 5) refresh();
       if (j == 7) apply();
-      tk_load<MB, PROD>(ring[(j + kTkRing - 1) % kTkRing], kb + 16 * (i + kTkRing - 1) + col, grp, rc, rs, code_row,
+      tk_load<MB, PROD, KS>(ring[(j + kTkRing - 1) % kTkRing], kb + 16 * (i + kTkRing - 1) + col, grp, rc, rs, code_row,
                         sign_row, rn, rg);
-      TkB &bc = (j & 1) ? b1 : b0, &bn = (j & 1) ? b0 : b1;
+      TkB<KS> &bc = (j & 1) ? b1 : b0, &bn = (j & 1) ? b0 : b1;
       float &nuc = (j & 1) ? nu1 : nu0, &gac = (j & 1) ? ga1 : ga0;
       float &nun = (j & 1) ? nu0 : nu1, &gan = (j & 1) ? ga0 : ga1;
-      const TkKey<MB, PROD> &rk = ring[(j + 1) % kTkRing];
-      tk_lookup<MB, PROD>(rk, sbase, pbase, bn);
+      const TkKey<MB, PROD, KS> &rk = ring[(j + 1) % kTkRing];
+      tk_lookup<MB, PROD, KS>(rk, sbase, pbase, bn);
       nun = rk.nu;
       gan = rk.ga;
       step(bc, nuc, gac, kb + 16 * i);
@@ -511,7 +531,7 @@ size_t topk_workspace(const DeviceTables &t, int64_t nq, int64_t n_keys, int k) 
   return (prep + 255) / 256 * 256 + (lists + 255) / 256 * 256 + (size_t)nq * sizeof(int);
 }
 
-template <int MB, bool PROD>
+template <int MB, bool PROD, int KS>
 static hipError_t run_topk(const DeviceTables &t, const float *q, int64_t nq, const uint8_t *codes,
                            const uint8_t *signs, const float *norms, const float *rnorms, int64_t n_keys, int k,
                            float *ws, float *out_scores, int32_t *out_idx, hipStream_t st) {
@@ -525,11 +545,12 @@ static hipError_t run_topk(const DeviceTables &t, const float *q, int64_t nq, co
                      mscale, prep, gtau);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void *)k_topk<MB, PROD>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTkLds);
+  e = hipFuncSetAttribute((const void *)k_topk<MB, PROD, KS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kTkLds);
   if (e != hipSuccess) return e;
   const int64_t kps = (n_keys + S - 1) / S;
   const dim3 grid((unsigned)((nq + kTkWaves * kTkQ - 1) / (kTkWaves * kTkQ)), (unsigned)S);
-  hipLaunchKernelGGL((k_topk<MB, PROD>), grid, dim3(kTkThreads), kTkLds, st, prep, (int)nq, codes, t.code_row, signs,
+  hipLaunchKernelGGL((k_topk<MB, PROD, KS>), grid, dim3(kTkThreads), kTkLds, st, prep, (int)nq, codes, t.code_row, signs,
                      t.sign_row, norms, rnorms, n_keys, k, kps, t.logit_lut, lists, gtau);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_topk_merge, dim3((unsigned)nq), dim3(64), 0, st, lists, S, k, out_scores, out_idx);
@@ -543,9 +564,18 @@ hipError_t launch_topk(const DeviceTables &t, const float *q, int64_t nq, const 
   // buffer offsets are 32-bit
   if (n_keys * (t.code_row > t.sign_row ? t.code_row : t.sign_row) >= ((int64_t)1 << 31)) return hipErrorNotSupported;
   const bool prod = t.variant == 1;
-#define TQ_T(MB, P) \
-  if (t.mse_bits == MB && prod == P) \
-    return run_topk<MB, P>(t, q, nq, codes, signs, norms, rnorms, n_keys, k, (float *)ws, out_scores, out_idx, st);
+  const int ks = tk_steps(t.d);
+#define TQ_T(MB, P)                                                                                               \
+  if (t.mse_bits == MB && prod == P) {                                                                           \
+    if (ks == 4)                                                                                                 \
+      return run_topk<MB, P, 4>(t, q, nq, codes, signs, norms, rnorms, n_keys, k, (float *)ws, out_scores, out_idx, \
+                                st);                                                                             \
+    if (ks == 7)                                                                                                 \
+      return run_topk<MB, P, 7>(t, q, nq, codes, signs, norms, rnorms, n_keys, k, (float *)ws, out_scores, out_idx, \
+                                st);                                                                             \
+    return run_topk<MB, P, 8>(t, q, nq, codes, signs, norms, rnorms, n_keys, k, (float *)ws, out_scores, out_idx,   \
+                              st);                                                                               \
+  }
   TQ_T(0, true) TQ_T(1, false) TQ_T(1, true) TQ_T(2, false) TQ_T(2, true)
   TQ_T(3, false) TQ_T(3, true) TQ_T(4, false) TQ_T(4, true)
 #undef TQ_T

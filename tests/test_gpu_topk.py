@@ -45,7 +45,11 @@ def _stored(cd, keys):
     return out
 
 
-CASES = [(200, 2, O.PROD), (200, 4, O.PROD), (128, 3, O.MSE), (64, 1, O.PROD), (96, 5, O.PROD), (200, 4, O.MSE)]
+# d decides the scan's contraction steps: d <= 128 takes 4 (a lane group's codes are whole words), 128 < d
+# <= 224 takes 7 (7 mb code bytes and 7 sign bytes per lane group: unaligned runs unless mb = 4), and d > 224
+# takes 8
+CASES = [(200, 2, O.PROD), (200, 4, O.PROD), (128, 3, O.MSE), (64, 1, O.PROD), (96, 5, O.PROD), (200, 4, O.MSE),
+         (208, 3, O.PROD), (150, 2, O.MSE), (256, 3, O.PROD), (240, 2, O.MSE)]
 
 
 @pytest.mark.parametrize("d,bits,variant", CASES)
