@@ -119,9 +119,10 @@ int tq_dequantize(tq_handle h, const void *codes, const void *signs, const float
  * where k_hat is the tq_dequantize reconstruction.  q: [n_sets][nq][d] float32
  * (grouped-query attention passes the query heads of one KV head as one set).
  * The kernel rotates and projects each query once and never materialises
- * k_hat.  At d = 128 a set of up to 2^25 keys takes the streaming kernel;
- * longer sets (and other d) take the generic one, with the same results up
- * to fp32 rounding.  1 <= nq <= 64.  Errors: TQ_EINVAL, TQ_EHIP. */
+ * k_hat.  At d = 128 (mse bits <= 4) sets below 2^29 keys take the
+ * streaming kernel, in launches of at most 2^25 keys; longer sets (and other
+ * d) take the generic one, with the same results up to fp32 rounding.
+ * 1 <= nq <= 64.  Errors: TQ_EINVAL, TQ_EHIP. */
 int tq_logits(tq_handle h, const float *q, int64_t nq, const void *codes, const void *signs,
               const float *norms, const float *rnorms, int64_t n_sets, int64_t n_keys, float *out,
               void *stream);

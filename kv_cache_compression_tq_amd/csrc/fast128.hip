@@ -756,9 +756,32 @@ struct KeyRegs {
   float nv[kLogitTiles], gv[kLogitTiles];
 };
 
-// Largest key count the fused kernels address: every per-set byte offset
-// (key index times at most 64 bytes per row) stays below 2^31.
+// Largest key count one launch of the fused kernels addresses: every byte
+// offset into a key array (key index times at most 64 bytes per row) stays
+// below 2^31.  The logits take longer sets in chunks of this many keys.
 constexpr int64_t kFusedMaxKeys = int64_t(1) << 25;
+
+// Heads per logits launch: the output rows of a set's heads h0 .. h0 + hp -
+// 1 are addressed with 32-bit byte offsets, so hp n_keys 4 < 2^31 (8, the
+// kernel's head slots, below 2^26 keys; fewer above).  0: too many keys.
+static int logit_heads_per_launch(int64_t n_keys) {
+  int hp = 8;
+  while (hp > 0 && hp * n_keys * 4 >= (int64_t)kDropped) hp >>= 1;
+  return hp;
+}
+
+// Key ranges per workgroup for a launch over n keys of n_sets sets: about
+// one workgroup per CU overall, a whole number of iterations `unit` each.
+static int64_t logit_grid_x(int64_t n_sets, int64_t n, int64_t unit, int64_t *kpw) {
+  int64_t gx = (256 + n_sets - 1) / n_sets;
+  const int64_t max_gx = (n + unit - 1) / unit;
+  if (gx > max_gx) gx = max_gx;
+  if (gx < 1) gx = 1;
+  int64_t k = (n + gx - 1) / gx;
+  k = (k + unit - 1) / unit * unit;
+  *kpw = k;
+  return (n + k - 1) / k;
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t set_rsrc(const void *base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferFlags);
@@ -1147,7 +1170,7 @@ template <int MB, bool PROD>
 __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
     const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ codes,
     const uint8_t *__restrict__ signs, const float *__restrict__ norms,
-    const float *__restrict__ rnorms, int64_t n_keys, int groups, const float *__restrict__ PiT,
+    const float *__restrict__ rnorms, int64_t n_keys, int64_t set_keys, int groups, const float *__restrict__ PiT,
     const float *__restrict__ ST, const uint32_t *__restrict__ lut, float lut_inv_scale,
     int64_t keys_per_wg, float *__restrict__ out) {
   constexpr int CW = MB;  // code words per lane (32 coordinates)
@@ -1168,7 +1191,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   const int col = lane & 15, grp = lane >> 4;
   const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
   const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
-  const int64_t srow = (int64_t)s * n_keys;
+  const int64_t srow = (int64_t)s * set_keys;
   KeyRsrc kr;  // the set's arrays and the lane's offsets
   kr.c = set_rsrc(MB > 0 ? codes + srow * (16 * CW) : codes, MB > 0 ? n_keys * (16 * CW) : 0);
   kr.s = set_rsrc(PROD ? signs + srow * 16 : signs, PROD ? n_keys * 16 : 0);
@@ -1254,12 +1277,15 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   }
 
   const int hA = 2 * grp, hB = 2 * grp + 1;  // heads held by this lane
-  // logits of this set through a buffer resource: lanes without a head, and
-  // keys past the end, get an offset past num_records and store nothing
+  // logits of this set's heads h0 .. h0 + hc - 1 through a buffer resource
+  // (rows set_keys apart; out points at this launch's first key): lanes
+  // without a head, and keys past the end, get an offset past num_records
+  // and store nothing
   const __amdgpu_buffer_rsrc_t ro =
-      __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)s * nq * n_keys, 0, (int)(nq * n_keys * 4), kBufferFlags);
-  const uint32_t rowA = hA < hc ? (uint32_t)((h0 + hA) * n_keys) * 4 : kDropped;
-  const uint32_t rowB = hB < hc ? (uint32_t)((h0 + hB) * n_keys) * 4 : kDropped;
+      __builtin_amdgcn_make_buffer_rsrc(out + ((int64_t)s * nq + h0) * set_keys, 0, (int)(hc * set_keys * 4),
+                                        kBufferFlags);
+  const uint32_t rowA = hA < hc ? (uint32_t)(hA * set_keys) * 4 : kDropped;
+  const uint32_t rowB = hB < hc ? (uint32_t)(hB * set_keys) * 4 : kDropped;
   // each lane reads its own copy of every table entry (the tables start at
   // LDS address 0 and CODE_BYTES, so the copy offset is OR-ed in)
   const uint32_t code_base = 4 * (lane & (GM::COPIES - 1));
@@ -1280,8 +1306,8 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128(
   static_assert(W == 64 && kLogitWaves * 8 * W <= 2 * 4 * 8 * D, "staging fits the scratch");
   float *stage = scratch + wave * 8 * W;
   const int sh = lane >> 4, sk = 4 * (lane & 15);  // store lane: head sh (and sh + 4), keys sk .. sk + 3
-  const uint32_t rowS0 = sh < hc ? (uint32_t)((h0 + sh) * n_keys) * 4 : kDropped;
-  const uint32_t rowS1 = sh + 4 < hc ? (uint32_t)((h0 + sh + 4) * n_keys) * 4 : kDropped;
+  const uint32_t rowS0 = sh < hc ? (uint32_t)(sh * set_keys) * 4 : kDropped;
+  const uint32_t rowS1 = sh + 4 < hc ? (uint32_t)((sh + 4) * set_keys) * 4 : kDropped;
   auto score_store = [&](const KeyRegs<CW> &r, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
@@ -1439,7 +1465,7 @@ template <int MBO, int MBR>
 __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128_mixed(
     const float *__restrict__ q, int nq, int h0, int hc, const uint8_t *__restrict__ codes_o, int64_t row_o,
     const uint8_t *__restrict__ codes_r, int64_t row_r, const float *__restrict__ norms_o,
-    const float *__restrict__ norms_r, int64_t n_keys, int groups, const float *__restrict__ RT,
+    const float *__restrict__ norms_r, int64_t n_keys, int64_t set_keys, int groups, const float *__restrict__ RT,
     const uint32_t *__restrict__ lut_o, float inv_o, const uint32_t *__restrict__ lut_r, float inv_r,
     int64_t keys_per_wg, float *__restrict__ out) {
   using GO = LutGeom<MBO>;
@@ -1459,7 +1485,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128_mixed(
   const int col = lane & 15, grp = lane >> 4;
   const int64_t kbeg = (int64_t)blockIdx.x * keys_per_wg;
   const int64_t kend = kbeg + keys_per_wg < n_keys ? kbeg + keys_per_wg : n_keys;
-  const int64_t srow = (int64_t)s * n_keys;
+  const int64_t srow = (int64_t)s * set_keys;
   MixKeyRsrc kr;
   kr.co = set_rsrc(codes_o + srow * row_o, n_keys * row_o);
   kr.cr = set_rsrc(codes_r + srow * row_r, n_keys * row_r);
@@ -1539,9 +1565,10 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128_mixed(
 
   const int hA = 2 * grp, hB = 2 * grp + 1;  // heads held by this lane
   const __amdgpu_buffer_rsrc_t ro =
-      __builtin_amdgcn_make_buffer_rsrc(out + (int64_t)s * nq * n_keys, 0, (int)(nq * n_keys * 4), kBufferFlags);
-  const uint32_t rowA = hA < hc ? (uint32_t)((h0 + hA) * n_keys) * 4 : kDropped;
-  const uint32_t rowB = hB < hc ? (uint32_t)((h0 + hB) * n_keys) * 4 : kDropped;
+      __builtin_amdgcn_make_buffer_rsrc(out + ((int64_t)s * nq + h0) * set_keys, 0, (int)(hc * set_keys * 4),
+                                        kBufferFlags);
+  const uint32_t rowA = hA < hc ? (uint32_t)(hA * set_keys) * 4 : kDropped;
+  const uint32_t rowB = hB < hc ? (uint32_t)(hB * set_keys) * 4 : kDropped;
   const uint32_t base_o = 4 * (lane & (GO::COPIES - 1)), base_r = 4 * (lane & (GR::COPIES - 1));
   auto grab = [&]() {
     const uint32_t v = atomicAdd(counter + lane, 1u);  // lane 0's word is the block counter
@@ -1558,8 +1585,8 @@ __global__ __launch_bounds__(kLogitThreads, 1) void k_logits128_mixed(
   static_assert(W == 64 && kLogitWaves * 8 * W <= 8 * 8 * D, "staging fits the scratch");
   float *stage = scratch + wave * 8 * W;
   const int sh = lane >> 4, sk = 4 * (lane & 15);
-  const uint32_t rowS0 = sh < hc ? (uint32_t)((h0 + sh) * n_keys) * 4 : kDropped;
-  const uint32_t rowS1 = sh + 4 < hc ? (uint32_t)((h0 + sh + 4) * n_keys) * 4 : kDropped;
+  const uint32_t rowS0 = sh < hc ? (uint32_t)(sh * set_keys) * 4 : kDropped;
+  const uint32_t rowS1 = sh + 4 < hc ? (uint32_t)((sh + 4) * set_keys) * 4 : kDropped;
   auto score_store = [&](const MixKeyRegs &r, int64_t tb) {
 #pragma unroll
     for (int u = 0; u < KT; ++u) {
@@ -2274,31 +2301,36 @@ hipError_t run_quant(const DeviceTables &t, const void *x, int64_t n_sets, int64
   return hipGetLastError();
 }
 
+// Sets longer than kFusedMaxKeys keys run as several launches, one per
+// chunk of keys (the key arrays and the output advanced to the chunk, with
+// the set stride n_keys passed alongside); each launch scores up to
+// logit_heads_per_launch(n_keys) heads.
 template <int MB, bool PROD>
 hipError_t run_logits(const DeviceTables &t, const float *q, int64_t nq, const uint8_t *codes,
                       const uint8_t *signs, const float *norms, const float *rnorms, int64_t n_sets,
                       int64_t n_keys, float *out, hipStream_t st) {
   const int64_t unit = kLogitWaves * 16 * kLogitTiles;  // keys per workgroup iteration
-  int64_t gx = (256 + n_sets - 1) / n_sets;             // about one workgroup per CU
-  const int64_t max_gx = (n_keys + unit - 1) / unit;
-  if (gx > max_gx) gx = max_gx;
-  if (gx < 1) gx = 1;
-  int64_t kpw = (n_keys + gx - 1) / gx;
-  kpw = (kpw + unit - 1) / unit * unit;
-  gx = (n_keys + kpw - 1) / kpw;
-  // a set's logits are addressed with 32-bit byte offsets below the dropped-store offset
-  if (nq * n_keys * 4 >= (int64_t)kDropped || n_keys > kFusedMaxKeys) return hipErrorNotSupported;
+  const int hp = logit_heads_per_launch(n_keys);
+  if (hp == 0) return hipErrorNotSupported;
   const size_t lds = LutGeom<MB>::CODE_BYTES + kSignBytes + kQueryBytes + 2 * 4 * 8 * D * 4 + 64 * 4;
   hipError_t e0 = hipFuncSetAttribute((const void *)k_logits128<MB, PROD>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e0 != hipSuccess) return e0;
-  for (int64_t h0 = 0; h0 < nq; h0 += 8) {
-    const int hc = (int)(nq - h0 < 8 ? nq - h0 : 8);
-    hipLaunchKernelGGL((k_logits128<MB, PROD>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kLogitThreads), lds,
-                       st, q, (int)nq, (int)h0, hc, codes, signs, norms, rnorms, n_keys, t.groups,
-                       t.PiT, t.ST, t.logit_lut, t.lut_inv_scale, kpw, out);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  for (int64_t k0 = 0; k0 < n_keys; k0 += kFusedMaxKeys) {
+    const int64_t n = n_keys - k0 < kFusedMaxKeys ? n_keys - k0 : kFusedMaxKeys;
+    int64_t kpw;
+    const int64_t gx = logit_grid_x(n_sets, n, unit, &kpw);
+    const uint8_t *ck = MB > 0 ? codes + k0 * (16 * MB) : codes;
+    const uint8_t *sk = PROD ? signs + k0 * 16 : signs;
+    const float *gk = PROD ? rnorms + k0 : rnorms;
+    for (int64_t h0 = 0; h0 < nq; h0 += hp) {
+      const int hc = (int)(nq - h0 < hp ? nq - h0 : hp);
+      hipLaunchKernelGGL((k_logits128<MB, PROD>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kLogitThreads), lds,
+                         st, q, (int)nq, (int)h0, hc, ck, sk, norms + k0, gk, n, n_keys, t.groups, t.PiT, t.ST,
+                         t.logit_lut, t.lut_inv_scale, kpw, out + k0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
@@ -2309,27 +2341,26 @@ hipError_t run_logits_mixed(const DeviceTables &to, const DeviceTables &tr, cons
                             const float *norms_r, int64_t n_sets, int64_t n_keys, int groups, float *out,
                             hipStream_t st) {
   const int64_t unit = kLogitWaves * 16 * kLogitTiles;  // keys per workgroup iteration
-  int64_t gx = (256 + n_sets - 1) / n_sets;             // about one workgroup per CU
-  const int64_t max_gx = (n_keys + unit - 1) / unit;
-  if (gx > max_gx) gx = max_gx;
-  if (gx < 1) gx = 1;
-  int64_t kpw = (n_keys + gx - 1) / gx;
-  kpw = (kpw + unit - 1) / unit * unit;
-  gx = (n_keys + kpw - 1) / kpw;
   const int64_t rmax = to.code_row > tr.code_row ? to.code_row : tr.code_row;
-  if (nq * n_keys * 4 >= (int64_t)kDropped || n_keys * rmax >= (int64_t)kDropped || n_keys > kFusedMaxKeys)
-    return hipErrorNotSupported;
+  const int hp = logit_heads_per_launch(n_keys);
+  if (hp == 0 || rmax > 64) return hipErrorNotSupported;
   const size_t lds = LutGeom<MBO>::CODE_BYTES + LutGeom<MBR>::CODE_BYTES + 2 * 8 * D * 4 + 8 * 8 * D * 4 + 64 * 4;
   hipError_t e0 = hipFuncSetAttribute((const void *)k_logits128_mixed<MBO, MBR>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e0 != hipSuccess) return e0;
-  for (int64_t h0 = 0; h0 < nq; h0 += 8) {
-    const int hc = (int)(nq - h0 < 8 ? nq - h0 : 8);
-    hipLaunchKernelGGL((k_logits128_mixed<MBO, MBR>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kLogitThreads),
-                       lds, st, q, (int)nq, (int)h0, hc, codes_o, to.code_row, codes_r, tr.code_row, norms_o, norms_r,
-                       n_keys, groups, RT, to.logit_lut, to.lut_inv_scale, tr.logit_lut, tr.lut_inv_scale, kpw, out);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  for (int64_t k0 = 0; k0 < n_keys; k0 += kFusedMaxKeys) {  // chunks as in run_logits
+    const int64_t n = n_keys - k0 < kFusedMaxKeys ? n_keys - k0 : kFusedMaxKeys;
+    int64_t kpw;
+    const int64_t gx = logit_grid_x(n_sets, n, unit, &kpw);
+    for (int64_t h0 = 0; h0 < nq; h0 += hp) {
+      const int hc = (int)(nq - h0 < hp ? nq - h0 : hp);
+      hipLaunchKernelGGL((k_logits128_mixed<MBO, MBR>), dim3((unsigned)gx, (unsigned)n_sets), dim3(kLogitThreads),
+                         lds, st, q, (int)nq, (int)h0, hc, codes_o + k0 * to.code_row, to.code_row,
+                         codes_r + k0 * tr.code_row, tr.code_row, norms_o + k0, norms_r + k0, n, n_keys, groups, RT,
+                         to.logit_lut, to.lut_inv_scale, tr.logit_lut, tr.lut_inv_scale, kpw, out + k0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

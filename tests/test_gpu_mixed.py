@@ -215,6 +215,36 @@ def test_mixed_decode_logits_full_size_sampled():
         check_rows(out[s][:, kt].cpu().numpy(), ref, f"set {s}")
 
 
+def test_mixed_fused_logits_past_the_key_chunk():
+    """The one-pass mixed logits on two sets of 2^25 + 64 keys (two chunks of
+    keys per set) and 10 heads (two head groups): sampled keys, those around
+    the chunk boundary and the last 64 among them, against the oracle."""
+    d, n_sets, n_keys, nq = 128, 2, (1 << 25) + 64, 10
+    rng = np.random.default_rng(21)
+    chans = np.stack([rng.permutation(d)[:64] for _ in range(2)])
+    mc = tq.MixedCodec(d, 2, tq.TQ_MSE, 0, chans, groups=2)
+    mx = O.make_mixed(d, 2, O.MSE, 0, chans, groups=2)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(22)
+    cache = mc.empty_codes(n_sets, n_keys)
+    for part in cache:
+        part["codes"].copy_(torch.randint(0, 256, part["codes"].shape, dtype=torch.uint8, device="cuda", generator=gen))
+        part["norms"].copy_(10.0 + torch.randn(part["norms"].shape, device="cuda", generator=gen))
+    q = torch.randn((n_sets, nq, d), device="cuda", generator=gen)
+    out = mc.logits(q, cache)
+    torch.cuda.synchronize()
+    ks = np.unique(np.concatenate([rng.choice(n_keys, 300, replace=False), np.arange(n_keys - 64, n_keys),
+                                   np.arange((1 << 25) - 32, (1 << 25) + 32)]))
+    kt = torch.from_numpy(ks).cuda()
+    for s in range(n_sets):
+        parts = tuple(dict(idx=O.unpack(p["codes"][s, kt].cpu().numpy(), cd.mse_bits, 64),
+                           norms=p["norms"][s, kt].cpu().numpy().astype(np.float64))
+                      for cd, p in ((mx.outlier, cache[0]), (mx.regular, cache[1])))
+        ref = O.mixed_logits_plain(mx, q[s].cpu().numpy().astype(np.float64), parts, s % 2)
+        check_rows(out[s][:, kt].cpu().numpy(), ref, f"set {s}")
+    del cache, out
+
+
 @pytest.mark.parametrize("n_out,bits,variant,nq", [(32, 2, O.PROD, 9), (4, 2, O.MSE, 1), (20, 3, O.MSE, 13)])
 def test_mixed_composed_logits_part_buffers_do_not_overlap(n_out, bits, variant, nq):
     """The composed logits path keeps the two parts' gathered queries and the

@@ -393,37 +393,45 @@ def test_logits_decode_config_full_size_sampled():
         check_rows(out[s][:, kt].cpu().numpy(), ref, f"set {s}")
 
 
-@pytest.mark.parametrize("n_keys,variant,bits", [(1 << 25, O.PROD, 4), ((1 << 25) + 64, O.PROD, 4),
-                                                 (1 << 25, O.MSE, 4), ((1 << 25) + 64, O.MSE, 4)])
-def test_logits_at_the_fused_key_limit(n_keys, variant, bits):
-    """One set of 2^25 keys (the most the fused logits kernel addresses; with
-    mse b = 4 its 64-byte code rows make the set's codes exactly 2^31 bytes)
-    and 2^25 + 64 (past it: the generic kernel takes over), 4 heads; sampled
-    keys, the last 64 among them, against the oracle."""
+@pytest.mark.parametrize("n_sets,n_keys,variant,bits,nq", [
+    (1, 1 << 25, O.PROD, 4, 4), (2, (1 << 25) + 64, O.PROD, 4, 10), (1, 1 << 25, O.MSE, 4, 4),
+    (1, (1 << 25) + 64, O.MSE, 4, 4), (1, (1 << 26) + 100, O.MSE, 2, 6)])
+def test_logits_past_the_fused_key_chunk(n_sets, n_keys, variant, bits, nq):
+    """Sets of 2^25 keys (the most one launch of the fused logits kernel
+    addresses; with mse b = 4 its 64-byte code rows make a set's codes exactly
+    2^31 bytes) and longer ones, which run as chunks of 2^25 keys: two sets
+    and two head groups (10 heads) at 2^25 + 64, and one set past 2^26 keys,
+    where a launch takes 4 heads so that its output rows stay within 32-bit
+    offsets.  Sampled keys (around each chunk boundary and the last 64 among
+    them) of every set against the oracle."""
     codec = tq.Codec(128, bits, variant, seed=0)
     cd = O.make_codec(128, bits, variant, 0)
     mb = cd.mse_bits
     gen = torch.Generator(device="cuda")
     gen.manual_seed(15)
-    keys = dict(codes=torch.randint(0, 256, (1, n_keys, codec.code_row), dtype=torch.uint8, device="cuda", generator=gen),
-                norms=10.0 + torch.randn((1, n_keys), device="cuda", generator=gen))
+    keys = dict(codes=torch.randint(0, 256, (n_sets, n_keys, codec.code_row), dtype=torch.uint8, device="cuda",
+                                    generator=gen),
+                norms=10.0 + torch.randn((n_sets, n_keys), device="cuda", generator=gen))
     if variant == O.PROD:
-        keys["signs"] = torch.randint(0, 256, (1, n_keys, codec.sign_row), dtype=torch.uint8, device="cuda",
+        keys["signs"] = torch.randint(0, 256, (n_sets, n_keys, codec.sign_row), dtype=torch.uint8, device="cuda",
                                       generator=gen)
-        keys["rnorms"] = torch.rand((1, n_keys), device="cuda", generator=gen) * 0.45 + 0.05
-    q = torch.randn((1, 4, 128), device="cuda", generator=gen)
+        keys["rnorms"] = torch.rand((n_sets, n_keys), device="cuda", generator=gen) * 0.45 + 0.05
+    q = torch.randn((n_sets, nq, 128), device="cuda", generator=gen)
     out = codec.logits(q, keys)
     torch.cuda.synchronize()
     rng = np.random.default_rng(16)
-    ks = np.unique(np.concatenate([rng.choice(n_keys, 300, replace=False), np.arange(n_keys - 64, n_keys)]))
+    edges = [np.arange(max(c - 32, 0), min(c + 32, n_keys)) for c in range(1 << 25, n_keys, 1 << 25)]
+    ks = np.unique(np.concatenate([rng.choice(n_keys, 300, replace=False), np.arange(n_keys - 64, n_keys), *edges]))
     kt = torch.from_numpy(ks).cuda()
-    sk = dict(idx=O.unpack(keys["codes"][0, kt].cpu().numpy(), mb, 128),
-              norms=keys["norms"][0, kt].cpu().numpy().astype(np.float64))
-    if variant == O.PROD:
-        sk["signs"] = O.bits_to_signs(O.unpack(keys["signs"][0, kt].cpu().numpy(), 1, 128))
-        sk["rnorms"] = keys["rnorms"][0, kt].cpu().numpy().astype(np.float64)
-    ref = O.logits_fast(cd, q[0].cpu().numpy().astype(np.float64), sk, 0)
-    check_rows(out[0][:, kt].cpu().numpy(), ref, f"n_keys {n_keys}")
+    for s in range(n_sets):
+        sk = dict(idx=O.unpack(keys["codes"][s, kt].cpu().numpy(), mb, 128),
+                  norms=keys["norms"][s, kt].cpu().numpy().astype(np.float64))
+        if variant == O.PROD:
+            sk["signs"] = O.bits_to_signs(O.unpack(keys["signs"][s, kt].cpu().numpy(), 1, 128))
+            sk["rnorms"] = keys["rnorms"][s, kt].cpu().numpy().astype(np.float64)
+        ref = O.logits_fast(cd, q[s].cpu().numpy().astype(np.float64), sk, 0)
+        check_rows(out[s][:, kt].cpu().numpy(), ref, f"n_keys {n_keys} set {s}")
+    del keys, out
 
 
 @pytest.mark.parametrize("bits", [4, 3])
