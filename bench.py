@@ -386,10 +386,10 @@ def other_paths_phase(torch, tq, workloads, x_kv, kv_only=False):
 def generic_paths(torch, tq, gen):
     """Logits of one set of 2^25 + 64 keys (the fused kernel in two chunks of
     keys), then the dimension-generic kernels on shapes the fast kernels hand
-    over to them: logits at d = 200 (NN index keys), and the quantize,
-    dequantize and logits of mse b = 5 at d = 128 (more than 4 bits).  Random
-    codes stand in for quantized keys where only the streaming rate
-    matters."""
+    over to them: logits at d = 200 (NN index keys), a top-64 search at d =
+    300 (score-then-select), and the quantize, dequantize and logits of mse
+    b = 5 at d = 128 (more than 4 bits).  Random codes stand in for
+    quantized keys where only the streaming rate matters."""
     res = {}
     nk = (1 << 25) + 64
     c = tq.Codec(128, 4, tq.TQ_PROD, seed=0)
@@ -415,6 +415,18 @@ def generic_paths(torch, tq, gen):
     res["generic_logits_d200_prod_b4_64q_ms"] = ms
     res["generic_logits_d200_prod_b4_64q_packed_gbs"] = 1_000_000 * (c.code_row + c.sign_row + 8) / (ms * 1e-3) / 1e9
     del x, kc, q, lo
+    # top-64 search at d = 300, prod b = 3 (past the fused scan's d <= 256): score-then-select through the
+    # generic logits kernel, 1000 queries x 10^5 keys
+    c = tq.Codec(300, 3, tq.TQ_PROD, seed=0)
+    x = torch.randn((1, 100_000, 300), device="cuda", generator=gen)
+    kc = c.empty_codes(1, 100_000)
+    c.quantize(x, out=kc)
+    keys = {k: (None if v is None else v[0]) for k, v in kc.items()}
+    q = torch.randn((1000, 300), device="cuda", generator=gen)
+    ms = _mean_launch_ms(torch, lambda: c.topk(q, keys, 64), reps=3)
+    res["generic_topk_d300_prod_b3_1000q_100k_top64_ms"] = ms
+    res["generic_topk_d300_prod_b3_pairs_per_s"] = 1000 * 100_000 / (ms * 1e-3)
+    del x, kc, keys, q
     # mse b = 5 at d = 128 (KV shape, 16 sets x 32768): generic quantize, dequantize, logits
     c = tq.Codec(128, 5, tq.TQ_MSE, seed=0, groups=8)
     x = torch.randn((16, 32768, 128), device="cuda", generator=gen).to(torch.bfloat16)

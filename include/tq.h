@@ -178,11 +178,14 @@ int tq_attention_static(tq_handle hk, tq_handle hv, const float *q, int64_t nq, 
  * estimates <q[i], k_hat[t]> (the tq_logits values), best first; equal
  * scores are ordered by key index.  out_scores: [nq][k] float32, out_idx:
  * [nq][k] int32.  The scan is fused with the selection: no score matrix is
- * written.  ([ttakun] 索引速度: the same codes serve vector search; the
- * inner-product estimator as in tq_logits.)  Handles d <= 256 with at most
- * 4 mse bits (else TQ_EUNSUPPORTED).  1 <= k <= 64, n_keys >= k.
+ * written when d <= 256, mse bits <= 4 and the index fits 32-bit offsets.
+ * Other codecs score 65536-key chunks of 64-query blocks into the
+ * workspace with the tq_logits kernels and select from those (the same
+ * estimates up to fp32 rounding, slower).  ([ttakun] 索引速度: the same codes serve vector search;
+ * the inner-product estimator as in tq_logits.)  1 <= k <= 64, n_keys >= k.
  * workspace: caller-owned device memory, 256-byte aligned, of at least the
- * tq_topk_workspace size; scratch.  Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP. */
+ * tq_topk_workspace size (0 when nq is 0); scratch.  Errors: TQ_EINVAL,
+ * TQ_EHIP. */
 int tq_topk_workspace(tq_handle h, int64_t nq, int64_t n_keys, int k, size_t *bytes);
 int tq_topk(tq_handle h, const float *q, int64_t nq, const void *codes, const void *signs, const float *norms,
             const float *rnorms, int64_t n_keys, int k, float *out_scores, int32_t *out_idx, void *workspace,

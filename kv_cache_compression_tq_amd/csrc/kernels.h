@@ -137,9 +137,9 @@ hipError_t launch_attention128(const DeviceTables &tk, const DeviceTables &tv, c
                                const float *krnorms, const uint8_t *vcodes, const float *vnorms, int64_t n_sets,
                                int64_t n_keys, float scale, float *part, float *out, hipStream_t st);
 
-// Top-k maximum inner product search over one set of keys, d <= 256 and
-// mse bits <= 4: topk_workspace returns the bytes of `ws` (0 when the codec
-// is not handled).  out_idx is int32.
+// Top-k maximum inner product search over one set of keys: the fused scan
+// for d <= 256 and mse bits <= 4, else score-then-select through the logits
+// kernels.  topk_workspace returns the bytes of `ws`.  out_idx is int32.
 size_t topk_workspace(const DeviceTables &t, int64_t nq, int64_t n_keys, int k);
 hipError_t launch_topk(const DeviceTables &t, const float *q, int64_t nq, const uint8_t *codes, const uint8_t *signs,
                        const float *norms, const float *rnorms, int64_t n_keys, int k, void *ws, float *out_scores,

@@ -184,30 +184,34 @@ __device__ __forceinline__ bool tk_better(float s, int i, float cs, int ci) {
   return s > cs || (s == cs && i < ci);
 }
 
-// Insert `cnt` buffered candidates into one query's list (lane l holds its
-// l-th best; lanes >= k hold -inf), one candidate at a time.  Used by the
-// final merge of the ranges' lists.
-__device__ __forceinline__ void tk_insert(float &ls, int &li, const float2 *cand, int cnt, int k, int lane) {
-  for (int c = 0; c < cnt; ++c) {
-    const float2 e = cand[c];
-    const float cs = e.x;
-    const int ci = __float_as_int(e.y);
-    const int pos = __popcll(__ballot(tk_better(ls, li, cs, ci)));
-    if (pos < k) {
-      const float us = __shfl_up(ls, 1);
-      const int ui = __shfl_up(li, 1);
-      if (lane > pos) {
-        ls = us;
-        li = ui;
-      } else if (lane == pos) {
-        ls = cs;
-        li = ci;
-      }
-    }
+// Put candidate (cs, ci) into one query's list (lane l holds its l-th
+// best; lanes >= k hold entries worse than the k-th) when it beats the k-th
+// best: the entries below it move down one lane.
+__device__ __forceinline__ void tk_insert_one(float &ls, int &li, float cs, int ci, int lane) {
+  const int pos = __popcll(__ballot(tk_better(ls, li, cs, ci)));
+  const float us = __shfl_up(ls, 1);
+  const int ui = __shfl_up(li, 1);
+  if (lane > pos) {
+    ls = us;
+    li = ui;
+  } else if (lane == pos) {
+    ls = cs;
+    li = ci;
   }
-  if (lane >= k) {
-    ls = -INFINITY;
-    li = 0x7fffffff;
+}
+
+// Merge a sorted list held one entry per lane (vs, vi: lane c holds entry c;
+// empty entries are -inf) into the running list.  Entries are taken best
+// first, so the first one that does not beat the running k-th best ends it.
+__device__ __forceinline__ void tk_insert_list(float &ls, int &li, float vs, int vi, int k, int lane) {
+  const int n = __popcll(__ballot(vs != -INFINITY));
+  for (int c = 0; c < n; ++c) {
+    const float cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vs), c));
+    const int ci = __builtin_amdgcn_readlane(vi, c);
+    const float ts = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), k - 1));
+    const int ti = __builtin_amdgcn_readlane(li, k - 1);
+    if (!tk_better(cs, ci, ts, ti)) break;
+    tk_insert_one(ls, li, cs, ci, lane);
   }
 }
 
@@ -466,15 +470,75 @@ __global__ __launch_bounds__(64) void k_topk_merge(const float2 *__restrict__ li
   const int q = blockIdx.x, lane = threadIdx.x;
   float ls = -INFINITY;
   int li = 0x7fffffff;
-  for (int s = 0; s < S; ++s) {
-    const float2 *l = lists + ((int64_t)q * S + s) * k;
-    int n = 0;  // entries of this list (lists are sorted; -inf entries are empty slots)
-    while (n < k && l[n].x != -INFINITY) ++n;
-    tk_insert(ls, li, l, n, k, lane);
+  for (int s = 0; s < S; ++s) {  // each list sorted, -inf entries empty
+    const float2 e = lane < k ? lists[((int64_t)q * S + s) * k + lane] : float2{-INFINITY, 0.f};
+    tk_insert_list(ls, li, e.x, __float_as_int(e.y), k, lane);
   }
   if (lane < k) {
     out_scores[(int64_t)q * k + lane] = ls;
     out_idx[(int64_t)q * k + lane] = li;
+  }
+}
+
+// ---- score-then-select search for the codecs the fused scan does not take
+// (d > 256, more than 4 mse bits, or an index past its 32-bit offsets): the
+// logits kernels score a chunk of keys for a block of queries into the
+// workspace, k_topk_select keeps each segment's best k, and k_topk_fold
+// folds the segments' lists into the query's running list.
+
+// One wave per (segment, query row) of a logits block [rows][n]: the best k
+// of keys seg p .. of row i (key numbers offset by key0), into slot 1 + p of
+// the row's `slots` lists of k entries.
+__global__ __launch_bounds__(64) void k_topk_select(const float *__restrict__ logits, int64_t n, int seg, int k,
+                                                    int key0, int slots, float2 *__restrict__ lists) {
+  const int p = blockIdx.x, i = blockIdx.y, lane = threadIdx.x;
+  const float *row = logits + (int64_t)i * n;
+  const int64_t b = (int64_t)p * seg, e = b + seg < n ? b + seg : n;
+  float ls = -INFINITY;
+  int li = 0x7fffffff;
+  float ts = -INFINITY;  // the running k-th best
+  int ti = 0x7fffffff;
+  for (int64_t j0 = b; j0 < e; j0 += 64) {
+    const int64_t j = j0 + lane;
+    const bool in = j < e;
+    const float v = in ? row[j] : -INFINITY;
+    const int id = key0 + (int)j;
+    uint64_t m = __ballot(in && tk_better(v, id, ts, ti));
+    while (m != 0) {  // candidates of this block, lowest key first
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const float cs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+      const int ci = __builtin_amdgcn_readlane(id, src);
+      if (tk_better(cs, ci, ts, ti)) {
+        tk_insert_one(ls, li, cs, ci, lane);
+        ts = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), k - 1));
+        ti = __builtin_amdgcn_readlane(li, k - 1);
+      }
+    }
+  }
+  if (lane < k) lists[((int64_t)i * slots + 1 + p) * k + lane] = float2{ls, __int_as_float(li)};
+}
+
+// One wave per query row: merge lists first .. count - 1 of the row's
+// `slots`, then store the result in list 0 (out_scores null) or as the
+// final top k of query q0 + i.
+__global__ __launch_bounds__(64) void k_topk_fold(float2 *__restrict__ lists, int slots, int first, int count, int k,
+                                                  int64_t q0, float *__restrict__ out_scores,
+                                                  int32_t *__restrict__ out_idx) {
+  const int i = blockIdx.x, lane = threadIdx.x;
+  float ls = -INFINITY;
+  int li = 0x7fffffff;
+  for (int s = first; s < count; ++s) {
+    const float2 e = lane < k ? lists[((int64_t)i * slots + s) * k + lane] : float2{-INFINITY, 0.f};
+    tk_insert_list(ls, li, e.x, __float_as_int(e.y), k, lane);
+  }
+  if (lane < k) {
+    if (out_scores) {
+      out_scores[(q0 + i) * k + lane] = ls;
+      out_idx[(q0 + i) * k + lane] = li;
+    } else {
+      lists[(int64_t)i * slots * k + lane] = float2{ls, __int_as_float(li)};
+    }
   }
 }
 
@@ -524,8 +588,58 @@ static int topk_splits(int64_t nq, int64_t n_keys) {
   return (int)best;
 }
 
+// Score-then-select geometry: blocks of kFbQueries queries (the logits
+// kernels' head count per set), chunks of at most kFbKeys keys, segments of
+// kFbSeg keys per selection wave.
+constexpr int64_t kFbQueries = 64;
+constexpr int64_t kFbKeys = 65536;
+constexpr int kFbSeg = 2048;
+constexpr int kFbSlots = 1 + (int)(kFbKeys / kFbSeg);  // the running list, then one per segment
+
+static bool fused_topk_handles(const DeviceTables &t, int64_t n_keys) {
+  // the scan's buffer offsets are 32-bit
+  return t.d <= kTkPad && t.mse_bits <= 4 && t.logit_lut &&
+         n_keys * (t.code_row > t.sign_row ? t.code_row : t.sign_row) < ((int64_t)1 << 31);
+}
+
+static size_t fallback_workspace(int64_t nq, int64_t n_keys, int k) {
+  const int64_t qb = nq < kFbQueries ? nq : kFbQueries, c = n_keys < kFbKeys ? n_keys : kFbKeys;
+  return ((size_t)qb * c * sizeof(float) + 255) / 256 * 256 + (size_t)qb * kFbSlots * k * sizeof(float2);
+}
+
+static hipError_t run_topk_fallback(const DeviceTables &t, const float *q, int64_t nq, const uint8_t *codes,
+                                    const uint8_t *signs, const float *norms, const float *rnorms, int64_t n_keys,
+                                    int k, void *ws, float *out_scores, int32_t *out_idx, hipStream_t st) {
+  const int64_t qb = nq < kFbQueries ? nq : kFbQueries, cmax = n_keys < kFbKeys ? n_keys : kFbKeys;
+  float *lg = (float *)ws;
+  float2 *lists = (float2 *)((char *)ws + ((size_t)qb * cmax * sizeof(float) + 255) / 256 * 256);
+  const bool prod = t.variant == 1;
+  for (int64_t q0 = 0; q0 < nq; q0 += kFbQueries) {
+    const int64_t nb = nq - q0 < kFbQueries ? nq - q0 : kFbQueries;
+    for (int64_t k0 = 0; k0 < n_keys; k0 += kFbKeys) {
+      const int64_t n = n_keys - k0 < kFbKeys ? n_keys - k0 : kFbKeys;
+      const uint8_t *ck = t.mse_bits > 0 ? codes + k0 * t.code_row : codes;
+      const uint8_t *sk = prod ? signs + k0 * t.sign_row : signs;
+      const float *gk = prod ? rnorms + k0 : rnorms;
+      // the block's queries are the heads of one set; logits [nb][n]
+      hipError_t e = launch_logits128(t, q + q0 * t.d, nb, ck, sk, norms + k0, gk, 1, n, lg, st);
+      if (e == hipErrorNotSupported) e = launch_logits_generic(t, q + q0 * t.d, nb, ck, sk, norms + k0, gk, 1, n, lg, st);
+      if (e != hipSuccess) return e;
+      const int parts = (int)((n + kFbSeg - 1) / kFbSeg);
+      hipLaunchKernelGGL(k_topk_select, dim3((unsigned)parts, (unsigned)nb), dim3(64), 0, st, lg, n, kFbSeg, k,
+                         (int)k0, kFbSlots, lists);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      const bool last = k0 + n >= n_keys;
+      hipLaunchKernelGGL(k_topk_fold, dim3((unsigned)nb), dim3(64), 0, st, lists, kFbSlots, k0 == 0 ? 1 : 0,
+                         1 + parts, k, q0, last ? out_scores : nullptr, last ? out_idx : nullptr);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 size_t topk_workspace(const DeviceTables &t, int64_t nq, int64_t n_keys, int k) {
-  if (t.d > kTkPad || t.mse_bits > 4 || !t.logit_lut) return 0;
+  if (!fused_topk_handles(t, n_keys)) return fallback_workspace(nq, n_keys, k);
   const size_t prep = (size_t)nq * 2 * kTkPad * sizeof(float);
   const size_t lists = (size_t)nq * topk_splits(nq, n_keys) * k * sizeof(float2);
   return (prep + 255) / 256 * 256 + (lists + 255) / 256 * 256 + (size_t)nq * sizeof(int);
@@ -560,9 +674,8 @@ static hipError_t run_topk(const DeviceTables &t, const float *q, int64_t nq, co
 hipError_t launch_topk(const DeviceTables &t, const float *q, int64_t nq, const uint8_t *codes, const uint8_t *signs,
                        const float *norms, const float *rnorms, int64_t n_keys, int k, void *ws, float *out_scores,
                        int32_t *out_idx, hipStream_t st) {
-  if (t.d > kTkPad || t.mse_bits > 4 || !t.logit_lut) return hipErrorNotSupported;
-  // buffer offsets are 32-bit
-  if (n_keys * (t.code_row > t.sign_row ? t.code_row : t.sign_row) >= ((int64_t)1 << 31)) return hipErrorNotSupported;
+  if (!fused_topk_handles(t, n_keys))
+    return run_topk_fallback(t, q, nq, codes, signs, norms, rnorms, n_keys, k, ws, out_scores, out_idx, st);
   const bool prod = t.variant == 1;
   const int ks = tk_steps(t.d);
 #define TQ_T(MB, P)                                                                                               \

@@ -593,9 +593,7 @@ int tq_topk_workspace(tq_handle h, int64_t nq, int64_t n_keys, int k, size_t *by
   if (!bytes) return fail(TQ_EINVAL, "bytes is NULL");
   if (nq < 0 || nq > 65535 * 128) return fail(TQ_EINVAL, "nq out of range");
   if (k < 1 || k > 64 || n_keys < k) return fail(TQ_EINVAL, "need 1 <= k <= 64 and n_keys >= k");
-  const size_t b = tq::topk_workspace(h->dev, nq, n_keys, k);
-  if (b == 0) return fail(TQ_EUNSUPPORTED, "top-k search needs d <= 256 and at most 4 mse bits");
-  *bytes = b;
+  *bytes = tq::topk_workspace(h->dev, nq, n_keys, k);  // 0 when nq is 0
   return TQ_OK;
 }
 
@@ -617,7 +615,6 @@ int tq_topk(tq_handle h, const float *q, int64_t nq, const void *codes, const vo
   if ((st = launch_fault("tq_topk"))) return st;
   hipError_t e = tq::launch_topk(h->dev, q, nq, (const uint8_t *)codes, (const uint8_t *)signs, norms, rnorms, n_keys,
                                  k, workspace, out_scores, out_idx, (hipStream_t)stream);
-  if (e == hipErrorNotSupported) return fail(TQ_EUNSUPPORTED, "index too large for the top-k kernel");
   return e == hipSuccess ? TQ_OK : hip_fail(e, "top-k launch");
 }
 

@@ -74,6 +74,38 @@ def test_topk_oracle_codes(d, bits, variant, k):
     check_topk(sc.cpu().numpy(), ix.cpu().numpy(), full, k, f"d={d} b={bits}")
 
 
+@pytest.mark.parametrize("d,bits,variant", [(300, 3, O.PROD), (128, 6, O.MSE), (520, 2, O.PROD), (64, 8, O.MSE)])
+def test_topk_score_then_select(d, bits, variant):
+    """Codecs the fused scan does not take (d > 256, more than 4 mse bits):
+    the logits kernels score 65536-key chunks of 64-query blocks and the
+    selection keeps each segment's best k.  70 queries (two blocks) over
+    70000 keys (two chunks), with equal keys inside a chunk and across the
+    chunk boundary (ties go to the lower index)."""
+    nq, n = 70, 70000
+    rng = np.random.default_rng(d + bits)
+    x = rng.standard_normal((n, d))
+    x[5] = x[900]
+    x[66000] = x[10]
+    q = rng.standard_normal((nq, d)).astype(np.float32)
+    q[3] = x[66000]  # a query whose best keys are the equal pair 10 and 66000
+    cd = O.make_codec(d, bits, variant, 23)
+    codec = tq.Codec(d, bits, variant, seed=23)
+    if variant == O.MSE:
+        idx, nu, _ = O.quantize_mse(cd, x)
+        keys = dict(idx=idx, norms=nu.astype(np.float32).astype(np.float64))
+    else:
+        r = O.quantize_prod(cd, x)
+        keys = dict(idx=r["idx"], signs=r["signs"], norms=r["norms"].astype(np.float32).astype(np.float64),
+                    rnorms=r["rnorms"].astype(np.float32).astype(np.float64))
+    stored = _stored(cd, keys)
+    full = O.logits_fast(cd, q.astype(np.float64), keys)
+    for k in (1, 10, 64):
+        sc, ix = codec.topk(_cuda(q), stored, k)
+        check_topk(sc.cpu().numpy(), ix.cpu().numpy(), full, k, f"d={d} b={bits} k={k}")
+        if k >= 2:
+            assert ix[3, 0].item() == 10 and ix[3, 1].item() == 66000, "equal keys: the lower index first"
+
+
 def test_topk_small_index_and_single_key_range():
     d, n, k = 200, 64, 64  # k equals the index size: every key, sorted
     rng = np.random.default_rng(3)
