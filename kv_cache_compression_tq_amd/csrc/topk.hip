@@ -542,26 +542,40 @@ __global__ __launch_bounds__(64) void k_topk_fold(float2 *__restrict__ lists, in
   }
 }
 
-// q~ = Pi q and p = S q per query (one workgroup each), zero-padded to 256;
-// q~ is scaled for the code table (1 / alpha, or c1 for 1-bit codes decoded
-// as signs), p by sqrt(pi/2) / d.
-__global__ __launch_bounds__(kTkPad) void k_topk_qprep(const float *__restrict__ q, int d, int prod, int mse_bits,
-                                                       const float *__restrict__ PiT, const float *__restrict__ ST,
-                                                       float mscale, float *__restrict__ out, int *__restrict__ gtau) {
-  __shared__ float qs[kTkPad];
-  const int r = blockIdx.x, j = threadIdx.x;
-  qs[j] = j < d ? q[(int64_t)r * d + j] : 0.f;
+// q~ = Pi q and p = S q of kTkPrepQ queries per workgroup (each element of
+// Pi^T and S^T read from L2 serves all of them), zero-padded to 256; q~ is
+// scaled for the code table (1 / alpha, or c1 for 1-bit codes decoded as
+// signs), p by sqrt(pi/2) / d.
+constexpr int kTkPrepQ = 16;
+
+__global__ __launch_bounds__(kTkPad) void k_topk_qprep(const float *__restrict__ q, int nq, int d, int prod,
+                                                       int mse_bits, const float *__restrict__ PiT,
+                                                       const float *__restrict__ ST, float mscale,
+                                                       float *__restrict__ out, int *__restrict__ gtau) {
+  __shared__ float qs[kTkPrepQ][kTkPad];
+  const int r0 = blockIdx.x * kTkPrepQ, j = threadIdx.x;
+  const int nr = nq - r0 < kTkPrepQ ? nq - r0 : kTkPrepQ;
+  for (int r = 0; r < kTkPrepQ; ++r) qs[r][j] = r < nr && j < d ? q[(int64_t)(r0 + r) * d + j] : 0.f;
   __syncthreads();
-  float a = 0.f, b = 0.f;
+  float a[kTkPrepQ], b[kTkPrepQ];
+#pragma unroll
+  for (int r = 0; r < kTkPrepQ; ++r) a[r] = b[r] = 0.f;
   if (j < d) {
     for (int kk = 0; kk < d; ++kk) {
-      if (mse_bits > 0) a = fmaf(PiT[(size_t)kk * d + j], qs[kk], a);  // (Pi q)_j
-      if (prod) b = fmaf(ST[(size_t)kk * d + j], qs[kk], b);            // (S q)_j
+      const float pi = mse_bits > 0 ? PiT[(size_t)kk * d + j] : 0.f;  // (Pi q)_j
+      const float sj = prod ? ST[(size_t)kk * d + j] : 0.f;           // (S q)_j
+#pragma unroll
+      for (int r = 0; r < kTkPrepQ; ++r) {
+        a[r] = fmaf(pi, qs[r][kk], a[r]);
+        b[r] = fmaf(sj, qs[r][kk], b[r]);
+      }
     }
   }
-  out[((int64_t)r * 2 + 0) * kTkPad + j] = a * mscale;
-  out[((int64_t)r * 2 + 1) * kTkPad + j] = b * (kQjlScale / (float)d);
-  if (j == 0) gtau[r] = tk_key(-INFINITY);  // the shared threshold starts empty
+  for (int r = 0; r < nr; ++r) {
+    out[((int64_t)(r0 + r) * 2 + 0) * kTkPad + j] = a[r] * mscale;
+    out[((int64_t)(r0 + r) * 2 + 1) * kTkPad + j] = b[r] * (kQjlScale / (float)d);
+    if (j == 0) gtau[r0 + r] = tk_key(-INFINITY);  // the shared threshold starts empty
+  }
 }
 
 }  // namespace
@@ -655,8 +669,8 @@ static hipError_t run_topk(const DeviceTables &t, const float *q, int64_t nq, co
   int *gtau = (int *)((char *)lists + ((size_t)nq * S * k * sizeof(float2) + 255) / 256 * 256);
   // 1-bit codes are decoded as signs: c[idx] = c1 (2 idx - 1)
   const float mscale = MB == 1 ? t.pos_cent[0] : t.lut_inv_scale;
-  hipLaunchKernelGGL(k_topk_qprep, dim3((unsigned)nq), dim3(kTkPad), 0, st, q, t.d, PROD ? 1 : 0, MB, t.PiT, t.ST,
-                     mscale, prep, gtau);
+  hipLaunchKernelGGL(k_topk_qprep, dim3((unsigned)((nq + kTkPrepQ - 1) / kTkPrepQ)), dim3(kTkPad), 0, st, q, (int)nq,
+                     t.d, PROD ? 1 : 0, MB, t.PiT, t.ST, mscale, prep, gtau);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute((const void *)k_topk<MB, PROD, KS>, hipFuncAttributeMaxDynamicSharedMemorySize,
