@@ -8,13 +8,13 @@
 // vector).  A workgroup computes two output panels (256 coordinates) for 128
 // vectors, so that each float32 input element split into bf16 hi/lo on the
 // vector ALU feeds twice the MFMAs of a one-panel workgroup.  The contraction
-// runs in units of 64 elements (two K steps): a unit's fragments of both
-// panels' blocks fill one 64 KB LDS buffer (direct global-to-LDS loads), the
-// inputs come through registers, and two workgroups share a CU, so one's
-// MFMAs run while the other waits for its next unit.  Units wholly past d are
-// skipped.  After the last unit each panel's codes are searched and packed
-// exactly as at d = 128.  Launches too small to fill the chip with pairs keep
-// one panel per workgroup.
+// runs one K step (32 elements) at a time: the step's fragments of both
+// panels' blocks fill one 32 KB half of a 64 KB LDS buffer (direct
+// global-to-LDS loads) while the MFMAs of the previous step read the other
+// half, the inputs come one step ahead through registers, and two workgroups
+// share a CU.  Steps wholly past d are skipped.  After the last step each
+// panel's codes are searched and packed exactly as at d = 128.  Launches too
+// small to fill the chip with pairs keep one panel per workgroup.
 //
 // TurboQuant_prod adds a second pass.  The QJL signs need the residual of the
 // whole vector, so they are taken as sign(S x - nu M c[idx]) = sign(S r)
@@ -79,34 +79,103 @@ __device__ __forceinline__ void stage_unit(const u32x4 *blk0, const u32x4 *blk1,
   }
 }
 
-// Input fragments of one unit for the lane's two vectors: elements
-// 128 c + 64 kh + 32 kk + 8 grp .. + 8 (bf16 pairs, or raw float32).
+// One K step (k = 0..3 of contraction chunk c) of the blocks of both panels
+// into a 32 KB half of the unit buffer: buffer fragment 2 m + hl (row tile
+// m = 0..15; tiles 8..15 are the second panel's) is fragment 2 (4 (m % 8) +
+// k) + hl of that panel's block.  Each wave moves 8 fragments of 1 KB.
+__device__ __forceinline__ void stage_step(const u32x4 *blk0, const u32x4 *blk1, bool two, int k, u32x4 *dst,
+                                           int wave, int lane) {
+  constexpr int kStepFrags = kUnitFrags / 2;
+#pragma unroll
+  for (int i = 0; i < kStepFrags / kTiledWaves; ++i) {
+    const int fi = wave * (kStepFrags / kTiledWaves) + i, m = fi >> 1, hl = fi & 1;
+    if (m >= 8 && !two) continue;  // wave-uniform
+    const u32x4 *blk = m < 8 ? blk0 : blk1;
+    __builtin_amdgcn_global_load_lds((const void *)(blk + (2 * ((m & 7) * 4 + k) + hl) * kFragVec + lane),
+                                     (__attribute__((address_space(3))) void *)(dst + fi * kFragVec), 16, 0, 0);
+  }
+}
+
+// Input fragments of one K step for the lane's two vectors: elements e_step +
+// 8 grp .. + 8 (zero past d).
 template <bool F32IN>
-struct XUnit {
-  u32x4 v[2][2][F32IN ? 2 : 1];
+struct XStep {
+  u32x4 v[2][F32IN ? 2 : 1];
 };
 
 template <bool F32IN>
-__device__ __forceinline__ void load_unit(XUnit<F32IN> &r, const void *xin, const int64_t (&row)[2], int e_unit, int d,
+__device__ __forceinline__ void load_step(XStep<F32IN> &r, const void *xin, const int64_t (&row)[2], int e_step, int d,
                                           int grp) {
+  const int e0 = e_step + 8 * grp;  // d is a multiple of 8: groups are all in or all out
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int e0 = e_unit + 32 * kk + 8 * grp;  // d is a multiple of 8: groups are all in or all out
-      if (e0 < d) {
-        if constexpr (F32IN) {
-          const u32x4 *p = (const u32x4 *)((const float *)xin + row[t] * d + e0);
-          r.v[t][kk][0] = p[0];
-          r.v[t][kk][1] = p[1];
-        } else {
-          r.v[t][kk][0] = *(const u32x4 *)((const uint16_t *)xin + row[t] * d + e0);
-        }
+  for (int t = 0; t < 2; ++t) {
+    if (e0 < d) {
+      if constexpr (F32IN) {
+        const u32x4 *p = (const u32x4 *)((const float *)xin + row[t] * d + e0);
+        r.v[t][0] = p[0];
+        r.v[t][1] = p[1];
       } else {
+        r.v[t][0] = *(const u32x4 *)((const uint16_t *)xin + row[t] * d + e0);
+      }
+    } else {
 #pragma unroll
-        for (int h = 0; h < (F32IN ? 2 : 1); ++h) r.v[t][kk][h] = u32x4{0, 0, 0, 0};
+      for (int h = 0; h < (F32IN ? 2 : 1); ++h) r.v[t][h] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+// acc[t][m] += one staged K step x the step's B operands (split into bf16
+// hi/lo for float32 input), in four groups of eight fragments, each group
+// read before its MFMAs; also ||x||^2 of the elements when NSQ.
+template <bool F32IN, bool NSQ>
+__device__ __forceinline__ void mma_step(const XStep<F32IN> &x, const u32x4 *buf, int frag_lane, bool two,
+                                         f32x4 (&acc)[2][16], float (&nsq)[2]) {
+  u32x4 bh[2], bl[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if constexpr (F32IN) {
+      const f32x4 a = __builtin_bit_cast(f32x4, x.v[t][0]);
+      const f32x4 b = __builtin_bit_cast(f32x4, x.v[t][1]);
+      const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      split8(f, bh[t], bl[t]);
+      if constexpr (NSQ) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) nsq[t] = fmaf(f[i], f[i], nsq[t]);
+      }
+    } else {
+      bh[t] = x.v[t][0];
+      bl[t] = bh[t];
+      if constexpr (NSQ) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = bf16_lo(bh[t][i]), hi = bf16_hi(bh[t][i]);
+          nsq[t] = fmaf(lo, lo, fmaf(hi, hi, nsq[t]));
+        }
       }
     }
+  }
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    if (gq >= 2 && !two) break;  // wave-uniform: the pair's second panel is absent
+    u32x4 fh[4], fl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = 2 * (4 * gq + i);
+      fh[i] = buf[f * kFragVec + frag_lane];
+      fl[i] = buf[(f + 1) * kFragVec + frag_lane];
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the group's 8 LDS reads
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4 &c = acc[t][4 * gq + i];
+        c = mfma_bf16(fh[i], bh[t], c);
+        c = mfma_bf16(fl[i], bh[t], c);
+        if constexpr (F32IN) c = mfma_bf16(fh[i], bl[t], c);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8 * (F32IN ? 3 : 2), 0);  // then their MFMAs
+  }
 }
 
 // acc[t][m] += unit (LDS) x B operands, for row tiles m < 8 (one panel) or
@@ -146,57 +215,41 @@ __device__ __forceinline__ void mma_unit_ops(const u32x4 *buf, int frag_lane, bo
   }
 }
 
-// The same with the unit's input elements as B operands, split into bf16 hi/lo
-// (float32 input) K step by K step; also ||x||^2 of the elements when NSQ.
-template <bool F32IN, bool NSQ>
-__device__ __forceinline__ void mma_unit(const XUnit<F32IN> &x, const u32x4 *buf, int frag_lane, bool two,
-                                         f32x4 (&acc)[2][16], float (&nsq)[2]) {
-  mma_unit_ops<F32IN>(buf, frag_lane, two, acc, [&](int kk, u32x4(&bh)[2], u32x4(&bl)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if constexpr (F32IN) {
-        const f32x4 a = __builtin_bit_cast(f32x4, x.v[t][kk][0]);
-        const f32x4 b = __builtin_bit_cast(f32x4, x.v[t][kk][1]);
-        const float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        split8(f, bh[t], bl[t]);
-        if constexpr (NSQ) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) nsq[t] = fmaf(f[i], f[i], nsq[t]);
-        }
-      } else {
-        bh[t] = x.v[t][kk][0];
-        bl[t] = bh[t];
-        if constexpr (NSQ) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float lo = bf16_lo(bh[t][i]), hi = bf16_hi(bh[t][i]);
-            nsq[t] = fmaf(lo, lo, fmaf(hi, hi, nsq[t]));
-          }
-        }
-      }
-    }
-  });
-}
-
 // Rotation (or projection) of the workgroup's 128 vectors for the panel pair,
-// over the input chunks: units of 64 contraction elements stream through one
-// 64 KB LDS buffer (two workgroups share a CU, so one's MFMAs run while the
-// other waits for its unit).  Units wholly past d are skipped.
+// over the input chunks, one K step (32 contraction elements) at a time: the
+// step's fragments of both panels' blocks are staged by direct global-to-LDS
+// loads into one 32 KB half of the unit buffer while the MFMAs of the step
+// before run from the other half, and the step's inputs come one step ahead
+// through registers.  One barrier per step: after it every wave's share of
+// the step has landed and every wave is done with the half the next stage
+// overwrites.  Steps wholly past d are skipped.
 template <bool F32IN, bool NSQ>
 __device__ __forceinline__ void rotate_pair(const void *xin, const u32x4 *img0, const u32x4 *img1, bool two,
                                             u32x4 *buf, const TiledArgs &a, const int64_t (&row)[2], int wave,
                                             int lane, int grp, f32x4 (&acc)[2][16], float (&nsq)[2]) {
-  XUnit<F32IN> xa;
-  for (int u = 0; 64 * u < a.d; ++u) {
-    const int c = u >> 1, kh = u & 1;
-    if (u > 0) __syncthreads();  // every wave is done with the previous unit
-    stage_unit(img0 + (size_t)c * kImageVec, img1 + (size_t)c * kImageVec, two, kh, buf, wave, lane);
-    load_unit<F32IN>(xa, xin, row, 64 * u, a.d, grp);
-    __builtin_amdgcn_s_waitcnt(0);
+  const int steps = (a.d + 31) / 32;
+  u32x4 *const h0 = buf, *const h1 = buf + (kUnitFrags / 2) * kFragVec;
+  XStep<F32IN> x0, x1;
+  // step ks: wait for its stage and inputs, then stage step ks + 1 into the
+  // other half and run step ks (the loop is unrolled by two so that every
+  // register and buffer choice is static)
+  auto step = [&](int ks, const XStep<F32IN> &xc, XStep<F32IN> &xn, const u32x4 *hc, u32x4 *hn) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of step ks (and its inputs)
     __syncthreads();
+    if (ks + 1 < steps) {
+      const int c = (ks + 1) >> 2, k = (ks + 1) & 3;
+      stage_step(img0 + (size_t)c * kImageVec, img1 + (size_t)c * kImageVec, two, k, hn, wave, lane);
+      load_step<F32IN>(xn, xin, row, 32 * (ks + 1), a.d, grp);
+    }
     int frag_lane = lane;
     asm volatile("" : "+v"(frag_lane));
-    mma_unit<F32IN, NSQ>(xa, buf, frag_lane, two, acc, nsq);
+    mma_step<F32IN, NSQ>(xc, hc, frag_lane, two, acc, nsq);
+  };
+  stage_step(img0, img1, two, 0, h0, wave, lane);
+  load_step<F32IN>(x0, xin, row, 0, a.d, grp);
+  for (int ks = 0; ks < steps; ks += 2) {
+    step(ks, x0, x1, h0, h1);
+    if (ks + 1 < steps) step(ks + 1, x1, x0, h1, h0);
   }
 }
 
