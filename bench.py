@@ -491,6 +491,38 @@ def ceilings_phase(torch, tq):
         flops = grid * 4 * iters * 8 * 2.0 * 16 * 16 * 32
         res[f"mfma_{name}_tflops"] = flops / (ms * 1e-3) / 1e12
     del out
+    res["issue"] = issue_probe(torch, tq)
+    return res
+
+
+def issue_probe(torch, tq):
+    """What a SIMD issues with one wave (as the d = 128 quantize runs) and with
+    two: 48 independent float FMAs, 16 bf16 MFMAs, or both interleaved per
+    iteration, one workgroup per CU.  Rates come from events around the launch
+    (ns per instruction per SIMD); `ghz` is the waves' own clock reading
+    (shader counter over the 100 MHz real-time counter, median over waves),
+    and cycles = ns x ghz."""
+    grid, iters = 256, 4096
+    ev = _events(torch, 2)
+    res = {}
+    for wps in (1, 2):
+        out = torch.zeros(2 * grid * 4 * wps, dtype=torch.int32, device="cuda")
+        for mode, name, instrs in ((0, "valu48", 48), (1, "mfma16", 16), (2, "mfma16_valu48", 64)):
+            tq.probe_issue(mode, wps, 16, grid, out)   # load the kernel
+            torch.cuda.synchronize()
+            ev[0].record()
+            tq.probe_issue(mode, wps, iters, grid, out)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1])
+            d = out.view(-1, 2).cpu().numpy().astype(np.uint32).astype(np.float64)
+            ghz = float(np.median(d[:, 0] / (d[:, 1] * 10.0)))
+            ns = ms * 1e6 / (iters * instrs * wps)              # per instruction per SIMD
+            res[f"{name}_{wps}w"] = dict(ns_per_instr=round(ns, 3), ghz=round(ghz, 3),
+                                         cycles_per_instr=round(ns * ghz, 2))
+        del out
+    res["note"] = ("per SIMD: valu48 = 48 independent float FMAs, mfma16 = 16 bf16 16x16x32 MFMAs, "
+                   "mfma16_valu48 = both, one MFMA then three FMAs; 1w / 2w = waves per SIMD; event-timed")
     return res
 
 

@@ -271,9 +271,17 @@ int tq_dense_logits(const float *q, int64_t nq, const void *keys, int dtype, int
  * 2 in_bytes / 9, 1 KiB, 2 in_bytes / 9).  grid: workgroups of 256 threads.
  * tq_probe_mfma: `grid` workgroups of 4 waves, each running iters x 8 back-
  * to-back 16x16x32 MFMAs (bf16, or f16 when f16 != 0); out: grid x 256
- * floats.  Errors: TQ_EINVAL, TQ_EHIP. */
+ * floats.
+ * tq_probe_issue: `grid` workgroups of waves_per_simd (1 or 2) x 4 waves,
+ * each running iters iterations of 48 independent float32 FMAs (mode 0), 16
+ * back-to-back bf16 MFMAs (mode 1), or both interleaved as one MFMA and three
+ * FMAs (mode 2).  out (device): 2 uint32 per wave in launch order, the
+ * wave's shader-clock cycles over the loop and its ticks of the 100 MHz real
+ * time counter, so cycles / (ticks x 10 ns) is the clock it ran at; grid <=
+ * 4096.  Errors: TQ_EINVAL, TQ_EHIP. */
 int tq_probe_stream(int kind, const void *in, int64_t in_bytes, void *out, int64_t out_bytes, int grid, void *stream);
 int tq_probe_mfma(int f16, int64_t iters, int grid, float *out, void *stream);
+int tq_probe_issue(int mode, int waves_per_simd, int64_t iters, int grid, uint32_t *out, void *stream);
 
 /* Static text for a status code. */
 const char *tq_strerror(int status);

@@ -11,7 +11,8 @@ import ctypes
 import os
 
 __all__ = ["Codec", "MixedCodec", "lib", "library_path", "TQ_MSE", "TQ_PROD", "TQ_F32", "TQ_BF16", "TQ_F16",
-           "TQError", "EXPORTED_SYMBOLS", "row_bytes", "dense_logits", "probe_stream", "probe_mfma"]
+           "TQError", "EXPORTED_SYMBOLS", "row_bytes", "dense_logits", "probe_stream", "probe_mfma",
+           "probe_issue"]
 
 TQ_MSE, TQ_PROD = 0, 1
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
@@ -49,6 +50,7 @@ _SIGS = {
     "tq_dense_logits": (_INT, [_P, _I64, _P, _INT, _INT, _I64, _I64, _P, _P]),
     "tq_probe_stream": (_INT, [_INT, _P, _I64, _P, _I64, _INT, _P]),
     "tq_probe_mfma": (_INT, [_INT, _I64, _INT, _P, _P]),
+    "tq_probe_issue": (_INT, [_INT, _INT, _I64, _INT, _P, _P]),
     "tq_strerror": (ctypes.c_char_p, [_INT]),
     "tq_last_error": (ctypes.c_char_p, []),
     "tq_get_tables": (_INT, [_P, _INT, _P, _P, _P, _P]),
@@ -474,6 +476,12 @@ def probe_stream(kind: int, src, dst, grid: int, stream=None):
 def probe_mfma(f16: bool, iters: int, grid: int, out, stream=None):
     """Back-to-back MFMAs with no memory traffic (tq_probe_mfma)."""
     _check(lib().tq_probe_mfma(int(f16), iters, grid, _ptr(out), _stream(stream)), "tq_probe_mfma")
+
+
+def probe_issue(mode: int, waves_per_simd: int, iters: int, grid: int, out, stream=None):
+    """Instruction-issue loops, per-wave cycles and real time (tq_probe_issue);
+    out: int32 CUDA tensor of 2 * grid * 4 * waves_per_simd entries."""
+    _check(lib().tq_probe_issue(mode, waves_per_simd, iters, grid, _ptr(out), _stream(stream)), "tq_probe_issue")
 
 
 def host_tables(d: int, bits: int, variant: int, seed: int, group: int = 0):

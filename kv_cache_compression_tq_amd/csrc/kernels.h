@@ -60,6 +60,8 @@ hipError_t launch_dense_logits128(const float *q, int64_t nq, const void *keys, 
 int64_t probe_stream_tiles(int kind, int64_t in_bytes);
 int64_t probe_stream_out_bytes(int kind, int64_t tiles);
 hipError_t launch_probe_stream(int kind, const void *in, void *out, int64_t tiles, int grid, hipStream_t st);
+hipError_t launch_probe_issue(int mode, int waves_per_simd, int64_t iters, int grid, uint32_t *out,
+                              hipStream_t st);
 hipError_t launch_probe_mfma(int f16, int64_t iters, int grid, float *out, hipStream_t st);
 
 hipError_t launch_quant_generic(const DeviceTables &t, const void *x, int dtype, int64_t n_sets,

@@ -13,6 +13,11 @@
 //   instead of whole 1 KiB runs.
 // k_probe_mfma: back-to-back 16x16x32 bf16 (or f16) MFMAs on eight
 //   independent accumulators per wave, no memory traffic.
+// k_probe_issue: what one wave (or two waves sharing a SIMD) can issue: per
+//   iteration 48 independent float FMAs (mode 0), 16 bf16 MFMAs (mode 1), or
+//   both, one MFMA then three FMAs (mode 2).  Each wave records its shader
+//   clock cycles and its real time (100 MHz counter) over the loop, which give
+//   cycles per instruction and the clock the chip ran at.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -108,6 +113,50 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_mfma(int64_t iters, flo
   out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
 }
 
+template <int MODE>
+__global__ __launch_bounds__(512) void k_probe_issue(int64_t iters, uint32_t *__restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  u32x4 a = {(uint32_t)lane * 0x00010001u, 0x3c003c00u, 0x3c003c00u, (uint32_t)lane};
+  const u32x4 b = {0x3c003c00u, (uint32_t)lane, 0x3c003c00u, 0x3c003c00u};
+  asm volatile("" : "+a"(a));  // the A operand in an AGPR, as in the quantize kernel
+  f32x4 c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = f32x4{0, 0, 0, (float)i};
+  float f[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) f[i] = lane * 0.01f + i;
+  const float r0 = 0.999f + lane * 1e-6f, r1 = 0.001f - lane * 1e-7f;
+  const uint64_t t0 = __builtin_amdgcn_s_memtime(), q0 = __builtin_amdgcn_s_memrealtime();
+  for (int64_t it = 0; it < iters; ++it) {
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int v = 0; v < 48; ++v) f[v & 15] = fmaf(f[v & 15], r0, r1);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        c[j & 7] = mfma_bf16(a, b, c[j & 7]);
+        if constexpr (MODE == 2) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+          for (int v = 0; v < 3; ++v) f[(3 * j + v) & 15] = fmaf(f[(3 * j + v) & 15], r0, r1);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
+    }
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime(), q1 = __builtin_amdgcn_s_memrealtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += c[i][0] + c[i][1] + c[i][2] + c[i][3];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += f[i];
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (lane == 0) {
+    out[2 * wave] = (uint32_t)(t1 - t0);
+    out[2 * wave + 1] = (uint32_t)(q1 - q0) | (sum == 1.2345e-30f ? 1u : 0u);  // keeps the work alive
+  }
+}
+
 template <int R, int W>
 hipError_t run_stream(const void *in, void *out, int64_t tiles, int grid, hipStream_t st) {
   hipLaunchKernelGGL((k_probe_stream<R, W>), dim3(grid), dim3(kProbeThreads), 0, st, (const u32x4 *)in,
@@ -142,6 +191,18 @@ hipError_t launch_probe_stream(int kind, const void *in, void *out, int64_t tile
       return hipGetLastError();
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_probe_issue(int mode, int waves_per_simd, int64_t iters, int grid, uint32_t *out,
+                              hipStream_t st) {
+  const dim3 block((unsigned)(256 * waves_per_simd));
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(k_probe_issue<0>, dim3(grid), block, 0, st, iters, out); break;
+    case 1: hipLaunchKernelGGL(k_probe_issue<1>, dim3(grid), block, 0, st, iters, out); break;
+    case 2: hipLaunchKernelGGL(k_probe_issue<2>, dim3(grid), block, 0, st, iters, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_probe_mfma(int f16, int64_t iters, int grid, float *out, hipStream_t st) {

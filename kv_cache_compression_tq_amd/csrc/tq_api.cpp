@@ -893,6 +893,14 @@ int tq_probe_stream(int kind, const void *in, int64_t in_bytes, void *out, int64
   return e == hipSuccess ? TQ_OK : hip_fail(e, "probe launch");
 }
 
+int tq_probe_issue(int mode, int waves_per_simd, int64_t iters, int grid, uint32_t *out, void *stream) {
+  if (mode < 0 || mode > 2 || waves_per_simd < 1 || waves_per_simd > 2 || iters < 0 || grid < 1 ||
+      grid > 4096 || !out)
+    return fail(TQ_EINVAL, "bad probe arguments");
+  const hipError_t e = tq::launch_probe_issue(mode, waves_per_simd, iters, grid, out, (hipStream_t)stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "probe launch");
+}
+
 int tq_probe_mfma(int f16, int64_t iters, int grid, float *out, void *stream) {
   if (iters < 0 || grid < 1 || grid > (1 << 20) || !out) return fail(TQ_EINVAL, "bad probe arguments");
   const hipError_t e = tq::launch_probe_mfma(f16 != 0, iters, grid, out, (hipStream_t)stream);

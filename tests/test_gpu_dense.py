@@ -60,3 +60,30 @@ def test_stream_probes_write_the_xor_of_what_they_read():
         acc = np.bitwise_xor.reduce(a, axis=1)
         want = np.stack([acc + np.uint32(j) for j in range(w)], axis=1)
         assert np.array_equal(dst.cpu().numpy().view(np.uint32).reshape(tiles, w, 64, 4), want), kind
+
+
+def test_issue_probe_reports_cycles_and_clock_per_wave():
+    """Every wave of every mode writes its loop's shader cycles and real-time
+    ticks; more iterations take proportionally more cycles, and the clock they
+    imply lies within the chip's range."""
+    grid = 8
+    for wps in (1, 2):
+        for mode in (0, 1, 2):
+            res = []
+            for iters in (256, 1024):
+                out = torch.zeros(2 * grid * 4 * wps, dtype=torch.int32, device="cuda")
+                tq.probe_issue(mode, wps, iters, grid, out)
+                torch.cuda.synchronize()
+                d = out.view(-1, 2).cpu().numpy().astype(np.uint32).astype(np.float64)
+                assert np.all(d[:, 0] > 0) and np.all(d[:, 1] > 0), (mode, wps)
+                ghz = d[:, 0] / (d[:, 1] * 10.0)
+                assert np.all((ghz > 0.3) & (ghz < 4.0)), (mode, wps, ghz.min(), ghz.max())
+                res.append(np.median(d[:, 0]))
+            assert 2.5 < res[1] / res[0] < 5.5, (mode, wps, res)
+
+
+def test_issue_probe_rejects_bad_arguments():
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    for args in ((3, 1, 16, 1), (0, 0, 16, 1), (0, 3, 16, 1), (0, 1, -1, 1), (0, 1, 16, 0), (0, 1, 16, 5000)):
+        with pytest.raises(tq.TQError):
+            tq.probe_issue(*args, out)
