@@ -450,7 +450,8 @@ def ceilings_phase(torch, tq):
     kernels: streams over 1 GiB of input (each after a 1 GiB fill of another
     buffer, so no input is still held in the 256 MB Infinity Cache) at the
     read/write mixes of the hot-path kernels, and a matrix-core loop with no
-    memory traffic.  GB/s count bytes read plus bytes written."""
+    memory traffic.  GB/s count bytes read plus bytes written.  The 1:8 mix
+    (the d = 128 dequantize's) reads 128 MiB, cold, and writes 1 GiB."""
     grid = 2048                                   # 8 workgroups of 4 waves per CU
     n_in = 1 << 30
     src = torch.empty(n_in // 4, dtype=torch.int32, device="cuda").fill_(0x1234567)
@@ -459,10 +460,11 @@ def ceilings_phase(torch, tq):
     ev = _events(torch, 2)
     res = {}
     kinds = (("copy", 0, 1, 1), ("mix_4r1w", 1, 4, 1), ("mix_9r2w", 2, 9, 2), ("read_only", 3, 1, 0),
-             ("mix_9r2w_logits_rows", 4, 9, 2))
+             ("mix_9r2w_logits_rows", 4, 9, 2), ("mix_1r8w", 5, 1, 8))
     for name, kind, r, w in kinds:
         tile_in = r * 64 * 16
-        used = n_in // tile_in * tile_in
+        cap = n_in if w <= r else n_in * r // w      # the 1:8 mix reads 128 MiB and writes 1 GiB
+        used = cap // tile_in * tile_in
         moved = used + used // r * w
         times = []
         for rep in range(4):

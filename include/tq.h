@@ -266,9 +266,10 @@ int tq_dense_logits(const float *q, int64_t nq, const void *keys, int dtype, int
  * aligned): kind 0 copies (reads and writes the same bytes), 1 reads 4 bytes
  * per byte written (the d = 128 quantize's mix), 2 reads 9 per 2 written (the
  * decode logits' mix), 3 only reads, 4 is the mix of kind 2 with the logits
- * kernel's store pattern (4-byte stores into four rows).  Whole 16 KiB / 36 KiB
- * tiles only; out must hold what the kind writes (in_bytes, in_bytes / 4,
- * 2 in_bytes / 9, 1 KiB, 2 in_bytes / 9).  grid: workgroups of 256 threads.
+ * kernel's store pattern (4-byte stores into four rows), 5 writes 8 bytes per
+ * byte read (the d = 128 dequantize's mix).  Whole 16 KiB / 36 KiB tiles only;
+ * out must hold what the kind writes (in_bytes, in_bytes / 4, 2 in_bytes / 9,
+ * 1 KiB, 2 in_bytes / 9, 8 in_bytes).  grid: workgroups of 256 threads.
  * tq_probe_mfma: `grid` workgroups of 4 waves, each running iters x 8 back-
  * to-back 16x16x32 MFMAs (bf16, or f16 when f16 != 0); out: grid x 256
  * floats.

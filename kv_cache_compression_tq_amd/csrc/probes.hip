@@ -7,7 +7,8 @@
 //   words written are the XOR of the words read, so no load can be dropped.
 //   R:W = 1:1 is a copy, 4:1 the read/write mix of the d = 128 quantize (256 B
 //   read per 68 B written), 9:2 that of the decode logits (72 B per key read,
-//   16 B written), 1:0 a read-only stream.
+//   16 B written), 1:8 that of the d = 128 dequantize (68 B read per 512 B
+//   written), 1:0 a read-only stream.
 // k_probe_rows: the logits mix with the logits kernel's store pattern: per
 //   16-key tile, 4-byte stores into four output rows (16 keys x 4 bytes each),
 //   instead of whole 1 KiB runs.
@@ -167,14 +168,14 @@ hipError_t run_stream(const void *in, void *out, int64_t tiles, int grid, hipStr
 }  // namespace
 
 int64_t probe_stream_tiles(int kind, int64_t in_bytes) {
-  static const int reads[] = {1, 4, 9, 1, 9};
-  if (kind < 0 || kind > 4) return -1;
+  static const int reads[] = {1, 4, 9, 1, 9, 1};
+  if (kind < 0 || kind > 5) return -1;
   return in_bytes / (reads[kind] * 64 * 16);
 }
 
 int64_t probe_stream_out_bytes(int kind, int64_t tiles) {
-  static const int writes[] = {1, 1, 2, 0, 0};
-  if (kind < 0 || kind > 4) return -1;
+  static const int writes[] = {1, 1, 2, 0, 0, 8};
+  if (kind < 0 || kind > 5) return -1;
   if (kind == 4) return tiles * 128 * 4 * 4;  // 4 rows of 128 keys per tile
   return tiles * writes[kind] * 64 * 16;
 }
@@ -189,6 +190,7 @@ hipError_t launch_probe_stream(int kind, const void *in, void *out, int64_t tile
       hipLaunchKernelGGL(k_probe_rows, dim3(grid), dim3(kProbeThreads), 0, st, (const u32x4 *)in, (float *)out,
                          tiles, tiles * 128);
       return hipGetLastError();
+    case 5: return run_stream<1, 8>(in, out, tiles, grid, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -881,7 +881,7 @@ int tq_dense_logits(const float *q, int64_t nq, const void *keys, int dtype, int
 
 int tq_probe_stream(int kind, const void *in, int64_t in_bytes, void *out, int64_t out_bytes, int grid, void *stream) {
   const int64_t tiles = tq::probe_stream_tiles(kind, in_bytes);
-  if (tiles < 0) return fail(TQ_EINVAL, "kind must be in [0, 4]");
+  if (tiles < 0) return fail(TQ_EINVAL, "kind must be in [0, 5]");
   if (tiles == 0) return TQ_OK;
   if (!in || !aligned16(in) || !out || !aligned16(out)) return fail(TQ_EINVAL, "in/out NULL or not 16-byte aligned");
   if (out_bytes < tq::probe_stream_out_bytes(kind, tiles) || out_bytes < 1024)

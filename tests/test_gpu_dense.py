@@ -48,9 +48,9 @@ def test_dense_logits_decode_shape_sampled():
 
 
 def test_stream_probes_write_the_xor_of_what_they_read():
-    """Kinds 0-2 write, for every 64-unit tile, the XOR of the R words a lane
+    """Kinds 0-2 and 5 write, for every 64-unit tile, the XOR of the R words a lane
     read (plus the output word's index in its unit): checked on the host."""
-    for kind, (r, w) in ((0, (1, 1)), (1, (4, 1)), (2, (9, 2))):
+    for kind, (r, w) in ((0, (1, 1)), (1, (4, 1)), (2, (9, 2)), (5, (1, 8))):
         tiles = 7
         src = torch.randint(0, 2 ** 31 - 1, (tiles * r * 64 * 4,), dtype=torch.int32, device="cuda")
         dst = torch.zeros((tiles * w * 64 * 4,), dtype=torch.int32, device="cuda")
