@@ -768,9 +768,14 @@ def main():
             "vectors_per_s": 2 * ap["sets"] / (ap["append_ms"] * 1e-3),
         }
     if other is not None:
+        if ceil is not None:   # the d = 128 dequantize against the stream with its 1:8 read/write mix
+            for v in ("mse", "prod"):
+                k = f"kv_{v}_b4_dequantize_gbs"
+                if k in other:
+                    other[f"kv_{v}_b4_dequantize_frac_of_mix_ceiling"] = other[k] / ceil["mix_1r8w_gbs"]
         line["other_paths"] = other
     if ceil is not None:
-        line["ceilings"] = dict(ceil, note="in-tree probe kernels (probes.hip): 1 GiB streams, cold, GB/s on "
+        line["ceilings"] = dict(ceil, note="in-tree probe kernels (probes.hip): 1 GiB streams (the 1:8 mix: 128 MiB read), cold, GB/s on "
                                            "bytes read + written; MFMA loops with no memory traffic")
     if probes is not None:
         line["hbm_probes"] = probes
